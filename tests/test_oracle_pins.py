@@ -1,0 +1,439 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics
+(closed forms, brute force, invariants). CPU only.
+
+Each test is chosen so that a plausible slip in the oracle (a swapped nibble,
+a transposed matrix, a dropped term, a wrong sign, a wrong tie-break) fails.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f16bits(v):
+    return np.array(v, dtype=np.float16).view(np.uint16)
+
+
+def pack_codes(q):
+    """Test-side packing of integer codes [N, K] into the byte format:
+    byte j holds codes 2j (low nibble) and 2j+1 (high nibble)."""
+    q = np.asarray(q, dtype=np.uint8)
+    out = np.zeros((q.shape[0], q.shape[1] // 2), dtype=np.uint8)
+    for j in range(q.shape[1] // 2):
+        out[:, j] = q[:, 2 * j] | (q[:, 2 * j + 1] << 4)
+    return out
+
+
+def sb_array(s, b, N, G):
+    sb = np.zeros((N, G, 2), dtype=np.uint16)
+    sb[..., 0] = f16bits(s)
+    sb[..., 1] = f16bits(b)
+    return sb
+
+
+# ----------------------------------------------------------------------------
+# O1 dequant
+# ----------------------------------------------------------------------------
+def test_dequant_closed_form_group():
+    # codes 0..15 repeated, s = 1/8, b = -1  ->  W = q/8 - 1 exactly
+    q = np.tile(np.arange(16), 4)[None, :]
+    W = oracle.dequant_matrix(pack_codes(q), sb_array(0.125, -1.0, 1, 1))
+    expect = np.tile(np.arange(16), 4) / 8.0 - 1.0
+    assert np.array_equal(W[0], expect)
+
+
+@pytest.mark.parametrize("pos", [0, 1, 2, 31, 62, 63])
+def test_dequant_single_nibble_order(pos):
+    q = np.zeros((1, 64), dtype=np.uint8)
+    q[0, pos] = 9
+    W = oracle.dequant_matrix(pack_codes(q), sb_array(0.5, 0.25, 1, 1))
+    expect = np.full(64, 0.25)
+    expect[pos] = 0.25 + 4.5
+    assert np.array_equal(W[0], expect)
+
+
+def test_dequant_single_nibble_raw_byte():
+    # byte 3 = 0x70: code 7 at element 7 (high nibble), code 0 at element 6
+    packed = np.zeros((1, 32), dtype=np.uint8)
+    packed[0, 3] = 0x70
+    W = oracle.dequant_matrix(packed, sb_array(1.0, 0.0, 1, 1))
+    assert W[0, 7] == 7.0 and W[0, 6] == 0.0 and W[0].sum() == 7.0
+
+
+def test_dequant_groups_and_zero_scale():
+    N, K = 2, 192
+    q = np.full((N, K), 3)
+    sb = np.zeros((N, 3, 2), dtype=np.uint16)
+    for g, (s, b) in enumerate([(1.0, 0.0), (2.0, 10.0), (0.0, -7.5)]):
+        sb[:, g, 0] = f16bits(s)
+        sb[:, g, 1] = f16bits(b)
+    W = oracle.dequant_matrix(pack_codes(q), sb)
+    assert np.all(W[:, :64] == 3.0)
+    assert np.all(W[:, 64:128] == 16.0)
+    assert np.all(W[:, 128:] == -7.5)      # s = 0 gives the bias alone
+
+
+def test_quantiser_roundtrip_bound():
+    w = synth.gaussian((8, 256), 0.02, ("pin", "roundtrip"))
+    packed, sb = synth.quantize_g64(w)
+    W = oracle.dequant_matrix(packed.numpy(), sb.view(torch.int16).numpy().view(np.uint16))
+    s = oracle.f16_to_f64(sb[..., 0].view(torch.int16).numpy().view(np.uint16))
+    b = oracle.f16_to_f64(sb[..., 1].view(torch.int16).numpy().view(np.uint16))
+    wn = w.double().numpy().reshape(8, 4, 64)
+    err = np.abs(wn - W.reshape(8, 4, 64))
+    lo = b[..., None]
+    hi = b[..., None] + 15 * s[..., None]
+    inside = (wn >= lo) & (wn <= hi)
+    # codes within range: error at most half a step (plus fp32 division slack)
+    assert np.all(err[inside] <= (s[..., None] / 2 * (1 + 1e-3) + 1e-9).repeat(64, -1)[inside])
+    # clipped codes: error bounded by the fp16 rounding of the range ends
+    assert np.all(err <= s[..., None] * 0.5 + 2e-4)
+
+
+def test_blob_regions_and_orientation():
+    d, f = 128, 64
+    # gate codes 1, up codes 2, down codes 3 with s = 1, b = 0; plus one marker
+    gq = np.full((f, d), 1, dtype=np.uint8)
+    uq = np.full((f, d), 2, dtype=np.uint8)
+    dq = np.full((d, f), 3, dtype=np.uint8)
+    gq[5, 70] = 15   # gate row 5, column 70
+    dq[100, 9] = 14  # down row 100, column 9
+    parts = [pack_codes(gq), pack_codes(uq), pack_codes(dq),
+             sb_array(1.0, 0.0, f, d // 64), sb_array(1.0, 0.0, f, d // 64), sb_array(1.0, 0.0, d, f // 64)]
+    blob = np.concatenate([p.reshape(-1).view(np.uint8) for p in parts])
+    assert blob.size == oracle.blob_bytes(d, f) == 27 * d * f // 16
+    Wg, Wu, Wd = oracle.unpack_blob(blob, d, f)
+    assert Wg.shape == (f, d) and Wu.shape == (f, d) and Wd.shape == (d, f)
+    assert Wg[5, 70] == 15 and Wg.sum() == f * d + 14
+    assert np.all(Wu == 2)
+    assert Wd[100, 9] == 14 and Wd.sum() == 3 * d * f + 11
+
+
+def test_blob_size_matches_pages_checkpoint():
+    """4.5 bits per weight (int4 + fp16 scale + fp16 bias per 64) puts a 35B
+    model at 35e9*4.5/8 = 19.7 GB, the pages' 19.5 GB at 4-bit; an fp32-scale
+    format (5 bits, 21.9 GB) or a bias-free one (4.25 bits, 18.6 GB) would not."""
+    g = json.load(open(os.path.join(GOLDEN, "pages_figures.json")))
+    d, f = 2048, 512
+    bits = oracle.blob_bytes(d, f) * 8 / (3 * d * f)
+    assert bits == 4.5
+    gb = g["checkpoint_35b_gb"]["params"] * bits / 8 / 1e9
+    assert abs(gb - g["checkpoint_35b_gb"]["value"]) / g["checkpoint_35b_gb"]["value"] < 0.02
+    assert oracle.blob_bytes(d, f) == 1769472
+
+
+# ----------------------------------------------------------------------------
+# O2 RMSNorm and bf16 rounding
+# ----------------------------------------------------------------------------
+def test_rmsnorm_constant_row():
+    d, c, eps = 64, 0.7, 1e-6
+    gamma = np.linspace(0.5, 1.5, d)
+    u = oracle.rmsnorm(np.full(d, c), gamma, eps)
+    assert np.allclose(u, gamma * c / math.sqrt(c * c + eps), rtol=0, atol=1e-15)
+
+
+def test_rmsnorm_unit_rms_and_scale():
+    x = np.random.default_rng(1).standard_normal(256) * 3.0
+    u = oracle.rmsnorm(x, np.ones(256), 0.0)
+    assert abs(np.sqrt(np.mean(u * u)) - 1.0) < 1e-14
+    u2 = oracle.rmsnorm(5.0 * x, np.ones(256), 0.0)
+    assert np.allclose(u, u2, atol=1e-14)
+
+
+def test_round_bf16_ties_and_neighbours():
+    rng = np.random.default_rng(3)
+    # random positive/negative normal bf16 values
+    exps = rng.integers(-60, 60, 500)
+    mant = rng.integers(128, 256, 500)
+    sign = rng.choice([-1.0, 1.0], 500)
+    v = sign * np.ldexp(mant.astype(np.float64), exps - 8)   # exactly 8 significant bits
+    assert np.array_equal(oracle.round_bf16(v), v)
+    ulp = np.ldexp(1.0, exps - 8)
+    mid = v + sign * ulp / 2            # halfway to the next value away from zero
+    r = oracle.round_bf16(mid)
+    even_is_v = (mant % 2 == 0)
+    expect = np.where(even_is_v, v, v + sign * ulp)
+    assert np.array_equal(r, expect)
+    tiny = ulp * 2.0 ** -20
+    assert np.array_equal(oracle.round_bf16(mid - sign * tiny), v)
+    assert np.array_equal(oracle.round_bf16(mid + sign * tiny), v + sign * ulp)
+
+
+def test_bf16_decode_known_patterns():
+    assert oracle.bf16_to_f64(np.uint16(0x3F80)) == 1.0
+    assert oracle.bf16_to_f64(np.uint16(0xC000)) == -2.0
+    assert oracle.bf16_to_f64(np.uint16(0x4300)) == 128.0
+    assert oracle.bf16_to_f64(np.uint16(0x3E80)) == 0.25
+
+
+# ----------------------------------------------------------------------------
+# O3-O5 routing
+# ----------------------------------------------------------------------------
+def precedes(z, a, b):
+    return z[a] > z[b] or (z[a] == z[b] and a < b)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_topk_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(2, 9))
+    k = int(rng.integers(1, E + 1))
+    z = rng.integers(-3, 4, E).astype(np.float64)  # many exact ties
+    idx = list(oracle.topk(z, k))
+    # brute force: the unique k-subset whose members precede every non-member
+    ok = [S for S in itertools.combinations(range(E), k)
+          if all(precedes(z, a, b) for a in S for b in range(E) if b not in S)]
+    assert len(ok) == 1 and sorted(idx) == list(ok[0])
+    assert all(precedes(z, idx[i], idx[i + 1]) for i in range(k - 1))
+
+
+def test_topk_exact_ties_lowest_index():
+    z = np.array([1.0, 3.0, 3.0, 2.0, 3.0])
+    assert list(oracle.topk(z, 2)) == [1, 2]
+    assert list(oracle.topk(z, 3)) == [1, 2, 4]
+    assert list(oracle.topk(z, 5)) == [1, 2, 4, 3, 0]
+
+
+def test_route_weights_closed_form():
+    z = np.array([0.0, math.log(2.0), math.log(3.0), -5.0])
+    idx, w = oracle.route(z, 2)
+    assert list(idx) == [2, 1]
+    assert np.allclose(w, [3 / 5, 2 / 5], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_route_weights_invariants(seed):
+    rng = np.random.default_rng(100 + seed)
+    z = rng.standard_normal(256)
+    idx, w = oracle.route(z, 4)
+    assert abs(w.sum() - 1.0) < 1e-12 and np.all(w > 0)
+    assert np.all(np.diff(w) <= 0)   # descending logits give descending weights
+    idx2, w2 = oracle.route(z + 37.25, 4)
+    assert np.array_equal(idx, idx2) and np.allclose(w, w2, atol=1e-14)
+
+
+def test_head_logits_bias_and_history():
+    E, d = 6, 64
+    H = np.zeros((E, d), dtype=np.uint16)   # +0.0 everywhere
+    u = np.ones(d)
+    bias = np.arange(E, dtype=np.float64)
+    Mc = 10.0 * np.eye(E)
+    Mp = np.zeros((E, E)); Mp[2, 0] = 100.0   # prev contains 2 -> boosts expert 0
+    z = oracle.head_logits(H, u, bias, Mc, [1, 3], Mp, [2, -1])
+    assert np.array_equal(z, [100.0, 11.0, 2.0, 13.0, 4.0, 5.0])
+    # H contribution: single nonzero row entry, bf16 0x3F80 = 1.0 at (4, 7)
+    H2 = np.zeros((E, d), dtype=np.uint16); H2[4, 7] = 0x3F80
+    u2 = np.zeros(d); u2[7] = 2.5
+    assert np.array_equal(oracle.head_logits(H2, u2), [0, 0, 0, 0, 2.5, 0])
+
+
+# ----------------------------------------------------------------------------
+# O6 expert FFN with permutation structure (closed form)
+# ----------------------------------------------------------------------------
+def perm_expert(d, f, pg, pu, pd, sg, su, sd):
+    """Blob whose matrices are scaled permutation-selectors: Wg[n, pg[n]] = 15*sg, etc."""
+    gq = np.zeros((f, d), np.uint8); uq = np.zeros((f, d), np.uint8); dq = np.zeros((d, f), np.uint8)
+    gq[np.arange(f), pg] = 15
+    uq[np.arange(f), pu] = 15
+    dq[np.arange(d), pd] = 15
+    parts = [pack_codes(gq), pack_codes(uq), pack_codes(dq),
+             sb_array(sg, 0.0, f, d // 64), sb_array(su, 0.0, f, d // 64), sb_array(sd, 0.0, d, f // 64)]
+    return np.concatenate([p.reshape(-1).view(np.uint8) for p in parts])
+
+
+def silu_scalar(a):
+    return a / (1.0 + math.exp(-a))
+
+
+def test_expert_ffn_closed_form():
+    d, f = 128, 64
+    rng = np.random.default_rng(7)
+    pg = rng.permutation(d)[:f]
+    pu = rng.permutation(d)[:f]
+    pd = rng.integers(0, f, d)
+    blob = perm_expert(d, f, pg, pu, pd, 0.0625, 0.125, 0.25)
+    u = rng.standard_normal(d)
+    o = oracle.expert_ffn(oracle.unpack_blob(blob, d, f), u)
+    a = [15 * 0.0625 * u[pg[n]] for n in range(f)]
+    c = [15 * 0.125 * u[pu[n]] for n in range(f)]
+    h = [silu_scalar(a[n]) * c[n] for n in range(f)]
+    expect = np.array([15 * 0.25 * h[pd[i]] for i in range(d)])
+    assert np.allclose(o, expect, rtol=1e-14, atol=1e-15)
+
+
+def test_silu_values():
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-12
+    assert abs(oracle.silu(-40.0)) < 1e-15
+    assert abs(oracle.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+
+
+# ----------------------------------------------------------------------------
+# O7-O9 block
+# ----------------------------------------------------------------------------
+def tiny_layer(E=8, k=2, d=128, f=64, fs=64, r=4, seed=0, identical=False, shared_gate=True):
+    sh = synth.Shape("pin_tiny", d=d, E=E, k=k, f=f, fs=fs, r=r, alpha=8.0, act="f32")
+    w = synth.layer_weights(sh, seed, tag="pin")
+    store = synth.to_numpy_bytes(w["store"])
+    if identical:
+        store = np.repeat(store[:1], E, axis=0)
+    lw = oracle.LayerWeights(
+        d=d, E=E, k=k, f=f, fs=fs, r=r, alpha=8.0, eps=1e-6, act="f32", store=store,
+        shared=synth.to_numpy_bytes(w["shared"]) if fs else None,
+        shared_gate=synth.bf16_bits(w["shared_gate"]) if (fs and shared_gate) else None,
+        lora_a=synth.bf16_bits(w["lora_a"]) if r else None, lora_b=synth.bf16_bits(w["lora_b"]) if r else None,
+        gamma=w["gamma"].double().numpy(), head=synth.bf16_bits(w["head"]), router=synth.bf16_bits(w["router"]))
+    return lw
+
+
+def test_block_identical_experts_combine():
+    lw = tiny_layer(identical=True, fs=0, r=0)
+    u = np.random.default_rng(0).standard_normal(lw.d)
+    single = oracle.expert_ffn(lw.expert(0), u)
+    y = oracle.moe_block(lw, u, [3, 5], [0.3, 0.7])
+    assert np.allclose(y, single, rtol=1e-13, atol=1e-15)
+
+
+def test_block_k1_and_linearity_in_weights():
+    lw = tiny_layer(fs=0, r=0)
+    u = np.random.default_rng(1).standard_normal(lw.d)
+    o2 = oracle.expert_ffn(lw.expert(2), u)
+    o6 = oracle.expert_ffn(lw.expert(6), u)
+    assert np.array_equal(oracle.moe_block(lw, u, [2], [1.0]), o2)
+    y = oracle.moe_block(lw, u, [6, 2], [0.25, 0.75])
+    assert np.allclose(y, 0.25 * o6 + 0.75 * o2, rtol=1e-14, atol=1e-15)
+
+
+def test_shared_gate_half_at_zero():
+    lw = tiny_layer(r=0)
+    lw.shared_gate = np.zeros(lw.d, dtype=np.uint16)
+    u = np.random.default_rng(2).standard_normal(lw.d)
+    y = oracle.moe_block(lw, u, [1], [1.0])
+    expect = oracle.expert_ffn(lw.expert(1), u) + 0.5 * oracle.expert_ffn(lw.shared_expert(), u)
+    assert np.allclose(y, expect, rtol=1e-14, atol=1e-15)
+
+
+def test_lora_rank1_closed_form_and_noop():
+    lw = tiny_layer(fs=0, r=1)
+    d = lw.d
+    a = np.zeros(d); a[3] = 2.0; a[10] = -0.5
+    bvec = np.zeros(d); bvec[7] = 0.25
+    lw.lora_a = oracle.bf16_bits_of(a)[None, :]
+    lw.lora_b = oracle.bf16_bits_of(bvec)[:, None]
+    u = np.random.default_rng(3).standard_normal(d)
+    base = oracle.expert_ffn(lw.expert(0), u)
+    y = oracle.moe_block(lw, u, [0], [1.0])
+    delta = np.zeros(d); delta[7] = lw.alpha * 0.25 * (2.0 * u[3] - 0.5 * u[10])
+    assert np.allclose(y - base, delta, rtol=1e-13, atol=1e-14)
+    lw.lora_b = np.zeros((d, 1), dtype=np.uint16)
+    assert np.array_equal(oracle.moe_block(lw, u, [0], [1.0]), base)
+
+
+def test_relabel_experts_invariance():
+    lw = tiny_layer()
+    u = np.random.default_rng(4).standard_normal(lw.d)
+    y = oracle.moe_block(lw, u, [1, 4], [0.6, 0.4])
+    perm = np.random.default_rng(5).permutation(lw.E)     # new slot of old expert e = perm[e]
+    store2 = np.empty_like(lw.store)
+    store2[perm] = lw.store
+    lw2 = tiny_layer()
+    lw2.store = store2
+    y2 = oracle.moe_block(lw2, u, [perm[1], perm[4]], [0.6, 0.4])
+    assert np.array_equal(y, y2)
+
+
+# ----------------------------------------------------------------------------
+# O11 dataflow
+# ----------------------------------------------------------------------------
+def small_stack(L=4, seed=0, act="bf16"):
+    layers = []
+    for l in range(L):
+        lw = tiny_layer(seed=100 * seed + l)
+        lw.act = act
+        layers.append(lw)
+    return layers
+
+
+def test_prefill_equals_sequential_decode():
+    """Head l on token i routes layer l+1 on token i+1 in prefill, exactly as
+    head l at step t routes layer l+1 at step t+1 in decode: prefill rows must
+    equal a B=1 decode run whose step inputs are the prefill tokens."""
+    layers = small_stack()
+    T = 6
+    xs = np.random.default_rng(9).standard_normal((T, 1, layers[0].d))
+    xp, recs = oracle.stack_prefill(layers, xs[:, 0, :])
+    steps = oracle.stack_decode(layers, xs, T)
+    for t in range(T):
+        assert np.array_equal(steps[t].x_out[0], xp[t])
+        for l in range(len(layers)):
+            assert np.array_equal(steps[t].routes[l][0][0], recs[l]["route"][0][t])
+    # the routing really is the shifted prediction (layer >= 1, token >= 1)
+    for l in range(1, len(layers)):
+        assert np.array_equal(recs[l]["route"][0][1:], recs[l - 1]["pred"][0][:-1])
+
+
+def test_batch_rows_equal_single_rows():
+    layers = small_stack(L=2)
+    lw = layers[0]
+    x = np.random.default_rng(11).standard_normal((3, lw.d))
+    xo, y, u, used, pred, z = oracle.decode_layer(lw, x, None, lw.k)
+    for b in range(3):
+        xo1, y1, *_ = oracle.decode_layer(lw, x[b:b + 1], None, lw.k)
+        assert np.array_equal(y[b], y1[0]) and np.array_equal(xo[b], xo1[0])
+
+
+def test_decode_step0_self_routes_then_predicted():
+    layers = small_stack(L=3)
+    xs = np.random.default_rng(12).standard_normal((3, 2, layers[0].d))
+    recs = oracle.stack_decode(layers, xs, 3)
+    assert all(recs[0].self_routed)
+    assert recs[1].self_routed == [True, False, False]
+    for l in (1, 2):
+        assert np.array_equal(recs[2].routes[l][0], recs[1].preds[l - 1][0])
+
+
+# ----------------------------------------------------------------------------
+# O12 staging plan
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(30))
+def test_plan_slots_properties(seed):
+    rng = np.random.default_rng(seed)
+    C = int(rng.integers(1, 7))
+    E = 12
+    resident = [int(e) for e in rng.permutation(E)[:C]]
+    for s in range(C):
+        if rng.random() < 0.3:
+            resident[s] = -1
+    n = int(rng.integers(0, C + 1))
+    wanted = list(rng.choice(E, n, replace=True))
+    new, copies = oracle.plan_slots(resident, wanted)
+    want = set(int(e) for e in wanted)
+    assert want <= set(new)                                     # staged set covers routed set
+    assert len(copies) == len(want - set(resident))             # minimal copies
+    for s in range(C):                                          # sticky
+        if resident[s] in want:
+            assert new[s] == resident[s]
+    for s, e in copies:
+        assert resident[s] not in want and new[s] == e
+    # deterministic order: missing ids ascending fill free slots ascending
+    assert [e for _, e in copies] == sorted(e for _, e in copies)
+    assert [s for s, _ in copies] == sorted(s for s, _ in copies)
+
+
+def test_plan_slots_capacity():
+    with pytest.raises(ValueError):
+        oracle.plan_slots([-1, -1], [1, 2, 3])
+
+
+def test_head_input_width_from_pages():
+    g = json.load(open(os.path.join(GOLDEN, "pages_figures.json")))["head_input_width_35b"]
+    assert g["d_model"] + 2 * g["experts"] == g["value"]
