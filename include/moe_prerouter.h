@@ -1,0 +1,222 @@
+/*
+ * moe_prerouter.h -- C ABI of the MI355X (gfx950) per-layer MoE block library.
+ *
+ * The block (per layer, per token):
+ *   u      = RMSNorm(x) rounded to the activation dtype     (when the norm is fused)
+ *   routing: the top-k experts predicted for this layer one token earlier by
+ *            the previous layer's prerouter head, used as the routing itself
+ *            ("prediction-as-routing": xyznot.com reading guide of "The Other
+ *            Half of the Memory Wall", Key ideas and Key terms); rows with no
+ *            prediction self-route with this layer's own router (the reactive
+ *            on-demand mode of the guide's Results section)
+ *   y      = sum_j w_j FFN_{e_j}(u) + sigmoid(g_s . u) FFN_shared(u)
+ *            + (alpha/r) B A u                     (guide, Method: unmerged adapter execution)
+ *   FFN(u) = Wd (silu(Wg u) * (Wu u)), W = s*q + b, int4 affine groups of 64
+ *            (ai.info news article on Edge0, section on the 35B version)
+ *   pred   = top-k of this layer's head on u: the routing of the next layer
+ *            at the next token (guide, Method: prerouter head architecture;
+ *            Q&A: why one token ahead)
+ *   x_out  = x + y                                    (when the residual is fused)
+ *
+ * Conventions
+ *   - Every function returns MOE_OK (0) or a negative MOE_E_* code; no C++
+ *     exception crosses the ABI. MOE_E_HIP keeps the failing hipError_t,
+ *     readable with moe_last_hip_error().
+ *   - "device" pointers are HIP device memory of the current device; "host
+ *     pinned" pointers come from hipHostMalloc (or torch pin_memory). Streams
+ *     are hipStream_t passed as void* (NULL = the default stream).
+ *   - The caller owns every buffer it passes and keeps it alive until
+ *     moe_layer_destroy. The library keeps pointers and copies no weight; it
+ *     allocates only its host handle, HIP events and a small pinned host
+ *     buffer for read-backs.
+ *   - A layer handle is not thread-safe. Calls on one handle must not overlap
+ *     on different streams; separate handles are independent.
+ *   - Routing indices are int32, routing weights fp32, logits fp64 inside.
+ *     Top-k order is (logit descending, expert index ascending); weights are
+ *     the softmax over the selected logits (equal to the full softmax
+ *     renormalised over the top-k).
+ *
+ * Byte formats
+ *   expert blob (d = model dim, f = expert intermediate, 64-groups along K):
+ *     gate q [f][d/2] | up q [f][d/2] | down q [d][f/2] (uint8, element k of a
+ *     row in byte k/2, low nibble for even k) | gate (s,b) fp16 [f][d/64][2] |
+ *     up (s,b) fp16 [f][d/64][2] | down (s,b) fp16 [d][f/64][2];
+ *     27*d*f/16 bytes; weight = s*q + b.
+ *   bf16 matrices are row-major [rows][d].
+ */
+#ifndef MOE_PREROUTER_H
+#define MOE_PREROUTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define MOE_OK               0
+#define MOE_E_INVALID       -1  /* bad argument: null pointer, size, index   */
+#define MOE_E_UNSUPPORTED   -2  /* shape or option this build does not serve */
+#define MOE_E_CAPACITY      -3  /* workspace or slab too small               */
+#define MOE_E_HIP           -4  /* a HIP runtime call failed                 */
+#define MOE_E_NOT_STAGED    -5  /* device flag: a routed expert was not in the slab */
+#define MOE_E_BAD_INDEX     -6  /* device flag: routing index outside [0, E)  */
+#define MOE_E_TIMEOUT       -7  /* device flag: a bounded device-side wait expired */
+
+/* ---- activation dtype of the block input -------------------------------- */
+#define MOE_ACT_F32   0
+#define MOE_ACT_BF16  1
+
+/* ---- layer flags -------------------------------------------------------- */
+/* x_in is the fp32 residual stream: the call applies RMSNorm (gamma, eps),
+ * rounds u to the activation dtype and writes x_in + y to y_out.           */
+#define MOE_FUSE_NORM_RESIDUAL  0x1u
+/* expert_store / shared_blob are device memory holding every expert: no
+ * slab, no copies; moe_stage_experts only validates ids.                   */
+#define MOE_RESIDENT_STORE      0x2u
+
+typedef struct moe_layer_desc {
+    int   d_model;        /* d: multiple of 256, <= 8192                          */
+    int   n_experts;      /* E: routed experts, 1..1024                           */
+    int   top_k;          /* k: 1..8, <= E                                        */
+    int   d_ff;           /* f: routed expert intermediate, multiple of 64        */
+    int   d_ff_shared;    /* f_s: shared expert intermediate (0 = none; else == f) */
+    int   group_size;     /* must be 64                                           */
+    int   lora_rank;      /* r: 0..64 (0 = no LoRA branch)                        */
+    float lora_alpha;     /* alpha; the branch is scaled by alpha / r             */
+    float rms_eps;        /* epsilon of RMSNorm (fused norm only)                 */
+    int   act_dtype;      /* MOE_ACT_F32 or MOE_ACT_BF16                          */
+    int   max_tokens;     /* largest n_tok of any decode/prefill call             */
+    int   slab_slots;     /* streamed mode: routed-expert slots (>= distinct experts per call) */
+    int   next_n_experts; /* experts of the layer the head predicts (0 = no head) */
+    int   next_top_k;     /* k of the layer the head predicts                     */
+    unsigned flags;       /* MOE_FUSE_NORM_RESIDUAL | MOE_RESIDENT_STORE          */
+} moe_layer_desc;
+
+typedef struct moe_layer_weights {
+    /* E blobs back to back (E * blob bytes). Pinned host memory in streamed
+     * mode (it stands in for the SSD tier), device memory with RESIDENT.   */
+    const void*     expert_store;
+    /* one blob of the shared expert (f = d_ff_shared); same memory kind as
+     * expert_store; NULL iff d_ff_shared == 0.                             */
+    const void*     shared_blob;
+    const uint16_t* shared_gate;  /* device bf16 [d]; NULL: gate fixed at 1  */
+    const uint16_t* router;       /* device bf16 [E][d]: self-routing; may be NULL if never used */
+    const float*    router_bias;  /* device fp32 [E] or NULL                 */
+    const uint16_t* head;         /* device bf16 [E_next][d] or NULL (no prediction) */
+    const float*    head_bias;    /* device fp32 [E_next] or NULL            */
+    /* history one-hot terms of the head input (guide, Method: the head reads
+     * top-k one-hots of the predicted layer's routing at the current and the
+     * previous token): row j is added to the logits when expert j is in that
+     * one-hot set. device fp32 [E_next][E_next] or NULL.                   */
+    const float*    hist_cur;
+    const float*    hist_prev;
+    const uint16_t* lora_a;       /* device bf16 [r][d]                      */
+    const uint16_t* lora_b;       /* device bf16 [d][r]                      */
+    const float*    norm_gamma;   /* device fp32 [d]; needed with FUSE_NORM_RESIDUAL */
+} moe_layer_weights;
+
+/* Per-call inputs and outputs (all device memory). */
+typedef struct moe_io {
+    /* [n_tok][d]: fp32 residual stream with FUSE_NORM_RESIDUAL, else the
+     * block input u in the activation dtype.                               */
+    const void*    x_in;
+    /* fp32 [n_tok][d]: x_in + y (fused) or y; may alias x_in when fused.   */
+    float*         y_out;
+    /* int32 / fp32 [n_tok][k]: routing of this layer for each row, or NULL
+     * (every row self-routes). A row whose first index is negative
+     * self-routes with the layer's router.                                 */
+    const int32_t* route_idx;
+    const float*   route_w;
+    /* optional outputs [n_tok][k]: the routing this call used.              */
+    int32_t*       used_idx;
+    float*         used_w;
+    /* optional outputs [n_tok][k_next]: the head's prediction for the next
+     * layer (at the next token). NULL skips the head.                       */
+    int32_t*       pred_idx;
+    float*         pred_w;
+    /* optional inputs [n_tok][k_next] for the history terms (negative
+     * entries are absent): routing of the predicted layer at this token and
+     * at the previous token.                                               */
+    const int32_t* hist_cur;
+    const int32_t* hist_prev;
+    /* streamed mode only: nonzero forces the reactive path (route on the
+     * device, read the routing back, stage the missing experts, continue);
+     * implied when route_idx is NULL. Blocks the host until the read-back.  */
+    int            reactive;
+} moe_io;
+
+typedef struct moe_layer moe_layer;
+
+/* Bytes of one expert blob: 27*d*f/16 for group 64; 0 if unsupported. */
+size_t moe_expert_blob_bytes(int d_model, int d_ff, int group_size);
+
+/* Device workspace bytes a layer needs (slab in streamed mode, slot table,
+ * activations, routing and sort scratch for max_tokens); 0 on invalid desc. */
+size_t moe_layer_workspace_bytes(const moe_layer_desc* desc);
+
+/* Create a layer on the current device. d_workspace: device memory of at
+ * least moe_layer_workspace_bytes(desc), 256-byte aligned, owned by the
+ * caller. The struct contents are copied; the pointers inside are kept.
+ * Errors: MOE_E_INVALID (null/size), MOE_E_UNSUPPORTED (shape),
+ * MOE_E_CAPACITY (workspace too small), MOE_E_HIP.                         */
+int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w,
+                     void* d_workspace, size_t ws_bytes, moe_layer** out);
+
+/* Stage the experts the next call on this layer will use ("staged decode":
+ * fixed slots mapped by a device slot table; "incr_stack": only changed
+ * slots are rewritten -- guide, Key terms). h_expert_ids: host int32 ids
+ * (duplicates allowed), read before return. Experts already resident keep
+ * their slot; missing ones (ascending id) take the slots not holding a
+ * wanted expert (ascending slot). The copies (pinned host -> HBM slab) and
+ * the slot-table update are queued on copy_stream after the layer's last
+ * call finished (event); the next call on the layer waits for them. The
+ * shared expert is staged once, on the first call, into its own slot.
+ * Resident mode: ids are validated and nothing is copied.
+ * Errors: MOE_E_INVALID (id outside [0, E)), MOE_E_CAPACITY (more distinct
+ * ids than slab_slots), MOE_E_HIP.                                          */
+int moe_stage_experts(moe_layer* layer, const int32_t* h_expert_ids, int n_ids,
+                      void* copy_stream);
+
+/* Host copy of the current slot table (expert id per routed slot, -1 empty;
+ * n_slots entries) and the number of bytes copied by staging so far.        */
+int moe_layer_slots(const moe_layer* layer, int32_t* h_slot_expert, int n_slots,
+                    uint64_t* staged_bytes);
+
+/* Decode call for n_tok (1..max_tokens) independent tokens: grouped GEMV
+ * path. Asynchronous on `stream` except the reactive read-back.
+ * Errors (returned): MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_HIP. Device
+ * errors (NOT_STAGED, BAD_INDEX) set a sticky flag read by
+ * moe_layer_sync_status; the affected expert's contribution is dropped.    */
+int moe_decode_step(moe_layer* layer, const moe_io* io, int n_tok, void* stream);
+
+/* Prefill call for n_tok tokens of one sequence (or any rows): token-to-
+ * expert sort/permute and int4->bf16 MFMA grouped GEMM. Same io contract;
+ * pred row i is the head on token i, i.e. the routing of the next layer for
+ * token i+1 (the caller shifts it down by one row).                         */
+int moe_prefill(moe_layer* layer, const moe_io* io, int n_tok, void* stream);
+
+/* Wait for the device, return and clear the sticky device error flag
+ * (MOE_OK, MOE_E_NOT_STAGED, MOE_E_BAD_INDEX or MOE_E_TIMEOUT).             */
+int moe_layer_sync_status(moe_layer* layer);
+
+/* Release the handle, its events and its pinned read-back buffer (not the
+ * caller's memory). Safe on NULL.                                           */
+void moe_layer_destroy(moe_layer* layer);
+
+const char* moe_status_str(int status);
+int moe_last_hip_error(void);
+
+/* ---- pure host helper (no device use) ------------------------------------
+ * The sticky-slot plan moe_stage_experts applies. resident[n_slots]: expert
+ * per slot (-1 empty), updated in place. wanted[n_wanted] (duplicates ok).
+ * copies_slot/copies_expert receive up to n_slots entries; *n_copies is set.
+ * Returns MOE_OK, MOE_E_INVALID or MOE_E_CAPACITY (resident unchanged).     */
+int moe_plan_slots(int32_t* resident, int n_slots, const int32_t* wanted, int n_wanted,
+                   int n_experts, int32_t* copies_slot, int32_t* copies_expert, int* n_copies);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_PREROUTER_H */

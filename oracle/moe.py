@@ -276,10 +276,12 @@ def moe_block(lw: LayerWeights, u: np.ndarray, idx: Sequence[int], w: Sequence[f
 
 def block_input(lw: LayerWeights, x: np.ndarray, fused_norm: bool) -> np.ndarray:
     """u as the block sees it: RMSNorm(x) when the norm is fused, else x; then
-    rounded to bf16 when the block's activations are bf16."""
+    rounded (to nearest even) to the block's activation dtype, bf16 or fp32."""
     u = rmsnorm(x, lw.gamma, lw.eps) if fused_norm else np.asarray(x, dtype=np.float64)
     if lw.act == "bf16":
         u = round_bf16(u)
+    else:
+        u = u.astype(np.float32).astype(np.float64)   # fp32 activations
     return u
 
 

@@ -1,0 +1,268 @@
+"""Python binding of the MI355X MoE block library (libmoe_prerouter.so).
+
+Argument marshalling only: every step of the block runs in the library's HIP
+kernels. PyTorch provides device memory, pinned host memory and streams.
+The binding has the C ABI's names (moe_layer_create, moe_stage_experts,
+moe_decode_step, moe_prefill, ...) plus a small `MoeLayer` convenience class.
+Importing raises if the compiled library is absent: there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_prerouter.so")
+
+MOE_OK = 0
+MOE_E_INVALID = -1
+MOE_E_UNSUPPORTED = -2
+MOE_E_CAPACITY = -3
+MOE_E_HIP = -4
+MOE_E_NOT_STAGED = -5
+MOE_E_BAD_INDEX = -6
+MOE_E_TIMEOUT = -7
+
+MOE_ACT_F32 = 0
+MOE_ACT_BF16 = 1
+MOE_FUSE_NORM_RESIDUAL = 0x1
+MOE_RESIDENT_STORE = 0x2
+
+
+class moe_layer_desc(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int), ("n_experts", ctypes.c_int), ("top_k", ctypes.c_int),
+        ("d_ff", ctypes.c_int), ("d_ff_shared", ctypes.c_int), ("group_size", ctypes.c_int),
+        ("lora_rank", ctypes.c_int), ("lora_alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
+        ("act_dtype", ctypes.c_int), ("max_tokens", ctypes.c_int), ("slab_slots", ctypes.c_int),
+        ("next_n_experts", ctypes.c_int), ("next_top_k", ctypes.c_int), ("flags", ctypes.c_uint),
+    ]
+
+
+class moe_layer_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "expert_store", "shared_blob", "shared_gate", "router", "router_bias", "head", "head_bias",
+        "hist_cur", "hist_prev", "lora_a", "lora_b", "norm_gamma")]
+
+
+class moe_io(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x_in", "y_out", "route_idx", "route_w", "used_idx", "used_w", "pred_idx", "pred_w",
+        "hist_cur", "hist_prev")] + [("reactive", ctypes.c_int)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {moe_status_str(code)} ({code})"
+                         + (f", hip error {moe_last_hip_error()}" if code == MOE_E_HIP else ""))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m sparse_moe_decode_prerouter_amd.build` "
+            "(or __graft_entry__.build()) first. There is no non-HIP path.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "moe_expert_blob_bytes": (Z, [I, I, I]),
+        "moe_layer_workspace_bytes": (Z, [P]),
+        "moe_layer_create": (I, [P, P, P, Z, ctypes.POINTER(P)]),
+        "moe_stage_experts": (I, [P, P, I, P]),
+        "moe_layer_slots": (I, [P, P, I, P]),
+        "moe_decode_step": (I, [P, P, I, P]),
+        "moe_prefill": (I, [P, P, I, P]),
+        "moe_layer_sync_status": (I, [P]),
+        "moe_layer_destroy": (None, [P]),
+        "moe_status_str": (ctypes.c_char_p, [I]),
+        "moe_last_hip_error": (I, []),
+        "moe_plan_slots": (I, [P, I, P, I, I, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("moe_expert_blob_bytes", "moe_layer_workspace_bytes", "moe_layer_create", "moe_stage_experts",
+            "moe_layer_slots", "moe_decode_step", "moe_prefill", "moe_layer_sync_status", "moe_layer_destroy",
+            "moe_status_str", "moe_last_hip_error", "moe_plan_slots")
+
+
+# ---------------------------------------------------------------------------
+# C-ABI functions under their own names
+# ---------------------------------------------------------------------------
+def moe_expert_blob_bytes(d_model: int, d_ff: int, group_size: int = 64) -> int:
+    return _lib.moe_expert_blob_bytes(d_model, d_ff, group_size)
+
+
+def moe_layer_workspace_bytes(desc: moe_layer_desc) -> int:
+    return _lib.moe_layer_workspace_bytes(ctypes.byref(desc))
+
+
+def moe_layer_create(desc: moe_layer_desc, w: moe_layer_weights, ws_ptr: int, ws_bytes: int) -> int:
+    h = ctypes.c_void_p()
+    rc = _lib.moe_layer_create(ctypes.byref(desc), ctypes.byref(w), ctypes.c_void_p(ws_ptr), ws_bytes,
+                               ctypes.byref(h))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layer_create")
+    return h.value
+
+
+def moe_stage_experts(handle: int, ids: Sequence[int], copy_stream: int = 0) -> None:
+    arr = (ctypes.c_int32 * max(1, len(ids)))(*[int(i) for i in ids])
+    rc = _lib.moe_stage_experts(handle, arr, len(ids), ctypes.c_void_p(copy_stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stage_experts")
+
+
+def moe_layer_slots(handle: int, n_slots: int):
+    arr = (ctypes.c_int32 * max(1, n_slots))()
+    nb = ctypes.c_uint64()
+    rc = _lib.moe_layer_slots(handle, arr, n_slots, ctypes.byref(nb))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layer_slots")
+    return list(arr)[:n_slots], nb.value
+
+
+def moe_decode_step(handle: int, io: moe_io, n_tok: int, stream: int = 0) -> None:
+    rc = _lib.moe_decode_step(handle, ctypes.byref(io), n_tok, ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_decode_step")
+
+
+def moe_prefill(handle: int, io: moe_io, n_tok: int, stream: int = 0) -> None:
+    rc = _lib.moe_prefill(handle, ctypes.byref(io), n_tok, ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_prefill")
+
+
+def moe_layer_sync_status(handle: int) -> int:
+    return _lib.moe_layer_sync_status(handle)
+
+
+def moe_layer_destroy(handle: int) -> None:
+    _lib.moe_layer_destroy(handle)
+
+
+def moe_status_str(code: int) -> str:
+    return _lib.moe_status_str(code).decode()
+
+
+def moe_last_hip_error() -> int:
+    return _lib.moe_last_hip_error()
+
+
+def moe_plan_slots(resident: Sequence[int], wanted: Sequence[int], n_experts: int):
+    """Pure host: returns (new_resident, copies [(slot, expert)]) or raises MoeError."""
+    n = len(resident)
+    res = (ctypes.c_int32 * max(1, n))(*resident)
+    wa = (ctypes.c_int32 * max(1, len(wanted)))(*[int(x) for x in wanted])
+    cs = (ctypes.c_int32 * max(1, n))()
+    ce = (ctypes.c_int32 * max(1, n))()
+    nc = ctypes.c_int()
+    rc = _lib.moe_plan_slots(res, n, wa, len(wanted), n_experts, cs, ce, ctypes.byref(nc))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_plan_slots")
+    return list(res)[:n], [(cs[i], ce[i]) for i in range(nc.value)]
+
+
+# ---------------------------------------------------------------------------
+# convenience wrapper over torch tensors
+# ---------------------------------------------------------------------------
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class MoeLayer:
+    """One MoE layer bound to tensors the caller keeps alive (kept here too)."""
+
+    def __init__(self, *, d_model, n_experts, top_k, d_ff, d_ff_shared, lora_rank, lora_alpha, act_dtype,
+                 max_tokens, expert_store, shared_blob=None, shared_gate=None, router=None, router_bias=None,
+                 head=None, head_bias=None, next_n_experts=0, next_top_k=0, hist_cur=None, hist_prev=None,
+                 lora_a=None, lora_b=None, norm_gamma=None, rms_eps=1e-6, fuse_norm_residual=False,
+                 resident=True, slab_slots=0, device="cuda"):
+        import torch
+        self._keep = [expert_store, shared_blob, shared_gate, router, router_bias, head, head_bias, hist_cur,
+                      hist_prev, lora_a, lora_b, norm_gamma]
+        flags = (MOE_FUSE_NORM_RESIDUAL if fuse_norm_residual else 0) | (MOE_RESIDENT_STORE if resident else 0)
+        self.desc = moe_layer_desc(d_model, n_experts, top_k, d_ff, d_ff_shared, 64, lora_rank, float(lora_alpha),
+                                   float(rms_eps), act_dtype, max_tokens, slab_slots, next_n_experts, next_top_k,
+                                   flags)
+        self.weights = moe_layer_weights(*[_ptr(t) for t in self._keep])
+        nbytes = moe_layer_workspace_bytes(self.desc)
+        if nbytes == 0:
+            raise MoeError(MOE_E_UNSUPPORTED, "moe_layer_workspace_bytes")
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        base = self.workspace.data_ptr()
+        self._ws_ptr = (base + 255) // 256 * 256
+        self.handle = moe_layer_create(self.desc, self.weights, self._ws_ptr, nbytes)
+        self.top_k = top_k
+        self.next_top_k = next_top_k
+        self.d_model = d_model
+        self.slab_slots = slab_slots
+
+    def stage(self, ids, stream=None):
+        moe_stage_experts(self.handle, list(ids), _stream_ptr(stream))
+
+    def slots(self):
+        return moe_layer_slots(self.handle, self.slab_slots)
+
+    def _io(self, x, y, route_idx, route_w, used, pred, hist_cur, hist_prev, reactive):
+        import torch
+        n = x.shape[0]
+        dev = x.device
+        out = {"y": y}
+        if used:
+            out["used_idx"] = torch.empty((n, self.top_k), dtype=torch.int32, device=dev)
+            out["used_w"] = torch.empty((n, self.top_k), dtype=torch.float32, device=dev)
+        if pred:
+            out["pred_idx"] = torch.empty((n, self.next_top_k), dtype=torch.int32, device=dev)
+            out["pred_w"] = torch.empty((n, self.next_top_k), dtype=torch.float32, device=dev)
+        io = moe_io(_ptr(x), _ptr(y), _ptr(route_idx), _ptr(route_w), _ptr(out.get("used_idx")),
+                    _ptr(out.get("used_w")), _ptr(out.get("pred_idx")), _ptr(out.get("pred_w")),
+                    _ptr(hist_cur), _ptr(hist_prev), 1 if reactive else 0)
+        return io, out
+
+    def decode(self, x, route_idx=None, route_w=None, *, y=None, used=True, pred=True, hist_cur=None,
+               hist_prev=None, reactive=False, stream=None):
+        import torch
+        if y is None:
+            y = torch.empty((x.shape[0], self.d_model), dtype=torch.float32, device=x.device)
+        io, out = self._io(x, y, route_idx, route_w, used, pred, hist_cur, hist_prev, reactive)
+        moe_decode_step(self.handle, io, x.shape[0], _stream_ptr(stream))
+        return out
+
+    def prefill(self, x, route_idx=None, route_w=None, *, y=None, used=True, pred=True, hist_cur=None,
+                hist_prev=None, stream=None):
+        import torch
+        if y is None:
+            y = torch.empty((x.shape[0], self.d_model), dtype=torch.float32, device=x.device)
+        io, out = self._io(x, y, route_idx, route_w, used, pred, hist_cur, hist_prev, False)
+        moe_prefill(self.handle, io, x.shape[0], _stream_ptr(stream))
+        return out
+
+    def status(self) -> int:
+        return moe_layer_sync_status(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            moe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

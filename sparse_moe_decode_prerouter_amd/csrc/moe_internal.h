@@ -1,0 +1,168 @@
+// Internal structures of the MoE block library (host + device).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_prerouter.h"
+
+namespace moe {
+
+constexpr int kGroup = 64;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 1024;
+
+// device error flag bits (sticky until read by the host)
+enum : int { ERR_NOT_STAGED = 1, ERR_BAD_INDEX = 2, ERR_TIMEOUT = 4 };
+
+// Where a layer's expert weights are found on the device.
+struct ExpertView {
+    const uint8_t* base;          // slab (streamed) or store (resident)
+    const int32_t* slot_of;       // [E] slot per expert, -1 absent (streamed); nullptr: slot = expert
+    const int32_t* slot_tag;      // [slots] expert held per slot (streamed); nullptr: no check
+    const uint8_t* shared;        // shared blob (device) or nullptr
+    const int32_t* shared_tag;    // streamed: tag of the shared slot (== E when staged); nullptr: no check
+    size_t blob;                  // bytes per routed blob
+    size_t shared_blob;           // bytes of the shared blob
+    int E;
+};
+
+// Byte offsets inside a blob (see the format in moe_prerouter.h).
+struct BlobLayout {
+    size_t gate_q, up_q, down_q, gate_sb, up_sb, down_sb, total;
+    __host__ __device__ static BlobLayout make(int d, int f) {
+        BlobLayout L;
+        const size_t q = (size_t)d * f / 2, sb = (size_t)d * f / kGroup * 4;
+        L.gate_q = 0; L.up_q = q; L.down_q = 2 * q;
+        L.gate_sb = 3 * q; L.up_sb = 3 * q + sb; L.down_sb = 3 * q + 2 * sb;
+        L.total = 3 * q + 3 * sb;
+        return L;
+    }
+};
+
+// Device scratch of one layer (carved from the caller's workspace).
+struct Scratch {
+    int32_t* err;            // [1] sticky error flag
+    uint32_t* counters;      // [16] last-block counters (self-resetting)
+    int32_t* slot_of;        // [E]
+    int32_t* slot_tag;       // [slots + 1]; entry `slots` is the shared slot
+    uint8_t* slab;           // [(slots + 1) * blob] (streamed); shared slot last
+    float* u;                // [T][d] block input (exact act values) in fp32
+    uint32_t* u_pk;          // [T][d/2] bf16 pairs, GEMV order (hi part)
+    uint32_t* u_pk_lo;       // [T][d/2] lo part (f32 act) or nullptr
+    float* usum;             // [T][d/32] sums of hi part per 32-chunk
+    float* usum_lo;          // [T][d/32] or nullptr
+    double* logits_r;        // [T][E] router logits
+    double* logits_h;        // [T][E_next] head logits
+    int32_t* self_idx;       // [T][k]
+    float* self_w;           // [T][k]
+    int32_t* used_idx;       // [T][k]
+    float* used_w;           // [T][k]
+    float* au;               // [T][r]  A u
+    float* sgate;            // [T]     sigmoid(g . u)
+    int32_t* sort_meta;      // [4]: n_active, n_assign, ...
+    int32_t* active;         // [min(E, T*k)] active experts ascending
+    int32_t* act_off;        // [.. + 1] start of each active expert's assignments
+    int32_t* perm;           // [T*k] assignment ids (t*k + j) sorted by (expert, id)
+    float* h;                // [T*k][f] routed expert hidden (sorted order)
+    float* hs;               // [T][fs] shared expert hidden
+    uint16_t* hb;            // prefill: [T*k][f] bf16 hi of h (sorted order)
+    uint16_t* hb_lo;         // prefill: lo part
+    uint16_t* hsb;           // prefill: [T][fs] bf16 hi of shared h
+    uint16_t* hsb_lo;
+    int32_t* rowmap;         // prefill: [T*k] token of each sorted assignment
+};
+
+}  // namespace moe
+
+struct moe_layer {
+    moe_layer_desc desc;
+    moe_layer_weights w;
+    moe::Scratch s;
+    moe::BlobLayout L, Ls;
+    size_t blob, sblob;
+    int slots;                 // routed slots (streamed)
+    bool resident;
+    int dev;
+    // host mirror of the slab
+    int32_t* h_slot_expert;    // [slots]
+    int32_t* h_last_staged;    // [slots] last wanted set (sorted, -1 padded)
+    int n_last_staged;
+    bool shared_staged;
+    uint64_t staged_bytes;
+    hipEvent_t ev_staged, ev_done;
+    bool staged_pending, done_recorded;
+    int32_t* h_readback;       // pinned [max_tokens * k]
+};
+
+// ---- kernel launchers (kernels_*.hip) -------------------------------------
+namespace moe {
+
+struct PrologueArgs {
+    const void* x; int x_is_bf16; int fused; const float* gamma; float eps;
+    int act_bf16; int d; int n_tok;
+    float* u; uint32_t* u_pk; uint32_t* u_pk_lo; float* usum; float* usum_lo;
+};
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
+
+struct RouteArgs {
+    // router (self-routing rows) and head (prediction) logits + top-k, plus
+    // LoRA A u and the shared gate, all from bf16 weights on the fp32 u
+    const float* u; int d; int n_tok;
+    const uint16_t* router; const float* router_bias; int E; int k;
+    const int32_t* route_idx;           // rows to self-route: idx[t*k] < 0 or route_idx == nullptr
+    const uint16_t* head; const float* head_bias; int En; int kn;
+    const float* hist_cur_m; const float* hist_prev_m; const int32_t* hist_cur; const int32_t* hist_prev;
+    const uint16_t* lora_a; int r;
+    const uint16_t* sgate_w;
+    double* logits_r; double* logits_h;
+    int32_t* self_idx; float* self_w; int32_t* pred_idx; float* pred_w;
+    float* au; float* sgate;
+    uint32_t* counters;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct SortArgs {
+    const int32_t* route_idx; const float* route_w; const int32_t* self_idx; const float* self_w;
+    int n_tok; int k; int E;
+    int32_t* used_idx; float* used_w; int32_t* user_used_idx; float* user_used_w;
+    int32_t* meta; int32_t* active; int32_t* act_off; int32_t* perm;
+    int32_t* err;
+};
+hipError_t launch_sort(const SortArgs& a, hipStream_t s);
+
+struct GemvArgs {
+    ExpertView ev; int d; int f; int fs; int k; int n_tok;
+    const int32_t* meta; const int32_t* active; const int32_t* act_off; const int32_t* perm;
+    const float* used_w; const float* sgate;
+    const uint32_t* u_pk; const uint32_t* u_pk_lo; const float* usum; const float* usum_lo;
+    float* h; float* hs;
+    // down / epilogue
+    const float* x; int fused; const float* au; const uint16_t* lora_b; int r; float lora_scale;
+    float* y;
+    int32_t* err;
+    int max_active;
+};
+hipError_t launch_gateup(const GemvArgs& a, hipStream_t s);
+hipError_t launch_down(const GemvArgs& a, hipStream_t s);
+
+struct PrefillArgs {
+    GemvArgs g;
+    const float* u;            // fp32 u [T][d]
+    uint16_t* hb; uint16_t* hb_lo; uint16_t* hsb; uint16_t* hsb_lo;
+    int32_t* rowmap;
+};
+hipError_t launch_prefill_gateup(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s);
+
+struct SlotUpdate {
+    int n;
+    int slot[64];
+    int old_e[64];
+    int new_e[64];
+    int shared_tag;   // >= 0: write into slot_tag[shared_slot]
+    int shared_slot;
+};
+hipError_t launch_slot_update(int32_t* slot_of, int32_t* slot_tag, const SlotUpdate& u, hipStream_t s);
+
+}  // namespace moe
