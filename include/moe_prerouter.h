@@ -145,6 +145,10 @@ typedef struct moe_io {
      * device, read the routing back, stage the missing experts, continue);
      * implied when route_idx is NULL. Blocks the host until the read-back.  */
     int            reactive;
+    /* decode only: nonzero when some rows of a non-NULL route_idx may start
+     * with a negative index (those rows self-route, which adds a router
+     * launch); zero promises every row is given. Prefill always checks.     */
+    int            self_rows;
 } moe_io;
 
 typedef struct moe_layer moe_layer;
@@ -204,6 +208,50 @@ int moe_layer_sync_status(moe_layer* layer);
 /* Release the handle, its events and its pinned read-back buffer (not the
  * caller's memory). Safe on NULL.                                           */
 void moe_layer_destroy(moe_layer* layer);
+
+/* ---- stack of layers ------------------------------------------------------
+ * A stack of n_layers layers (each with MOE_FUSE_NORM_RESIDUAL, the same d
+ * and top_k, a router, and a head on every layer but the last) driven with
+ * the one-token-ahead dataflow (guide, Q&A: why one token ahead): head l at
+ * token t predicts the routing of layer l+1 at token t+1, and that
+ * prediction is the routing. Launches only (no host synchronisation, no
+ * allocation; in streamed mode the reactive layer-0 staging reads back), so
+ * resident-mode calls can be captured into a HIP graph. moe_stack_create
+ * allocates the prefill routing scratch (max_tokens * k entries); destroy
+ * frees it.
+ *
+ * moe_stack_decode: one decode step for n_tok independent sequences.
+ *   x_in       device fp32 [n_tok][d]: step input (may equal x_out)
+ *   x_out      device fp32 [n_tok][d]: residual stream after the last layer
+ *   route_*    device [n_layers][n_tok][k]: this step's routing (entry l = 0
+ *              and every entry on the first step are ignored: those layers
+ *              self-route with their router)
+ *   pred_*     device [n_layers][n_tok][k] out: pred[l] for l >= 1 (pred[0]
+ *              is left untouched); the next step's route
+ *   used_*     optional out [n_layers][n_tok][k]: routing each layer used
+ *   hist_prev  optional in [n_layers][n_tok][k]: routing each layer used at
+ *              the previous step (history one-hot of the previous token);
+ *              the current-token history of head l is route[l+1].
+ * moe_stack_prefill: n_tok tokens of one sequence. Token i >= 1 at layer
+ *   l >= 1 uses head l-1's prediction on token i-1 (shifted on the device);
+ *   token 0 and layer 0 self-route. x is updated in place; used_* as above;
+ *   pred_* (optional) receive each head's unshifted predictions.            */
+typedef struct moe_stack moe_stack;
+int moe_stack_create(moe_layer* const* layers, int n_layers, moe_stack** out);
+int moe_stack_decode(moe_stack* st, const float* x_in, float* x_out, int n_tok,
+                     const int32_t* route_idx, const float* route_w, int32_t* pred_idx, float* pred_w,
+                     int32_t* used_idx, float* used_w, const int32_t* hist_prev, int first_step, void* stream);
+int moe_stack_prefill(moe_stack* st, float* x, int n_tok, int32_t* used_idx, float* used_w,
+                      int32_t* pred_idx, float* pred_w, void* stream);
+void moe_stack_destroy(moe_stack* st);
+
+/* ---- measurement --------------------------------------------------------
+ * With profiling on, every kernel launch of this layer is bracketed by HIP
+ * events on its stream; moe_layer_kernel_ms returns the durations of the most
+ * recent launches of the router (self-routing), K_A (norm + gate/up + head)
+ * and K_B (down + combine + epilogue) kernels, -1 where not launched.        */
+int moe_layer_set_profiling(moe_layer* layer, int enable);
+int moe_layer_kernel_ms(moe_layer* layer, float* ms_router, float* ms_a, float* ms_b);
 
 const char* moe_status_str(int status);
 int moe_last_hip_error(void);

@@ -13,7 +13,7 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_prerouter.so")
+LIB_PATH = os.environ.get("MOE_PREROUTER_LIB", os.path.join(_HERE, "libmoe_prerouter.so"))
 
 MOE_OK = 0
 MOE_E_INVALID = -1
@@ -49,7 +49,7 @@ class moe_layer_weights(ctypes.Structure):
 class moe_io(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x_in", "y_out", "route_idx", "route_w", "used_idx", "used_w", "pred_idx", "pred_w",
-        "hist_cur", "hist_prev")] + [("reactive", ctypes.c_int)]
+        "hist_cur", "hist_prev")] + [("reactive", ctypes.c_int), ("self_rows", ctypes.c_int)]
 
 
 class MoeError(RuntimeError):
@@ -79,6 +79,12 @@ def _load():
         "moe_status_str": (ctypes.c_char_p, [I]),
         "moe_last_hip_error": (I, []),
         "moe_plan_slots": (I, [P, I, P, I, I, P, P, P]),
+        "moe_stack_create": (I, [P, I, ctypes.POINTER(P)]),
+        "moe_stack_decode": (I, [P, P, P, I, P, P, P, P, P, P, P, I, P]),
+        "moe_stack_prefill": (I, [P, P, I, P, P, P, P, P]),
+        "moe_stack_destroy": (None, [P]),
+        "moe_layer_set_profiling": (I, [P, I]),
+        "moe_layer_kernel_ms": (I, [P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -90,7 +96,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_expert_blob_bytes", "moe_layer_workspace_bytes", "moe_layer_create", "moe_stage_experts",
             "moe_layer_slots", "moe_decode_step", "moe_prefill", "moe_layer_sync_status", "moe_layer_destroy",
-            "moe_status_str", "moe_last_hip_error", "moe_plan_slots")
+            "moe_status_str", "moe_last_hip_error", "moe_plan_slots", "moe_stack_create", "moe_stack_decode",
+            "moe_stack_prefill", "moe_stack_destroy", "moe_layer_set_profiling", "moe_layer_kernel_ms")
 
 
 # ---------------------------------------------------------------------------
@@ -171,6 +178,49 @@ def moe_plan_slots(resident: Sequence[int], wanted: Sequence[int], n_experts: in
     return list(res)[:n], [(cs[i], ce[i]) for i in range(nc.value)]
 
 
+def moe_stack_create(handles: Sequence[int]) -> int:
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    h = ctypes.c_void_p()
+    rc = _lib.moe_stack_create(arr, len(handles), ctypes.byref(h))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stack_create")
+    return h.value
+
+
+def moe_stack_decode(stack: int, x_in: int, x_out: int, n_tok: int, route_idx: Optional[int],
+                     route_w: Optional[int], pred_idx: int, pred_w: int, used_idx: Optional[int],
+                     used_w: Optional[int], hist_prev: Optional[int], first_step: bool, stream: int = 0) -> None:
+    rc = _lib.moe_stack_decode(stack, x_in, x_out, n_tok, route_idx, route_w, pred_idx, pred_w, used_idx, used_w,
+                               hist_prev, 1 if first_step else 0, ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stack_decode")
+
+
+def moe_stack_prefill(stack: int, x: int, n_tok: int, used_idx: Optional[int], used_w: Optional[int],
+                      pred_idx: Optional[int], pred_w: Optional[int], stream: int = 0) -> None:
+    rc = _lib.moe_stack_prefill(stack, x, n_tok, used_idx, used_w, pred_idx, pred_w, ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stack_prefill")
+
+
+def moe_stack_destroy(stack: int) -> None:
+    _lib.moe_stack_destroy(stack)
+
+
+def moe_layer_set_profiling(handle: int, enable: bool) -> None:
+    rc = _lib.moe_layer_set_profiling(handle, 1 if enable else 0)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layer_set_profiling")
+
+
+def moe_layer_kernel_ms(handle: int):
+    r, a, b = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
+    rc = _lib.moe_layer_kernel_ms(handle, ctypes.byref(r), ctypes.byref(a), ctypes.byref(b))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layer_kernel_ms")
+    return r.value, a.value, b.value
+
+
 # ---------------------------------------------------------------------------
 # convenience wrapper over torch tensors
 # ---------------------------------------------------------------------------
@@ -219,7 +269,7 @@ class MoeLayer:
     def slots(self):
         return moe_layer_slots(self.handle, self.slab_slots)
 
-    def _io(self, x, y, route_idx, route_w, used, pred, hist_cur, hist_prev, reactive):
+    def _io(self, x, y, route_idx, route_w, used, pred, hist_cur, hist_prev, reactive, self_rows=0):
         import torch
         n = x.shape[0]
         dev = x.device
@@ -232,15 +282,15 @@ class MoeLayer:
             out["pred_w"] = torch.empty((n, self.next_top_k), dtype=torch.float32, device=dev)
         io = moe_io(_ptr(x), _ptr(y), _ptr(route_idx), _ptr(route_w), _ptr(out.get("used_idx")),
                     _ptr(out.get("used_w")), _ptr(out.get("pred_idx")), _ptr(out.get("pred_w")),
-                    _ptr(hist_cur), _ptr(hist_prev), 1 if reactive else 0)
+                    _ptr(hist_cur), _ptr(hist_prev), 1 if reactive else 0, 1 if self_rows else 0)
         return io, out
 
     def decode(self, x, route_idx=None, route_w=None, *, y=None, used=True, pred=True, hist_cur=None,
-               hist_prev=None, reactive=False, stream=None):
+               hist_prev=None, reactive=False, self_rows=False, stream=None):
         import torch
         if y is None:
             y = torch.empty((x.shape[0], self.d_model), dtype=torch.float32, device=x.device)
-        io, out = self._io(x, y, route_idx, route_w, used, pred, hist_cur, hist_prev, reactive)
+        io, out = self._io(x, y, route_idx, route_w, used, pred, hist_cur, hist_prev, reactive, self_rows)
         moe_decode_step(self.handle, io, x.shape[0], _stream_ptr(stream))
         return out
 
@@ -256,9 +306,48 @@ class MoeLayer:
     def status(self) -> int:
         return moe_layer_sync_status(self.handle)
 
+    def set_profiling(self, enable: bool = True):
+        moe_layer_set_profiling(self.handle, enable)
+
+    def kernel_ms(self):
+        return moe_layer_kernel_ms(self.handle)
+
     def close(self):
         if getattr(self, "handle", None):
             moe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class MoeStack:
+    """A stack of MoeLayer objects driven one decode step at a time
+    (moe_stack_decode). Routing buffers are [L][n_tok][k] device tensors; the
+    step's predictions feed the next step, so callers rotate two buffers."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        self.handle = moe_stack_create([L.handle for L in self.layers])
+        self.k = self.layers[0].top_k
+
+    def decode(self, x, route_idx, route_w, pred_idx, pred_w, *, x_out=None, used_idx=None, used_w=None,
+               hist_prev=None, first_step=False, stream=None):
+        xo = x if x_out is None else x_out
+        moe_stack_decode(self.handle, x.data_ptr(), xo.data_ptr(), x.shape[0], _ptr(route_idx), _ptr(route_w),
+                         pred_idx.data_ptr(), pred_w.data_ptr(), _ptr(used_idx), _ptr(used_w), _ptr(hist_prev),
+                         first_step, _stream_ptr(stream))
+
+    def prefill(self, x, *, used_idx=None, used_w=None, pred_idx=None, pred_w=None, stream=None):
+        moe_stack_prefill(self.handle, x.data_ptr(), x.shape[0], _ptr(used_idx), _ptr(used_w), _ptr(pred_idx),
+                          _ptr(pred_w), _stream_ptr(stream))
+
+    def close(self):
+        if getattr(self, "handle", None):
+            moe_stack_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -3,6 +3,7 @@
 // combine + shared expert + LoRA + residual).
 #include "device_common.h"
 #include "moe_internal.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -79,68 +80,6 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 constexpr int kRouteRowsPerBlock = 16;   // 4 waves x 4 rows
 
-__device__ void topk_rows(const double* logits, int E, int k, int n_tok, const float* bias,
-                          const float* mc, const int32_t* hc, const float* mp, const int32_t* hp,
-                          const int32_t* route_idx, int kroute, int32_t* out_idx, float* out_w) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int t = wave; t < n_tok; t += 4) {
-        if (route_idx && route_idx[(size_t)t * kroute] >= 0) continue;   // row has its routing
-        double v[kMaxExperts / 64];
-        const int per = (E + 63) / 64;
-        for (int m = 0; m < per; ++m) {
-            const int e = lane + 64 * m;
-            double z = -INFINITY;
-            if (e < E) {
-                z = ld_dev(logits + (size_t)t * E + e);
-                if (bias) z += (double)bias[e];
-                if (mc && hc) {
-                    for (int j = 0; j < k; ++j) {
-                        const int h = hc[(size_t)t * k + j];
-                        bool dup = false;
-                        for (int jj = 0; jj < j; ++jj) dup |= hc[(size_t)t * k + jj] == h;
-                        if (h >= 0 && h < E && !dup) z += (double)mc[(size_t)h * E + e];
-                    }
-                }
-                if (mp && hp) {
-                    for (int j = 0; j < k; ++j) {
-                        const int h = hp[(size_t)t * k + j];
-                        bool dup = false;
-                        for (int jj = 0; jj < j; ++jj) dup |= hp[(size_t)t * k + jj] == h;
-                        if (h >= 0 && h < E && !dup) z += (double)mp[(size_t)h * E + e];
-                    }
-                }
-            }
-            v[m] = z;
-        }
-        double sel_v[kMaxTopK];
-        int sel_i[kMaxTopK];
-        for (int j = 0; j < k; ++j) {
-            double bv = -INFINITY; int bi = 0x7fffffff;
-            for (int m = 0; m < per; ++m) {
-                const int e = lane + 64 * m;
-                if (e < E && better(v[m], e, bv, bi)) { bv = v[m]; bi = e; }
-            }
-            for (int o = 32; o > 0; o >>= 1) {
-                const double ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-            }
-            sel_v[j] = bv; sel_i[j] = bi;
-            for (int m = 0; m < per; ++m)
-                if (lane + 64 * m == bi) v[m] = -INFINITY;
-        }
-        if (lane == 0) {
-            double ssum = 0.0;
-            double ex[kMaxTopK];
-            for (int j = 0; j < k; ++j) { ex[j] = exp(sel_v[j] - sel_v[0]); ssum += ex[j]; }
-            for (int j = 0; j < k; ++j) {
-                out_idx[(size_t)t * k + j] = sel_i[j];
-                out_w[(size_t)t * k + j] = (float)(ex[j] / ssum);
-            }
-        }
-    }
-}
-
 __global__ void __launch_bounds__(256) k_route(RouteArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nr_router = a.router ? a.E : 0;
@@ -200,10 +139,10 @@ __global__ void __launch_bounds__(256) k_route(RouteArgs a) {
     __syncthreads();
     if (!is_last) return;
     if (job == 0)
-        topk_rows(a.logits_r, a.E, a.k, a.n_tok, a.router_bias, nullptr, nullptr, nullptr, nullptr,
+        topk_rows(true, a.logits_r, a.E, a.k, a.n_tok, a.router_bias, nullptr, nullptr, nullptr, nullptr,
                   a.route_idx, a.k, a.self_idx, a.self_w);
     else
-        topk_rows(a.logits_h, a.En, a.kn, a.n_tok, a.head_bias, a.hist_cur_m, a.hist_cur, a.hist_prev_m,
+        topk_rows(true, a.logits_h, a.En, a.kn, a.n_tok, a.head_bias, a.hist_cur_m, a.hist_cur, a.hist_prev_m,
                   a.hist_prev, nullptr, a.kn, a.pred_idx, a.pred_w);
 }
 

@@ -92,6 +92,7 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.active = c.take<int32_t>(nas + 1);
     S.act_off = c.take<int32_t>(nas + 1);
     S.perm = c.take<int32_t>(T * K);
+    S.wsort = c.take<float>(T * K);
     S.h = c.take<float>(T * K * d->d_ff);
     S.hs = c.take<float>(T * std::max(1, d->d_ff_shared));
     S.hb = c.take<uint16_t>(T * K * d->d_ff);
@@ -171,7 +172,106 @@ int check_io(const moe_layer* L, const moe_io* io, int n_tok) {
     return MOE_OK;
 }
 
-int run_block(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill) {
+int reactive_stage(moe_layer* L, const int32_t* d_idx, int n_tok, hipStream_t st) {
+    // the routing exists only on the device now: read it back and stage it
+    const size_t nk = (size_t)n_tok * L->desc.top_k;
+    HIPCHK(hipMemcpyAsync(L->h_readback, d_idx, nk * sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    std::vector<int32_t> want;
+    for (size_t i = 0; i < nk; ++i)
+        if (L->h_readback[i] >= 0 && L->h_readback[i] < L->desc.n_experts) want.push_back(L->h_readback[i]);
+    std::sort(want.begin(), want.end());
+    want.erase(std::unique(want.begin(), want.end()), want.end());
+    return stage_set(L, want, st);
+}
+
+// merged routing (given rows + self rows) into `dst`, for the reactive read-back
+__global__ void k_merge_route(const int32_t* ridx, const int32_t* sidx, int32_t* dst, int n, int k) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int t = i / k;
+    dst[i] = (ridx && ridx[(size_t)t * k] >= 0) ? ridx[i] : sidx[i];
+}
+
+int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill);
+
+int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
+    const moe_layer_desc& D = L->desc;
+    // shapes outside the fused two-kernel path take the general grouped-GEMV path
+    if (!dec_fast_path_ok(D.d_model, D.d_ff, n_tok, D.top_k)) return run_prefill(L, io, n_tok, st, false);
+    const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
+    if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
+    const bool need_router = io->route_idx == nullptr || io->self_rows;
+    if (need_router && !L->w.router) return MOE_E_INVALID;
+
+    DecAArgs a{};
+    a.x = io->x_in;
+    a.x_is_bf16 = (!fused && D.act_dtype == MOE_ACT_BF16) ? 1 : 0;
+    a.fused = fused; a.gamma = L->w.norm_gamma; a.eps = D.rms_eps;
+    a.act_bf16 = D.act_dtype == MOE_ACT_BF16; a.d = D.d_model; a.n_tok = n_tok;
+    a.route_idx = io->route_idx; a.route_w = io->route_w;
+    a.self_idx = need_router ? L->s.self_idx : nullptr; a.self_w = need_router ? L->s.self_w : nullptr;
+    a.k = D.top_k; a.E = D.n_experts;
+    a.ev = view_of(L); a.f = D.d_ff; a.fs = D.d_ff_shared;
+    a.head = io->pred_idx ? L->w.head : nullptr; a.En = io->pred_idx ? D.next_n_experts : 0;
+    a.lora_a = D.lora_rank ? L->w.lora_a : nullptr; a.r = D.lora_rank;
+    a.sgate_w = D.d_ff_shared ? L->w.shared_gate : nullptr;
+    a.h = L->s.h; a.hs = L->s.hs; a.logits_h = L->s.logits_h; a.au = L->s.au; a.sgate = L->s.sgate;
+    a.meta = L->s.sort_meta; a.active = L->s.active; a.act_off = L->s.act_off; a.perm = L->s.perm;
+    a.wsort = L->s.wsort;
+    a.used_idx = L->s.used_idx; a.used_w = L->s.used_w; a.user_used_idx = io->used_idx; a.user_used_w = io->used_w;
+    a.err = L->s.err;
+    dec_a_blocks(D.d_model, D.d_ff, D.d_ff_shared, n_tok, D.top_k, D.n_experts, a.En, D.lora_rank,
+                 a.sgate_w != nullptr, &a.nb_h, &a.nb_head, &a.nb_misc);
+
+    if (need_router) {
+        RouteArgs r{};
+        r.router = L->w.router; r.router_bias = L->w.router_bias; r.E = D.n_experts; r.k = D.top_k;
+        r.route_idx = io->route_idx; r.logits_r = L->s.logits_r;
+        r.self_idx = L->s.self_idx; r.self_w = L->s.self_w; r.counters = L->s.counters;
+        if (L->profiling) HIPCHK(hipEventRecord(L->ev_t[0], st));
+        HIPCHK(launch_dec_r(a, r, st));
+        if (L->profiling) { HIPCHK(hipEventRecord(L->ev_t[1], st)); L->ev_t_used[0] = true; }
+    }
+    if (!L->resident && (io->route_idx == nullptr || io->reactive)) {
+        const int n = n_tok * D.top_k;
+        const int32_t* src = L->s.self_idx;
+        if (io->route_idx) {
+            hipLaunchKernelGGL(k_merge_route, dim3((n + 255) / 256), dim3(256), 0, st, io->route_idx,
+                               need_router ? L->s.self_idx : io->route_idx, L->s.used_idx, n, D.top_k);
+            HIPCHK(hipGetLastError());
+            src = L->s.used_idx;
+        }
+        int rc = reactive_stage(L, src, n_tok, st);
+        if (rc != MOE_OK) return rc;
+    }
+    if (L->profiling) HIPCHK(hipEventRecord(L->ev_t[2], st));
+    HIPCHK(launch_dec_a(a, st));
+    if (L->profiling) { HIPCHK(hipEventRecord(L->ev_t[3], st)); L->ev_t_used[1] = true; }
+
+    DecBArgs b{};
+    b.ev = a.ev; b.d = D.d_model; b.f = D.d_ff; b.fs = D.d_ff_shared; b.k = D.top_k; b.n_tok = n_tok;
+    b.meta = L->s.sort_meta; b.active = L->s.active; b.act_off = L->s.act_off; b.perm = L->s.perm;
+    b.wsort = L->s.wsort; b.sgate = (D.d_ff_shared && L->w.shared_gate) ? L->s.sgate : nullptr;
+    b.h = L->s.h; b.hs = L->s.hs;
+    b.x = (const float*)io->x_in; b.fused = fused;
+    b.au = L->s.au; b.lora_b = D.lora_rank ? L->w.lora_b : nullptr; b.r = D.lora_rank;
+    b.lora_scale = D.lora_rank ? D.lora_alpha / (float)D.lora_rank : 0.f;
+    b.y = io->y_out;
+    b.logits_h = L->s.logits_h; b.En = D.next_n_experts; b.kn = D.next_top_k; b.head_bias = L->w.head_bias;
+    b.hist_cur_m = L->w.hist_cur; b.hist_prev_m = L->w.hist_prev; b.hist_cur = io->hist_cur; b.hist_prev = io->hist_prev;
+    b.pred_idx = io->pred_idx; b.pred_w = io->pred_w;
+    b.err = L->s.err;
+    b.nb_rows = dec_b_row_blocks(D.d_model);
+    if (L->profiling) HIPCHK(hipEventRecord(L->ev_t[4], st));
+    HIPCHK(launch_dec_b(b, st));
+    if (L->profiling) { HIPCHK(hipEventRecord(L->ev_t[5], st)); L->ev_t_used[2] = true; }
+    HIPCHK(hipEventRecord(L->ev_done, st));
+    L->done_recorded = true;
+    return MOE_OK;
+}
+
+int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill) {
     const moe_layer_desc& D = L->desc;
     const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
     if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
@@ -353,13 +453,13 @@ int moe_decode_step(moe_layer* L, const moe_io* io, int n_tok, void* stream) {
     int rc = check_io(L, io, n_tok);
     if (rc != MOE_OK) return rc;
     if (n_tok * L->desc.top_k > 4096 || n_tok > 256) return MOE_E_UNSUPPORTED;
-    return run_block(L, io, n_tok, (hipStream_t)stream, false);
+    return run_decode(L, io, n_tok, (hipStream_t)stream);
 }
 
 int moe_prefill(moe_layer* L, const moe_io* io, int n_tok, void* stream) {
     int rc = check_io(L, io, n_tok);
     if (rc != MOE_OK) return rc;
-    return run_block(L, io, n_tok, (hipStream_t)stream, true);
+    return run_prefill(L, io, n_tok, (hipStream_t)stream, true);
 }
 
 int moe_layer_sync_status(moe_layer* L) {
@@ -377,12 +477,151 @@ int moe_layer_sync_status(moe_layer* L) {
 
 void moe_layer_destroy(moe_layer* L) {
     if (!L) return;
+    for (int i = 0; i < 6; ++i)
+        if (L->ev_t[i]) (void)hipEventDestroy(L->ev_t[i]);
     if (L->ev_staged) (void)hipEventDestroy(L->ev_staged);
     if (L->ev_done) (void)hipEventDestroy(L->ev_done);
     if (L->h_readback) (void)hipHostFree(L->h_readback);
     delete[] L->h_slot_expert;
     delete[] L->h_last_staged;
     delete L;
+}
+
+int moe_layer_set_profiling(moe_layer* L, int enable) {
+    if (!L) return MOE_E_INVALID;
+    if (enable && !L->ev_t[0]) {
+        for (int i = 0; i < 6; ++i) HIPCHK(hipEventCreate(&L->ev_t[i]));
+    }
+    L->profiling = enable != 0;
+    for (int i = 0; i < 3; ++i) L->ev_t_used[i] = false;
+    return MOE_OK;
+}
+
+int moe_layer_kernel_ms(moe_layer* L, float* ms_router, float* ms_a, float* ms_b) {
+    if (!L) return MOE_E_INVALID;
+    float* outs[3] = {ms_router, ms_a, ms_b};
+    for (int i = 0; i < 3; ++i) {
+        if (!outs[i]) continue;
+        *outs[i] = -1.f;
+        if (L->ev_t_used[i] && L->ev_t[2 * i]) {
+            HIPCHK(hipEventSynchronize(L->ev_t[2 * i + 1]));
+            HIPCHK(hipEventElapsedTime(outs[i], L->ev_t[2 * i], L->ev_t[2 * i + 1]));
+        }
+    }
+    return MOE_OK;
+}
+
+int moe_stack_create(moe_layer* const* layers, int n, moe_stack** out) {
+    if (!out || !layers || n < 1) return MOE_E_INVALID;
+    *out = nullptr;
+    for (int l = 0; l < n; ++l) {
+        const moe_layer* L = layers[l];
+        if (!L) return MOE_E_INVALID;
+        if (!(L->desc.flags & MOE_FUSE_NORM_RESIDUAL)) return MOE_E_INVALID;
+        if (L->desc.d_model != layers[0]->desc.d_model || L->desc.top_k != layers[0]->desc.top_k) return MOE_E_INVALID;
+        if (l + 1 < n && (!L->w.head || L->desc.next_n_experts != layers[l + 1]->desc.n_experts ||
+                          L->desc.next_top_k != layers[l + 1]->desc.top_k))
+            return MOE_E_INVALID;
+        if (!L->w.router) return MOE_E_INVALID;
+    }
+    moe_stack* S = new (std::nothrow) moe_stack();
+    if (!S) return MOE_E_INVALID;
+    S->layers = new moe_layer*[n];
+    for (int l = 0; l < n; ++l) S->layers[l] = layers[l];
+    S->n = n;
+    // prefill scratch for the shifted routing, sized by the smallest max_tokens
+    int T = layers[0]->desc.max_tokens;
+    for (int l = 1; l < n; ++l) T = std::min(T, layers[l]->desc.max_tokens);
+    const size_t per = (size_t)T * layers[0]->desc.top_k;
+    hipError_t e = hipMalloc(&S->d_shift_idx, per * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&S->d_shift_w, per * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(&S->d_pred_idx, per * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&S->d_pred_w, per * sizeof(float));
+    if (e != hipSuccess) { g_last_hip = (int)e; moe_stack_destroy(S); return MOE_E_HIP; }
+    S->shift_cap = per;
+    *out = S;
+    return MOE_OK;
+}
+
+int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, const int32_t* route_idx,
+                     const float* route_w, int32_t* pred_idx, float* pred_w, int32_t* used_idx, float* used_w,
+                     const int32_t* hist_prev, int first_step, void* stream) {
+    if (!S || !x_in || !x_out || !pred_idx || !pred_w) return MOE_E_INVALID;
+    if (!first_step && (!route_idx || !route_w)) return MOE_E_INVALID;
+    const int k = S->layers[0]->desc.top_k;
+    const size_t per = (size_t)n_tok * k;
+    for (int l = 0; l < S->n; ++l) {
+        moe_layer* L = S->layers[l];
+        moe_io io{};
+        io.x_in = l == 0 ? x_in : x_out;
+        io.y_out = x_out;
+        const bool self = first_step || l == 0;
+        io.route_idx = self ? nullptr : route_idx + l * per;
+        io.route_w = self ? nullptr : route_w + l * per;
+        io.used_idx = used_idx ? used_idx + l * per : nullptr;
+        io.used_w = used_w ? used_w + l * per : nullptr;
+        if (l + 1 < S->n) {
+            io.pred_idx = pred_idx + (l + 1) * per;
+            io.pred_w = pred_w + (l + 1) * per;
+            io.hist_cur = first_step ? nullptr : route_idx + (l + 1) * per;
+            io.hist_prev = hist_prev ? hist_prev + (l + 1) * per : nullptr;
+        }
+        int rc = moe_decode_step(L, &io, n_tok, stream);
+        if (rc != MOE_OK) return rc;
+    }
+    return MOE_OK;
+}
+
+// dst row i = src row i-1, row 0 = -1 (no prediction: self-route)
+__global__ void k_shift_rows(const int32_t* si, const float* sw, int32_t* di, float* dw, int n_tok, int k) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_tok * k) return;
+    const int t = i / k;
+    di[i] = t == 0 ? -1 : si[i - k];
+    dw[i] = t == 0 ? 0.f : sw[i - k];
+}
+
+int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, float* used_w, int32_t* pred_idx,
+                      float* pred_w, void* stream) {
+    if (!S || !x || n_tok < 1) return MOE_E_INVALID;
+    const int k = S->layers[0]->desc.top_k;
+    const size_t per = (size_t)n_tok * k;
+    hipStream_t st = (hipStream_t)stream;
+    if (per > S->shift_cap) return MOE_E_INVALID;
+    for (int l = 0; l < S->n; ++l) {
+        moe_layer* L = S->layers[l];
+        moe_io io{};
+        io.x_in = x;
+        io.y_out = x;
+        if (l > 0) {
+            const int32_t* src_i = pred_idx ? pred_idx + l * per : S->d_pred_idx;
+            const float* src_w = pred_w ? pred_w + l * per : S->d_pred_w;
+            hipLaunchKernelGGL(k_shift_rows, dim3((per + 255) / 256), dim3(256), 0, st, src_i, src_w,
+                               S->d_shift_idx, S->d_shift_w, n_tok, k);
+            HIPCHK(hipGetLastError());
+            io.route_idx = S->d_shift_idx;
+            io.route_w = S->d_shift_w;
+        }
+        io.used_idx = used_idx ? used_idx + l * per : nullptr;
+        io.used_w = used_w ? used_w + l * per : nullptr;
+        if (l + 1 < S->n) {
+            io.pred_idx = pred_idx ? pred_idx + (l + 1) * per : S->d_pred_idx;
+            io.pred_w = pred_w ? pred_w + (l + 1) * per : S->d_pred_w;
+        }
+        int rc = moe_prefill(L, &io, n_tok, stream);
+        if (rc != MOE_OK) return rc;
+    }
+    return MOE_OK;
+}
+
+void moe_stack_destroy(moe_stack* S) {
+    if (!S) return;
+    if (S->d_shift_idx) (void)hipFree(S->d_shift_idx);
+    if (S->d_shift_w) (void)hipFree(S->d_shift_w);
+    if (S->d_pred_idx) (void)hipFree(S->d_pred_idx);
+    if (S->d_pred_w) (void)hipFree(S->d_pred_w);
+    delete[] S->layers;
+    delete S;
 }
 
 const char* moe_status_str(int status) {

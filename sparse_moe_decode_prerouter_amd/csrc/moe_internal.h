@@ -4,7 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/moe_prerouter.h"
+#include "moe_prerouter.h"
 
 namespace moe {
 
@@ -64,6 +64,7 @@ struct Scratch {
     int32_t* active;         // [min(E, T*k)] active experts ascending
     int32_t* act_off;        // [.. + 1] start of each active expert's assignments
     int32_t* perm;           // [T*k] assignment ids (t*k + j) sorted by (expert, id)
+    float* wsort;            // [T*k] routing weight of each sorted assignment
     float* h;                // [T*k][f] routed expert hidden (sorted order)
     float* hs;               // [T][fs] shared expert hidden
     uint16_t* hb;            // prefill: [T*k][f] bf16 hi of h (sorted order)
@@ -93,6 +94,21 @@ struct moe_layer {
     hipEvent_t ev_staged, ev_done;
     bool staged_pending, done_recorded;
     int32_t* h_readback;       // pinned [max_tokens * k]
+    // kernel timing (profiling mode)
+    bool profiling;
+    hipEvent_t ev_t[6];        // router start/end, A start/end, B start/end
+    bool ev_t_used[3];
+};
+
+struct moe_stack {
+    moe_layer** layers;
+    int n;
+    // prefill scratch: shifted routing and per-layer predictions (device)
+    int32_t* d_shift_idx;
+    float* d_shift_w;
+    int32_t* d_pred_idx;
+    float* d_pred_w;
+    size_t shift_cap;        // entries
 };
 
 // ---- kernel launchers (kernels_*.hip) -------------------------------------
@@ -154,6 +170,41 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill_gateup(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s);
+
+struct DecAArgs {
+    const void* x; int x_is_bf16; int fused; const float* gamma; float eps; int act_bf16; int d; int n_tok;
+    const int32_t* route_idx; const float* route_w;   // given routing (rows with idx < 0: self) or nullptr
+    const int32_t* self_idx; const float* self_w;     // router result for self rows, or nullptr
+    int k; int E;
+    ExpertView ev; int f; int fs;
+    const uint16_t* head; int En;
+    const uint16_t* lora_a; int r; const uint16_t* sgate_w;
+    float* h; float* hs; double* logits_h; float* au; float* sgate;
+    int32_t* meta; int32_t* active; int32_t* act_off; int32_t* perm; float* wsort;
+    int32_t* used_idx; float* used_w; int32_t* user_used_idx; float* user_used_w;
+    int32_t* err;
+    int nb_h, nb_head, nb_misc;
+};
+hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s);
+bool dec_fast_path_ok(int d, int f, int n_tok, int k);
+int dec_b_row_blocks(int d);
+hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s);
+int dec_a_blocks(int d, int f, int fs, int n_tok, int k, int E, int En, int r, bool sgate, int* nb_h, int* nb_head,
+                 int* nb_misc);
+
+struct DecBArgs {
+    ExpertView ev; int d; int f; int fs; int k; int n_tok;
+    const int32_t* meta; const int32_t* active; const int32_t* act_off; const int32_t* perm; const float* wsort;
+    const float* sgate; const float* h; const float* hs;
+    const float* x; int fused; const float* au; const uint16_t* lora_b; int r; float lora_scale;
+    float* y;
+    // head top-k (extra block)
+    const double* logits_h; int En; int kn; const float* head_bias; const float* hist_cur_m; const float* hist_prev_m;
+    const int32_t* hist_cur; const int32_t* hist_prev; int32_t* pred_idx; float* pred_w;
+    int32_t* err;
+    int nb_rows;
+};
+hipError_t launch_dec_b(const DecBArgs& a, hipStream_t s);
 
 struct SlotUpdate {
     int n;
