@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_prerouter.so")
-SOURCES = ["moe_api.hip", "kernels_decode.hip", "kernels_dec2.hip", "kernels_prefill.hip"]
+SOURCES = ["moe_api.hip", "kernels_decode.hip", "kernels_dec2.hip", "kernels_deca.hip", "kernels_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,84 +1,26 @@
-// Fused decode kernels: two launches per layer.
-//   K_A: RMSNorm prologue + routing digest + int4 gate/up GEMV with SwiGLU
-//        (routed experts and the shared expert) + prerouter head logits +
-//        LoRA A u + shared-expert gate.
+// Fused decode kernels, two launches per layer (K_A is in kernels_deca.hip):
 //   K_B: int4 down GEMV + routing-weighted combine + sigmoid-gated shared
-//        expert + LoRA B + residual; one extra block takes the head's top-k.
+//        expert + LoRA B + residual; block 0 takes the head's top-k.
 //   K_R: self-routing (router GEMV + top-k) for rows with no prediction.
 //
 // Latency structure (batch-1 decode is bound by dependent round trips, not
-// by bandwidth): every block issues all loads that do not depend on the
-// routing at kernel start, resolves the routing with one wave, issues the
-// routed expert loads, and only then computes. Block-wide barriers here wait
+// by bandwidth): loads that do not depend on the routing are issued at
+// kernel start, the routing digest is read, the routed expert rows are
+// issued, and only then is anything computed. Block-wide barriers here wait
 // for LDS traffic only (lds_barrier), so global loads stay in flight across
 // them; HIP's __syncthreads would drain them.
 // Decode sizes: n_tok <= 16 and n_tok * k <= 64.
 #include "device_common.h"
 #include "moe_internal.h"
 #include "topk.h"
+#include "dec_common.h"
 
 namespace moe {
 
-constexpr int kMaxAssign = 64;          // n_tok * k on this path
-constexpr int kInvalidExpert = 0xFFFF;
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ void lds_barrier() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS ops are done
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Token->expert digest built by wave 0: distinct experts ascending, where each
-// expert's assignments start, and assignments sorted by (expert, id). Keys
-// carry the assignment id, so they are unique and a key's rank is its slot.
-struct Digest {
-    int n_active, n_valid;
-    int active[kMaxAssign + 1];
-    int off[kMaxAssign + 1];
-    int perm[kMaxAssign];
-    int eidx[kMaxAssign];
-    float ew[kMaxAssign];
-    uint32_t sorted[kMaxAssign];
-};
 
 __device__ __forceinline__ bool row_given(const int32_t* route_idx, int t, int k) {
     return route_idx && route_idx[(size_t)t * k] >= 0;
-}
-
-// wave 0 only; `e`, `w` are this lane's merged routing entry (lane < n)
-__device__ void wave_digest(Digest& D, int n, int e, float w, bool report, int32_t* err, int E) {
-    const int lane = threadIdx.x & 63;
-    const bool in = lane < n;
-    const bool ok = in && e >= 0 && e < E;
-    if (in && !ok && report) set_err(err, ERR_BAD_INDEX);
-    const uint32_t key = in ? (((uint32_t)(ok ? e : kInvalidExpert) << 16) | (uint32_t)lane) : 0xFFFFFFFFu;
-    if (in) { D.eidx[lane] = ok ? e : -1; D.ew[lane] = w; }
-    int rank = 0;
-    for (int j = 0; j < n; ++j) rank += (uint32_t)__shfl((int)key, j, 64) < key;
-    if (in) D.sorted[rank] = key;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const uint32_t sk = in ? D.sorted[lane] : 0xFFFFFFFFu;
-    const int ep = (int)(sk >> 16);
-    const bool valid = in && ep != kInvalidExpert;
-    const int prev = __shfl_up(ep, 1, 64);
-    const bool start = valid && (lane == 0 || prev != ep);
-    const unsigned long long m = __ballot(start);
-    const unsigned long long vm = __ballot(valid);
-    if (start) {
-        const int ai = __popcll(m & ((1ull << lane) - 1ull));
-        D.active[ai] = ep;
-        D.off[ai] = lane;
-    }
-    if (valid) D.perm[lane] = (int)(sk & 0xFFFFu);
-    if (lane == 0) {
-        const int na = __popcll(m), nv = __popcll(vm);
-        D.n_active = na; D.n_valid = nv; D.off[na] = nv;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -88,7 +30,7 @@ __device__ void wave_digest(Digest& D, int n, int e, float w, bool report, int32
 // (4 dwords per 8 elements: (e_p, e_{p+4})) and per-32-chunk sums.
 // ---------------------------------------------------------------------------
 struct URegs {
-    float x[8];
+    uint32_t x[8];    // raw words: 8 fp32, or 4 bf16 pairs (converted in u_finish)
     float g[8];
 };
 
@@ -97,12 +39,10 @@ __device__ __forceinline__ void u_load(const DecAArgs& a, int t, int grp, URegs&
     if (grp * 8 >= d) return;
     if (a.x_is_bf16) {
         const u32x4 v = *(const u32x4*)((const uint16_t*)a.x + (size_t)t * d + grp * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { r.x[2 * i] = bf16_to_f32(w[i] & 0xFFFF); r.x[2 * i + 1] = bf16_to_f32(w[i] >> 16); }
+        r.x[0] = v.x; r.x[1] = v.y; r.x[2] = v.z; r.x[3] = v.w;
     } else {
-        const float4 v0 = *(const float4*)((const float*)a.x + (size_t)t * d + grp * 8);
-        const float4 v1 = *(const float4*)((const float*)a.x + (size_t)t * d + grp * 8 + 4);
+        const u32x4 v0 = *(const u32x4*)((const float*)a.x + (size_t)t * d + grp * 8);
+        const u32x4 v1 = *(const u32x4*)((const float*)a.x + (size_t)t * d + grp * 8 + 4);
         r.x[0] = v0.x; r.x[1] = v0.y; r.x[2] = v0.z; r.x[3] = v0.w;
         r.x[4] = v1.x; r.x[5] = v1.y; r.x[6] = v1.z; r.x[7] = v1.w;
     }
@@ -114,17 +54,29 @@ __device__ __forceinline__ void u_load(const DecAArgs& a, int t, int grp, URegs&
     }
 }
 
+__device__ __forceinline__ void u_values(const DecAArgs& a, const URegs& r, float (&xv)[8]) {
+    if (a.x_is_bf16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { xv[2 * i] = bf16_to_f32(r.x[i] & 0xFFFF); xv[2 * i + 1] = bf16_to_f32(r.x[i] >> 16); }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xv[i] = __uint_as_float(r.x[i]);
+    }
+}
+
 // d <= 8 * kThreads (2048): one group per thread
 __device__ void u_finish(const DecAArgs& a, int grp, const URegs& r, float* su, uint32_t* upk, uint32_t* upk_lo,
                          float* usum, float* usum_lo, double* red) {
     const int d = a.d, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool mine = grp * 8 < d;
+    float xv[8];
+    u_values(a, r, xv);
     double inv = 1.0;
     if (a.fused) {
         double ss = 0.0;
         if (mine) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ss += (double)r.x[i] * (double)r.x[i];
+            for (int i = 0; i < 8; ++i) ss += (double)xv[i] * (double)xv[i];
         }
         for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
         if (lane == 0) red[wave] = ss;
@@ -139,7 +91,7 @@ __device__ void u_finish(const DecAArgs& a, int grp, const URegs& r, float* su, 
     if (mine) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const double uv = a.fused ? ((double)r.x[i] * inv) * (double)r.g[i] : (double)r.x[i];
+            const double uv = a.fused ? ((double)xv[i] * inv) * (double)r.g[i] : (double)xv[i];
             if (a.act_bf16) { hb[i] = f64_to_bf16(uv); uf[i] = bf16_to_f32(hb[i]); }
             else { uf[i] = (float)uv; hb[i] = f32_to_bf16(uf[i]); }
         }
@@ -178,20 +130,6 @@ __device__ void u_finish(const DecAArgs& a, int grp, const URegs& r, float* su, 
     lds_barrier();
 }
 
-// sum over one 32-element chunk of (128 + q) * u, u in GEMV-ordered pairs
-__device__ __forceinline__ float chunk_dot_lds(const u32x4 w, const uint32_t* up, float acc) {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4 uv = *(const u32x4*)(up + 4 * i);
-        acc = dot2_bf16(nib_pair_bf16(ws[i], 0), uv.x, acc);
-        acc = dot2_bf16(nib_pair_bf16(ws[i], 1), uv.y, acc);
-        acc = dot2_bf16(nib_pair_bf16(ws[i], 2), uv.z, acc);
-        acc = dot2_bf16(nib_pair_bf16(ws[i], 3), uv.w, acc);
-    }
-    return acc;
-}
-
 // bf16 row (d elements) dot fp32 u in LDS, fp64 accumulation; lane covers
 // elements lane*8 + 512*m
 template <int NLD>
@@ -226,181 +164,7 @@ __device__ __forceinline__ void bf16_row_load(u32x4 (&wr)[NLD], const uint16_t* 
     }
 }
 
-constexpr int kHRowsPerBlock = 8;     // h rows (gate row + up row) per K_A block: 2 per wave
-constexpr int kHeadRowsPerBlock = 4;  // bf16 rows per K_A block: 1 per wave
-
-// K_A (d <= 2048: one 16-byte chunk per lane and weight row)
-__global__ void __launch_bounds__(kThreads) k_dec_a(DecAArgs a) {
-    constexpr int kNld = 4;
-    extern __shared__ __align__(16) uint8_t lds[];
-    __shared__ Digest D;
-    __shared__ double red[kWaves];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int d = a.d;
-    const int n_assign = a.n_tok * a.k;
-    const bool role_h = (int)blockIdx.x < a.nb_h;
-    const bool role_head = !role_h && (int)blockIdx.x < a.nb_h + a.nb_head;
-
-    // ---- level 0: loads that need no routing. The routing loads go first:
-    // the memory counter is in order, so waiting for them must not also wait
-    // for the activation and weight loads issued after them.
-    int me = -1; float mw = 0.f;
-    if (role_h && wave == 0) {
-        int vr = -1, vs = -1;
-        float vrw = 0.f, vsw = 0.f;
-        if (lane < n_assign) {
-            if (a.route_idx) { vr = a.route_idx[lane]; vrw = a.route_w[lane]; }
-            if (a.self_idx) { vs = a.self_idx[lane]; vsw = a.self_w[lane]; }
-        }
-        const int first = __shfl(vr, (lane / a.k) * a.k, 64);   // first entry of this lane's row
-        const bool given = a.route_idx && first >= 0;
-        me = given ? vr : vs;
-        mw = given ? vrw : vsw;
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    URegs ur;
-    u_load(a, 0, tid, ur);
-
-    if (role_h) {
-        const int u0 = blockIdx.x * kHRowsPerBlock;
-        const bool shared = u0 < a.fs;
-        const int f = shared ? a.fs : a.f;
-        const int row0 = shared ? u0 : (u0 - a.fs) % a.f;
-        const int slot = shared ? -1 : (u0 - a.fs) / a.f;
-        const BlobLayout L = BlobLayout::make(d, f);
-        const int LPR = d / 32;                     // lanes per row (<= 64)
-        const int RPW = 64 / LPR;                   // rows per wave-load
-        const int hw = kHRowsPerBlock / kWaves;     // h rows per wave (2)
-        const int rsub = lane / LPR, c0 = lane % LPR;
-        u32x4 wg[2], wu[2];
-        uint32_t sg[2], su[2];
-        bool rv[2];
-        int rrow[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int hr = q * RPW + rsub;
-            rrow[q] = row0 + wave * hw + hr;
-            rv[q] = hr < hw && (q == 0 || RPW < hw) && rrow[q] < f;
-        }
-        const uint8_t* blob = nullptr;
-        auto issue = [&]() {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                if (rv[q] && blob) {
-                    const size_t row = rrow[q];
-                    wg[q] = __builtin_nontemporal_load((const u32x4*)(blob + L.gate_q + row * (d / 2) + c0 * 16));
-                    wu[q] = __builtin_nontemporal_load((const u32x4*)(blob + L.up_q + row * (d / 2) + c0 * 16));
-                    sg[q] = __builtin_nontemporal_load((const uint32_t*)(blob + L.gate_sb + (row * (d / 64) + c0 / 2) * 4));
-                    su[q] = __builtin_nontemporal_load((const uint32_t*)(blob + L.up_sb + (row * (d / 64) + c0 / 2) * 4));
-                }
-            }
-        };
-        if (shared) {
-            blob = a.ev.shared;
-            if (blob && a.ev.shared_tag && *a.ev.shared_tag != a.ev.E) {
-                if (tid == 0) set_err(a.err, ERR_NOT_STAGED);
-                blob = nullptr;
-            }
-            issue();
-        }
-        // ---- level 1: routing digest (wave 0), then the routed expert's rows
-        if (wave == 0 && (!shared || blockIdx.x == 0)) wave_digest(D, n_assign, me, mw, blockIdx.x == 0, a.err, a.E);
-        lds_barrier();
-        int pos0 = 0, pos1 = a.n_tok;
-        if (!shared) {
-            if (slot >= D.n_active) return;
-            const int e = D.active[slot];
-            pos0 = D.off[slot]; pos1 = D.off[slot + 1];
-            if (!a.ev.slot_of) blob = a.ev.base + (size_t)e * a.ev.blob;
-            else {
-                const int s = a.ev.slot_of[e];
-                if (s < 0 || (a.ev.slot_tag && a.ev.slot_tag[s] != e)) {
-                    if (tid == 0) set_err(a.err, ERR_NOT_STAGED);
-                    blob = nullptr;
-                } else blob = a.ev.base + (size_t)s * a.ev.blob;
-            }
-            issue();
-        }
-        if (blockIdx.x == 0) {
-            for (int i = tid; i < n_assign; i += kThreads) {
-                a.used_idx[i] = D.eidx[i];
-                a.used_w[i] = D.ew[i];
-                if (a.user_used_idx) a.user_used_idx[i] = D.eidx[i];
-                if (a.user_used_w) a.user_used_w[i] = D.ew[i];
-            }
-            for (int i = tid; i < D.n_active; i += kThreads) { a.active[i] = D.active[i]; a.act_off[i] = D.off[i]; }
-            for (int i = tid; i < D.n_valid; i += kThreads) { a.perm[i] = D.perm[i]; a.wsort[i] = D.ew[D.perm[i]]; }
-            if (tid == 0) { a.meta[0] = D.n_active; a.meta[1] = D.n_valid; a.act_off[D.n_active] = D.n_valid; }
-        }
-        // ---- activations and dot products
-        uint32_t* upk = (uint32_t*)lds;                                     // [d/2]
-        uint32_t* upk_lo = a.act_bf16 ? nullptr : upk + d / 2;              // [d/2]
-        float* us = (float*)(lds + (a.act_bf16 ? (size_t)d * 2 : (size_t)d * 4));   // [d/32]
-        float* us_lo = a.act_bf16 ? nullptr : us + d / 32;
-        int t_loaded = 0;
-        for (int pi = pos0; pi < pos1; ++pi) {
-            const int t = shared ? pi : D.perm[pi] / a.k;
-            if (t != t_loaded) { u_load(a, t, tid, ur); t_loaded = t; }
-            u_finish(a, tid, ur, nullptr, upk, upk_lo, us, us_lo, red);
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                float ga = 0.f, ua = 0.f;
-                if (rv[q] && blob) {
-                    float accg = chunk_dot_lds(wg[q], upk + c0 * 16, 0.f);
-                    float accu = chunk_dot_lds(wu[q], upk + c0 * 16, 0.f);
-                    float usm = us[c0];
-                    if (upk_lo) {
-                        accg = chunk_dot_lds(wg[q], upk_lo + c0 * 16, accg);
-                        accu = chunk_dot_lds(wu[q], upk_lo + c0 * 16, accu);
-                        usm += us_lo[c0];
-                    }
-                    const float s1 = f16_to_f32(sg[q] & 0xFFFF), b1 = f16_to_f32(sg[q] >> 16);
-                    const float s2 = f16_to_f32(su[q] & 0xFFFF), b2 = f16_to_f32(su[q] >> 16);
-                    ga = s1 * accg + (b1 - 128.f * s1) * usm;
-                    ua = s2 * accu + (b2 - 128.f * s2) * usm;
-                }
-                ga = group_sum(ga, LPR);
-                ua = group_sum(ua, LPR);
-                if (rv[q] && c0 == 0) {
-                    const float hv = blob ? silu_f32(ga) * ua : 0.f;
-                    if (shared) a.hs[(size_t)t * f + rrow[q]] = hv;
-                    else a.h[(size_t)pi * f + rrow[q]] = hv;
-                }
-            }
-            lds_barrier();   // LDS u is rewritten for the next token
-        }
-        return;
-    }
-
-    // ---- bf16 rows accumulated in fp64: head rows, or LoRA A rows + shared gate
-    int row0, nrows;
-    if (role_head) { row0 = (blockIdx.x - a.nb_h) * kHeadRowsPerBlock; nrows = a.En; }
-    else {
-        row0 = (blockIdx.x - a.nb_h - a.nb_head) * kHeadRowsPerBlock;
-        nrows = (a.lora_a ? a.r : 0) + (a.sgate_w ? 1 : 0);
-    }
-    const int row = row0 + wave;
-    const bool valid = row < nrows;
-    const uint16_t* w = nullptr;
-    if (valid) {
-        if (role_head) w = a.head + (size_t)row * d;
-        else w = (a.lora_a && row < a.r) ? a.lora_a + (size_t)row * d : a.sgate_w;
-    }
-    u32x4 wr[kNld];
-    bf16_row_load<kNld>(wr, w, d, valid);
-    float* suf = (float*)lds;
-    for (int t = 0; t < a.n_tok; ++t) {
-        if (t > 0) u_load(a, t, tid, ur);
-        u_finish(a, tid, ur, suf, nullptr, nullptr, nullptr, nullptr, red);
-        const double acc = bf16_row_dot<kNld>(wr, suf, d, valid);
-        if (valid && lane == 0) {
-            if (role_head) a.logits_h[(size_t)t * a.En + row] = acc;
-            else if (a.lora_a && row < a.r) a.au[(size_t)t * a.r + row] = (float)acc;
-            else a.sgate[t] = (float)(1.0 / (1.0 + exp(-acc)));
-        }
-        lds_barrier();
-    }
-}
+constexpr int kHeadRowsPerBlock = 4;  // router rows per K_R block: 1 per wave
 
 // ---------------------------------------------------------------------------
 // K_R: self-routing for rows with no prediction: RMSNorm prologue + router
@@ -449,216 +213,274 @@ hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s) {
     return hipGetLastError();
 }
 
-int dec_a_blocks(int d, int f, int fs, int n_tok, int k, int E, int En, int r, bool sgate, int* nb_h, int* nb_head,
-                 int* nb_misc) {
-    const int max_active = n_tok * k < E ? n_tok * k : E;
-    *nb_h = (fs + max_active * f + kHRowsPerBlock - 1) / kHRowsPerBlock;
-    *nb_head = (En + kHeadRowsPerBlock - 1) / kHeadRowsPerBlock;
-    *nb_misc = (r + (sgate ? 1 : 0) + kHeadRowsPerBlock - 1) / kHeadRowsPerBlock;
-    (void)d;
-    return *nb_h + *nb_head + *nb_misc;
-}
-
-hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s) {
-    if (a.d > 2048 || a.n_tok * a.k > kMaxAssign) return hipErrorInvalidValue;
-    const size_t d = a.d;
-    const size_t lds_h = (a.act_bf16 ? d * 2 : d * 4) + (a.act_bf16 ? d / 32 * 4 : d / 16 * 4);
-    const size_t lds = lds_h > d * 4 ? lds_h : d * 4;
-    const int nb = a.nb_h + a.nb_head + a.nb_misc;
-    hipLaunchKernelGGL(k_dec_a, dim3(nb), dim3(kThreads), lds, s, a);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
-// K_B: each block owns 4 output rows. Slot s (shared expert first, then the
-// active experts ascending) is handled by wave s % 4, which computes Wd h for
-// the block's 4 rows and every token of the slot into an LDS partial; the
-// partials are then summed per (token, row) in slot order (fixed order, so
-// results are identical run to run) with LoRA B and the residual.
+// K_B: int4 down GEMV + combine. Block 0 takes the head's top-k (it is
+// dispatched first, so it overlaps the rest); every other block owns RB
+// consecutive output rows.
+//
+// Lane layout (F = d_ff): a Wd row holds F/2 bytes of packed int4, i.e.
+// LPR = F/8 dwords; lane c of a row group owns dword c, so it needs h
+// elements [8c, 8c+8) only (no lane loads h it does not use). RPP = 64/LPR
+// rows are covered per pass and kPassB passes per block: RB = kPassB * RPP.
+// Each wave runs the routed experts s = wave, wave + 4, ... and kPassB/4 of
+// the shared expert's passes, so all four waves do the same program: every
+// wave reads the routing digest itself (no cross-wave wait) and all loads
+// that need no routing are issued before the digest is consumed.
+// Partial sums go to LDS indexed by assignment id (t*k + j) or shared
+// token, and each (token, row) output sums them in routing order, so the
+// result does not depend on how slots are spread over waves.
 // ---------------------------------------------------------------------------
-constexpr int kRowsB = 4;
-constexpr int kMaxSlotsB = kMaxAssign + 1;
+constexpr int kPassB = 8;
 constexpr int kMaxTokB = 16;
 
-struct BSlots {
-    int n_active, nslots;
-    int active[kMaxAssign + 1];
-    int off[kMaxAssign + 1];
-    int perm[kMaxAssign];
-    float w[kMaxAssign];
+template <int F>
+struct BGeo {
+    static constexpr int LPR = F / 8;
+    static constexpr int RPP = 64 / LPR;
+    static constexpr int RB = kPassB * RPP;
 };
 
-// f <= 2048: one 16-byte chunk per lane and Wd row
-__global__ void __launch_bounds__(kThreads) k_dec_b(DecBArgs a) {
-    __shared__ BSlots S;
-    __shared__ float part[kMaxSlotsB * kMaxTokB * kRowsB];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if ((int)blockIdx.x == a.nb_rows) {
+// LoRA B row (r bf16) . LoRA A output row (r fp32): the loads are issued
+// together up front and the products summed later, in q order.
+constexpr int kLoraChunks = 2;                // r <= 16, r % 8 == 0
+struct LoraRegs {
+    u32x4 b[kLoraChunks];
+    float4 u[2 * kLoraChunks];
+};
+__device__ __forceinline__ void lora_issue(LoraRegs& R, const uint16_t* brow, const float* urow, int r) {
+#pragma unroll
+    for (int c = 0; c < kLoraChunks; ++c) {
+        const int cc = 8 * c < r ? c : 0;
+        R.b[c] = *(const u32x4*)(brow + 8 * cc);
+        R.u[2 * c] = *(const float4*)(urow + 8 * cc);
+        R.u[2 * c + 1] = *(const float4*)(urow + 8 * cc + 4);
+    }
+}
+__device__ __forceinline__ float lora_dot(const LoraRegs& R, int r) {
+    float l = 0.f;
+#pragma unroll
+    for (int c = 0; c < kLoraChunks; ++c) {
+        if (8 * c < r) {
+            const uint32_t bw[4] = {R.b[c].x, R.b[c].y, R.b[c].z, R.b[c].w};
+            const float uu[8] = {R.u[2 * c].x, R.u[2 * c].y, R.u[2 * c].z, R.u[2 * c].w,
+                                 R.u[2 * c + 1].x, R.u[2 * c + 1].y, R.u[2 * c + 1].z, R.u[2 * c + 1].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                l += bf16_to_f32(bw[i] & 0xFFFF) * uu[2 * i];
+                l += bf16_to_f32(bw[i] >> 16) * uu[2 * i + 1];
+            }
+        }
+    }
+    return l;
+}
+
+// One expert's Wd rows for this lane: NP passes of (dword of int4, (s,b)).
+template <int NP>
+struct DownRegs {
+    uint32_t q[NP];
+    uint32_t sb[NP];
+};
+
+// Rows row_first + i * STEP, i < NP: one base address, compile-time offsets.
+template <int F, int NP, int STEP>
+__device__ __forceinline__ void down_issue(DownRegs<NP>& R, const uint8_t* blob, const BlobLayout& L, int row_first) {
+    using G = BGeo<F>;
+    const int lane = threadIdx.x & 63, c = lane % G::LPR;
+    const uint32_t* q = (const uint32_t*)(blob + L.down_q) + (size_t)row_first * (F / 8) + c;
+    const uint32_t* sb = (const uint32_t*)(blob + L.down_sb) + (size_t)row_first * (F / 64) + c / 8;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        R.q[i] = __builtin_nontemporal_load(q + i * STEP * (F / 8));
+        R.sb[i] = __builtin_nontemporal_load(sb + i * STEP * (F / 64));
+    }
+}
+
+__device__ __forceinline__ void h_issue(float4 (&hv)[2], const float* hrow, int c) {
+    hv[0] = *(const float4*)(hrow + 8 * c);
+    hv[1] = *(const float4*)(hrow + 8 * c + 4);
+}
+
+// Per-lane partial of each pass: sum_j (s q_j + b) h_j over the lane's 8 elements.
+template <int NP>
+__device__ __forceinline__ void down_partial(const DownRegs<NP>& R, const float4 (&hv)[2], float (&o)[NP]) {
+    const float h[8] = {hv[0].x, hv[0].y, hv[0].z, hv[0].w, hv[1].x, hv[1].y, hv[1].z, hv[1].w};
+    float hs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hs += h[j];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += (float)((R.q[i] >> (4 * j)) & 0xFu) * h[j];
+        o[i] = f16_to_f32(R.sb[i] & 0xFFFF) * acc + f16_to_f32(R.sb[i] >> 16) * hs;
+    }
+}
+
+template <int F>
+__global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
+    using G = BGeo<F>;
+    constexpr int NPS = kPassB / kWaves;           // shared-expert passes per wave
+    __shared__ float part[(kMaxAssign + kMaxTokB) * G::RB];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (blockIdx.x == 0) {
         if (a.pred_idx)
             topk_rows(false, a.logits_h, a.En, a.kn, a.n_tok, a.head_bias, a.hist_cur_m, a.hist_cur, a.hist_prev_m,
                       a.hist_prev, nullptr, a.kn, a.pred_idx, a.pred_w);
         return;
     }
-    const int d = a.d, f = a.f, n_tok = a.n_tok;
-    const int n_assign = n_tok * a.k;
-    const int row_base = blockIdx.x * kRowsB;
-    const int has_shared = a.fs ? 1 : 0;
-    const BlobLayout L = BlobLayout::make(d, f);
-    const int LPR = f / 32;                       // lanes per Wd row (<= 64)
-    const int g = lane / LPR, c0 = lane % LPR;
+    const int d = a.d, n_tok = a.n_tok, k = a.k;
+    const int n_assign = n_tok * k;
+    const int row0 = (blockIdx.x - 1) * G::RB;
+    const bool has_shared = a.fs != 0;
+    const BlobLayout L = BlobLayout::make(d, F);
+    const int c = lane % G::LPR, rsub = lane / G::LPR;
 
-    // ---- level 0: routing digest from K_A (no dependent loads), epilogue
-    // operands, the shared expert's rows and hidden state
-    int v_meta = 0, v_act = 0, v_off = 0, v_perm = 0;
-    float v_w = 0.f;
-    const int nas = n_assign < a.ev.E ? n_assign : a.ev.E;   // entries of active/act_off in use
-    if (wave == 0) {
-        v_meta = a.meta[0];
-        if (lane <= nas) { v_act = a.active[lane < nas ? lane : 0]; v_off = a.act_off[lane]; }
-        if (lane < n_assign) { v_perm = a.perm[lane]; v_w = a.wsort[lane]; }
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const int et = tid / kRowsB, er = tid % kRowsB, erow = row_base + er;
-    const bool ep_on = et < n_tok && erow < d;
-    float ep_x = 0.f, ep_l = 0.f;
-    if (ep_on) {
-        if (a.fused) ep_x = a.x[(size_t)et * d + erow];
-        if (a.lora_b && a.r) {
-            float l = 0.f;
-            for (int q = 0; q < a.r; ++q) l += bf16_to_f32(a.lora_b[(size_t)erow * a.r + q]) * a.au[(size_t)et * a.r + q];
-            ep_l = a.lora_scale * l;
-        }
-    }
-    const int grow = row_base + g;                // each LPR-lane group owns one of the 4 rows
-    const bool rvalid = g < kRowsB && grow < d;
-    const uint8_t* sh_blob = nullptr;
-    if (has_shared) {
-        sh_blob = a.ev.shared;
-        if (sh_blob && a.ev.shared_tag && *a.ev.shared_tag != a.ev.E) sh_blob = nullptr;
-    }
-    struct SlotPrep {
-        int s, p0, p1;
-        bool on, sh, hpre;
-        const uint8_t* blob;
-        u32x4 wd;
-        uint32_t sbv;
-        float4 hv[8];
-    };
-    auto load_rows = [&](SlotPrep& P) {
-        if (rvalid && P.blob) {
-            P.wd = __builtin_nontemporal_load((const u32x4*)(P.blob + L.down_q + (size_t)grow * (f / 2) + c0 * 16));
-            P.sbv = __builtin_nontemporal_load((const uint32_t*)(P.blob + L.down_sb + ((size_t)grow * (f / 64) + c0 / 2) * 4));
-        }
-        P.hpre = P.p1 - P.p0 == 1;
-        if (P.hpre && rvalid && P.blob) {
-            const float* hrow = P.sh ? a.hs + (size_t)P.p0 * f : a.h + (size_t)P.p0 * f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) P.hv[i] = *(const float4*)(hrow + 32 * c0 + 4 * i);
-        }
-    };
-    SlotPrep shp{};
-    shp.on = has_shared && wave == 0;
-    if (shp.on) {
-        shp.s = 0; shp.p0 = 0; shp.p1 = n_tok; shp.sh = true; shp.blob = sh_blob;
-        load_rows(shp);
-    }
-    if (wave == 0) {
-        if (lane <= nas) { S.active[lane] = v_act; S.off[lane] = v_off; }
-        // entries at or beyond n_valid were not written by K_A (invalid routing
-        // indices): keep any index read from them inside [0, n_assign)
-        if (lane < n_assign) {
-            S.perm[lane] = v_perm < 0 ? 0 : (v_perm >= n_assign ? n_assign - 1 : v_perm);
-            S.w[lane] = v_w;
-        }
-        if (lane == 0) { S.n_active = v_meta; S.nslots = v_meta + has_shared; }
-    }
+    // ---- level 0, identical in every wave. The digest loads go first; all
+    // other loads need no routing and are issued unconditionally (clamped
+    // indices, a stand-in blob when there is none), so waiting for the
+    // digest never waits for them.
+    const int n_active = a.meta[0];
+    const int n_valid = a.meta[1];
+    const int v_act = a.active[lane];
+    const int v_off = a.act_off[lane];
+    const int v_perm = a.perm[lane];
+    const float v_w = a.wsort[lane];
+    const float v_sg = (a.sgate ? a.sgate : a.wsort)[lane < n_tok ? lane : 0];
+    // epilogue operands: thread -> (token, row)
+    const int ep_n = n_tok * G::RB;
+    const int ep_q = tid < ep_n ? tid : 0;
+    const int et = ep_q / G::RB, er = ep_q % G::RB;
+    const float ep_x = a.fused ? a.x[(size_t)et * d + row0 + er] : 0.f;
+    const bool lora_on = a.lora_b && a.r;
+    const bool lora_vec = lora_on && (a.r & 7) == 0 && a.r <= 8 * kLoraChunks;
+    LoraRegs lr;
+    if (lora_vec) lora_issue(lr, a.lora_b + (size_t)(row0 + er) * a.r, a.au + (size_t)et * a.r, a.r);
+    // shared expert: passes [NPS*wave, NPS*wave + NPS), token 0's hidden state
+    const uint8_t* sh_blob = has_shared && a.ev.shared ? a.ev.shared : a.ev.base;
+    DownRegs<NPS> shr;
+    down_issue<F, NPS, G::RPP>(shr, sh_blob, L, row0 + NPS * wave * G::RPP + rsub);
+    const int sh_tag = *(a.ev.shared_tag ? a.ev.shared_tag : a.meta);
+    const bool sh_ok = has_shared && a.ev.shared && (!a.ev.shared_tag || sh_tag == a.ev.E);
+    float4 shh[2];
+    h_issue(shh, has_shared ? a.hs : a.h, c);
+    // zero the partials: entries of invalid assignments are never written
+    for (int i = tid; i < (n_assign + n_tok) * G::RB; i += kThreads) part[i] = 0.f;
     lds_barrier();
-    const int nslots = S.nslots;
-    auto resolve = [&](SlotPrep& P, int s) {
-        P.s = s;
-        P.on = s < nslots;
-        P.sh = false;
-        if (!P.on) return;
-        const int ai = s - has_shared;
-        const int e = S.active[ai];
-        P.p0 = S.off[ai]; P.p1 = S.off[ai + 1];
-        if (!a.ev.slot_of) P.blob = a.ev.base + (size_t)e * a.ev.blob;
-        else {
-            const int sl = a.ev.slot_of[e];
-            P.blob = (sl < 0 || (a.ev.slot_tag && a.ev.slot_tag[sl] != e)) ? nullptr : a.ev.base + (size_t)sl * a.ev.blob;
-        }
-        load_rows(P);
+
+    // ---- level 1: routed experts, two slots in flight per wave. The first
+    // pair is issued before the shared expert is computed (its loads are the
+    // oldest, so waiting for them does not wait for the routed rows).
+    auto blob_of = [&](int s) -> const uint8_t* {
+        if (s >= n_active) return nullptr;
+        const int e = __builtin_amdgcn_readlane(v_act, s);
+        if (!a.ev.slot_of) return a.ev.base + (size_t)e * a.ev.blob;
+        const int sl = a.ev.slot_of[e];
+        if (sl < 0 || (a.ev.slot_tag && a.ev.slot_tag[sl] != e)) return nullptr;
+        return a.ev.base + (size_t)sl * a.ev.blob;
     };
-    auto compute = [&](SlotPrep& P) {
-        if (!P.on) return;
-        if (lane < n_tok * kRowsB) part[(P.s * kMaxTokB + lane / kRowsB) * kRowsB + lane % kRowsB] = 0.f;
-        for (int p = P.p0; p < P.p1; ++p) {
-            int t; float wgt;
-            if (P.sh) { t = p; wgt = a.sgate ? a.sgate[t] : 1.f; }
-            else { t = S.perm[p] / a.k; wgt = S.w[p]; }
-            float o = 0.f;
-            if (rvalid && P.blob) {
-                float4 hv4[8];
-                if (P.hpre) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) hv4[i] = P.hv[i];
-                } else {
-                    const float* hrow = P.sh ? a.hs + (size_t)p * f : a.h + (size_t)p * f;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) hv4[i] = *(const float4*)(hrow + 32 * c0 + 4 * i);
-                }
-                const uint32_t ws[4] = {P.wd.x, P.wd.y, P.wd.z, P.wd.w};
-                float accq = 0.f, hsum = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float hv[8] = {hv4[2 * i].x, hv4[2 * i].y, hv4[2 * i].z, hv4[2 * i].w,
-                                         hv4[2 * i + 1].x, hv4[2 * i + 1].y, hv4[2 * i + 1].z, hv4[2 * i + 1].w};
-#pragma unroll
-                    for (int n = 0; n < 8; ++n) {
-                        accq += (float)((ws[i] >> (4 * n)) & 0xFu) * hv[n];
-                        hsum += hv[n];
-                    }
-                }
-                o = f16_to_f32(P.sbv & 0xFFFF) * accq + f16_to_f32(P.sbv >> 16) * hsum;
+    auto slot_compute = [&](const DownRegs<kPassB>& R, const uint8_t* blob, int s, const float4 (&h0)[2]) {
+        const int p0 = __builtin_amdgcn_readlane(v_off, s);
+        const int p1 = s + 1 < n_active ? __builtin_amdgcn_readlane(v_off, s + 1) : n_valid;
+        for (int p = p0; p < p1; ++p) {
+            float4 hv[2];
+            if (p == p0) { hv[0] = h0[0]; hv[1] = h0[1]; }
+            else h_issue(hv, a.h + (size_t)p * F, c);
+            float o[kPassB];
+            down_partial<kPassB>(R, hv, o);
+            int pass;
+            const float tot = row_reduce<float, kPassB, G::LPR>(o, &pass);
+            const int aid = __builtin_amdgcn_readlane(v_perm, p);
+            const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_w), p));
+            if (blob && (c % (G::LPR / kPassB)) == 0 && aid >= 0 && aid < n_assign)
+                part[aid * G::RB + pass * G::RPP + rsub] = wgt * tot;
+        }
+    };
+    auto pair_issue = [&](int s0, DownRegs<kPassB>& R0, DownRegs<kPassB>& R1, float4 (&h0)[2], float4 (&h1)[2],
+                          const uint8_t*& b0, const uint8_t*& b1) {
+        const int s1 = s0 + kWaves;
+        b0 = blob_of(s0);
+        b1 = blob_of(s1);
+        down_issue<F, kPassB, G::RPP>(R0, b0 ? b0 : a.ev.base, L, row0 + rsub);
+        down_issue<F, kPassB, G::RPP>(R1, b1 ? b1 : a.ev.base, L, row0 + rsub);
+        const int q0 = s0 < n_active ? __builtin_amdgcn_readlane(v_off, s0) : 0;
+        const int q1 = s1 < n_active ? __builtin_amdgcn_readlane(v_off, s1) : 0;
+        h_issue(h0, a.h + (size_t)q0 * F, c);
+        h_issue(h1, a.h + (size_t)q1 * F, c);
+    };
+    {
+        DownRegs<kPassB> R0, R1;
+        float4 h0[2], h1[2];
+        const uint8_t *b0, *b1;
+        pair_issue(wave, R0, R1, h0, h1, b0, b1);
+        if (has_shared) {
+            for (int t = 0; t < n_tok; ++t) {
+                float4 hv[2];
+                if (t == 0) { hv[0] = shh[0]; hv[1] = shh[1]; }
+                else h_issue(hv, a.hs + (size_t)t * F, c);
+                float o[NPS];
+                down_partial<NPS>(shr, hv, o);
+                int pass;
+                const float tot = row_reduce<float, NPS, G::LPR>(o, &pass);
+                const float wgt = a.sgate ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_sg), t)) : 1.f;
+                if (sh_ok && (c % (G::LPR / NPS)) == 0)
+                    part[(n_assign + t) * G::RB + (NPS * wave + pass) * G::RPP + rsub] = wgt * tot;
             }
-            o = group_sum(o, LPR);
-            if (g < kRowsB && c0 == 0 && P.blob) part[(P.s * kMaxTokB + t) * kRowsB + g] = wgt * o;
         }
-    };
-    // ---- level 1: each wave's slots, two at a time with all their loads in flight
-    // (slot 0 is the shared expert when present; it was prepared at level 0)
-    for (int s0 = wave; s0 < nslots; s0 += 2 * kWaves) {
-        SlotPrep A{}, Bp{};
-        if (has_shared && s0 == 0) A = shp;
-        else resolve(A, s0);
-        resolve(Bp, s0 + kWaves);
-        compute(A);
-        compute(Bp);
+        if (wave < n_active) slot_compute(R0, b0, wave, h0);
+        if (wave + kWaves < n_active) slot_compute(R1, b1, wave + kWaves, h1);
+    }
+    for (int s0 = wave + 2 * kWaves; s0 < n_active; s0 += 2 * kWaves) {
+        DownRegs<kPassB> R0, R1;
+        float4 h0[2], h1[2];
+        const uint8_t *b0, *b1;
+        pair_issue(s0, R0, R1, h0, h1, b0, b1);
+        slot_compute(R0, b0, s0, h0);
+        if (s0 + kWaves < n_active) slot_compute(R1, b1, s0 + kWaves, h1);
     }
     lds_barrier();
-    if (ep_on) {
-        float y = 0.f;
-        for (int s = 0; s < nslots; ++s) y += part[(s * kMaxTokB + et) * kRowsB + er];
-        y += ep_l;
-        if (a.fused) y = ep_x + y;
-        a.y[(size_t)et * d + erow] = y;
+
+    // ---- epilogue: shared, then routed in routing order, LoRA B, residual
+    if (tid < ep_n) {
+        float y = has_shared ? part[(n_assign + et) * G::RB + er] : 0.f;
+        for (int j = 0; j < k; ++j) y += part[(et * k + j) * G::RB + er];
+        if (lora_on) {
+            float l = 0.f;
+            if (lora_vec) l = lora_dot(lr, a.r);
+            else
+                for (int q = 0; q < a.r; ++q)
+                    l += bf16_to_f32(a.lora_b[(size_t)(row0 + er) * a.r + q]) * a.au[(size_t)et * a.r + q];
+            y += a.lora_scale * l;
+        }
+        if (a.fused) y += ep_x;
+        a.y[(size_t)et * d + row0 + er] = y;
     }
 }
 
+int dec_b_rows_per_block(int f) { return kPassB * (64 / (f / 8)); }
+
 hipError_t launch_dec_b(const DecBArgs& a, hipStream_t s) {
-    if (a.n_tok > kMaxTokB || a.n_tok * a.k > kMaxAssign || a.f > 512) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_dec_b, dim3(a.nb_rows + 1), dim3(kThreads), 0, s, a);
+    if (a.n_tok > kMaxTokB || a.n_tok * a.k > kMaxAssign || (a.fs && a.fs != a.f)) return hipErrorInvalidValue;
+    const int rb = dec_b_rows_per_block(a.f);
+    if (a.d % rb || a.n_tok * rb > kThreads) return hipErrorInvalidValue;
+    const dim3 grid(1 + a.d / rb), block(kThreads);
+    switch (a.f) {
+        case 64: hipLaunchKernelGGL(k_dec_b<64>, grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL(k_dec_b<128>, grid, block, 0, s, a); break;
+        case 256: hipLaunchKernelGGL(k_dec_b<256>, grid, block, 0, s, a); break;
+        case 512: hipLaunchKernelGGL(k_dec_b<512>, grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
-}  // namespace moe
-
-namespace moe {
-int dec_b_row_blocks(int d) { return (d + kRowsB - 1) / kRowsB; }
-
-bool dec_fast_path_ok(int d, int f, int n_tok, int k) {
+bool dec_fast_path_ok(int d, int f, int fs, int n_tok, int k) {
     const bool dpow = d >= 256 && d <= 2048 && (d & (d - 1)) == 0;
     const bool fpow = f >= 64 && f <= 512 && (f & (f - 1)) == 0;
-    return dpow && fpow && n_tok <= kMaxTokB && n_tok * k <= kMaxAssign;
+    if (!dpow || !fpow || (fs && fs != f)) return false;
+    const int rb = dec_b_rows_per_block(f), ra = dec_a_hrows_per_block(d);
+    return d % rb == 0 && f % ra == 0 && fs % ra == 0 && n_tok <= kMaxTokB && n_tok * k <= kMaxAssign &&
+           n_tok * rb <= kThreads;
 }
+
 }  // namespace moe

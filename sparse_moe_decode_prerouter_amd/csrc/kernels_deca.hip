@@ -1,0 +1,427 @@
+// K_A of the fused decode path: RMSNorm prologue + routing digest + int4
+// gate/up GEMV with SwiGLU (routed experts and the shared expert) +
+// prerouter head logits + LoRA A u + shared-expert gate, in one launch.
+//
+// A block (4 waves) computes the block input u of a token once: thread g
+// owns elements [8g, 8g+8), the RMSNorm sum of squares is reduced in fp64
+// over the block, and u, rounded once to the activation dtype, goes to LDS
+// in the layout the dot products read without bank conflicts. Each wave then
+// multiplies its weight rows: a lane owns one 32-element chunk of a row
+// (LPR = d/32 lanes per row), i.e. 16 bytes of packed int4 or 64 bytes of a
+// bf16 row.
+//
+// Latency: every load that needs no routing (routing entries, x, gamma, the
+// shared expert's rows, the bf16 rows) is issued at kernel start, without
+// branches around it, so the compiler's in-order wait counts stay exact; each
+// routed wave sorts the routing itself (registers + its own LDS slice) and
+// issues its expert's rows before u is computed.
+#include "device_common.h"
+#include "moe_internal.h"
+#include "dec_common.h"
+
+namespace moe {
+
+constexpr int kAPass = 2;                 // int4 h-row passes per wave
+constexpr int kABPass = 1;                // bf16-row passes per wave
+
+template <int D>
+struct AGeo {
+    static constexpr int LPR = D / 32;    // lanes per weight row
+    static constexpr int RPW = 64 / LPR;  // rows per pass
+    static constexpr int HROWS = kWaves * kAPass * RPW;    // h rows per block
+    static constexpr int BROWS = kWaves * kABPass * RPW;   // bf16 rows per block
+    static constexpr int C = D / 32;      // 32-element chunks
+};
+
+int dec_a_hrows_per_block(int d) { return kWaves * kAPass * (64 / (d / 32)); }
+int dec_a_brows_per_block(int d) { return kWaves * kABPass * (64 / (d / 32)); }
+
+// ---- block input u in LDS -------------------------------------------------
+// pk: [4 pieces][C chunks][4 dwords] bf16 pairs in GEMV order: dword p of
+//     piece i of chunk c is (e_{32c+8i+p}, e_{32c+8i+p+4}); lane c reads
+//     piece i of its chunk at step i, consecutive lanes at consecutive 16 B.
+// pk_lo: same for the lo part (f32 activations).
+// uf: [8 pieces][C chunks][4 floats] activation values.
+// usum, usum_lo: [C] chunk sums of the hi / lo parts.
+template <int D>
+struct ULds {
+    uint32_t pk[4 * D / 8];
+    uint32_t pk_lo[4 * D / 8];
+    float uf[D];
+    float usum[D / 32], usum_lo[D / 32];
+    double red[kWaves];
+};
+
+struct XThread {
+    uint32_t w[8];      // 8 fp32 words, or 4 bf16 pairs
+    float g[8];
+};
+
+template <bool XB>
+__device__ __forceinline__ void x_issue(const DecAArgs& a, int t, int e0, uint32_t (&w)[8]) {
+    if (XB) {
+        const u32x4 v = *(const u32x4*)((const uint16_t*)a.x + (size_t)t * a.d + e0);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+        const u32x4 v0 = *(const u32x4*)((const float*)a.x + (size_t)t * a.d + e0);
+        const u32x4 v1 = *(const u32x4*)((const float*)a.x + (size_t)t * a.d + e0 + 4);
+        w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+        w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+    }
+}
+
+template <bool XB>
+__device__ __forceinline__ float x_elem(const uint32_t (&w)[8], int i) {
+    return XB ? bf16_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFF) : __uint_as_float(w[i]);
+}
+
+// All threads of the block: u of one token into LDS (two block barriers).
+template <int D, bool XB>
+__device__ __forceinline__ void u_to_lds(const DecAArgs& a, const XThread& X, ULds<D>& S) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool mine = tid * 8 < D;
+    double inv = 1.0;
+    if (a.fused) {
+        double ss = 0.0;
+        if (mine) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double xv = x_elem<XB>(X.w, i);
+                ss += xv * xv;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        if (lane == 0) S.red[wave] = ss;
+        lds_barrier();
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += S.red[w];
+        inv = 1.0 / sqrt(tot / (double)D + (double)a.eps);
+    }
+    uint32_t hb[8], lb[8];
+    float uf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double xv = x_elem<XB>(X.w, j);
+        const double uv = a.fused ? (xv * inv) * (double)X.g[j] : xv;
+        if (a.act_bf16) { hb[j] = f64_to_bf16(uv); uf[j] = bf16_to_f32(hb[j]); }
+        else { uf[j] = (float)uv; hb[j] = f32_to_bf16(uf[j]); }
+        lb[j] = f32_to_bf16(uf[j] - bf16_to_f32(hb[j]));
+    }
+    float sh = 0.f, sl = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { sh += bf16_to_f32(hb[j]); sl += bf16_to_f32(lb[j]); }
+    const int c = tid >> 2, i = tid & 3;                 // chunk, piece
+    if (mine) {
+        u32x4 v;
+        v.x = hb[0] | (hb[4] << 16); v.y = hb[1] | (hb[5] << 16); v.z = hb[2] | (hb[6] << 16); v.w = hb[3] | (hb[7] << 16);
+        *(u32x4*)&S.pk[(i * AGeo<D>::C + c) * 4] = v;
+        if (!a.act_bf16) {
+            u32x4 l;
+            l.x = lb[0] | (lb[4] << 16); l.y = lb[1] | (lb[5] << 16); l.z = lb[2] | (lb[6] << 16); l.w = lb[3] | (lb[7] << 16);
+            *(u32x4*)&S.pk_lo[(i * AGeo<D>::C + c) * 4] = l;
+        }
+        *(float4*)&S.uf[((2 * i) * AGeo<D>::C + c) * 4] = make_float4(uf[0], uf[1], uf[2], uf[3]);
+        *(float4*)&S.uf[((2 * i + 1) * AGeo<D>::C + c) * 4] = make_float4(uf[4], uf[5], uf[6], uf[7]);
+    }
+    // chunk sums: the 4 threads of a chunk are 4 consecutive lanes
+    sh += __shfl_xor(sh, 1, 64); sh += __shfl_xor(sh, 2, 64);
+    sl += __shfl_xor(sl, 1, 64); sl += __shfl_xor(sl, 2, 64);
+    if (mine && i == 0) { S.usum[c] = sh; S.usum_lo[c] = sl; }
+    lds_barrier();
+}
+
+// ---- int4 gate/up rows ----------------------------------------------------
+struct GateUpRegs {
+    u32x4 g[kAPass], u[kAPass];
+    uint32_t sg[kAPass], su[kAPass];
+};
+
+template <int D>
+__device__ __forceinline__ void gateup_issue(GateUpRegs& R, const uint8_t* blob, const BlobLayout& L, int row_first) {
+    using G = AGeo<D>;
+    const int c = (threadIdx.x & 63) % G::LPR;
+    const u32x4* gq = (const u32x4*)(blob + L.gate_q) + (size_t)row_first * (D / 32) + c;
+    const u32x4* uq = (const u32x4*)(blob + L.up_q) + (size_t)row_first * (D / 32) + c;
+    const uint32_t* gs = (const uint32_t*)(blob + L.gate_sb) + (size_t)row_first * (D / 64) + c / 2;
+    const uint32_t* us = (const uint32_t*)(blob + L.up_sb) + (size_t)row_first * (D / 64) + c / 2;
+#pragma unroll
+    for (int i = 0; i < kAPass; ++i) {
+        R.g[i] = __builtin_nontemporal_load(gq + i * G::RPW * (D / 32));
+        R.u[i] = __builtin_nontemporal_load(uq + i * G::RPW * (D / 32));
+        R.sg[i] = __builtin_nontemporal_load(gs + i * G::RPW * (D / 64));
+        R.su[i] = __builtin_nontemporal_load(us + i * G::RPW * (D / 64));
+    }
+}
+
+// sum over the chunk of (128 + q) * u
+__device__ __forceinline__ float chunk_dot(u32x4 w, const u32x4 (&up)[4], float acc) {
+    // opaque copy: keeps the nibble unpacking after u is ready instead of
+    // hoisted out of the position loop, where it would wait for the weights
+    asm volatile("" : "+v"(w));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc = dot2_bf16(nib_pair_bf16(ws[i], 0), up[i].x, acc);
+        acc = dot2_bf16(nib_pair_bf16(ws[i], 1), up[i].y, acc);
+        acc = dot2_bf16(nib_pair_bf16(ws[i], 2), up[i].z, acc);
+        acc = dot2_bf16(nib_pair_bf16(ws[i], 3), up[i].w, acc);
+    }
+    return acc;
+}
+
+// h = silu(gate . u) * (up . u) for the wave's rows; the lanes that hold a
+// row's total write h_out[row].
+template <int D>
+__device__ __forceinline__ void gateup_rows(const GateUpRegs& R, const ULds<D>& S, bool with_lo, bool ok,
+                                            float* h_out, int row_first) {
+    using G = AGeo<D>;
+    const int lane = threadIdx.x & 63, c = lane % G::LPR, rsub = lane / G::LPR;
+    u32x4 up[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) up[i] = *(const u32x4*)&S.pk[(i * G::C + c) * 4];
+    float usm = S.usum[c];
+    if (with_lo) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = *(const u32x4*)&S.pk_lo[(i * G::C + c) * 4];
+        usm += S.usum_lo[c];
+    }
+    float ga[kAPass], ua[kAPass];
+#pragma unroll
+    for (int i = 0; i < kAPass; ++i) {
+        float accg = chunk_dot(R.g[i], up, 0.f);
+        float accu = chunk_dot(R.u[i], up, 0.f);
+        if (with_lo) {
+            accg = chunk_dot(R.g[i], lo, accg);
+            accu = chunk_dot(R.u[i], lo, accu);
+        }
+        uint32_t sgw = R.sg[i], suw = R.su[i];
+        asm volatile("" : "+v"(sgw), "+v"(suw));   // opaque copies, as in chunk_dot
+        const float s1 = f16_to_f32(sgw & 0xFFFF), b1 = f16_to_f32(sgw >> 16);
+        const float s2 = f16_to_f32(suw & 0xFFFF), b2 = f16_to_f32(suw >> 16);
+        ga[i] = s1 * accg + (b1 - 128.f * s1) * usm;
+        ua[i] = s2 * accu + (b2 - 128.f * s2) * usm;
+    }
+    int pg, pu;
+    const float g = row_reduce<float, kAPass, G::LPR>(ga, &pg);
+    const float u = row_reduce<float, kAPass, G::LPR>(ua, &pu);
+    if (c % (G::LPR / kAPass) == 0) h_out[row_first + pg * G::RPW + rsub] = ok ? silu_f32(g) * u : 0.f;
+}
+
+// ---- routing digest of one wave -------------------------------------------
+// Entry `lane` (< n) routes to expert e. Sorted by (expert, entry), invalid
+// entries last; sorted position p is held by lane p.
+struct WaveDigest {
+    int n_active, n_valid;
+    unsigned long long starts;   // bit p: sorted position p starts an expert
+    uint32_t sk;                 // sorted key of position `lane`: expert << 16 | entry
+};
+
+__device__ __forceinline__ WaveDigest wave_digest(int n, int e, int E, uint32_t* sl) {
+    const int lane = threadIdx.x & 63;
+    const bool in = lane < n;
+    const bool ok = in && e >= 0 && e < E;
+    const uint32_t key = in ? (((uint32_t)(ok ? e : 0xFFFF) << 16) | (uint32_t)lane) : 0xFFFFFFFFu;
+    int rank = 0;
+    for (int j = 0; j < n; ++j) rank += (uint32_t)__shfl((int)key, j, 64) < key;
+    if (in) sl[rank] = key;
+    wave_lds_sync();
+    WaveDigest W;
+    W.sk = in ? sl[lane] : 0xFFFFFFFFu;
+    const int ep = (int)(W.sk >> 16);
+    const bool valid = in && ep != 0xFFFF;
+    const int prev = __shfl_up(ep, 1, 64);
+    const bool start = valid && (lane == 0 || prev != ep);
+    W.starts = __ballot(start);
+    W.n_active = __popcll(W.starts);
+    W.n_valid = __popcll(__ballot(valid));
+    return W;
+}
+
+// position of the s-th set bit of m (s < popcount(m))
+__device__ __forceinline__ int nth_set(unsigned long long m, int s) {
+    for (int i = 0; i < s; ++i) m &= m - 1;
+    return __ffsll((long long)m) - 1;
+}
+
+// ---- the kernel -----------------------------------------------------------
+template <int D, bool XB>
+__global__ void __launch_bounds__(kThreads) k_dec_a(DecAArgs a) {
+    using G = AGeo<D>;
+    __shared__ __align__(16) ULds<D> S;
+    __shared__ uint32_t sl[kWaves][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane % G::LPR, rsub = lane / G::LPR;
+    const int n_tok = a.n_tok, k = a.k, n_assign = n_tok * k;
+    const bool role_h = (int)blockIdx.x < a.nb_h;
+    const bool with_lo = !a.act_bf16;
+    const int e0 = tid * 8 < D ? tid * 8 : 0;       // this thread's elements of x
+
+    // ---- level 0 (all threads, no branches around loads): routing entries
+    // first, then x and gamma
+    const int li = lane < n_assign ? lane : 0;
+    const int32_t* ri = a.route_idx ? a.route_idx : a.self_idx;
+    const float* rw = a.route_idx ? a.route_w : a.self_w;
+    const int32_t* si = a.self_idx ? a.self_idx : ri;
+    const float* sw = a.self_idx ? a.self_w : rw;
+    const int vr = ri[li], vs = si[li];
+    const float vrw = rw[li], vsw = sw[li];
+    const int sh_tag = *(a.ev.shared_tag ? a.ev.shared_tag : a.meta);
+    XThread X;
+    x_issue<XB>(a, 0, e0, X.w);
+    {
+        // unconditional (a stand-in of 8 readable floats when there is no
+        // norm): a load under a branch would make its result wait at the join
+        const float* gp = a.fused ? a.gamma + e0 : a.wsort;
+        const float4 g0 = *(const float4*)gp, g1 = *(const float4*)(gp + 4);
+        X.g[0] = g0.x; X.g[1] = g0.y; X.g[2] = g0.z; X.g[3] = g0.w;
+        X.g[4] = g1.x; X.g[5] = g1.y; X.g[6] = g1.z; X.g[7] = g1.w;
+    }
+
+    if (role_h) {
+        const int u0 = blockIdx.x * G::HROWS;                 // first h row of the block
+        const bool shared = u0 < a.fs;
+        const int f = shared ? a.fs : a.f;
+        const int brow = shared ? u0 : (u0 - a.fs) % a.f;     // block's first row in its expert
+        const int slot = shared ? -1 : (u0 - a.fs) / a.f;
+        const int row0 = brow + wave * kAPass * G::RPW;       // wave's first row
+        const BlobLayout Lf = BlobLayout::make(D, f);
+        GateUpRegs R;
+        const uint8_t* blob = nullptr;
+        if (shared) {
+            blob = a.ev.shared;
+            gateup_issue<D>(R, blob ? blob : a.ev.base, Lf, row0 + rsub);
+        }
+        int p0 = 0, p1 = n_tok;
+        bool ok;
+        WaveDigest W{};
+        if (!shared) {
+            // ---- level 1: routing merged per token row, sorted in registers
+            const int first = __shfl(vr, (lane / k) * k, 64);
+            const bool given = a.route_idx && first >= 0;
+            const int me = lane < n_assign ? (given ? vr : vs) : -1;
+            const float mw = given ? vrw : vsw;
+            W = wave_digest(n_assign, me, a.E, sl[wave]);
+            if ((int)blockIdx.x * G::HROWS == a.fs && wave == 0) {
+                // the first routed block publishes the digest and the routing
+                // used (read by K_B and the caller)
+                const bool in = lane < n_assign;
+                const bool bad = in && (me < 0 || me >= a.E);
+                if (__ballot(bad) && lane == 0) set_err(a.err, ERR_BAD_INDEX);
+                const int ep = (int)(W.sk >> 16);
+                const int aid = (int)(W.sk & 0xFFFF);
+                const bool valid = lane < W.n_valid;
+                const float wsorted = __shfl(mw, valid ? aid : 0, 64);
+                if (in) {
+                    a.used_idx[lane] = bad ? -1 : me;
+                    a.used_w[lane] = mw;
+                    if (a.user_used_idx) a.user_used_idx[lane] = bad ? -1 : me;
+                    if (a.user_used_w) a.user_used_w[lane] = mw;
+                }
+                if ((W.starts >> lane) & 1ull) {
+                    const int ai = __popcll(W.starts & ((1ull << lane) - 1ull));
+                    a.active[ai] = ep;
+                    a.act_off[ai] = lane;
+                }
+                if (valid) { a.perm[lane] = aid; a.wsort[lane] = wsorted; }
+                if (lane == 0) { a.meta[0] = W.n_active; a.meta[1] = W.n_valid; a.act_off[W.n_active] = W.n_valid; }
+            }
+            if (slot >= W.n_active) return;                   // uniform over the block
+            p0 = nth_set(W.starts, slot);
+            p1 = slot + 1 < W.n_active ? nth_set(W.starts, slot + 1) : W.n_valid;
+            const int e = __builtin_amdgcn_readlane((int)(W.sk >> 16), p0);
+            if (!a.ev.slot_of) blob = a.ev.base + (size_t)e * a.ev.blob;
+            else {
+                const int s = a.ev.slot_of[e];
+                blob = (s < 0 || (a.ev.slot_tag && a.ev.slot_tag[s] != e)) ? nullptr : a.ev.base + (size_t)s * a.ev.blob;
+            }
+            gateup_issue<D>(R, blob ? blob : a.ev.base, Lf, row0 + rsub);
+            if (!blob && tid == 0) set_err(a.err, ERR_NOT_STAGED);
+            ok = blob != nullptr;
+        } else {
+            ok = blob && !(a.ev.shared_tag && sh_tag != a.ev.E);
+            if (!ok && blob && blockIdx.x == 0 && tid == 0) set_err(a.err, ERR_NOT_STAGED);
+        }
+        // ---- level 2: per position, u of its token (whole block), then the rows
+        int t_loaded = 0;
+        for (int p = p0; p < p1; ++p) {
+            const int t = shared ? p : (int)(__builtin_amdgcn_readlane((int)(W.sk & 0xFFFF), p)) / k;
+            if (t != t_loaded) { x_issue<XB>(a, t, e0, X.w); t_loaded = t; }
+            u_to_lds<D, XB>(a, X, S);
+            float* h_out = shared ? a.hs + (size_t)t * f : a.h + (size_t)p * f;
+            gateup_rows<D>(R, S, with_lo, ok, h_out, row0);
+            lds_barrier();                                    // u is rewritten for the next position
+        }
+        return;
+    }
+
+    // ---- bf16 rows accumulated in fp64: head rows, or LoRA A rows + shared gate
+    const bool role_head = (int)blockIdx.x < a.nb_h + a.nb_head;
+    const int row0 = (blockIdx.x - (role_head ? a.nb_h : a.nb_h + a.nb_head)) * G::BROWS + wave * G::RPW;
+    const int nrows = role_head ? a.En : (a.lora_a ? a.r : 0) + (a.sgate_w ? 1 : 0);
+    int row = row0 + rsub;
+    const bool rvalid = row < nrows;
+    row = rvalid ? row : nrows - 1;
+    const uint16_t* wrow = role_head ? a.head + (size_t)row * D
+                                     : ((a.lora_a && row < a.r) ? a.lora_a + (size_t)row * D : a.sgate_w);
+    u32x4 wb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wb[q] = __builtin_nontemporal_load((const u32x4*)(wrow + 32 * c) + q);
+    for (int t = 0; t < n_tok; ++t) {
+        if (t > 0) x_issue<XB>(a, t, e0, X.w);
+        u_to_lds<D, XB>(a, X, S);
+        double acc = 0.0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // elements 8q..8q+7 of the lane's chunk = uf pieces 2q, 2q+1
+            const float4 u0 = *(const float4*)&S.uf[((2 * q) * G::C + c) * 4];
+            const float4 u1 = *(const float4*)&S.uf[((2 * q + 1) * G::C + c) * 4];
+            const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            u32x4 wv = wb[q];
+            asm volatile("" : "+v"(wv));   // opaque copy: the widening stays in the token loop
+            const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc += (double)bf16_to_f32(ws[j] & 0xFFFF) * (double)uu[2 * j];
+                acc += (double)bf16_to_f32(ws[j] >> 16) * (double)uu[2 * j + 1];
+            }
+        }
+#pragma unroll
+        for (int o = G::LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (c == 0 && rvalid) {
+            if (role_head) a.logits_h[(size_t)t * a.En + row] = acc;
+            else if (a.lora_a && row < a.r) a.au[(size_t)t * a.r + row] = (float)acc;
+            else a.sgate[t] = (float)(1.0 / (1.0 + exp(-acc)));
+        }
+        lds_barrier();
+    }
+}
+
+int dec_a_blocks(int d, int f, int fs, int n_tok, int k, int E, int En, int r, bool sgate, int* nb_h, int* nb_head,
+                 int* nb_misc) {
+    const int hr = dec_a_hrows_per_block(d), br = dec_a_brows_per_block(d);
+    const int max_active = n_tok * k < E ? n_tok * k : E;
+    *nb_h = (fs + max_active * f + hr - 1) / hr;
+    *nb_head = (En + br - 1) / br;
+    *nb_misc = (r + (sgate ? 1 : 0) + br - 1) / br;
+    return *nb_h + *nb_head + *nb_misc;
+}
+
+hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s) {
+    const int hr = dec_a_hrows_per_block(a.d);
+    if (a.n_tok * a.k > kMaxAssign || a.f % hr || a.fs % hr) return hipErrorInvalidValue;
+    const dim3 grid(a.nb_h + a.nb_head + a.nb_misc), block(kThreads);
+    const bool xb = a.x_is_bf16 != 0;
+    switch (a.d) {
+        case 256: if (xb) hipLaunchKernelGGL((k_dec_a<256, true>), grid, block, 0, s, a); else hipLaunchKernelGGL((k_dec_a<256, false>), grid, block, 0, s, a); break;
+        case 512: if (xb) hipLaunchKernelGGL((k_dec_a<512, true>), grid, block, 0, s, a); else hipLaunchKernelGGL((k_dec_a<512, false>), grid, block, 0, s, a); break;
+        case 1024: if (xb) hipLaunchKernelGGL((k_dec_a<1024, true>), grid, block, 0, s, a); else hipLaunchKernelGGL((k_dec_a<1024, false>), grid, block, 0, s, a); break;
+        case 2048: if (xb) hipLaunchKernelGGL((k_dec_a<2048, true>), grid, block, 0, s, a); else hipLaunchKernelGGL((k_dec_a<2048, false>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

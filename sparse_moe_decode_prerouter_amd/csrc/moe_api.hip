@@ -87,12 +87,14 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.used_idx = c.take<int32_t>(T * K);
     S.used_w = c.take<float>(T * K);
     S.au = c.take<float>(T * std::max(1, d->lora_rank));
-    S.sgate = c.take<float>(T);
+    S.sgate = c.take<float>(std::max<size_t>(T, 64));
     S.sort_meta = c.take<int32_t>(4);
-    S.active = c.take<int32_t>(nas + 1);
-    S.act_off = c.take<int32_t>(nas + 1);
-    S.perm = c.take<int32_t>(T * K);
-    S.wsort = c.take<float>(T * K);
+    // the digest arrays are at least one wavefront wide: the decode kernels
+    // read 64 entries unconditionally and use the valid ones
+    S.active = c.take<int32_t>(std::max<size_t>(nas + 1, 64));
+    S.act_off = c.take<int32_t>(std::max<size_t>(nas + 1, 64));
+    S.perm = c.take<int32_t>(std::max<size_t>(T * K, 64));
+    S.wsort = c.take<float>(std::max<size_t>(T * K, 64));
     S.h = c.take<float>(T * K * d->d_ff);
     S.hs = c.take<float>(T * std::max(1, d->d_ff_shared));
     S.hb = c.take<uint16_t>(T * K * d->d_ff);
@@ -198,7 +200,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
 int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
     const moe_layer_desc& D = L->desc;
     // shapes outside the fused two-kernel path take the general grouped-GEMV path
-    if (!dec_fast_path_ok(D.d_model, D.d_ff, n_tok, D.top_k)) return run_prefill(L, io, n_tok, st, false);
+    if (!dec_fast_path_ok(D.d_model, D.d_ff, D.d_ff_shared, n_tok, D.top_k)) return run_prefill(L, io, n_tok, st, false);
     const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
     if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
     const bool need_router = io->route_idx == nullptr || io->self_rows;
@@ -262,7 +264,6 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
     b.hist_cur_m = L->w.hist_cur; b.hist_prev_m = L->w.hist_prev; b.hist_cur = io->hist_cur; b.hist_prev = io->hist_prev;
     b.pred_idx = io->pred_idx; b.pred_w = io->pred_w;
     b.err = L->s.err;
-    b.nb_rows = dec_b_row_blocks(D.d_model);
     if (L->profiling) HIPCHK(hipEventRecord(L->ev_t[4], st));
     HIPCHK(launch_dec_b(b, st));
     if (L->profiling) { HIPCHK(hipEventRecord(L->ev_t[5], st)); L->ev_t_used[2] = true; }

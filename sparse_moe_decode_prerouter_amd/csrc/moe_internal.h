@@ -186,8 +186,8 @@ struct DecAArgs {
     int nb_h, nb_head, nb_misc;
 };
 hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s);
-bool dec_fast_path_ok(int d, int f, int n_tok, int k);
-int dec_b_row_blocks(int d);
+bool dec_fast_path_ok(int d, int f, int fs, int n_tok, int k);
+int dec_a_hrows_per_block(int d);
 hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s);
 int dec_a_blocks(int d, int f, int fs, int n_tok, int k, int E, int En, int r, bool sgate, int* nb_h, int* nb_head,
                  int* nb_misc);
@@ -202,7 +202,6 @@ struct DecBArgs {
     const double* logits_h; int En; int kn; const float* head_bias; const float* hist_cur_m; const float* hist_prev_m;
     const int32_t* hist_cur; const int32_t* hist_prev; int32_t* pred_idx; float* pred_w;
     int32_t* err;
-    int nb_rows;
 };
 hipError_t launch_dec_b(const DecBArgs& a, hipStream_t s);
 

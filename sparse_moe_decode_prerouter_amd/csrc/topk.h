@@ -6,65 +6,89 @@
 
 namespace moe {
 
-__device__ inline void topk_rows(bool coherent, const double* logits, int E, int k, int n_tok, const float* bias,
-                          const float* mc, const int32_t* hc, const float* mp, const int32_t* hp,
-                          const int32_t* route_idx, int kroute, int32_t* out_idx, float* out_w) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+// PER logits per lane (E <= 64 * PER), held in registers with fixed indices.
+template <int PER>
+__device__ __forceinline__ void topk_row(bool coherent, const double* logits, int E, int k, int t, const float* bias,
+                                const float* mc, const int32_t* hc, const float* mp, const int32_t* hp,
+                                int32_t* out_idx, float* out_w) {
+    const int lane = threadIdx.x & 63;
+    double v[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+        const int e = lane + 64 * m;
+        const int ec = e < E ? e : 0;
+        v[m] = coherent ? ld_dev(logits + (size_t)t * E + ec) : logits[(size_t)t * E + ec];
+    }
+    if (bias) {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int e = lane + 64 * m;
+            v[m] += (double)bias[e < E ? e : 0];
+        }
+    }
+    // history terms: each distinct valid expert of the previous routings adds its row
+    for (int src = 0; src < 2; ++src) {
+        const float* M = src ? mp : mc;
+        const int32_t* H = src ? hp : hc;
+        if (!M || !H) continue;
+        for (int j = 0; j < k; ++j) {
+            const int h = H[(size_t)t * k + j];
+            bool dup = false;
+            for (int jj = 0; jj < j; ++jj) dup |= H[(size_t)t * k + jj] == h;
+            if (h < 0 || h >= E || dup) continue;
+#pragma unroll
+            for (int m = 0; m < PER; ++m) {
+                const int e = lane + 64 * m;
+                v[m] += (double)M[(size_t)h * E + (e < E ? e : 0)];
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < PER; ++m)
+        if (lane + 64 * m >= E) v[m] = -INFINITY;
+    // lane j keeps the j-th selection (no dynamically indexed arrays)
+    double my_v = -INFINITY;
+    int my_i = 0;
+    for (int j = 0; j < k; ++j) {
+        double bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int e = lane + 64 * m;
+            if (e < E && better(v[m], e, bv, bi)) { bv = v[m]; bi = e; }
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+            const double ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        }
+        if (lane == j) { my_v = bv; my_i = bi; }
+#pragma unroll
+        for (int m = 0; m < PER; ++m)
+            if (lane + 64 * m == bi) v[m] = -INFINITY;
+    }
+    // softmax over the k selected logits, summed in selection order
+    const double top = __shfl(my_v, 0, 64);
+    const double ex = lane < k ? exp(my_v - top) : 0.0;
+    double ssum = 0.0;
+    for (int j = 0; j < k; ++j) ssum += __shfl(ex, j, 64);
+    if (lane < k) {
+        out_idx[(size_t)t * k + lane] = my_i;
+        out_w[(size_t)t * k + lane] = (float)(ex / ssum);
+    }
+}
+
+__device__ __forceinline__ void topk_rows(bool coherent, const double* logits, int E, int k, int n_tok, const float* bias,
+                                 const float* mc, const int32_t* hc, const float* mp, const int32_t* hp,
+                                 const int32_t* route_idx, int kroute, int32_t* out_idx, float* out_w) {
+    const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     for (int t = wave; t < n_tok; t += nwaves) {
         if (route_idx && route_idx[(size_t)t * kroute] >= 0) continue;   // row has its routing
-        double v[kMaxExperts / 64];
-        const int per = (E + 63) / 64;
-        for (int m = 0; m < per; ++m) {
-            const int e = lane + 64 * m;
-            double z = -INFINITY;
-            if (e < E) {
-                z = coherent ? ld_dev(logits + (size_t)t * E + e) : logits[(size_t)t * E + e];
-                if (bias) z += (double)bias[e];
-                if (mc && hc) {
-                    for (int j = 0; j < k; ++j) {
-                        const int h = hc[(size_t)t * k + j];
-                        bool dup = false;
-                        for (int jj = 0; jj < j; ++jj) dup |= hc[(size_t)t * k + jj] == h;
-                        if (h >= 0 && h < E && !dup) z += (double)mc[(size_t)h * E + e];
-                    }
-                }
-                if (mp && hp) {
-                    for (int j = 0; j < k; ++j) {
-                        const int h = hp[(size_t)t * k + j];
-                        bool dup = false;
-                        for (int jj = 0; jj < j; ++jj) dup |= hp[(size_t)t * k + jj] == h;
-                        if (h >= 0 && h < E && !dup) z += (double)mp[(size_t)h * E + e];
-                    }
-                }
-            }
-            v[m] = z;
-        }
-        double sel_v[kMaxTopK];
-        int sel_i[kMaxTopK];
-        for (int j = 0; j < k; ++j) {
-            double bv = -INFINITY; int bi = 0x7fffffff;
-            for (int m = 0; m < per; ++m) {
-                const int e = lane + 64 * m;
-                if (e < E && better(v[m], e, bv, bi)) { bv = v[m]; bi = e; }
-            }
-            for (int o = 32; o > 0; o >>= 1) {
-                const double ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-            }
-            sel_v[j] = bv; sel_i[j] = bi;
-            for (int m = 0; m < per; ++m)
-                if (lane + 64 * m == bi) v[m] = -INFINITY;
-        }
-        if (lane == 0) {
-            double ssum = 0.0;
-            double ex[kMaxTopK];
-            for (int j = 0; j < k; ++j) { ex[j] = exp(sel_v[j] - sel_v[0]); ssum += ex[j]; }
-            for (int j = 0; j < k; ++j) {
-                out_idx[(size_t)t * k + j] = sel_i[j];
-                out_w[(size_t)t * k + j] = (float)(ex[j] / ssum);
-            }
-        }
+        if (E <= 64) topk_row<1>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
+        else if (E <= 128) topk_row<2>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
+        else if (E <= 256) topk_row<4>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
+        else if (E <= 512) topk_row<8>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
+        else topk_row<16>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
     }
 }
 

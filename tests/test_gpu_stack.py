@@ -87,7 +87,13 @@ def test_stack_forced_routing(B):
         assert err <= STACK_TOL
         for l in range(L):
             assert np.array_equal(g[t]["used"][l], recs[t].routes[l][0]), (t, l)
-            assert np.allclose(g[t]["used_w"][l], recs[t].routes[l][1], rtol=1e-5, atol=1e-6)
+            if t > 0 and l > 0:
+                # forced: both sides take the same given weights
+                assert np.allclose(g[t]["used_w"][l], recs[t].routes[l][1], rtol=1e-5, atol=1e-6), (t, l)
+            else:
+                # self-routed from each side's own residual stream (which agree to the
+                # stack tolerance), so the softmax weights agree to the prediction bound
+                assert np.allclose(g[t]["used_w"][l], recs[t].routes[l][1], rtol=2e-3, atol=1e-4), (t, l)
         for l in range(L - 1):
             for b in range(B):
                 got = g[t]["pred"][l + 1][b]
