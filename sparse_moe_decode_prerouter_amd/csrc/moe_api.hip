@@ -97,11 +97,9 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.wsort = c.take<float>(std::max<size_t>(T * K, 64));
     S.h = c.take<float>(T * K * d->d_ff);
     S.hs = c.take<float>(T * std::max(1, d->d_ff_shared));
-    S.hb = c.take<uint16_t>(T * K * d->d_ff);
-    S.hb_lo = c.take<uint16_t>(T * K * d->d_ff);
-    S.hsb = c.take<uint16_t>(T * std::max(1, d->d_ff_shared));
-    S.hsb_lo = c.take<uint16_t>(T * std::max(1, d->d_ff_shared));
-    S.rowmap = c.take<int32_t>(T * K);
+    S.tiles = c.take<uint32_t>(prefill_max_tiles((int)T, (int)K, (int)E));
+    S.ob = c.take<float>(T * K * D);
+    S.obs = c.take<float>(T * D);
     (void)Kn;
     return align_up(c.off, 256);
 }
@@ -289,8 +287,8 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     pa.u = L->s.u; pa.u_pk = L->s.u_pk; pa.u_pk_lo = L->s.u_pk_lo; pa.usum = L->s.usum; pa.usum_lo = L->s.usum_lo;
     HIPCHK(launch_prologue(pa, st));
 
-    RouteArgs ra{};
-    ra.u = L->s.u; ra.d = D.d_model; ra.n_tok = n_tok;
+    RouteMMArgs ra{};
+    ra.u_pk = L->s.u_pk; ra.u_pk_lo = L->s.u_pk_lo; ra.d = D.d_model; ra.n_tok = n_tok;
     ra.router = L->w.router; ra.router_bias = L->w.router_bias; ra.E = D.n_experts; ra.k = D.top_k;
     ra.route_idx = io->route_idx;
     ra.head = io->pred_idx ? L->w.head : nullptr; ra.head_bias = L->w.head_bias;
@@ -302,8 +300,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     ra.self_idx = L->s.self_idx; ra.self_w = L->s.self_w;
     ra.pred_idx = io->pred_idx; ra.pred_w = io->pred_w;
     ra.au = L->s.au; ra.sgate = L->s.sgate;
-    ra.counters = L->s.counters;
-    HIPCHK(launch_route(ra, st));
+    HIPCHK(launch_route_mm(ra, st));
 
     SortArgs sa{};
     sa.route_idx = io->route_idx; sa.route_w = io->route_w;
@@ -342,14 +339,16 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     ga.y = io->y_out;
     ga.err = L->s.err;
     ga.max_active = std::min(D.n_experts, n_tok * D.top_k);
-    if (prefill) {
+    if (prefill_mm_ok(D.d_model, D.d_ff, D.d_ff_shared)) {
+        // grouped GEMM on the matrix cores (prefill and large decode batches)
         PrefillArgs pf{};
         pf.g = ga;
-        pf.u = L->s.u;
-        pf.hb = L->s.hb; pf.hb_lo = L->s.hb_lo; pf.hsb = L->s.hsb; pf.hsb_lo = L->s.hsb_lo;
-        pf.rowmap = L->s.rowmap;
-        HIPCHK(launch_prefill_gateup(pf, st));
-        HIPCHK(launch_prefill_down(pf, st));
+        pf.tiles = L->s.tiles;
+        pf.max_tiles = prefill_max_tiles(n_tok, D.top_k, D.n_experts);
+        pf.meta_w = L->s.sort_meta;
+        pf.ob = L->s.ob; pf.obs = L->s.obs;
+        pf.used_idx = L->s.used_idx; pf.used_w = L->s.used_w;
+        HIPCHK(launch_prefill(pf, st));
     } else {
         HIPCHK(launch_gateup(ga, st));
         HIPCHK(launch_down(ga, st));

@@ -67,11 +67,9 @@ struct Scratch {
     float* wsort;            // [T*k] routing weight of each sorted assignment
     float* h;                // [T*k][f] routed expert hidden (sorted order)
     float* hs;               // [T][fs] shared expert hidden
-    uint16_t* hb;            // prefill: [T*k][f] bf16 hi of h (sorted order)
-    uint16_t* hb_lo;         // prefill: lo part
-    uint16_t* hsb;           // prefill: [T][fs] bf16 hi of shared h
-    uint16_t* hsb_lo;
-    int32_t* rowmap;         // prefill: [T*k] token of each sorted assignment
+    uint32_t* tiles;         // prefill: grouped-GEMM work list
+    float* ob;               // prefill: [T*k][d] routed expert outputs by assignment
+    float* obs;              // prefill: [T][d] shared expert outputs
 };
 
 }  // namespace moe
@@ -138,6 +136,21 @@ struct RouteArgs {
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
+// routing-side GEMM for many tokens (prefill, large decode batches)
+struct RouteMMArgs {
+    const uint32_t* u_pk; const uint32_t* u_pk_lo; int d; int n_tok;
+    const uint16_t* router; const float* router_bias; int E; int k;
+    const int32_t* route_idx;           // rows to self-route: idx[t*k] < 0 or route_idx == nullptr
+    const uint16_t* head; const float* head_bias; int En; int kn;
+    const float* hist_cur_m; const float* hist_prev_m; const int32_t* hist_cur; const int32_t* hist_prev;
+    const uint16_t* lora_a; int r;
+    const uint16_t* sgate_w;
+    double* logits_r; double* logits_h;
+    int32_t* self_idx; float* self_w; int32_t* pred_idx; float* pred_w;
+    float* au; float* sgate;
+};
+hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s);
+
 struct SortArgs {
     const int32_t* route_idx; const float* route_w; const int32_t* self_idx; const float* self_w;
     int n_tok; int k; int E;
@@ -164,12 +177,14 @@ hipError_t launch_down(const GemvArgs& a, hipStream_t s);
 
 struct PrefillArgs {
     GemvArgs g;
-    const float* u;            // fp32 u [T][d]
-    uint16_t* hb; uint16_t* hb_lo; uint16_t* hsb; uint16_t* hsb_lo;
-    int32_t* rowmap;
+    uint32_t* tiles; int max_tiles;      // work list of the grouped GEMM
+    int32_t* meta_w;                     // meta[2] = number of tiles (written by the tile kernel)
+    float* ob; float* obs;               // down outputs: [T*k][d] by assignment, [T][d] shared
+    const int32_t* used_idx; const float* used_w;
 };
-hipError_t launch_prefill_gateup(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s);
+int prefill_max_tiles(int T, int K, int E);
+bool prefill_mm_ok(int d, int f, int fs);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 struct DecAArgs {
     const void* x; int x_is_bf16; int fused; const float* gamma; float eps; int act_bf16; int d; int n_tok;
