@@ -246,10 +246,12 @@ int moe_stack_prefill(moe_stack* st, float* x, int n_tok, int32_t* used_idx, flo
 void moe_stack_destroy(moe_stack* st);
 
 /* ---- measurement --------------------------------------------------------
- * With profiling on, every kernel launch of this layer is bracketed by HIP
- * events on its stream; moe_layer_kernel_ms returns the durations of the most
- * recent launches of the router (self-routing), K_A (norm + gate/up + head)
- * and K_B (down + combine + epilogue) kernels, -1 where not launched.        */
+ * With profiling on, each decode kernel of this layer is launched with HIP
+ * kernel-timestamp events (the dispatch's own begin and end, as a kernel
+ * trace reports them, not the gaps between launches); moe_layer_kernel_ms
+ * returns the durations of the most recent launches of the router
+ * (self-routing), K_A (norm + gate/up + head) and K_B (down + combine +
+ * epilogue) kernels, -1 where not launched. Not for use under graph capture. */
 int moe_layer_set_profiling(moe_layer* layer, int enable);
 int moe_layer_kernel_ms(moe_layer* layer, float* ms_router, float* ms_a, float* ms_b);
 

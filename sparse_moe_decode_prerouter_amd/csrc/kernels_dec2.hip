@@ -206,10 +206,10 @@ __global__ void __launch_bounds__(kThreads) k_dec_r(DecAArgs a, RouteArgs r) {
               r.route_idx, r.k, r.self_idx, r.self_w);
 }
 
-hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s) {
+hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s, const KTime* tm) {
     if (a.d > 2048) return hipErrorInvalidValue;
     const int nb = (r.E + kHeadRowsPerBlock - 1) / kHeadRowsPerBlock;
-    hipLaunchKernelGGL(k_dec_r, dim3(nb), dim3(kThreads), (size_t)a.d * 4, s, a, r);
+    MOE_LAUNCH(k_dec_r, dim3(nb), dim3(kThreads), (size_t)a.d * 4, s, tm, a, r);
     return hipGetLastError();
 }
 
@@ -459,16 +459,16 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
 
 int dec_b_rows_per_block(int f) { return kPassB * (64 / (f / 8)); }
 
-hipError_t launch_dec_b(const DecBArgs& a, hipStream_t s) {
+hipError_t launch_dec_b(const DecBArgs& a, hipStream_t s, const KTime* tm) {
     if (a.n_tok > kMaxTokB || a.n_tok * a.k > kMaxAssign || (a.fs && a.fs != a.f)) return hipErrorInvalidValue;
     const int rb = dec_b_rows_per_block(a.f);
     if (a.d % rb || a.n_tok * rb > kThreads) return hipErrorInvalidValue;
     const dim3 grid(1 + a.d / rb), block(kThreads);
     switch (a.f) {
-        case 64: hipLaunchKernelGGL(k_dec_b<64>, grid, block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL(k_dec_b<128>, grid, block, 0, s, a); break;
-        case 256: hipLaunchKernelGGL(k_dec_b<256>, grid, block, 0, s, a); break;
-        case 512: hipLaunchKernelGGL(k_dec_b<512>, grid, block, 0, s, a); break;
+        case 64: MOE_LAUNCH(k_dec_b<64>, grid, block, 0, s, tm, a); break;
+        case 128: MOE_LAUNCH(k_dec_b<128>, grid, block, 0, s, tm, a); break;
+        case 256: MOE_LAUNCH(k_dec_b<256>, grid, block, 0, s, tm, a); break;
+        case 512: MOE_LAUNCH(k_dec_b<512>, grid, block, 0, s, tm, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -409,16 +409,16 @@ int dec_a_blocks(int d, int f, int fs, int n_tok, int k, int E, int En, int r, b
     return *nb_h + *nb_head + *nb_misc;
 }
 
-hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s) {
+hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s, const KTime* tm) {
     const int hr = dec_a_hrows_per_block(a.d);
     if (a.n_tok * a.k > kMaxAssign || a.f % hr || a.fs % hr) return hipErrorInvalidValue;
     const dim3 grid(a.nb_h + a.nb_head + a.nb_misc), block(kThreads);
     const bool xb = a.x_is_bf16 != 0;
     switch (a.d) {
-        case 256: if (xb) hipLaunchKernelGGL((k_dec_a<256, true>), grid, block, 0, s, a); else hipLaunchKernelGGL((k_dec_a<256, false>), grid, block, 0, s, a); break;
-        case 512: if (xb) hipLaunchKernelGGL((k_dec_a<512, true>), grid, block, 0, s, a); else hipLaunchKernelGGL((k_dec_a<512, false>), grid, block, 0, s, a); break;
-        case 1024: if (xb) hipLaunchKernelGGL((k_dec_a<1024, true>), grid, block, 0, s, a); else hipLaunchKernelGGL((k_dec_a<1024, false>), grid, block, 0, s, a); break;
-        case 2048: if (xb) hipLaunchKernelGGL((k_dec_a<2048, true>), grid, block, 0, s, a); else hipLaunchKernelGGL((k_dec_a<2048, false>), grid, block, 0, s, a); break;
+        case 256: if (xb) MOE_LAUNCH((k_dec_a<256, true>), grid, block, 0, s, tm, a); else MOE_LAUNCH((k_dec_a<256, false>), grid, block, 0, s, tm, a); break;
+        case 512: if (xb) MOE_LAUNCH((k_dec_a<512, true>), grid, block, 0, s, tm, a); else MOE_LAUNCH((k_dec_a<512, false>), grid, block, 0, s, tm, a); break;
+        case 1024: if (xb) MOE_LAUNCH((k_dec_a<1024, true>), grid, block, 0, s, tm, a); else MOE_LAUNCH((k_dec_a<1024, false>), grid, block, 0, s, tm, a); break;
+        case 2048: if (xb) MOE_LAUNCH((k_dec_a<2048, true>), grid, block, 0, s, tm, a); else MOE_LAUNCH((k_dec_a<2048, false>), grid, block, 0, s, tm, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

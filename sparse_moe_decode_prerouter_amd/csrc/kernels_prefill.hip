@@ -303,6 +303,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
 // O[assignment][d] (routed) or O_s[token][d] (shared), unweighted.
 // ---------------------------------------------------------------------------
 constexpr int kDnRows = 128;
+constexpr int kDnSub = 1;                    // 128-row sub-blocks per block (more measured slower)
 constexpr int kHRow = kStageK * 4 + 16;      // LDS bytes per position row of a stage (padded)
 
 struct DnLds {
@@ -362,27 +363,31 @@ __global__ void __launch_bounds__(256) k_pf_down(PrefillArgs a) {
     const bool shared = it.slot < 0;
     const int f = shared ? g.fs : g.f;
     const int d = g.d;
-    const int rb0 = blockIdx.y * kDnRows;
-    if (rb0 >= d || it.M <= 0) return;
+    const int rbb = blockIdx.y * kDnRows * kDnSub;           // block's first row
+    if (rbb >= d || it.M <= 0) return;
     const uint8_t* blob = pf_blob(g, it.slot);
     const int NS = f / kStageK;
+    const int nsub = min(kDnSub, (d - rbb + kDnRows - 1) / kDnRows);
+    const int NZ = nsub * NS;                                 // stages over all sub-blocks
     const float* hbase = shared ? g.hs : g.h;
     if (tid < kTileM) prow[tid] = it.p0 + (tid < it.M ? tid : it.M - 1);
     __syncthreads();
     const BlobLayout L = BlobLayout::make(d, f);
     const uint8_t* wb = blob ? blob : g.ev.base;
     DnRegs R;
-    dn_stage_load(R, 0, wb, L, d, f, rb0, prow, hbase);
+    dn_stage_load(R, 0, wb, L, d, f, rbb, prow, hbase);
     dn_stage_store(R, S[0]);
     __syncthreads();
     const int ml = lane & 15, pc = lane >> 4;
     constexpr int NJ = kDnRows / 64;
+    const bool ok = blob != nullptr;
     f32x4 acc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int st = 0; st < NS; ++st) {
-        const DnLds& C = S[st & 1];
-        if (st + 1 < NS) dn_stage_load(R, st + 1, wb, L, d, f, rb0, prow, hbase);
+    for (int z = 0; z < NZ; ++z) {
+        const DnLds& C = S[z & 1];
+        const int st = z % NS, rb0 = rbb + (z / NS) * kDnRows;
+        if (z + 1 < NZ) dn_stage_load(R, (z + 1) % NS, wb, L, d, f, rbb + ((z + 1) / NS) * kDnRows, prow, hbase);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             // this lane's 16 elements of group q: pieces 2pc, 2pc+1 of position ml
@@ -431,22 +436,26 @@ __global__ void __launch_bounds__(256) k_pf_down(PrefillArgs a) {
                 for (int i = 0; i < 4; ++i) acc[j][i] += sv * pp[i] + cv * hsm[i];
             }
         }
-        if (st + 1 < NS) dn_stage_store(R, S[(st + 1) & 1]);
-        __syncthreads();
-    }
-    const bool ok = blob != nullptr;
+        if (st == NS - 1) {
+            // sub-block done: write its rows, start the next one
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int n = rb0 + wave * (16 * NJ) + 16 * j + ml;
-        if (n >= d) continue;
+            for (int j = 0; j < NJ; ++j) {
+                const int n = rb0 + wave * (16 * NJ) + 16 * j + ml;
+                if (n < d) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 4 * pc + i;
-            if (m >= it.M) continue;
-            const float o = ok ? acc[j][i] : 0.f;
-            if (shared) a.obs[(size_t)(it.p0 + m) * d + n] = o;
-            else a.ob[(size_t)g.perm[it.p0 + m] * d + n] = o;
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 4 * pc + i;
+                        if (m >= it.M) continue;
+                        const float o = ok ? acc[j][i] : 0.f;
+                        if (shared) a.obs[(size_t)(it.p0 + m) * d + n] = o;
+                        else a.ob[(size_t)g.perm[it.p0 + m] * d + n] = o;
+                    }
+                }
+                acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
+        if (z + 1 < NZ) dn_stage_store(R, S[(z + 1) & 1]);
+        __syncthreads();
     }
 }
 
@@ -454,23 +463,50 @@ __global__ void __launch_bounds__(256) k_pf_down(PrefillArgs a) {
 // Combine per (token, row): shared (gated), routed in routing order
 // (weighted), LoRA B, residual.
 // ---------------------------------------------------------------------------
+constexpr int kCombTok = 8;
+
 __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
     const GemvArgs& g = a.g;
-    const int t = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x, d = g.d;
+    const int n = blockIdx.x * 256 + threadIdx.x, d = g.d;
+    const int t0 = blockIdx.y * kCombTok;
     if (n >= d) return;
-    float y = 0.f;
-    if (g.fs && g.ev.shared) y = (g.sgate ? g.sgate[t] : 1.f) * a.obs[(size_t)t * d + n];
-    for (int j = 0; j < g.k; ++j) {
-        const int aid = t * g.k + j;
-        if (a.used_idx[aid] >= 0) y += a.used_w[aid] * a.ob[(size_t)aid * d + n];
+    const bool lora = g.lora_b && g.r;
+    const bool lvec = lora && g.r % 8 == 0 && g.r <= 32;
+    u32x4 lb[4];
+    if (lvec)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lb[c] = *(const u32x4*)(g.lora_b + (size_t)n * g.r + 8 * (8 * c < g.r ? c : 0));
+    for (int tt = 0; tt < kCombTok; ++tt) {
+        const int t = t0 + tt;
+        if (t >= g.n_tok) break;
+        float y = 0.f;
+        if (g.fs && g.ev.shared) y = (g.sgate ? g.sgate[t] : 1.f) * a.obs[(size_t)t * d + n];
+        for (int j = 0; j < g.k; ++j) {
+            const int aid = t * g.k + j;
+            if (a.used_idx[aid] >= 0) y += a.used_w[aid] * a.ob[(size_t)aid * d + n];
+        }
+        if (lora) {
+            float l = 0.f;
+            const float* au = g.au + (size_t)t * g.r;
+            if (lvec) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (8 * c >= g.r) break;
+                    const uint32_t w[4] = {lb[c].x, lb[c].y, lb[c].z, lb[c].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        l += bf16_to_f32(w[i] & 0xFFFF) * au[8 * c + 2 * i];
+                        l += bf16_to_f32(w[i] >> 16) * au[8 * c + 2 * i + 1];
+                    }
+                }
+            } else {
+                for (int q = 0; q < g.r; ++q) l += bf16_to_f32(g.lora_b[(size_t)n * g.r + q]) * au[q];
+            }
+            y += g.lora_scale * l;
+        }
+        if (g.fused) y += g.x[(size_t)t * d + n];
+        g.y[(size_t)t * d + n] = y;
     }
-    if (g.lora_b && g.r) {
-        float l = 0.f;
-        for (int q = 0; q < g.r; ++q) l += bf16_to_f32(g.lora_b[(size_t)n * g.r + q]) * g.au[(size_t)t * g.r + q];
-        y += g.lora_scale * l;
-    }
-    if (g.fused) y += g.x[(size_t)t * d + n];
-    g.y[(size_t)t * d + n] = y;
 }
 
 // ---------------------------------------------------------------------------
@@ -514,14 +550,26 @@ __global__ void __launch_bounds__(256) k_route_mm(RouteMMArgs a) {
     const uint32_t* aql = a.u_pk_lo ? a.u_pk_lo + (size_t)tok * (d / 2) + 4 * pc : nullptr;
     const u32x4* wq = (const u32x4*)(w + 8 * pc);
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int c = 0; c < d / 32; ++c) {
-        const u32x4 av = *(const u32x4*)(aq + 16 * c);
-        const u32x4 bv = bf16_pairs_p4(wq[4 * c]);
-        f32x4 p = {0.f, 0.f, 0.f, 0.f};
-        p = mfma16(av, bv, p);
-        if (aql) p = mfma16(*(const u32x4*)(aql + 16 * c), bv, p);
+    constexpr int kB = 8;                      // k-steps whose loads are issued together
+    for (int c0 = 0; c0 < d / 32; c0 += kB) {
+        u32x4 av[kB], al[kB], wv[kB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += (double)p[i];
+        for (int c = 0; c < kB; ++c) {
+            const int cc = c0 + c < d / 32 ? c0 + c : d / 32 - 1;
+            av[c] = *(const u32x4*)(aq + 16 * cc);
+            wv[c] = wq[4 * cc];
+            if (aql) al[c] = *(const u32x4*)(aql + 16 * cc);
+        }
+#pragma unroll
+        for (int c = 0; c < kB; ++c) {
+            if (c0 + c >= d / 32) break;
+            const u32x4 bv = bf16_pairs_p4(wv[c]);
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+            p = mfma16(av[c], bv, p);
+            if (aql) p = mfma16(al[c], bv, p);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += (double)p[i];
+        }
     }
     if (!row_ok) return;
     const int r = blockIdx.x * 16 + ml;
@@ -588,9 +636,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     if (g.u_pk_lo) hipLaunchKernelGGL(k_pf_gateup<true>, ggrid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_pf_gateup<false>, ggrid, dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pf_down, dim3(a.max_tiles, (g.d + kDnRows - 1) / kDnRows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_pf_down, dim3(a.max_tiles, (g.d + kDnRows * kDnSub - 1) / (kDnRows * kDnSub)), dim3(256), 0,
+                       s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pf_combine, dim3((g.d + 255) / 256, g.n_tok), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_pf_combine, dim3((g.d + 255) / 256, (g.n_tok + kCombTok - 1) / kCombTok), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

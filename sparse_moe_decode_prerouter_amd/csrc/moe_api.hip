@@ -229,9 +229,9 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
         r.router = L->w.router; r.router_bias = L->w.router_bias; r.E = D.n_experts; r.k = D.top_k;
         r.route_idx = io->route_idx; r.logits_r = L->s.logits_r;
         r.self_idx = L->s.self_idx; r.self_w = L->s.self_w; r.counters = L->s.counters;
-        if (L->profiling) HIPCHK(hipEventRecord(L->ev_t[0], st));
-        HIPCHK(launch_dec_r(a, r, st));
-        if (L->profiling) { HIPCHK(hipEventRecord(L->ev_t[1], st)); L->ev_t_used[0] = true; }
+        const KTime tr{L->profiling ? L->ev_t[0] : nullptr, L->profiling ? L->ev_t[1] : nullptr};
+        HIPCHK(launch_dec_r(a, r, st, &tr));
+        if (L->profiling) L->ev_t_used[0] = true;
     }
     if (!L->resident && (io->route_idx == nullptr || io->reactive)) {
         const int n = n_tok * D.top_k;
@@ -245,9 +245,9 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
         int rc = reactive_stage(L, src, n_tok, st);
         if (rc != MOE_OK) return rc;
     }
-    if (L->profiling) HIPCHK(hipEventRecord(L->ev_t[2], st));
-    HIPCHK(launch_dec_a(a, st));
-    if (L->profiling) { HIPCHK(hipEventRecord(L->ev_t[3], st)); L->ev_t_used[1] = true; }
+    const KTime ta{L->profiling ? L->ev_t[2] : nullptr, L->profiling ? L->ev_t[3] : nullptr};
+    HIPCHK(launch_dec_a(a, st, &ta));
+    if (L->profiling) L->ev_t_used[1] = true;
 
     DecBArgs b{};
     b.ev = a.ev; b.d = D.d_model; b.f = D.d_ff; b.fs = D.d_ff_shared; b.k = D.top_k; b.n_tok = n_tok;
@@ -262,9 +262,9 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
     b.hist_cur_m = L->w.hist_cur; b.hist_prev_m = L->w.hist_prev; b.hist_cur = io->hist_cur; b.hist_prev = io->hist_prev;
     b.pred_idx = io->pred_idx; b.pred_w = io->pred_w;
     b.err = L->s.err;
-    if (L->profiling) HIPCHK(hipEventRecord(L->ev_t[4], st));
-    HIPCHK(launch_dec_b(b, st));
-    if (L->profiling) { HIPCHK(hipEventRecord(L->ev_t[5], st)); L->ev_t_used[2] = true; }
+    const KTime tb{L->profiling ? L->ev_t[4] : nullptr, L->profiling ? L->ev_t[5] : nullptr};
+    HIPCHK(launch_dec_b(b, st, &tb));
+    if (L->profiling) L->ev_t_used[2] = true;
     HIPCHK(hipEventRecord(L->ev_done, st));
     L->done_recorded = true;
     return MOE_OK;

@@ -5,8 +5,22 @@
 #include <stdint.h>
 
 #include "moe_prerouter.h"
+#include <hip/hip_ext.h>
 
 namespace moe {
+
+// Optional kernel timestamps: when set, the launch records the kernel's own
+// start and end (the dispatch's begin/end timestamps), not the stream gaps.
+struct KTime {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+#define MOE_LAUNCH(kern, grid, block, shm, stream, tm, ...)                                                  \
+    do {                                                                                                     \
+        if ((tm) && (tm)->start)                                                                             \
+            hipExtLaunchKernelGGL(kern, grid, block, shm, stream, (tm)->start, (tm)->stop, 0, __VA_ARGS__);  \
+        else                                                                                                 \
+            hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);                                 \
+    } while (0)
 
 constexpr int kGroup = 64;
 constexpr int kMaxTopK = 8;
@@ -200,10 +214,10 @@ struct DecAArgs {
     int32_t* err;
     int nb_h, nb_head, nb_misc;
 };
-hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s);
+hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s, const KTime* tm = nullptr);
 bool dec_fast_path_ok(int d, int f, int fs, int n_tok, int k);
 int dec_a_hrows_per_block(int d);
-hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s);
+hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s, const KTime* tm = nullptr);
 int dec_a_blocks(int d, int f, int fs, int n_tok, int k, int E, int En, int r, bool sgate, int* nb_h, int* nb_head,
                  int* nb_misc);
 
@@ -218,7 +232,7 @@ struct DecBArgs {
     const int32_t* hist_cur; const int32_t* hist_prev; int32_t* pred_idx; float* pred_w;
     int32_t* err;
 };
-hipError_t launch_dec_b(const DecBArgs& a, hipStream_t s);
+hipError_t launch_dec_b(const DecBArgs& a, hipStream_t s, const KTime* tm = nullptr);
 
 struct SlotUpdate {
     int n;
