@@ -62,9 +62,9 @@ def gpu_layer(shape: synth.Shape, w: dict, *, fused: bool, resident: bool = True
         lora_rank=shape.r, lora_alpha=shape.alpha,
         act_dtype=moe.MOE_ACT_BF16 if act == "bf16" else moe.MOE_ACT_F32, max_tokens=max_tokens,
         expert_store=store, shared_blob=shared, shared_gate=dv(w["shared_gate"]), router=dv(w["router"]),
-        head=dv(w["head"]) if head else None, head_bias=dv(w.get("head_bias")),
+        head=dv(w["head"]) if head else None, head_bias=dv(w.get("head_bias")) if head else None,
         next_n_experts=shape.E if head else 0, next_top_k=shape.k if head else 0,
-        hist_cur=dv(w.get("hist_cur")), hist_prev=dv(w.get("hist_prev")),
+        hist_cur=dv(w.get("hist_cur")) if head else None, hist_prev=dv(w.get("hist_prev")) if head else None,
         lora_a=dv(w["lora_a"]), lora_b=dv(w["lora_b"]), norm_gamma=dv(w["gamma"]), rms_eps=shape.eps,
         fuse_norm_residual=fused, resident=resident, slab_slots=slab_slots)
 
