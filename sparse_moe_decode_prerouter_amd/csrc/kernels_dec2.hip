@@ -321,6 +321,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
     using G = BGeo<F>;
     constexpr int NPS = kPassB / kWaves;           // shared-expert passes per wave
     __shared__ float part[(kMaxAssign + kMaxTokB) * G::RB];
+    __shared__ uint32_t sl[kWaves][64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (blockIdx.x == 0) {
@@ -336,17 +337,12 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
     const BlobLayout L = BlobLayout::make(d, F);
     const int c = lane % G::LPR, rsub = lane / G::LPR;
 
-    // ---- level 0, identical in every wave. The digest loads go first; all
-    // other loads need no routing and are issued unconditionally (clamped
-    // indices, a stand-in blob when there is none), so waiting for the
-    // digest never waits for them.
-    const int n_active = a.meta[0];
-    const int n_valid = a.meta[1];
-    const int v_act = a.active[lane];
-    const int v_off = a.act_off[lane];
-    const int v_perm = a.perm[lane];
-    const float v_w = a.wsort[lane];
-    const float v_sg = (a.sgate ? a.sgate : a.wsort)[lane < n_tok ? lane : 0];
+    // ---- level 0, identical in every wave. The routing entries go first
+    // (K_A read them on every XCD, so they are L2 hits); all other loads need
+    // no routing and are issued unconditionally (clamped indices, stand-in
+    // pointers), so waiting for the routing never waits for them.
+    const RouteIn rin = route_load(a.route_idx, a.route_w, a.self_idx, a.self_w, n_assign);
+    const float v_sg = (a.sgate ? a.sgate : (const float*)a.err)[lane < n_tok ? lane : 0];
     // epilogue operands: thread -> (token, row)
     const int ep_n = n_tok * G::RB;
     const int ep_q = tid < ep_n ? tid : 0;
@@ -360,7 +356,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
     const uint8_t* sh_blob = has_shared && a.ev.shared ? a.ev.shared : a.ev.base;
     DownRegs<NPS> shr;
     down_issue<F, NPS, G::RPP>(shr, sh_blob, L, row0 + NPS * wave * G::RPP + rsub);
-    const int sh_tag = *(a.ev.shared_tag ? a.ev.shared_tag : a.meta);
+    const int sh_tag = *(a.ev.shared_tag ? a.ev.shared_tag : a.err);
     const bool sh_ok = has_shared && a.ev.shared && (!a.ev.shared_tag || sh_tag == a.ev.E);
     float4 shh[2];
     h_issue(shh, has_shared ? a.hs : a.h, c);
@@ -368,20 +364,26 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
     for (int i = tid; i < (n_assign + n_tok) * G::RB; i += kThreads) part[i] = 0.f;
     lds_barrier();
 
-    // ---- level 1: routed experts, two slots in flight per wave. The first
-    // pair is issued before the shared expert is computed (its loads are the
+    // ---- level 1: this wave sorts the routing (registers + its LDS slice),
+    // then the routed experts, two slots in flight per wave. The first pair
+    // is issued before the shared expert is computed (its loads are the
     // oldest, so waiting for them does not wait for the routed rows).
+    int me;
+    float mw;
+    route_merge(rin, a.route_idx != nullptr, k, n_assign, &me, &mw);
+    const WaveDigest W = wave_digest(n_assign, me, a.E, sl[wave]);
+    const int n_active = W.n_active, n_valid = W.n_valid;
     auto blob_of = [&](int s) -> const uint8_t* {
         if (s >= n_active) return nullptr;
-        const int e = __builtin_amdgcn_readlane(v_act, s);
+        const int e = __builtin_amdgcn_readlane((int)(W.sk >> 16), nth_set(W.starts, s));
         if (!a.ev.slot_of) return a.ev.base + (size_t)e * a.ev.blob;
         const int sl = a.ev.slot_of[e];
         if (sl < 0 || (a.ev.slot_tag && a.ev.slot_tag[sl] != e)) return nullptr;
         return a.ev.base + (size_t)sl * a.ev.blob;
     };
     auto slot_compute = [&](const DownRegs<kPassB>& R, const uint8_t* blob, int s, const float4 (&h0)[2]) {
-        const int p0 = __builtin_amdgcn_readlane(v_off, s);
-        const int p1 = s + 1 < n_active ? __builtin_amdgcn_readlane(v_off, s + 1) : n_valid;
+        const int p0 = nth_set(W.starts, s);
+        const int p1 = s + 1 < n_active ? nth_set(W.starts, s + 1) : n_valid;
         for (int p = p0; p < p1; ++p) {
             float4 hv[2];
             if (p == p0) { hv[0] = h0[0]; hv[1] = h0[1]; }
@@ -390,8 +392,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
             down_partial<kPassB>(R, hv, o);
             int pass;
             const float tot = row_reduce<float, kPassB, G::LPR>(o, &pass);
-            const int aid = __builtin_amdgcn_readlane(v_perm, p);
-            const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_w), p));
+            const int aid = __builtin_amdgcn_readlane((int)(W.sk & 0xFFFF), p);
+            const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mw), aid < n_assign ? aid : 0));
             if (blob && (c % (G::LPR / kPassB)) == 0 && aid >= 0 && aid < n_assign)
                 part[aid * G::RB + pass * G::RPP + rsub] = wgt * tot;
         }
@@ -403,8 +405,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
         b1 = blob_of(s1);
         down_issue<F, kPassB, G::RPP>(R0, b0 ? b0 : a.ev.base, L, row0 + rsub);
         down_issue<F, kPassB, G::RPP>(R1, b1 ? b1 : a.ev.base, L, row0 + rsub);
-        const int q0 = s0 < n_active ? __builtin_amdgcn_readlane(v_off, s0) : 0;
-        const int q1 = s1 < n_active ? __builtin_amdgcn_readlane(v_off, s1) : 0;
+        const int q0 = s0 < n_active ? nth_set(W.starts, s0) : 0;
+        const int q1 = s1 < n_active ? nth_set(W.starts, s1) : 0;
         h_issue(h0, a.h + (size_t)q0 * F, c);
         h_issue(h1, a.h + (size_t)q1 * F, c);
     };
@@ -455,6 +457,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
         if (a.fused) y += ep_x;
         a.y[(size_t)et * d + row0 + er] = y;
     }
+}
+
+__global__ void __launch_bounds__(kThreads) k_topk_job(TopkJob j, int n_tok) {
+    topk_rows(false, j.logits, j.En, j.kn, n_tok, j.bias, j.mc, j.hc, j.mp, j.hp, nullptr, j.kn, j.pred_idx, j.pred_w);
+}
+
+hipError_t launch_topk_job(const TopkJob& j, int n_tok, hipStream_t s) {
+    hipLaunchKernelGGL(k_topk_job, dim3(1), dim3(kThreads), 0, s, j, n_tok);
+    return hipGetLastError();
 }
 
 int dec_b_rows_per_block(int f) { return kPassB * (64 / (f / 8)); }

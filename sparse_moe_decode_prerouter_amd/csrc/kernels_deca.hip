@@ -18,6 +18,7 @@
 #include "device_common.h"
 #include "moe_internal.h"
 #include "dec_common.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -209,42 +210,6 @@ __device__ __forceinline__ void gateup_rows(const GateUpRegs& R, const ULds<D>& 
     if (c % (G::LPR / kAPass) == 0) h_out[row_first + pg * G::RPW + rsub] = ok ? silu_f32(g) * u : 0.f;
 }
 
-// ---- routing digest of one wave -------------------------------------------
-// Entry `lane` (< n) routes to expert e. Sorted by (expert, entry), invalid
-// entries last; sorted position p is held by lane p.
-struct WaveDigest {
-    int n_active, n_valid;
-    unsigned long long starts;   // bit p: sorted position p starts an expert
-    uint32_t sk;                 // sorted key of position `lane`: expert << 16 | entry
-};
-
-__device__ __forceinline__ WaveDigest wave_digest(int n, int e, int E, uint32_t* sl) {
-    const int lane = threadIdx.x & 63;
-    const bool in = lane < n;
-    const bool ok = in && e >= 0 && e < E;
-    const uint32_t key = in ? (((uint32_t)(ok ? e : 0xFFFF) << 16) | (uint32_t)lane) : 0xFFFFFFFFu;
-    int rank = 0;
-    for (int j = 0; j < n; ++j) rank += (uint32_t)__shfl((int)key, j, 64) < key;
-    if (in) sl[rank] = key;
-    wave_lds_sync();
-    WaveDigest W;
-    W.sk = in ? sl[lane] : 0xFFFFFFFFu;
-    const int ep = (int)(W.sk >> 16);
-    const bool valid = in && ep != 0xFFFF;
-    const int prev = __shfl_up(ep, 1, 64);
-    const bool start = valid && (lane == 0 || prev != ep);
-    W.starts = __ballot(start);
-    W.n_active = __popcll(W.starts);
-    W.n_valid = __popcll(__ballot(valid));
-    return W;
-}
-
-// position of the s-th set bit of m (s < popcount(m))
-__device__ __forceinline__ int nth_set(unsigned long long m, int s) {
-    for (int i = 0; i < s; ++i) m &= m - 1;
-    return __ffsll((long long)m) - 1;
-}
-
 // ---- the kernel -----------------------------------------------------------
 template <int D, bool XB>
 __global__ void __launch_bounds__(kThreads) k_dec_a(DecAArgs a) {
@@ -261,13 +226,7 @@ __global__ void __launch_bounds__(kThreads) k_dec_a(DecAArgs a) {
 
     // ---- level 0 (all threads, no branches around loads): routing entries
     // first, then x and gamma
-    const int li = lane < n_assign ? lane : 0;
-    const int32_t* ri = a.route_idx ? a.route_idx : a.self_idx;
-    const float* rw = a.route_idx ? a.route_w : a.self_w;
-    const int32_t* si = a.self_idx ? a.self_idx : ri;
-    const float* sw = a.self_idx ? a.self_w : rw;
-    const int vr = ri[li], vs = si[li];
-    const float vrw = rw[li], vsw = sw[li];
+    const RouteIn rin = route_load(a.route_idx, a.route_w, a.self_idx, a.self_w, n_assign);
     const int sh_tag = *(a.ev.shared_tag ? a.ev.shared_tag : a.meta);
     XThread X;
     x_issue<XB>(a, 0, e0, X.w);
@@ -299,10 +258,9 @@ __global__ void __launch_bounds__(kThreads) k_dec_a(DecAArgs a) {
         WaveDigest W{};
         if (!shared) {
             // ---- level 1: routing merged per token row, sorted in registers
-            const int first = __shfl(vr, (lane / k) * k, 64);
-            const bool given = a.route_idx && first >= 0;
-            const int me = lane < n_assign ? (given ? vr : vs) : -1;
-            const float mw = given ? vrw : vsw;
+            int me;
+            float mw;
+            route_merge(rin, a.route_idx != nullptr, k, n_assign, &me, &mw);
             W = wave_digest(n_assign, me, a.E, sl[wave]);
             if ((int)blockIdx.x * G::HROWS == a.fs && wave == 0) {
                 // the first routed block publishes the digest and the routing
@@ -357,6 +315,14 @@ __global__ void __launch_bounds__(kThreads) k_dec_a(DecAArgs a) {
         return;
     }
 
+    if ((int)blockIdx.x >= a.nb_h + a.nb_head + a.nb_misc) {
+        // the previous layer's head top-k, deferred to this launch (its logits
+        // were written two launches ago; the prediction is for the next step)
+        const TopkJob& j = a.topk;
+        topk_rows<kDeferMaxPer>(false, j.logits, j.En, j.kn, n_tok, j.bias, j.mc, j.hc, j.mp, j.hp, nullptr, j.kn,
+                                j.pred_idx, j.pred_w);
+        return;
+    }
     // ---- bf16 rows accumulated in fp64: head rows, or LoRA A rows + shared gate
     const bool role_head = (int)blockIdx.x < a.nb_h + a.nb_head;
     const int row0 = (blockIdx.x - (role_head ? a.nb_h : a.nb_h + a.nb_head)) * G::BROWS + wave * G::RPW;
@@ -412,7 +378,7 @@ int dec_a_blocks(int d, int f, int fs, int n_tok, int k, int E, int En, int r, b
 hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s, const KTime* tm) {
     const int hr = dec_a_hrows_per_block(a.d);
     if (a.n_tok * a.k > kMaxAssign || a.f % hr || a.fs % hr) return hipErrorInvalidValue;
-    const dim3 grid(a.nb_h + a.nb_head + a.nb_misc), block(kThreads);
+    const dim3 grid(a.nb_h + a.nb_head + a.nb_misc + (a.topk.pred_idx ? 1 : 0)), block(kThreads);
     const bool xb = a.x_is_bf16 != 0;
     switch (a.d) {
         case 256: if (xb) MOE_LAUNCH((k_dec_a<256, true>), grid, block, 0, s, tm, a); else MOE_LAUNCH((k_dec_a<256, false>), grid, block, 0, s, tm, a); break;

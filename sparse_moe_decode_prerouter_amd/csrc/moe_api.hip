@@ -195,10 +195,18 @@ __global__ void k_merge_route(const int32_t* ridx, const int32_t* sidx, int32_t*
 
 int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill);
 
-int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
+// defer_in: a previous layer's head top-k to run inside this layer's K_A.
+// defer_out (stack mode): this layer's head top-k is not run here but handed
+// back, for the next layer's K_A to run (its prediction is for the next step).
+int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const TopkJob* defer_in = nullptr,
+               TopkJob* defer_out = nullptr) {
     const moe_layer_desc& D = L->desc;
-    // shapes outside the fused two-kernel path take the general grouped-GEMV path
-    if (!dec_fast_path_ok(D.d_model, D.d_ff, D.d_ff_shared, n_tok, D.top_k)) return run_prefill(L, io, n_tok, st, false);
+    if (defer_out) defer_out->pred_idx = nullptr;
+    // shapes outside the fused two-kernel path take the general grouped-GEMM path
+    if (!dec_fast_path_ok(D.d_model, D.d_ff, D.d_ff_shared, n_tok, D.top_k)) {
+        if (defer_in && defer_in->pred_idx) HIPCHK(launch_topk_job(*defer_in, n_tok, st));
+        return run_prefill(L, io, n_tok, st, false);
+    }
     const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
     if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
     const bool need_router = io->route_idx == nullptr || io->self_rows;
@@ -223,6 +231,7 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
     a.err = L->s.err;
     dec_a_blocks(D.d_model, D.d_ff, D.d_ff_shared, n_tok, D.top_k, D.n_experts, a.En, D.lora_rank,
                  a.sgate_w != nullptr, &a.nb_h, &a.nb_head, &a.nb_misc);
+    if (defer_in && defer_in->pred_idx) a.topk = *defer_in;
 
     if (need_router) {
         RouteArgs r{};
@@ -251,8 +260,9 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
 
     DecBArgs b{};
     b.ev = a.ev; b.d = D.d_model; b.f = D.d_ff; b.fs = D.d_ff_shared; b.k = D.top_k; b.n_tok = n_tok;
-    b.meta = L->s.sort_meta; b.active = L->s.active; b.act_off = L->s.act_off; b.perm = L->s.perm;
-    b.wsort = L->s.wsort; b.sgate = (D.d_ff_shared && L->w.shared_gate) ? L->s.sgate : nullptr;
+    b.E = D.n_experts;
+    b.route_idx = a.route_idx; b.route_w = a.route_w; b.self_idx = a.self_idx; b.self_w = a.self_w;
+    b.sgate = (D.d_ff_shared && L->w.shared_gate) ? L->s.sgate : nullptr;
     b.h = L->s.h; b.hs = L->s.hs;
     b.x = (const float*)io->x_in; b.fused = fused;
     b.au = L->s.au; b.lora_b = D.lora_rank ? L->w.lora_b : nullptr; b.r = D.lora_rank;
@@ -261,6 +271,13 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
     b.logits_h = L->s.logits_h; b.En = D.next_n_experts; b.kn = D.next_top_k; b.head_bias = L->w.head_bias;
     b.hist_cur_m = L->w.hist_cur; b.hist_prev_m = L->w.hist_prev; b.hist_cur = io->hist_cur; b.hist_prev = io->hist_prev;
     b.pred_idx = io->pred_idx; b.pred_w = io->pred_w;
+    if (defer_out && io->pred_idx && D.next_n_experts <= 64 * kDeferMaxPer) {
+        TopkJob& j = *defer_out;
+        j.logits = L->s.logits_h; j.En = D.next_n_experts; j.kn = D.next_top_k; j.bias = L->w.head_bias;
+        j.mc = L->w.hist_cur; j.hc = io->hist_cur; j.mp = L->w.hist_prev; j.hp = io->hist_prev;
+        j.pred_idx = io->pred_idx; j.pred_w = io->pred_w;
+        b.pred_idx = nullptr; b.pred_w = nullptr;
+    }
     b.err = L->s.err;
     const KTime tb{L->profiling ? L->ev_t[4] : nullptr, L->profiling ? L->ev_t[5] : nullptr};
     HIPCHK(launch_dec_b(b, st, &tb));
@@ -550,6 +567,8 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
     if (!first_step && (!route_idx || !route_w)) return MOE_E_INVALID;
     const int k = S->layers[0]->desc.top_k;
     const size_t per = (size_t)n_tok * k;
+    if (n_tok * k > 4096 || n_tok > 256) return MOE_E_UNSUPPORTED;
+    TopkJob pend{};
     for (int l = 0; l < S->n; ++l) {
         moe_layer* L = S->layers[l];
         moe_io io{};
@@ -566,9 +585,15 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
             io.hist_cur = first_step ? nullptr : route_idx + (l + 1) * per;
             io.hist_prev = hist_prev ? hist_prev + (l + 1) * per : nullptr;
         }
-        int rc = moe_decode_step(L, &io, n_tok, stream);
+        int rc = check_io(L, &io, n_tok);
         if (rc != MOE_OK) return rc;
+        TopkJob out{};
+        rc = run_decode(L, &io, n_tok, (hipStream_t)stream, pend.pred_idx ? &pend : nullptr,
+                        l + 1 < S->n ? &out : nullptr);
+        if (rc != MOE_OK) return rc;
+        pend = out;
     }
+    if (pend.pred_idx) HIPCHK(launch_topk_job(pend, n_tok, (hipStream_t)stream));
     return MOE_OK;
 }
 

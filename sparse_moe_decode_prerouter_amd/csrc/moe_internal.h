@@ -200,6 +200,15 @@ int prefill_max_tiles(int T, int K, int E);
 bool prefill_mm_ok(int d, int f, int fs);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
+// A head top-k run by a later launch than the one that wrote its logits
+// (only for E_next <= 64 * kDeferMaxPer; larger heads keep their own launch).
+constexpr int kDeferMaxPer = 4;
+struct TopkJob {
+    const double* logits; int En; int kn; const float* bias;
+    const float* mc; const int32_t* hc; const float* mp; const int32_t* hp;
+    int32_t* pred_idx; float* pred_w;
+};
+
 struct DecAArgs {
     const void* x; int x_is_bf16; int fused; const float* gamma; float eps; int act_bf16; int d; int n_tok;
     const int32_t* route_idx; const float* route_w;   // given routing (rows with idx < 0: self) or nullptr
@@ -213,17 +222,19 @@ struct DecAArgs {
     int32_t* used_idx; float* used_w; int32_t* user_used_idx; float* user_used_w;
     int32_t* err;
     int nb_h, nb_head, nb_misc;
+    TopkJob topk;          // pred_idx == nullptr: none
 };
 hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s, const KTime* tm = nullptr);
 bool dec_fast_path_ok(int d, int f, int fs, int n_tok, int k);
 int dec_a_hrows_per_block(int d);
+int dec_b_rows_per_block(int f);
 hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s, const KTime* tm = nullptr);
 int dec_a_blocks(int d, int f, int fs, int n_tok, int k, int E, int En, int r, bool sgate, int* nb_h, int* nb_head,
                  int* nb_misc);
 
 struct DecBArgs {
-    ExpertView ev; int d; int f; int fs; int k; int n_tok;
-    const int32_t* meta; const int32_t* active; const int32_t* act_off; const int32_t* perm; const float* wsort;
+    ExpertView ev; int d; int f; int fs; int k; int n_tok; int E;
+    const int32_t* route_idx; const float* route_w; const int32_t* self_idx; const float* self_w;
     const float* sgate; const float* h; const float* hs;
     const float* x; int fused; const float* au; const uint16_t* lora_b; int r; float lora_scale;
     float* y;
@@ -233,6 +244,7 @@ struct DecBArgs {
     int32_t* err;
 };
 hipError_t launch_dec_b(const DecBArgs& a, hipStream_t s, const KTime* tm = nullptr);
+hipError_t launch_topk_job(const TopkJob& j, int n_tok, hipStream_t s);
 
 struct SlotUpdate {
     int n;

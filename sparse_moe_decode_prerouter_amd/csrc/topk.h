@@ -78,6 +78,8 @@ __device__ __forceinline__ void topk_row(bool coherent, const double* logits, in
     }
 }
 
+// MAXPER bounds the register arrays instantiated (E <= 64 * MAXPER).
+template <int MAXPER = 16>
 __device__ __forceinline__ void topk_rows(bool coherent, const double* logits, int E, int k, int n_tok, const float* bias,
                                  const float* mc, const int32_t* hc, const float* mp, const int32_t* hp,
                                  const int32_t* route_idx, int kroute, int32_t* out_idx, float* out_w) {
@@ -85,10 +87,10 @@ __device__ __forceinline__ void topk_rows(bool coherent, const double* logits, i
     for (int t = wave; t < n_tok; t += nwaves) {
         if (route_idx && route_idx[(size_t)t * kroute] >= 0) continue;   // row has its routing
         if (E <= 64) topk_row<1>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
-        else if (E <= 128) topk_row<2>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
-        else if (E <= 256) topk_row<4>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
-        else if (E <= 512) topk_row<8>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
-        else topk_row<16>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
+        else if (E <= 128 || MAXPER < 4) topk_row<(MAXPER < 2 ? MAXPER : 2)>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
+        else if (E <= 256 || MAXPER < 8) topk_row<(MAXPER < 4 ? MAXPER : 4)>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
+        else if (E <= 512 || MAXPER < 16) topk_row<(MAXPER < 8 ? MAXPER : 8)>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
+        else topk_row<MAXPER>(coherent, logits, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
     }
 }
 
