@@ -16,7 +16,7 @@
 // with fp32 accumulation. The expert hidden state enters the down projection
 // as bf16 hi + lo (two MFMAs), so no operand is rounded beyond the
 // activation dtype.
-#include "device_common.h"
+#include "dec_common.h"
 #include "moe_internal.h"
 #include "topk.h"
 
@@ -44,23 +44,49 @@ __device__ __forceinline__ u32x4 nib4(uint32_t w) {
     return r;
 }
 
+// nib4 with the mask and the exponent held in registers (m = 0x000F000F,
+// c = 0x43004300), so that each pair is one and-or after its shift
+__device__ __forceinline__ u32x4 nib4v(uint32_t w, uint32_t m, uint32_t c) {
+    u32x4 r;
+    r.x = (w & m) | c;
+    r.y = ((w >> 4) & m) | c;
+    r.z = ((w >> 8) & m) | c;
+    r.w = ((w >> 12) & m) | c;
+    return r;
+}
+
 int prefill_max_tiles(int T, int K, int E) {
     const int nk = T * K;
     return (nk + kTileM - 1) / kTileM + (nk < E ? nk : E) + (T + kTileM - 1) / kTileM + 1;
 }
 
 // ---------------------------------------------------------------------------
-// Tile list: entry = (slot + 1) << 16 | first assignment of the tile within
-// the slot; slot -1 (code 0) is the shared expert with token tiles. meta[2]
-// = number of tiles. One block.
+// Tile list: the 16-row tiles of every active expert's sorted assignments,
+// then the 16-token tiles of the shared expert. Each record carries its blob,
+// resolved (and its staging checked) here once. meta[2] = tiles, meta[3] =
+// routed tiles. One block.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) k_pf_tiles(PrefillArgs a) {
     __shared__ int wsum[16];
     __shared__ int total;
+    const GemvArgs& g = a.g;
+    const ExpertView& ev = g.ev;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n_active = a.g.meta[0];
-    int cnt = 0;
-    if (tid < n_active) cnt = (a.g.act_off[tid + 1] - a.g.act_off[tid] + kTileM - 1) / kTileM;
+    const int n_active = g.meta[0];
+    int cnt = 0, off0 = 0, off1 = 0, blob = -1;
+    if (tid < n_active) {
+        off0 = g.act_off[tid];
+        off1 = g.act_off[tid + 1];
+        cnt = (off1 - off0 + kTileM - 1) / kTileM;
+        const int e = g.active[tid];
+        if (!ev.slot_of) {
+            blob = e;
+        } else {
+            const int sl = ev.slot_of[e];
+            blob = (sl < 0 || (ev.slot_tag && ev.slot_tag[sl] != e)) ? -1 : sl;
+        }
+        if (blob < 0) set_err(g.err, ERR_NOT_STAGED);
+    }
     int incl = cnt;
     for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(incl, o, 64);
@@ -75,45 +101,37 @@ __global__ void __launch_bounds__(1024) k_pf_tiles(PrefillArgs a) {
     }
     __syncthreads();
     const int start = wsum[wave] + incl - cnt;
-    for (int i = 0; i < cnt; ++i) a.tiles[start + i] = ((uint32_t)(tid + 1) << 16) | (uint32_t)(i * kTileM);
-    const int ns = a.g.fs ? (a.g.n_tok + kTileM - 1) / kTileM : 0;
-    for (int i = tid; i < ns; i += 1024) a.tiles[total + i] = (uint32_t)(i * kTileM);
-    if (tid == 0) a.meta_w[2] = total + ns;
+    for (int i = 0; i < cnt; ++i) {
+        const int p0 = off0 + i * kTileM;
+        *(int4*)(a.tiles + 4 * (start + i)) = make_int4(tid, p0, min(kTileM, off1 - p0), blob);
+    }
+    const int ns = g.fs ? (g.n_tok + kTileM - 1) / kTileM : 0;
+    int sblob = -1;
+    if (ns && ev.shared) {
+        if (ev.shared_tag && *ev.shared_tag != ev.E) { if (tid == 0) set_err(g.err, ERR_NOT_STAGED); }
+        else sblob = -2;
+    }
+    for (int i = tid; i < ns; i += 1024)
+        *(int4*)(a.tiles + 4 * (total + i)) = make_int4(-1, i * kTileM, min(kTileM, g.n_tok - i * kTileM), sblob);
+    if (tid == 0) { a.meta_w[2] = total + ns; a.meta_w[3] = total; }
 }
 
 struct PfItem {
     int slot;     // -1: shared expert
     int p0;       // first position (sorted assignment) or first token
     int M;        // rows of the tile (<= 16)
+    int blob;     // >= 0: blob index, -2: shared blob, -1: none
 };
 
 __device__ __forceinline__ PfItem pf_item(const PrefillArgs& a, int tile) {
-    const uint32_t code = a.tiles[tile];
+    const int4 t = *(const int4*)(a.tiles + 4 * tile);
     PfItem it;
-    it.slot = (int)(code >> 16) - 1;
-    const int m0 = (int)(code & 0xFFFFu);
-    if (it.slot < 0) {
-        it.p0 = m0;
-        it.M = min(kTileM, a.g.n_tok - m0);
-    } else {
-        it.p0 = a.g.act_off[it.slot] + m0;
-        it.M = min(kTileM, a.g.act_off[it.slot + 1] - it.p0);
-    }
+    it.slot = t.x; it.p0 = t.y; it.M = t.z; it.blob = t.w;
     return it;
 }
 
-__device__ __forceinline__ const uint8_t* pf_blob(const GemvArgs& g, int slot) {
-    const ExpertView& ev = g.ev;
-    if (slot < 0) {
-        if (!ev.shared) return nullptr;
-        if (ev.shared_tag && *ev.shared_tag != ev.E) { set_err(g.err, ERR_NOT_STAGED); return nullptr; }
-        return ev.shared;
-    }
-    const int e = g.active[slot];
-    if (!ev.slot_of) return ev.base + (size_t)e * ev.blob;
-    const int s = ev.slot_of[e];
-    if (s < 0 || (ev.slot_tag && ev.slot_tag[s] != e)) { set_err(g.err, ERR_NOT_STAGED); return nullptr; }
-    return ev.base + (size_t)s * ev.blob;
+__device__ __forceinline__ const uint8_t* pf_blob(const GemvArgs& g, int blob) {
+    return blob >= 0 ? g.ev.base + (size_t)blob * g.ev.blob : (blob == -2 ? g.ev.shared : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -210,7 +228,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
     const int f = shared ? g.fs : g.f;
     const int rb0 = blockIdx.y * kGuRows;
     if (rb0 >= f || it.M <= 0) return;
-    const uint8_t* blob = pf_blob(g, it.slot);
+    const uint8_t* blob = pf_blob(g, it.blob);
     const int d = g.d, G = d / 64, NS = d / kStageK;
     if (tid < kTileM) {
         const int p = it.p0 + (tid < it.M ? tid : it.M - 1);
@@ -295,168 +313,331 @@ __global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Down projection with LDS staging (same scheme as gate/up). Block = 16
-// positions x kDnRows rows of W_d; K = f walked in stages of 4 groups. A is
-// the expert hidden state, staged as fp32 and split into bf16 hi + lo when
-// read; its per-group sums (the b-term) come from the same values. Output:
-// O[assignment][d] (routed) or O_s[token][d] (shared), unweighted.
-// ---------------------------------------------------------------------------
-constexpr int kDnRows = 128;
-constexpr int kDnSub = 1;                    // 128-row sub-blocks per block (more measured slower)
-constexpr int kHRow = kStageK * 4 + 16;      // LDS bytes per position row of a stage (padded)
-
-struct DnLds {
-    uint8_t b[kDnRows * 128];
-    uint32_t sc[kDnRows][4];
-    uint8_t h[kTileM * kHRow];
+template <int V>
+struct IntC {
+    static constexpr int value = V;
 };
 
-struct DnRegs {
-    u32x4 b[kDnRows * 8 / 256];
-    u32x4 sc;
-    float4 h[kTileM * kStageK / 4 / 256];
+// ---------------------------------------------------------------------------
+// Down projection: a persistent grouped GEMM. A stage is 16 KB of W_d codes,
+// R = 32768 / f whole rows (contiguous in the blob), plus their scales; a
+// tile's stages walk its d / R row blocks. Block b of the grid takes the
+// stages [b Z / nb, (b + 1) Z / nb) of the flat list (routed tiles, then the
+// shared expert's), so every block streams the same number of bytes. Stages go
+// straight from HBM into a ring of kDnNst LDS buffers (direct-to-LDS loads,
+// kDnNst - 1 stages in flight); piece p of row r sits at slot p ^ (r mod n)
+// (n = 16-byte pieces per row) so that the MFMA reads of 16 rows spread over
+// the banks. A tile's expert hidden state h (16 positions x f, fp32) comes into
+// LDS the same way one tile ahead and is split once per tile into bf16 hi + lo
+// MFMA operands and per-group sums, held in registers. The block's tile records
+// and output rows are read once, at the start, so the loop issues no load that
+// it has to wait for. Wave w (of 8) owns rows 16 (w mod 4) + 64 j (+ 0..15) of
+// each stage and half of the groups (w / 4); the upper half's partial sums go
+// through LDS to the lower half, which adds them one stage later and stores.
+// Outputs: O[assignment][d] (routed) or O_s[token][d] (shared), unweighted.
+// ---------------------------------------------------------------------------
+constexpr int kDnThreads = 512;
+constexpr int kDnStage = 16384;              // code bytes per stage
+constexpr int kDnNst = 6;                    // ring depth
+constexpr int kDnMaxF = 512;                 // largest f (and f_shared); f >= 256
+constexpr int kDnTiles = 32;                 // tile records kept in LDS per block
+constexpr int kHstRow = kDnMaxF + 4;         // floats per position row of the staged h (padded)
+
+struct DnStage {
+    uint8_t b[kDnStage];                     // R rows of f / 2 bytes, pieces swizzled
+    uint8_t sc[kDnStage / 8];                // their (s, b) pairs: f / 16 bytes per row
+};
+struct DnOps {
+    float hst[kTileM * kHstRow];             // the next tile's h (fp32), as loaded
+    f32x4 part[2][2][4][64];                 // [stage parity][j][row tile][lane]: upper-half partial sums
+    int4 tinfo[kDnTiles];                    // the block's tile records
+    int prow[kDnTiles][kTileM];              // their output rows
 };
 
-__device__ __forceinline__ void dn_stage_load(DnRegs& R, int st, const uint8_t* wb, const BlobLayout& L, int d,
-                                              int f, int rb0, const int* prow, const float* hbase) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kDnRows * 8 / 256; ++i) {
-        const int pi = tid + 256 * i, r = pi >> 3, ps = pi & 7, pg = ps ^ (r & 7);
-        int row = rb0 + r;
-        row = row < d ? row : d - 1;
-        R.b[i] = *(const u32x4*)(wb + L.down_q + (size_t)row * (f / 2) + st * (kStageK / 2) + 16 * pg);
-    }
-    if (tid < kDnRows) {
-        int row = rb0 + tid;
-        row = row < d ? row : d - 1;
-        R.sc = *(const u32x4*)(wb + L.down_sb + (size_t)row * (f / 16) + st * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < kTileM * kStageK / 4 / 256; ++i) {
-        const int pa = tid + 256 * i, m = pa / (kStageK / 4), k = pa % (kStageK / 4);
-        R.h[i] = *(const float4*)(hbase + (size_t)prow[m] * f + st * kStageK + 4 * k);
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at LDS byte address lds + 16 l (lds wave-uniform). Written as asm so that
+// the compiler does not guard every later LDS read of the ring with a wait for
+// all of these loads; the ring's own waits (vm_wait) order them instead.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved; the clobber still keeps it live-safe
+__device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds) {
+    const uint32_t off = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(off), "v"(gptr) : "memory", "m0");
+}
+// The same with a 64-bit scalar base and a 32-bit per-lane offset.
+__device__ __forceinline__ void lds_dma16s(uint32_t voff, uint64_t sbase, const void* lds) {
+    const uint32_t off = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(off), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited for)
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// wait until this wave's loads of the stage `ahead` stages before the newest
+// issued one have landed (2 loads per stage per wave, 3 for waves 0-1; any
+// other load issued after that stage only makes the wait longer)
+__device__ __forceinline__ void dn_wait(int ahead, bool sc_wave) {
+    if (sc_wave) {
+        switch (ahead) {
+            case 0: vm_wait<0>(); break;
+            case 1: vm_wait<3>(); break;
+            case 2: vm_wait<6>(); break;
+            case 3: vm_wait<9>(); break;
+            default: vm_wait<12>(); break;
+        }
+    } else {
+        switch (ahead) {
+            case 0: vm_wait<0>(); break;
+            case 1: vm_wait<2>(); break;
+            case 2: vm_wait<4>(); break;
+            case 3: vm_wait<6>(); break;
+            default: vm_wait<8>(); break;
+        }
     }
 }
 
-__device__ __forceinline__ void dn_stage_store(const DnRegs& R, DnLds& S) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kDnRows * 8 / 256; ++i) *(u32x4*)&S.b[(tid + 256 * i) * 16] = R.b[i];
-    if (tid < kDnRows) *(u32x4*)&S.sc[tid][0] = R.sc;
-#pragma unroll
-    for (int i = 0; i < kTileM * kStageK / 4 / 256; ++i) {
-        const int pa = tid + 256 * i, m = pa / (kStageK / 4), k = pa % (kStageK / 4);
-        *(float4*)&S.h[m * kHRow + 16 * k] = R.h[i];
-    }
-}
+// stages of one tile of width f: d / R row blocks of R = 32768 / f rows
+__device__ __host__ __forceinline__ int dn_tile_stages(int d, int f) { return d * f / (2 * kDnStage); }
 
-__global__ void __launch_bounds__(256) k_pf_down(PrefillArgs a) {
+__global__ void __launch_bounds__(kDnThreads) k_pf_down(PrefillArgs a) {
+    static_assert(kDnNst - 2 <= 4, "dn_wait covers up to 4 stages ahead");
+    __shared__ __align__(16) DnStage ring[kDnNst];
+    __shared__ __align__(16) DnOps S;
     const GemvArgs& g = a.g;
-    __shared__ __align__(16) DnLds S[2];
-    __shared__ int prow[kTileM];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if ((int)blockIdx.x >= g.meta[2]) return;
-    const PfItem it = pf_item(a, blockIdx.x);
-    const bool shared = it.slot < 0;
-    const int f = shared ? g.fs : g.f;
     const int d = g.d;
-    const int rbb = blockIdx.y * kDnRows * kDnSub;           // block's first row
-    if (rbb >= d || it.M <= 0) return;
-    const uint8_t* blob = pf_blob(g, it.slot);
-    const int NS = f / kStageK;
-    const int nsub = min(kDnSub, (d - rbb + kDnRows - 1) / kDnRows);
-    const int NZ = nsub * NS;                                 // stages over all sub-blocks
-    const float* hbase = shared ? g.hs : g.h;
-    if (tid < kTileM) prow[tid] = it.p0 + (tid < it.M ? tid : it.M - 1);
-    __syncthreads();
-    const BlobLayout L = BlobLayout::make(d, f);
-    const uint8_t* wb = blob ? blob : g.ev.base;
-    DnRegs R;
-    dn_stage_load(R, 0, wb, L, d, f, rbb, prow, hbase);
-    dn_stage_store(R, S[0]);
-    __syncthreads();
-    const int ml = lane & 15, pc = lane >> 4;
-    constexpr int NJ = kDnRows / 64;
-    const bool ok = blob != nullptr;
-    f32x4 acc[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int z = 0; z < NZ; ++z) {
-        const DnLds& C = S[z & 1];
-        const int st = z % NS, rb0 = rbb + (z / NS) * kDnRows;
-        if (z + 1 < NZ) dn_stage_load(R, (z + 1) % NS, wb, L, d, f, rbb + ((z + 1) / NS) * kDnRows, prow, hbase);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            // this lane's 16 elements of group q: pieces 2pc, 2pc+1 of position ml
-            float e[16];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float4 x = *(const float4*)&C.h[ml * kHRow + q * 256 + pc * 64 + 16 * v];
-                e[4 * v] = x.x; e[4 * v + 1] = x.y; e[4 * v + 2] = x.z; e[4 * v + 3] = x.w;
-            }
-            u32x4 ahi[2], alo[2];
-            float hs = 0.f;
-#pragma unroll
-            for (int pq = 0; pq < 2; ++pq) {
-                uint32_t hi[8], lo[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    hi[i] = f32_to_bf16(e[8 * pq + i]);
-                    lo[i] = f32_to_bf16(e[8 * pq + i] - bf16_to_f32(hi[i]));
-                    hs += bf16_to_f32(hi[i]) + bf16_to_f32(lo[i]);
-                }
-                ahi[pq].x = hi[0] | (hi[4] << 16); ahi[pq].y = hi[1] | (hi[5] << 16);
-                ahi[pq].z = hi[2] | (hi[6] << 16); ahi[pq].w = hi[3] | (hi[7] << 16);
-                alo[pq].x = lo[0] | (lo[4] << 16); alo[pq].y = lo[1] | (lo[5] << 16);
-                alo[pq].z = lo[2] | (lo[6] << 16); alo[pq].w = lo[3] | (lo[7] << 16);
-            }
-            // group sum for position ml, then the sums of the C rows 4pc..4pc+3
-            hs += __shfl_xor(hs, 16, 64);
-            hs += __shfl_xor(hs, 32, 64);
-            float hsm[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hsm[i] = __shfl(hs, 4 * pc + i, 64);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int r = wave * (16 * NJ) + 16 * j + ml;
-                const int p = 2 * q + (pc >> 1);
-                const u32x2 w = *(const u32x2*)&C.b[r * 128 + ((p ^ (r & 7)) << 4) + ((pc & 1) << 3)];
-                const uint32_t sb = C.sc[r][q];
-                const u32x4 b0 = nib4(w.x), b1 = nib4(w.y);
-                f32x4 pp = {0.f, 0.f, 0.f, 0.f};
-                pp = mfma16(ahi[0], b0, pp);
-                pp = mfma16(ahi[1], b1, pp);
-                pp = mfma16(alo[0], b0, pp);
-                pp = mfma16(alo[1], b1, pp);
-                const float sv = f16_to_f32(sb & 0xFFFF), cv = f16_to_f32(sb >> 16) - 128.f * sv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[j][i] += sv * pp[i] + cv * hsm[i];
-            }
-        }
-        if (st == NS - 1) {
-            // sub-block done: write its rows, start the next one
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int n = rb0 + wave * (16 * NJ) + 16 * j + ml;
-                if (n < d) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int m = 4 * pc + i;
-                        if (m >= it.M) continue;
-                        const float o = ok ? acc[j][i] : 0.f;
-                        if (shared) a.obs[(size_t)(it.p0 + m) * d + n] = o;
-                        else a.ob[(size_t)g.perm[it.p0 + m] * d + n] = o;
-                    }
-                }
-                acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        if (z + 1 < NZ) dn_stage_store(R, S[(z + 1) & 1]);
-        __syncthreads();
+    const int nt = g.meta[2], nrt = g.meta[3];
+    const int nsr = dn_tile_stages(d, g.f), nss = g.fs ? dn_tile_stages(d, g.fs) : 1;
+    const int zr = nrt * nsr, Z = zr + (nt - nrt) * nss;
+    const int z0 = (int)((long long)Z * blockIdx.x / gridDim.x);
+    const int z1 = (int)((long long)Z * (blockIdx.x + 1) / gridDim.x);
+    if (z0 >= z1) return;
+    auto tile_of = [&](int z) { return z < zr ? z / nsr : nrt + (z - zr) / nss; };
+    auto sidx_of = [&](int z) { return z < zr ? z % nsr : (z - zr) % nss; };
+    const int t0 = tile_of(z0);
+    const int ntl = tile_of(z1 - 1) - t0 + 1;
+
+    // ---- the block's tile records and output rows (the launch sizes the grid
+    // so that no block spans more than kDnTiles tiles)
+    if (ntl > kDnTiles) {
+        if (tid == 0) set_err(g.err, ERR_BAD_INDEX);
+        return;
     }
+    if (tid < ntl) S.tinfo[tid] = *(const int4*)(a.tiles + 4 * (t0 + tid));
+    lds_barrier();
+    for (int i = tid; i < ntl * kTileM; i += kDnThreads) {
+        const int4 ti = S.tinfo[i / kTileM];
+        const int m = i % kTileM, p = ti.y + (m < ti.z ? m : ti.z - 1);
+        S.prow[i / kTileM][m] = ti.x < 0 ? p : g.perm[p];
+    }
+    auto tile_rec = [&](int t) -> int4 { return S.tinfo[t - t0]; };
+
+    // ---- h of tile t (16 positions x f fp32, rows past M repeat the last)
+    // into S.hst, row m at m * kHstRow (a wave's 64 pieces lie in one row)
+    auto issue_h = [&](int t) {
+        const int4 ti = tile_rec(t);
+        const bool sh = ti.x < 0;
+        const int f = sh ? g.fs : g.f;
+        const float* hb = sh ? g.hs : g.h;
+        const int lpr = f == 512 ? 7 : 6;            // log2 of the 16-byte pieces per row
+        for (int j = 0; j < 16 * f / 4 / kDnThreads; ++j) {
+            const int pw = wave * 64 + kDnThreads * j, pi = pw + lane;
+            const int m = pi >> lpr, c4 = pi & ((1 << lpr) - 1);
+            const int mw = pw >> lpr, cw = pw & ((1 << lpr) - 1);
+            const float* src = hb + (size_t)(ti.y + (m < ti.z ? m : ti.z - 1)) * f + 4 * c4;
+            lds_dma16(src, &S.hst[mw * kHstRow + 4 * cw]);
+        }
+    };
+
+    // ---- loader: issues the next stage (tile lt, stage ls of it) into ring
+    // slot lslot. Per tile: scalar bases of W_d's codes and scales, and the
+    // per-thread byte offsets of its pieces within a stage.
+    constexpr int kPj = kDnStage / 16 / kDnThreads;            // code pieces per thread per stage
+    int lt = t0, ls = sidx_of(z0), lns = 0, lslot = 0;
+    uint64_t lq = 0, lsb = 0;
+    uint32_t lvq[kPj];
+    auto loader_tile = [&](int t) {
+        const int4 ti = tile_rec(t);
+        const int f = ti.x < 0 ? g.fs : g.f;
+        const uint8_t* blob = pf_blob(g, ti.w);
+        const uint8_t* wb = blob ? blob : g.ev.base;
+        const BlobLayout L = BlobLayout::make(d, f);
+        lq = (uint64_t)(uintptr_t)(wb + L.down_q);
+        lsb = (uint64_t)(uintptr_t)(wb + L.down_sb);
+        lns = dn_tile_stages(d, f);
+        const int sh = f == 512 ? 4 : 3;                       // log2 of the pieces per row
+#pragma unroll
+        for (int j = 0; j < kPj; ++j) {
+            const int pi = wave * 64 + kDnThreads * j + lane, r = pi >> sh;
+            const int pg = (pi & ((1 << sh) - 1)) ^ (r & ((1 << sh) - 1));
+            lvq[j] = (uint32_t)(r * (f / 2) + 16 * pg);
+        }
+    };
+    auto issue = [&]() {
+        DnStage& st = ring[lslot];
+        const uint64_t bq = lq + (uint64_t)ls * kDnStage;
+#pragma unroll
+        for (int j = 0; j < kPj; ++j) lds_dma16s(lvq[j], bq, &st.b[(wave * 64 + kDnThreads * j) * 16]);
+        if (wave < 2)
+            lds_dma16s((uint32_t)(wave * 64 + lane) * 16u, lsb + (uint64_t)ls * (kDnStage / 8), &st.sc[wave * 64 * 16]);
+        lslot = lslot + 1 == kDnNst ? 0 : lslot + 1;
+        if (++ls == lns) {
+            ls = 0;
+            if (++lt < t0 + ntl) loader_tile(lt);
+        }
+    };
+
+    lds_barrier();                                            // tile records visible
+    issue_h(t0);
+    loader_tile(t0);
+    for (int i = 0; i < kDnNst - 1 && z0 + i < z1; ++i) issue();
+
+    // The A operand of this wave's groups (half of them) of the current tile,
+    // in registers: lane (ml, pc) holds, for group gq = 4 kh + q, elements
+    // 64 gq + 16 pc .. + 15 of position ml as bf16 hi and lo pairs (t = 0, 1:
+    // 8 elements each), and the group sums of positions 4 pc .. 4 pc + 3.
+    const int rt = wave & 3, kh = wave >> 2;
+    u32x4 rah[4][2], ral[4][2];
+    float4 rhs[4];
+    int ctile = -1, M = 0, cs = sidx_of(z0), cns = 1, cf = 0, cslot = 0;
+    int zh = -(1 << 30);                                      // iteration that issued the current h loads
+    bool shared = false, ok = false;
+    const int ml = lane & 15, pc = lane >> 4;
+    uint32_t nm = 0x000F000Fu, nc = 0x43004300u;
+    asm volatile("" : "+v"(nm), "+v"(nc));
+    // the lower half's pending outputs (stage of the previous iteration)
+    f32x4 pend[2];
+    bool have_pend = false;
+    int p_s = 0, p_tile = 0, p_M = 0, p_par = 0, p_nj = 0, p_R = 0;
+    bool p_shared = false, p_ok = false;
+
+    auto flush = [&]() {
+        // lower half: add the upper half's partials of the pending stage and store
+        const int* orow = S.prow[p_tile - t0];
+        float* dst = p_shared ? a.obs : a.ob;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (j >= p_nj) break;
+            const f32x4 o = pend[j] + S.part[p_par][j][rt][lane];
+            const int n = p_s * p_R + rt * 16 + 64 * j + ml;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * pc + i;
+                if (m < p_M) dst[(size_t)orow[m] * d + n] = p_ok ? o[i] : 0.f;
+            }
+        }
+    };
+
+    // one stage of width F: NJ row tiles per wave, 4 of the NG groups
+    auto stage_compute = [&](auto FW, const DnStage& st, int par) {
+        constexpr int F = decltype(FW)::value;
+        constexpr int R = 2 * kDnStage / F, NJ = R / 64, NG = F / 64, NP = F / 32, NQ = NG / 2;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int r = rt * 16 + 64 * j + ml;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int gq = kh * NQ + q, p = 2 * gq + (pc >> 1);
+                const u32x2 w = *(const u32x2*)&st.b[r * (F / 2) + ((p ^ (r & (NP - 1))) << 4) + ((pc & 1) << 3)];
+                const uint32_t sb = *(const uint32_t*)&st.sc[r * (F / 16) + 4 * gq];
+                const u32x4 b0 = nib4v(w.x, nm, nc), b1 = nib4v(w.y, nm, nc);
+                f32x4 pp = {0.f, 0.f, 0.f, 0.f};
+                pp = mfma16(rah[q][0], b0, pp);
+                pp = mfma16(rah[q][1], b1, pp);
+                pp = mfma16(ral[q][0], b0, pp);
+                pp = mfma16(ral[q][1], b1, pp);
+                const float sv = f16_to_f32(sb & 0xFFFF), cv = f16_to_f32(sb >> 16) - 128.f * sv;
+                const float4 hsm = rhs[q];
+                acc[0] = __builtin_fmaf(sv, pp[0], __builtin_fmaf(cv, hsm.x, acc[0]));
+                acc[1] = __builtin_fmaf(sv, pp[1], __builtin_fmaf(cv, hsm.y, acc[1]));
+                acc[2] = __builtin_fmaf(sv, pp[2], __builtin_fmaf(cv, hsm.z, acc[2]));
+                acc[3] = __builtin_fmaf(sv, pp[3], __builtin_fmaf(cv, hsm.w, acc[3]));
+            }
+            if (kh) S.part[par][j][rt][lane] = acc;
+            else pend[j] = acc;
+        }
+        p_nj = NJ;
+        p_R = R;
+    };
+
+    for (int z = z0; z < z1; ++z) {
+        const bool new_tile = ctile < 0 || cs == 0;
+        // the new tile's h loads are covered by the wait for stage z only if
+        // stage z was issued after them (it was issued in iteration z - kDnNst + 1)
+        if (new_tile && z - (kDnNst - 1) < zh) vm_wait<0>();
+        dn_wait(min(kDnNst - 2, z1 - 1 - z), wave < 2);
+        lds_barrier();               // stage z (and h) landed; stage z - 1 consumed, its partials written
+        if (have_pend && !kh) flush();
+        have_pend = false;
+        if (new_tile) {
+            // the tile's h becomes the A operand (each wave converts its half)
+            ctile = ctile < 0 ? t0 : ctile + 1;
+            const int4 ti = tile_rec(ctile);
+            shared = ti.x < 0;
+            cf = shared ? g.fs : g.f;
+            cns = dn_tile_stages(d, cf);
+            M = ti.z;
+            ok = ti.w != -1;
+            const int nq = cf / 128;                          // groups per half
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q >= nq) break;
+                const float* src = &S.hst[ml * kHstRow + (kh * nq + q) * 64 + 16 * pc];
+                float e[16];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float4 x = *(const float4*)(src + 4 * v);
+                    e[4 * v] = x.x; e[4 * v + 1] = x.y; e[4 * v + 2] = x.z; e[4 * v + 3] = x.w;
+                }
+                float hs = 0.f;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    uint32_t hi[8], lo[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        hi[i] = f32_to_bf16(e[8 * t + i]);
+                        lo[i] = f32_to_bf16(e[8 * t + i] - bf16_to_f32(hi[i]));
+                        hs += bf16_to_f32(hi[i]) + bf16_to_f32(lo[i]);
+                    }
+                    rah[q][t] = u32x4{hi[0] | (hi[4] << 16), hi[1] | (hi[5] << 16), hi[2] | (hi[6] << 16),
+                                      hi[3] | (hi[7] << 16)};
+                    ral[q][t] = u32x4{lo[0] | (lo[4] << 16), lo[1] | (lo[5] << 16), lo[2] | (lo[6] << 16),
+                                      lo[3] | (lo[7] << 16)};
+                }
+                // group sum of position ml, then those of positions 4 pc + i
+                hs += __shfl_xor(hs, 16, 64);
+                hs += __shfl_xor(hs, 32, 64);
+                rhs[q] = make_float4(__shfl(hs, 4 * pc, 64), __shfl(hs, 4 * pc + 1, 64), __shfl(hs, 4 * pc + 2, 64),
+                                     __shfl(hs, 4 * pc + 3, 64));
+            }
+            lds_barrier();                                    // every wave has read S.hst
+            if (ctile + 1 < t0 + ntl) {
+                issue_h(ctile + 1);
+                zh = z;
+            }
+        }
+        if (z + kDnNst - 1 < z1) issue();
+
+        const DnStage& st = ring[cslot];
+        const int par = (z - z0) & 1;
+        if (cf == 512) stage_compute(IntC<512>{}, st, par);
+        else stage_compute(IntC<256>{}, st, par);
+        have_pend = true;
+        p_s = cs; p_tile = ctile; p_M = M; p_par = par; p_shared = shared; p_ok = ok;
+        cslot = cslot + 1 == kDnNst ? 0 : cslot + 1;
+        if (++cs == cns) cs = 0;
+    }
+    lds_barrier();                                            // the last partials are written
+    if (have_pend && !kh) flush();
+    vm_wait<0>();                                             // no direct-to-LDS load outlives the block
 }
 
 // ---------------------------------------------------------------------------
@@ -622,7 +803,8 @@ hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s) {
 }
 
 bool prefill_mm_ok(int d, int f, int fs) {
-    return d % kStageK == 0 && d / 64 <= kMaxGroupsPf && f % kStageK == 0 && (fs == 0 || fs % kStageK == 0);
+    auto fok = [](int x) { return x == 256 || x == 512; };    // the down projection's stage widths
+    return d % kStageK == 0 && d % 128 == 0 && d / 64 <= kMaxGroupsPf && fok(f) && (fs == 0 || fok(fs));
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
@@ -636,8 +818,16 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     if (g.u_pk_lo) hipLaunchKernelGGL(k_pf_gateup<true>, ggrid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_pf_gateup<false>, ggrid, dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pf_down, dim3(a.max_tiles, (g.d + kDnRows * kDnSub - 1) / (kDnRows * kDnSub)), dim3(256), 0,
-                       s, a);
+    {
+        // enough blocks that none spans more than kDnTiles tiles: a block
+        // takes at most ceil(Z / nb) stages and a tile has at least ns_min
+        const long long nsr = dn_tile_stages(g.d, g.f), nss = g.fs ? dn_tile_stages(g.d, g.fs) : nsr;
+        const long long z_max = (long long)a.max_tiles * (nsr > nss ? nsr : nss);
+        const long long per = (long long)(kDnTiles - 2) * (nsr < nss ? nsr : nss) + 1;
+        long long nb = a.n_cu > 0 ? a.n_cu : 1;
+        if (nb * per < z_max) nb = (z_max + per - 1) / per;
+        hipLaunchKernelGGL(k_pf_down, dim3((unsigned)nb), dim3(kDnThreads), 0, s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_pf_combine, dim3((g.d + 255) / 256, (g.n_tok + kCombTok - 1) / kCombTok), dim3(256), 0, s, a);
     return hipGetLastError();

@@ -97,7 +97,7 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.wsort = c.take<float>(std::max<size_t>(T * K, 64));
     S.h = c.take<float>(T * K * d->d_ff);
     S.hs = c.take<float>(T * std::max(1, d->d_ff_shared));
-    S.tiles = c.take<uint32_t>(prefill_max_tiles((int)T, (int)K, (int)E));
+    S.tiles = c.take<int32_t>(4 * (size_t)prefill_max_tiles((int)T, (int)K, (int)E));
     S.ob = c.take<float>(T * K * D);
     S.obs = c.take<float>(T * D);
     (void)Kn;
@@ -363,6 +363,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
         pf.tiles = L->s.tiles;
         pf.max_tiles = prefill_max_tiles(n_tok, D.top_k, D.n_experts);
         pf.meta_w = L->s.sort_meta;
+        pf.n_cu = L->n_cu;
         pf.ob = L->s.ob; pf.obs = L->s.obs;
         pf.used_idx = L->s.used_idx; pf.used_w = L->s.used_w;
         HIPCHK(launch_prefill(pf, st));
@@ -416,6 +417,12 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w, voi
     L->blob = L->L.total;
     L->sblob = desc->d_ff_shared ? L->Ls.total : 0;
     L->resident = desc->flags & MOE_RESIDENT_STORE;
+    {
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+            ncu = 256;
+        L->n_cu = ncu;
+    }
     L->slots = L->resident ? 0 : desc->slab_slots;
     L->h_slot_expert = new int32_t[std::max(1, L->slots)];
     L->h_last_staged = new int32_t[std::max(1, L->slots)];

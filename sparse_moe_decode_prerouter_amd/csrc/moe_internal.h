@@ -81,7 +81,7 @@ struct Scratch {
     float* wsort;            // [T*k] routing weight of each sorted assignment
     float* h;                // [T*k][f] routed expert hidden (sorted order)
     float* hs;               // [T][fs] shared expert hidden
-    uint32_t* tiles;         // prefill: grouped-GEMM work list
+    int32_t* tiles;          // prefill: grouped-GEMM work list, 4 ints per tile
     float* ob;               // prefill: [T*k][d] routed expert outputs by assignment
     float* obs;              // prefill: [T][d] shared expert outputs
 };
@@ -96,6 +96,7 @@ struct moe_layer {
     size_t blob, sblob;
     int slots;                 // routed slots (streamed)
     bool resident;
+    int n_cu;                  // compute units of the device (persistent kernels)
     int dev;
     // host mirror of the slab
     int32_t* h_slot_expert;    // [slots]
@@ -191,8 +192,12 @@ hipError_t launch_down(const GemvArgs& a, hipStream_t s);
 
 struct PrefillArgs {
     GemvArgs g;
-    uint32_t* tiles; int max_tiles;      // work list of the grouped GEMM
-    int32_t* meta_w;                     // meta[2] = number of tiles (written by the tile kernel)
+    // work list of the grouped GEMM, one tile = {slot (-1: shared expert),
+    // first position, rows (<= 16), blob (>= 0: index in the store or slab,
+    // -2: shared blob, -1: not staged)}
+    int32_t* tiles; int max_tiles;
+    int32_t* meta_w;                     // tile kernel writes meta[2] = tiles, meta[3] = routed tiles
+    int n_cu;                            // blocks of the persistent down projection
     float* ob; float* obs;               // down outputs: [T*k][d] by assignment, [T][d] shared
     const int32_t* used_idx; const float* used_w;
 };
