@@ -12,248 +12,177 @@ namespace moe {
 // Fused: u = x / sqrt(mean(x^2) + eps) * gamma evaluated in fp64 and rounded
 // once to the activation dtype (RMSNorm prologue of the head input: the head
 // reads the post-norm hidden state -- reading guide, Method, prerouter head).
-// Writes u (fp32, exact act values), the GEMV-ordered bf16 pairs and the
-// per-32-chunk sums used by the int4 dot products.
+// Writes the GEMV-ordered bf16 pairs (and the lo parts for fp32 activations)
+// and the per-32-chunk sums used by the int4 dot products.
 // GEMV order of a 32-element chunk c: dword 4*i + p holds elements
 // (32c + 8i + p, 32c + 8i + p + 4), matching the nibble pairs that one
 // masked shift of a packed dword yields.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_prologue(PrologueArgs a) {
-    extern __shared__ float su[];          // [d]
-    __shared__ double red[256];
-    const int t = blockIdx.x, d = a.d, tid = threadIdx.x;
+    __shared__ double red[4];
+    const int t = blockIdx.x, d = a.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // thread tid takes the 8-element pieces tid, tid + 256, ...; piece pc is
+    // (chunk pc / 4, sub-block pc % 4), whose four pairs are dwords 4 pc .. + 3
+    auto load8 = [&](int pc, double* v) {
+        if (a.x_is_bf16) {
+            const u32x4 w = *(const u32x4*)((const uint16_t*)a.x + (size_t)t * d + 8 * pc);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = (double)bf16_to_f32(ws[i] & 0xFFFF);
+                v[2 * i + 1] = (double)bf16_to_f32(ws[i] >> 16);
+            }
+        } else {
+            const float4 x0 = *(const float4*)((const float*)a.x + (size_t)t * d + 8 * pc);
+            const float4 x1 = *(const float4*)((const float*)a.x + (size_t)t * d + 8 * pc + 4);
+            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+        }
+    };
     double ss = 0.0;
-    for (int j = tid; j < d; j += 256) {
-        double xv = a.x_is_bf16 ? (double)bf16_to_f32(((const uint16_t*)a.x)[(size_t)t * d + j])
-                                : (double)((const float*)a.x)[(size_t)t * d + j];
-        ss += xv * xv;
+    for (int pc = tid; pc < d / 8; pc += 256) {
+        double v[8];
+        load8(pc, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
     }
-    red[tid] = ss;
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) red[wave] = ss;
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (tid < o) red[tid] += red[tid + o];
-        __syncthreads();
-    }
-    const double den = sqrt(red[0] / (double)d + (double)a.eps);
-    for (int j = tid; j < d; j += 256) {
-        double xv = a.x_is_bf16 ? (double)bf16_to_f32(((const uint16_t*)a.x)[(size_t)t * d + j])
-                                : (double)((const float*)a.x)[(size_t)t * d + j];
-        double uv = a.fused ? (xv / den) * (double)a.gamma[j] : xv;
-        float uf = a.act_bf16 ? bf16_to_f32(f64_to_bf16(uv)) : (float)uv;
-        su[j] = uf;
-        a.u[(size_t)t * d + j] = uf;
-    }
-    __syncthreads();
-    for (int q = tid; q < d / 2; q += 256) {
-        const int c = q >> 4, r = q & 15, i = r >> 2, p = r & 3;
-        const int e0 = 32 * c + 8 * i + p;
-        const float v0 = su[e0], v1 = su[e0 + 4];
-        const uint32_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
-        a.u_pk[(size_t)t * (d / 2) + q] = h0 | (h1 << 16);
-        if (a.u_pk_lo) {
-            const uint32_t l0 = f32_to_bf16(v0 - bf16_to_f32(h0)), l1 = f32_to_bf16(v1 - bf16_to_f32(h1));
-            a.u_pk_lo[(size_t)t * (d / 2) + q] = l0 | (l1 << 16);
-        }
-    }
-    for (int c = tid; c < d / 32; c += 256) {
+    const double den = sqrt((red[0] + red[1] + red[2] + red[3]) / (double)d + (double)a.eps);
+    for (int pc = tid; pc < d / 8; pc += 256) {
+        double v[8];
+        load8(pc, v);
+        uint32_t hi[8], lo[8];
         float sh = 0.f, sl = 0.f;
-        for (int j = 0; j < 32; ++j) {
-            const float v = su[32 * c + j];
-            const float hv = bf16_to_f32(f32_to_bf16(v));
-            sh += hv;
-            sl += bf16_to_f32(f32_to_bf16(v - hv));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double uv = a.fused ? (v[i] / den) * (double)a.gamma[8 * pc + i] : v[i];
+            const float uf = a.act_bf16 ? bf16_to_f32(f64_to_bf16(uv)) : (float)uv;
+            hi[i] = f32_to_bf16(uf);
+            lo[i] = f32_to_bf16(uf - bf16_to_f32(hi[i]));
+            sh += bf16_to_f32(hi[i]);
+            sl += bf16_to_f32(lo[i]);
         }
-        a.usum[(size_t)t * (d / 32) + c] = sh;
-        if (a.usum_lo) a.usum_lo[(size_t)t * (d / 32) + c] = sl;
+        *(u32x4*)(a.u_pk + (size_t)t * (d / 2) + 4 * pc) =
+            u32x4{hi[0] | (hi[4] << 16), hi[1] | (hi[5] << 16), hi[2] | (hi[6] << 16), hi[3] | (hi[7] << 16)};
+        if (a.u_pk_lo)
+            *(u32x4*)(a.u_pk_lo + (size_t)t * (d / 2) + 4 * pc) =
+                u32x4{lo[0] | (lo[4] << 16), lo[1] | (lo[5] << 16), lo[2] | (lo[6] << 16), lo[3] | (lo[7] << 16)};
+        // the chunk's 4 pieces are 4 consecutive lanes
+        sh += __shfl_xor(sh, 1, 64);
+        sh += __shfl_xor(sh, 2, 64);
+        sl += __shfl_xor(sl, 1, 64);
+        sl += __shfl_xor(sl, 2, 64);
+        if ((pc & 3) == 0) {
+            a.usum[(size_t)t * (d / 32) + pc / 4] = sh;
+            if (a.usum_lo) a.usum_lo[(size_t)t * (d / 32) + pc / 4] = sl;
+        }
     }
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(k_prologue, dim3(a.n_tok), dim3(256), a.d * sizeof(float), s, a);
+    if (a.d % 64) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_prologue, dim3(a.n_tok), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// bf16-weight GEMVs on u, accumulated in fp64 (bf16 x fp32 products are exact
-// in fp64), followed by top-k and renormalised softmax in the last block.
-// Virtual row space: [router E | head En | lora_a r | shared gate 1].
+// Token to expert sort/permute, as a counting sort in one block: bucket sizes
+// by LDS atomics, their exclusive scan (the active experts, ascending, and
+// their offsets), placement into buckets, then each entry's rank among the
+// smaller assignment ids of its bucket, so that the order is by (expert,
+// assignment) whatever order the atomics took.
 // ---------------------------------------------------------------------------
-constexpr int kRouteRowsPerBlock = 16;   // 4 waves x 4 rows
+constexpr int kSortThreads = 1024;
 
-__global__ void __launch_bounds__(256) k_route(RouteArgs a) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nr_router = a.router ? a.E : 0;
-    const int nr_head = a.head ? a.En : 0;
-    const int nb_router = (nr_router + kRouteRowsPerBlock - 1) / kRouteRowsPerBlock;
-    const int nb_head = (nr_head + kRouteRowsPerBlock - 1) / kRouteRowsPerBlock;
-    const int nr_misc = (a.lora_a ? a.r : 0) + (a.sgate_w ? 1 : 0);
-    int job, row0, nrows;
-    if ((int)blockIdx.x < nb_router) { job = 0; row0 = blockIdx.x * kRouteRowsPerBlock; nrows = nr_router; }
-    else if ((int)blockIdx.x < nb_router + nb_head) { job = 1; row0 = (blockIdx.x - nb_router) * kRouteRowsPerBlock; nrows = nr_head; }
-    else { job = 2; row0 = (blockIdx.x - nb_router - nb_head) * kRouteRowsPerBlock; nrows = nr_misc; }
-    const int d = a.d;
-    for (int rr = 0; rr < kRouteRowsPerBlock / 4; ++rr) {
-        const int row = row0 + wave * (kRouteRowsPerBlock / 4) + rr;
-        if (row >= nrows) break;
-        const uint16_t* w;
-        if (job == 0) w = a.router + (size_t)row * d;
-        else if (job == 1) w = a.head + (size_t)row * d;
-        else w = (a.lora_a && row < a.r) ? a.lora_a + (size_t)row * d : a.sgate_w;
-        for (int t = 0; t < a.n_tok; ++t) {
-            if (job == 0 && a.route_idx && a.route_idx[(size_t)t * a.k] >= 0) continue;
-            const float* u = a.u + (size_t)t * d;
-            double acc = 0.0;
-            for (int j0 = lane * 8; j0 < d; j0 += 512) {
-                const u32x4 wv = *(const u32x4*)(w + j0);
-                const float4 u0 = *(const float4*)(u + j0);
-                const float4 u1 = *(const float4*)(u + j0 + 4);
-                acc += (double)bf16_to_f32(wv.x & 0xFFFF) * (double)u0.x;
-                acc += (double)bf16_to_f32(wv.x >> 16) * (double)u0.y;
-                acc += (double)bf16_to_f32(wv.y & 0xFFFF) * (double)u0.z;
-                acc += (double)bf16_to_f32(wv.y >> 16) * (double)u0.w;
-                acc += (double)bf16_to_f32(wv.z & 0xFFFF) * (double)u1.x;
-                acc += (double)bf16_to_f32(wv.z >> 16) * (double)u1.y;
-                acc += (double)bf16_to_f32(wv.w & 0xFFFF) * (double)u1.z;
-                acc += (double)bf16_to_f32(wv.w >> 16) * (double)u1.w;
-            }
-            acc = group_sum(acc, 64);
-            if (lane == 0) {
-                if (job == 0) st_dev(a.logits_r + (size_t)t * a.E + row, acc);
-                else if (job == 1) st_dev(a.logits_h + (size_t)t * a.En + row, acc);
-                else if (a.lora_a && row < a.r) a.au[(size_t)t * a.r + row] = (float)acc;
-                else a.sgate[t] = (float)(1.0 / (1.0 + exp(-acc)));
-            }
-        }
-    }
-    if (job == 2) return;
-    // last block of the job computes the top-k for every token
-    __builtin_amdgcn_s_waitcnt(0);
+size_t sort_lds_bytes(int n, int E) { return (size_t)(3 * E + 2 * n) * sizeof(int); }
+
+__global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
+    extern __shared__ int sm[];
+    const int n = a.n_tok * a.k, E = a.E;
+    int* cnt = sm;                 // [E] bucket sizes
+    int* fill = sm + E;            // [E] placement counters
+    int* off = sm + 2 * E;         // [E] bucket offsets
+    int* ex = sm + 3 * E;          // [n] expert of each assignment (-1: invalid)
+    int* tmp = sm + 3 * E + n;     // [n] assignments in bucket order (unordered within a bucket)
+    __shared__ int wsum[kSortThreads / 64];
+    __shared__ int wact[kSortThreads / 64];
+    __shared__ int tot_valid, tot_active;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += kSortThreads) { cnt[e] = 0; fill[e] = 0; }
     __syncthreads();
-    __shared__ int is_last;
-    if (threadIdx.x == 0) {
-        const unsigned total = job == 0 ? nb_router : nb_head;
-        const unsigned old = __hip_atomic_fetch_add(a.counters + job, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = old == total - 1;
-        if (is_last) __hip_atomic_store(a.counters + job, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < n; i += kSortThreads) {
+        const int t = i / a.k;
+        const bool self = !a.route_idx || a.route_idx[(size_t)t * a.k] < 0;
+        int e = self ? a.self_idx[i] : a.route_idx[i];
+        const float w = self ? a.self_w[i] : a.route_w[i];
+        if (e < 0 || e >= E) { set_err(a.err, ERR_BAD_INDEX); e = -1; }
+        a.used_idx[i] = e; a.used_w[i] = w;
+        if (a.user_used_idx) a.user_used_idx[i] = e;
+        if (a.user_used_w) a.user_used_w[i] = w;
+        ex[i] = e;
+        if (e >= 0) atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    if (!is_last) return;
-    if (job == 0)
-        topk_rows(true, a.logits_r, a.E, a.k, a.n_tok, a.router_bias, nullptr, nullptr, nullptr, nullptr,
-                  a.route_idx, a.k, a.self_idx, a.self_w);
-    else
-        topk_rows(true, a.logits_h, a.En, a.kn, a.n_tok, a.head_bias, a.hist_cur_m, a.hist_cur, a.hist_prev_m,
-                  a.hist_prev, nullptr, a.kn, a.pred_idx, a.pred_w);
-}
-
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
-    const int nb_router = a.router ? (a.E + kRouteRowsPerBlock - 1) / kRouteRowsPerBlock : 0;
-    const int nb_head = a.head ? (a.En + kRouteRowsPerBlock - 1) / kRouteRowsPerBlock : 0;
-    const int nr_misc = (a.lora_a ? a.r : 0) + (a.sgate_w ? 1 : 0);
-    const int nb_misc = (nr_misc + kRouteRowsPerBlock - 1) / kRouteRowsPerBlock;
-    const int nb = nb_router + nb_head + nb_misc;
-    if (nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_route, dim3(nb), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Token to expert sort/permute: keys (expert << 20 | assignment) sorted with
-// a bitonic network in LDS; segments give the active experts (ascending),
-// their offsets, and the assignment permutation.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(1024) k_sort(SortArgs a) {
-    extern __shared__ uint32_t keys[];
-    __shared__ int wsum[16];
-    __shared__ int tot;
-    const int n = a.n_tok * a.k;
-    int np2 = 1;
-    while (np2 < n) np2 <<= 1;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < np2; i += 1024) {
-        uint32_t key = 0xFFFFFFFFu;
-        if (i < n) {
-            const int t = i / a.k;
-            const bool self = !a.route_idx || a.route_idx[(size_t)t * a.k] < 0;
-            int e = self ? a.self_idx[i] : a.route_idx[i];
-            const float w = self ? a.self_w[i] : a.route_w[i];
-            if (e < 0 || e >= a.E) { set_err(a.err, ERR_BAD_INDEX); e = -1; }
-            a.used_idx[i] = e; a.used_w[i] = w;
-            if (a.user_used_idx) a.user_used_idx[i] = e;
-            if (a.user_used_w) a.user_used_w[i] = w;
-            if (e >= 0) key = ((uint32_t)e << 20) | (uint32_t)i;
-        }
-        keys[i] = key;
-    }
-    __syncthreads();
-    for (int size = 2; size <= np2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < np2 / 2; i += 1024) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool up = (lo & size) == 0;
-                const uint32_t x = keys[lo], y = keys[hi];
-                if ((x > y) == up) { keys[lo] = y; keys[hi] = x; }
-            }
-            __syncthreads();
-        }
-    }
-    // segment starts -> active list
-    const int per = (n + 1023) / 1024;
-    const int i0 = tid * per, i1 = min(n, i0 + per);
-    int cnt = 0;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t key = keys[i];
-        if (key == 0xFFFFFFFFu) break;
-        a.perm[i] = (int32_t)(key & 0xFFFFFu);
-        if (i == 0 || (keys[i - 1] >> 20) != (key >> 20)) ++cnt;
-    }
-    // block exclusive scan of cnt
-    int incl = cnt;
-    const int lane = tid & 63, wave = tid >> 6;
+    // exclusive scan over the buckets: thread tid owns experts [e0, e1)
+    const int per = (E + kSortThreads - 1) / kSortThreads;
+    const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+    int c = 0, na = 0;
+    for (int e = e0; e < e1; ++e) { c += cnt[e]; na += cnt[e] > 0; }
+    int ic = c, ia = na;
     for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
+        const int v = __shfl_up(ic, o, 64), u = __shfl_up(ia, o, 64);
+        if (lane >= o) { ic += v; ia += u; }
     }
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == 63) { wsum[wave] = ic; wact[wave] = ia; }
     __syncthreads();
     if (tid == 0) {
-        int acc = 0;
-        for (int w = 0; w < 16; ++w) { const int v = wsum[w]; wsum[w] = acc; acc += v; }
-        tot = acc;
-    }
-    __syncthreads();
-    int pos = wsum[wave] + incl - cnt;
-    int nvalid_local = 0;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t key = keys[i];
-        if (key == 0xFFFFFFFFu) break;
-        ++nvalid_local;
-        if (i == 0 || (keys[i - 1] >> 20) != (key >> 20)) {
-            a.active[pos] = (int32_t)(key >> 20);
-            a.act_off[pos] = i;
-            ++pos;
+        int s1 = 0, s2 = 0;
+        for (int w = 0; w < kSortThreads / 64; ++w) {
+            const int v = wsum[w], u = wact[w];
+            wsum[w] = s1; wact[w] = s2; s1 += v; s2 += u;
         }
+        tot_valid = s1; tot_active = s2;
     }
-    // number of valid keys: first invalid position
-    __shared__ int nvalid;
-    if (tid == 0) nvalid = n;
     __syncthreads();
-    for (int i = tid; i < n; i += 1024)
-        if (keys[i] == 0xFFFFFFFFu && (i == 0 || keys[i - 1] != 0xFFFFFFFFu)) nvalid = i;
+    int o1 = wsum[wave] + ic - c, o2 = wact[wave] + ia - na;
+    for (int e = e0; e < e1; ++e) {
+        off[e] = o1;
+        if (cnt[e] > 0) { a.active[o2] = e; a.act_off[o2] = o1; ++o2; }
+        o1 += cnt[e];
+    }
     __syncthreads();
+    for (int i = tid; i < n; i += kSortThreads) {
+        const int e = ex[i];
+        if (e >= 0) tmp[off[e] + atomicAdd(&fill[e], 1)] = i;
+    }
+    __syncthreads();
+    for (int s = tid; s < tot_valid; s += kSortThreads) {
+        const int i = tmp[s], e = ex[i], b0 = off[e], b1 = b0 + cnt[e];
+        int r = 0;
+        for (int q = b0; q < b1; ++q) r += tmp[q] < i;
+        a.perm[b0 + r] = i;
+    }
     if (tid == 0) {
-        a.act_off[tot] = nvalid;
-        a.meta[0] = tot;
-        a.meta[1] = nvalid;
+        a.act_off[tot_active] = tot_valid;
+        a.meta[0] = tot_active;
+        a.meta[1] = tot_valid;
     }
-    (void)nvalid_local;
 }
 
 hipError_t launch_sort(const SortArgs& a, hipStream_t s) {
-    int n = a.n_tok * a.k, np2 = 1;
-    while (np2 < n) np2 <<= 1;
-    hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), np2 * sizeof(uint32_t), s, a);
+    const size_t lds = sort_lds_bytes(a.n_tok * a.k, a.E);
+    if (lds > 64 * 1024) {
+        static bool raised = false;
+        if (lds > 160 * 1024) return hipErrorInvalidValue;
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute((const void*)k_sort, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+    }
+    hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, a);
     return hipGetLastError();
 }
 

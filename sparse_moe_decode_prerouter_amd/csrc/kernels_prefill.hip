@@ -642,52 +642,110 @@ __global__ void __launch_bounds__(kDnThreads) k_pf_down(PrefillArgs a) {
 
 // ---------------------------------------------------------------------------
 // Combine per (token, row): shared (gated), routed in routing order
-// (weighted), LoRA B, residual.
+// (weighted), LoRA B, residual. A thread takes 4 consecutive rows of
+// kCombTok tokens; every load of a term is issued for all its tokens before
+// any is used.
 // ---------------------------------------------------------------------------
-constexpr int kCombTok = 8;
+constexpr int kCombTok = 4;
 
 __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
     const GemvArgs& g = a.g;
-    const int n = blockIdx.x * 256 + threadIdx.x, d = g.d;
+    const int d = g.d, n = (blockIdx.x * 256 + threadIdx.x) * 4;
     const int t0 = blockIdx.y * kCombTok;
     if (n >= d) return;
-    const bool lora = g.lora_b && g.r;
-    const bool lvec = lora && g.r % 8 == 0 && g.r <= 32;
-    u32x4 lb[4];
-    if (lvec)
+    const int nt = min(kCombTok, g.n_tok - t0);
+    float4 y[kCombTok];
+    const bool sh = g.fs && g.ev.shared;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) lb[c] = *(const u32x4*)(g.lora_b + (size_t)n * g.r + 8 * (8 * c < g.r ? c : 0));
     for (int tt = 0; tt < kCombTok; ++tt) {
-        const int t = t0 + tt;
-        if (t >= g.n_tok) break;
-        float y = 0.f;
-        if (g.fs && g.ev.shared) y = (g.sgate ? g.sgate[t] : 1.f) * a.obs[(size_t)t * d + n];
-        for (int j = 0; j < g.k; ++j) {
-            const int aid = t * g.k + j;
-            if (a.used_idx[aid] >= 0) y += a.used_w[aid] * a.ob[(size_t)aid * d + n];
+        const int t = t0 + (tt < nt ? tt : 0);
+        y[tt] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (sh) {
+            const float sg = g.sgate ? g.sgate[t] : 1.f;
+            const float4 o = *(const float4*)(a.obs + (size_t)t * d + n);
+            y[tt] = make_float4(sg * o.x, sg * o.y, sg * o.z, sg * o.w);
         }
-        if (lora) {
-            float l = 0.f;
-            const float* au = g.au + (size_t)t * g.r;
-            if (lvec) {
+    }
+    for (int j = 0; j < g.k; ++j) {
+        float4 o[kCombTok];
+        float w[kCombTok];
+        bool v[kCombTok];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if (8 * c >= g.r) break;
-                    const uint32_t w[4] = {lb[c].x, lb[c].y, lb[c].z, lb[c].w};
+        for (int tt = 0; tt < kCombTok; ++tt) {
+            const int aid = (t0 + (tt < nt ? tt : 0)) * g.k + j;
+            v[tt] = a.used_idx[aid] >= 0;            // an invalid entry's row was never written
+            w[tt] = a.used_w[aid];
+            o[tt] = *(const float4*)(a.ob + (size_t)aid * d + n);
+        }
+#pragma unroll
+        for (int tt = 0; tt < kCombTok; ++tt) {
+            if (!v[tt]) continue;
+            y[tt].x += w[tt] * o[tt].x; y[tt].y += w[tt] * o[tt].y;
+            y[tt].z += w[tt] * o[tt].z; y[tt].w += w[tt] * o[tt].w;
+        }
+    }
+    if (g.lora_b && g.r) {
+        const int r = g.r;
+        float l[kCombTok][4];
+#pragma unroll
+        for (int tt = 0; tt < kCombTok; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l[tt][i] = 0.f;
+        if (r % 8 == 0 && r <= 32) {
+            u32x4 lb[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    lb[i][c] = *(const u32x4*)(g.lora_b + (size_t)(n + i) * r + 8 * (8 * c < r ? c : 0));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (8 * c >= r) break;
+#pragma unroll
+                for (int tt = 0; tt < kCombTok; ++tt) {
+                    const float* au = g.au + (size_t)(t0 + (tt < nt ? tt : 0)) * r + 8 * c;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        l += bf16_to_f32(w[i] & 0xFFFF) * au[8 * c + 2 * i];
-                        l += bf16_to_f32(w[i] >> 16) * au[8 * c + 2 * i + 1];
+                        const uint32_t wv[4] = {lb[i][c].x, lb[i][c].y, lb[i][c].z, lb[i][c].w};
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) {
+                            l[tt][i] += bf16_to_f32(wv[h] & 0xFFFF) * au[2 * h];
+                            l[tt][i] += bf16_to_f32(wv[h] >> 16) * au[2 * h + 1];
+                        }
                     }
                 }
-            } else {
-                for (int q = 0; q < g.r; ++q) l += bf16_to_f32(g.lora_b[(size_t)n * g.r + q]) * au[q];
             }
-            y += g.lora_scale * l;
+        } else {
+            for (int q = 0; q < r; ++q) {
+                float wq[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wq[i] = bf16_to_f32(g.lora_b[(size_t)(n + i) * r + q]);
+#pragma unroll
+                for (int tt = 0; tt < kCombTok; ++tt) {
+                    const float u = g.au[(size_t)(t0 + (tt < nt ? tt : 0)) * r + q];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) l[tt][i] += wq[i] * u;
+                }
+            }
         }
-        if (g.fused) y += g.x[(size_t)t * d + n];
-        g.y[(size_t)t * d + n] = y;
+#pragma unroll
+        for (int tt = 0; tt < kCombTok; ++tt) {
+            y[tt].x += g.lora_scale * l[tt][0]; y[tt].y += g.lora_scale * l[tt][1];
+            y[tt].z += g.lora_scale * l[tt][2]; y[tt].w += g.lora_scale * l[tt][3];
+        }
     }
+    if (g.fused) {
+        float4 x[kCombTok];
+#pragma unroll
+        for (int tt = 0; tt < kCombTok; ++tt) x[tt] = *(const float4*)(g.x + (size_t)(t0 + (tt < nt ? tt : 0)) * d + n);
+#pragma unroll
+        for (int tt = 0; tt < kCombTok; ++tt) {
+            y[tt].x += x[tt].x; y[tt].y += x[tt].y; y[tt].z += x[tt].z; y[tt].w += x[tt].w;
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kCombTok; ++tt)
+        if (tt < nt) *(float4*)(g.y + (size_t)(t0 + tt) * d + n) = y[tt];
 }
 
 // ---------------------------------------------------------------------------
@@ -695,7 +753,8 @@ __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
 // r | shared gate 1] x tokens. bf16 x bf16 products are exact in fp32; each
 // 32-wide k-step goes to a fresh fp32 accumulator and the steps are summed in
 // fp64, so a logit carries the rounding of at most one 32-term fp32 sum per
-// step. Grid: (16-row tiles, 64-token groups); wave w takes token tile w.
+// step. Grid: (16-row tiles, 16-token tiles); wave w takes the k-steps of
+// the w-th quarter of d and the quarters are summed in order.
 // B (weights) pairs are reordered to the (p, p + 4) order of u_pk.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 bf16_pairs_p4(u32x4 v) {
@@ -708,6 +767,8 @@ __device__ __forceinline__ u32x4 bf16_pairs_p4(u32x4 v) {
 }
 
 __global__ void __launch_bounds__(256) k_route_mm(RouteMMArgs a) {
+    constexpr int kMaxSteps = 16;              // 32-wide k-steps whose loads are issued together
+    __shared__ double red[3][64][4];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ml = lane & 15, pc = lane >> 4;
@@ -715,8 +776,7 @@ __global__ void __launch_bounds__(256) k_route_mm(RouteMMArgs a) {
     const int nr_router = a.router ? a.E : 0, nr_head = a.head ? a.En : 0;
     const int nr_lora = a.lora_a ? a.r : 0;
     const int R = nr_router + nr_head + nr_lora + (a.sgate_w ? 1 : 0);
-    const int t0 = (blockIdx.y * 4 + wave) * 16;
-    if (t0 >= T) return;
+    const int t0 = blockIdx.y * 16;
     // this lane's weight row (B side) and token (A side)
     int row = blockIdx.x * 16 + ml;
     const bool row_ok = row < R;
@@ -727,23 +787,27 @@ __global__ void __launch_bounds__(256) k_route_mm(RouteMMArgs a) {
     else if (row < nr_router + nr_head + nr_lora) w = a.lora_a + (size_t)(row - nr_router - nr_head) * d;
     else w = a.sgate_w;
     const int tok = t0 + ml < T ? t0 + ml : T - 1;
+    // wave w takes k-steps [w * ns, (w + 1) * ns) of the d / 32
+    const int ns = d / 128, c0 = wave * ns;
     const uint32_t* aq = a.u_pk + (size_t)tok * (d / 2) + 4 * pc;
     const uint32_t* aql = a.u_pk_lo ? a.u_pk_lo + (size_t)tok * (d / 2) + 4 * pc : nullptr;
     const u32x4* wq = (const u32x4*)(w + 8 * pc);
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    constexpr int kB = 8;                      // k-steps whose loads are issued together
-    for (int c0 = 0; c0 < d / 32; c0 += kB) {
-        u32x4 av[kB], al[kB], wv[kB];
+    for (int b0 = 0; b0 < ns; b0 += kMaxSteps) {
+        const int nb = min(kMaxSteps, ns - b0);
+        u32x4 av[kMaxSteps], al[kMaxSteps], wv[kMaxSteps];
+        // unconditional loads (indices clamped into the slice), so that the
+        // arrays stay in registers
 #pragma unroll
-        for (int c = 0; c < kB; ++c) {
-            const int cc = c0 + c < d / 32 ? c0 + c : d / 32 - 1;
+        for (int c = 0; c < kMaxSteps; ++c) {
+            const int cc = c0 + b0 + (c < nb ? c : nb - 1);
             av[c] = *(const u32x4*)(aq + 16 * cc);
             wv[c] = wq[4 * cc];
-            if (aql) al[c] = *(const u32x4*)(aql + 16 * cc);
+            al[c] = aql ? *(const u32x4*)(aql + 16 * cc) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int c = 0; c < kB; ++c) {
-            if (c0 + c >= d / 32) break;
+        for (int c = 0; c < kMaxSteps; ++c) {
+            if (c >= nb) continue;
             const u32x4 bv = bf16_pairs_p4(wv[c]);
             f32x4 p = {0.f, 0.f, 0.f, 0.f};
             p = mfma16(av[c], bv, p);
@@ -752,7 +816,16 @@ __global__ void __launch_bounds__(256) k_route_mm(RouteMMArgs a) {
             for (int i = 0; i < 4; ++i) acc[i] += (double)p[i];
         }
     }
-    if (!row_ok) return;
+    // the four k-slices are summed in slice order
+    if (wave > 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave - 1][lane][i] = acc[i];
+    __syncthreads();
+    if (wave > 0 || !row_ok) return;
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += red[s][lane][i];
     const int r = blockIdx.x * 16 + ml;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -788,10 +861,10 @@ __global__ void __launch_bounds__(256) k_route_topk(RouteMMArgs a) {
 }
 
 hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s) {
-    if (a.d % 32) return hipErrorInvalidValue;
+    if (a.d % 128) return hipErrorInvalidValue;
     const int R = (a.router ? a.E : 0) + (a.head ? a.En : 0) + (a.lora_a ? a.r : 0) + (a.sgate_w ? 1 : 0);
     if (R > 0) {
-        hipLaunchKernelGGL(k_route_mm, dim3((R + 15) / 16, (a.n_tok + 63) / 64), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_route_mm, dim3((R + 15) / 16, (a.n_tok + 15) / 16), dim3(256), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -829,7 +902,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(k_pf_down, dim3((unsigned)nb), dim3(kDnThreads), 0, s, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pf_combine, dim3((g.d + 255) / 256, (g.n_tok + kCombTok - 1) / kCombTok), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_pf_combine, dim3((g.d + 1023) / 1024, (g.n_tok + kCombTok - 1) / kCombTok), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -75,7 +75,6 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.slot_of = c.take<int32_t>(E);
     S.slot_tag = c.take<int32_t>(slots + 1);
     S.slab = resident ? nullptr : c.take<uint8_t>((slots + (d->d_ff_shared ? 1 : 0)) * blob);
-    S.u = c.take<float>(T * D);
     S.u_pk = c.take<uint32_t>(T * D / 2);
     S.u_pk_lo = f32 ? c.take<uint32_t>(T * D / 2) : nullptr;
     S.usum = c.take<float>(T * D / 32);
@@ -301,7 +300,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     pa.act_bf16 = D.act_dtype == MOE_ACT_BF16;
     pa.d = D.d_model;
     pa.n_tok = n_tok;
-    pa.u = L->s.u; pa.u_pk = L->s.u_pk; pa.u_pk_lo = L->s.u_pk_lo; pa.usum = L->s.usum; pa.usum_lo = L->s.usum_lo;
+    pa.u_pk = L->s.u_pk; pa.u_pk_lo = L->s.u_pk_lo; pa.usum = L->s.usum; pa.usum_lo = L->s.usum_lo;
     HIPCHK(launch_prologue(pa, st));
 
     RouteMMArgs ra{};

@@ -61,7 +61,6 @@ struct Scratch {
     int32_t* slot_of;        // [E]
     int32_t* slot_tag;       // [slots + 1]; entry `slots` is the shared slot
     uint8_t* slab;           // [(slots + 1) * blob] (streamed); shared slot last
-    float* u;                // [T][d] block input (exact act values) in fp32
     uint32_t* u_pk;          // [T][d/2] bf16 pairs, GEMV order (hi part)
     uint32_t* u_pk_lo;       // [T][d/2] lo part (f32 act) or nullptr
     float* usum;             // [T][d/32] sums of hi part per 32-chunk
@@ -130,14 +129,14 @@ namespace moe {
 struct PrologueArgs {
     const void* x; int x_is_bf16; int fused; const float* gamma; float eps;
     int act_bf16; int d; int n_tok;
-    float* u; uint32_t* u_pk; uint32_t* u_pk_lo; float* usum; float* usum_lo;
+    uint32_t* u_pk; uint32_t* u_pk_lo; float* usum; float* usum_lo;
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 
 struct RouteArgs {
     // router (self-routing rows) and head (prediction) logits + top-k, plus
-    // LoRA A u and the shared gate, all from bf16 weights on the fp32 u
-    const float* u; int d; int n_tok;
+    // LoRA A u and the shared gate, all from bf16 weights on the block input
+    int d; int n_tok;
     const uint16_t* router; const float* router_bias; int E; int k;
     const int32_t* route_idx;           // rows to self-route: idx[t*k] < 0 or route_idx == nullptr
     const uint16_t* head; const float* head_bias; int En; int kn;
@@ -149,7 +148,6 @@ struct RouteArgs {
     float* au; float* sgate;
     uint32_t* counters;
 };
-hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
 // routing-side GEMM for many tokens (prefill, large decode batches)
 struct RouteMMArgs {
