@@ -624,12 +624,13 @@ __global__ void __launch_bounds__(kDnThreads) k_pf_down(PrefillArgs a) {
                 zh = z;
             }
         }
-        if (z + kDnNst - 1 < z1) issue();
-
         const DnStage& st = ring[cslot];
         const int par = (z - z0) & 1;
         if (cf == 512) stage_compute(IntC<512>{}, st, par);
         else stage_compute(IntC<256>{}, st, par);
+        // the next stage's loads go out after this wave's compute, so that a
+        // full memory queue delays no compute
+        if (z + kDnNst - 1 < z1) issue();
         have_pend = true;
         p_s = cs; p_tile = ctile; p_M = M; p_par = par; p_shared = shared; p_ok = ok;
         cslot = cslot + 1 == kDnNst ? 0 : cslot + 1;
