@@ -106,6 +106,190 @@ class LazyStore:
         return self.cache[e]
 
 
+def make_layer(moe, shape, w, l, L, *, max_tokens, resident=True, store=None, shared=None, slab_slots=0,
+               head_bias=None, hist_cur=None):
+    return moe.MoeLayer(
+        d_model=shape.d, n_experts=shape.E, top_k=shape.k, d_ff=shape.f, d_ff_shared=shape.fs,
+        lora_rank=shape.r, lora_alpha=shape.alpha, act_dtype=moe.MOE_ACT_BF16, max_tokens=max_tokens,
+        expert_store=w["store"] if store is None else store, shared_blob=w["shared"] if shared is None else shared,
+        shared_gate=w["shared_gate"], router=w["router"], head=w["head"] if l + 1 < L else None,
+        head_bias=head_bias if l + 1 < L else None, hist_cur=hist_cur if l + 1 < L else None,
+        next_n_experts=shape.E if l + 1 < L else 0, next_top_k=shape.k if l + 1 < L else 0,
+        lora_a=w["lora_a"], lora_b=w["lora_b"], norm_gamma=w["gamma"], rms_eps=shape.eps,
+        fuse_norm_residual=True, resident=resident, slab_slots=slab_slots)
+
+
+def time_stack_steps(torch, stack, L, B, k, d, steps, warm, key, synth, shape, used=None):
+    """Graph-replayed decode steps of a stack (eager first step); returns
+    (ms per step, the last routing buffer)."""
+    dev = "cuda"
+    xbank = torch.stack([synth.activations(shape, B, (key, t), device=dev, dtype=torch.float32)
+                         for t in range(warm + steps)])
+    xout = torch.empty((B, d), dtype=torch.float32, device=dev)
+    pidx = [torch.full((L, B, k), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+    pw = [torch.zeros((L, B, k), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def step(t):
+        stack.decode(xbank[t], pidx[t % 2], pw[t % 2], pidx[(t + 1) % 2], pw[(t + 1) % 2], x_out=xout,
+                     first_step=(t == 0), used_idx=used)
+
+    step(0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm, stream=s):
+        for t in range(1, warm):
+            step(t)
+    with torch.cuda.graph(g_timed, stream=s):
+        for t in range(warm, warm + steps):
+            step(t)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_timed.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, pidx[(warm + steps) % 2]
+
+
+def extra_measurements(args, torch, np, moe, synth, shape, ws, layers):
+    """The other workloads of the method, each timed on this GPU: batched
+    decode with Zipf-popular, sticky routing; streamed decode (experts staged
+    per step from pinned host memory) against on-demand staging; one layer per
+    call at batch 1 and 4; a long prefill for the matrix-core rate."""
+    out = {}
+    L, k, d, E, blob = len(layers), shape.k, shape.d, shape.E, shape.blob_bytes
+
+    # ---- batched decode, B = 32, Zipf(1.1) popularity + stickiness (calibrated)
+    with open(os.path.join(ROOT, "tests", "golden", "zipf_calibration.json")) as fh:
+        cal = json.load(fh)
+    B = 32
+    hist = synth.sticky_history(E, cal["beta"], device="cuda")
+    zl = [make_layer(moe, shape, w, l, L, max_tokens=B,
+                     head_bias=synth.zipf_bias(E, cal["zipf_s"], cal["tau"], ("bench", l), device="cuda"),
+                     hist_cur=hist) for l, w in enumerate(ws)]
+    zs = moe.MoeStack(zl)
+    used = torch.full((L, B, k), -1, dtype=torch.int32, device="cuda")
+    ms, _ = time_stack_steps(torch, zs, L, B, k, d, 32, 5, "bench_zipf", synth, shape, used=used)
+    assert all(Lr.status() == 0 for Lr in zl)
+    u = used.cpu().numpy()
+    U = [len(set(u[l].ravel().tolist()) - {-1}) for l in range(L)]
+    bb = sum((x + 1) * blob for x in U) + (L - 1) * 2 * E * d + L * (4 * shape.r * d + 6 * d)
+    out["batched_decode_b32"] = {"tok_s": round(B / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+                                 "distinct_experts_per_layer": round(float(np.mean(U)), 1),
+                                 "algorithmic_GBs": round(bb / (ms * 1e-3) / 1e9, 1),
+                                 "hbm_frac": round(bb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
+    log(f"batched decode B={B} (Zipf + sticky): {ms * 1e3:.0f} us/step, {B / (ms / 1e3):.0f} tok/s, "
+        f"U={np.mean(U):.1f} experts/layer, {bb / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic")
+    zs.close()
+    for Lr in zl:
+        Lr.close()
+    del zl, zs
+
+    # ---- streamed decode, B = 1: every layer's routed experts staged per step
+    # from pinned host memory into a 5-slot HBM slab on a side stream (one pinned
+    # copy of a layer's experts serves all layers: the bytes moved are the same)
+    pstore = ws[0]["store"].cpu().pin_memory()
+    pshared = ws[0]["shared"].cpu().pin_memory()
+    sl = [make_layer(moe, shape, w, l, L, max_tokens=1, resident=False, store=pstore, shared=pshared,
+                     slab_slots=k + 1) for l, w in enumerate(ws)]
+    ss = moe.MoeStack(sl)
+    cs = torch.cuda.Stream()
+    xs = [synth.activations(shape, 1, ("bench_str", t), device="cuda", dtype=torch.float32) for t in range(24)]
+    xo = torch.empty((1, d), dtype=torch.float32, device="cuda")
+    pidx = [torch.full((L, 1, k), -1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    pw = [torch.zeros((L, 1, k), dtype=torch.float32, device="cuda") for _ in range(2)]
+
+    def streamed_step(t, reactive):
+        if reactive or t == 0:
+            # on demand: every layer routes itself and stages inside the call
+            ss.decode(xs[t], pidx[t % 2], pw[t % 2], pidx[(t + 1) % 2], pw[(t + 1) % 2], x_out=xo, first_step=True)
+            return
+        pred = pidx[t % 2].cpu().numpy()            # the previous step's predictions
+        for l in range(1, L):
+            sl[l].stage(sorted(set(int(e) for e in pred[l, 0] if e >= 0)), stream=cs)
+        ss.decode(xs[t], pidx[t % 2], pw[t % 2], pidx[(t + 1) % 2], pw[(t + 1) % 2], x_out=xo, first_step=False)
+
+    res = {}
+    for mode, reactive in (("prerouted", False), ("on_demand", True)):
+        for t in range(4):
+            streamed_step(t, reactive)
+        torch.cuda.synchronize()
+        b0 = sum(Lr.slots()[1] for Lr in sl)
+        n = 16
+        c0 = time.time()
+        for t in range(4, 4 + n):
+            streamed_step(t, reactive)
+        torch.cuda.synchronize()
+        el = time.time() - c0
+        moved = sum(Lr.slots()[1] for Lr in sl) - b0
+        assert all(Lr.status() == 0 for Lr in sl), [Lr.status() for Lr in sl]
+        res[mode] = {"tok_s": round(n / el, 1), "ms_per_step": round(el / n * 1e3, 3),
+                     "staged_MB_per_step": round(moved / n / 1e6, 1),
+                     "staging_GBs": round(moved / el / 1e9, 2)}
+        log(f"streamed decode ({mode}): {el / n * 1e3:.2f} ms/step, {n / el:.1f} tok/s, "
+            f"{moved / n / 1e6:.0f} MB staged/step, {moved / el / 1e9:.1f} GB/s host->HBM")
+    out["streamed_decode_b1"] = res
+    ss.close()
+    for Lr in sl:
+        Lr.close()
+    del sl, ss, pstore, pshared
+
+    # ---- one layer per call, batch 1 and 4 (given routing; graph of 64 calls)
+    lay = make_layer(moe, shape, ws[1], 1, L, max_tokens=4)
+    for B in (1, 4):
+        x = synth.activations(shape, B, ("bench_one", B), device="cuda", dtype=torch.float32)
+        ridx, rw = synth.random_routing(B, E, k, ("bench_one", B))
+        ridx, rw = ridx.cuda(), rw.cuda()
+        y = torch.empty_like(x)
+        lay.decode(x, ridx, rw, y=y)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(64):
+                lay.decode(x, ridx, rw, y=y)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(4):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 256
+        Ub = len(set(ridx.cpu().numpy().ravel().tolist()))
+        lb = (Ub + 1) * blob + 2 * E * d + 4 * shape.r * d + 6 * d
+        out[f"layer_decode_b{B}"] = {"us_per_call": round(us, 2), "algorithmic_GBs": round(lb / (us * 1e-6) / 1e9, 1)}
+        log(f"one layer, B={B}: {us:.2f} us/call, {lb / (us * 1e-6) / 1e9:.0f} GB/s algorithmic")
+    lay.close()
+
+    # ---- long prefill (T = 8192 tokens through one layer): the matrix-core rate
+    T = 8192
+    lay = make_layer(moe, shape, ws[1], 1, L, max_tokens=T)
+    x = synth.activations(shape, T, ("bench_long",), device="cuda", dtype=torch.float32)
+    y = torch.empty_like(x)
+    lay.prefill(x, y=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        lay.prefill(x, y=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    assert lay.status() == 0
+    flops = T * (6 * d * shape.f * (k + 1) + 2 * d * E * 2 + 4 * shape.r * d)
+    out["prefill_t8192_one_layer"] = {"ms": round(ms, 3), "tok_s": round(T / (ms / 1e3), 1),
+                                      "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                                      "mfma_frac_bf16": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+    log(f"prefill T={T}, one layer: {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s "
+        f"({flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12):.3f} of bf16 MFMA peak)")
+    lay.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +301,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads (batched, streamed, ...)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (scale for HBM counters)")
     args = ap.parse_args()
@@ -263,6 +448,8 @@ def main():
                    "mfma_frac_bf16": round(flops / (pms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 5)}
         log(f"prefill {T} tokens: {pms:.2f} ms, {prefill['value']:.0f} tok/s, hbm frac {prefill['hbm_frac']:.3f}")
 
+    extra = None if args.no_extra else extra_measurements(args, torch, np, moe, synth, shape, ws, layers)
+
     # ---- CPU baseline: the fp64 oracle on a bounded sample (1 decode step of the stack)
     cpu = None
     if not args.no_cpu:
@@ -317,6 +504,7 @@ def main():
         "kernel_b": {"kernel": "k_dec_b", "avg_launch_us": round(b_avg * 1e3, 3), "bytes_per_launch": bb_,
                      "achieved_GBs": round(bb_ / (b_avg * 1e-3) / 1e9, 1)},
         "prefill": prefill,
+        "other_workloads": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

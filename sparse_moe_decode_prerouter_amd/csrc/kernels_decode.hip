@@ -96,7 +96,7 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
 
-size_t sort_lds_bytes(int n, int E) { return (size_t)(3 * E + 2 * n) * sizeof(int); }
+size_t sort_lds_bytes(int n, int E) { return (size_t)(3 * E + n) * sizeof(int); }
 
 __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     extern __shared__ int sm[];
@@ -104,8 +104,8 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     int* cnt = sm;                 // [E] bucket sizes
     int* fill = sm + E;            // [E] placement counters
     int* off = sm + 2 * E;         // [E] bucket offsets
-    int* ex = sm + 3 * E;          // [n] expert of each assignment (-1: invalid)
-    int* tmp = sm + 3 * E + n;     // [n] assignments in bucket order (unordered within a bucket)
+    int* tmp = sm + 3 * E;         // [n] assignments in bucket order (unordered within a bucket)
+    const int32_t* ex = a.used_idx;  // expert of each assignment (-1: invalid), written below
     __shared__ int wsum[kSortThreads / 64];
     __shared__ int wact[kSortThreads / 64];
     __shared__ int tot_valid, tot_active;
@@ -121,7 +121,6 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
         a.used_idx[i] = e; a.used_w[i] = w;
         if (a.user_used_idx) a.user_used_idx[i] = e;
         if (a.user_used_w) a.user_used_w[i] = w;
-        ex[i] = e;
         if (e >= 0) atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
@@ -174,12 +173,14 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
 hipError_t launch_sort(const SortArgs& a, hipStream_t s) {
     const size_t lds = sort_lds_bytes(a.n_tok * a.k, a.E);
     if (lds > 64 * 1024) {
-        static bool raised = false;
-        if (lds > 160 * 1024) return hipErrorInvalidValue;
-        if (!raised) {
-            const hipError_t e = hipFuncSetAttribute((const void*)k_sort, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        // above the default dynamic LDS limit: raise it to what this call needs
+        // (the kernel's static LDS is a few hundred bytes of the 160 KiB)
+        static size_t raised = 0;
+        if (lds > 159 * 1024) return hipErrorInvalidValue;
+        if (lds > raised) {
+            const hipError_t e = hipFuncSetAttribute((const void*)k_sort, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
-            raised = true;
+            raised = lds;
         }
     }
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, a);

@@ -1,4 +1,5 @@
-"""GPU parity at full sizes: the 512-token prefill and a 32-token decode batch
+"""GPU parity at full sizes: the 512-token prefill (and a long 8192-token one)
+and a 32-token decode batch
 of one 35B-shape layer (the grouped-GEMM path), and the batched decode stack
 with the Zipf popularity + stickiness routing workload.
 
@@ -73,6 +74,13 @@ def sampled_layer_check(n_tok, prefill, seed, sample):
 def test_prefill_512_sampled():
     sample = [0, 1, 2, 77, 128, 255, 256, 300, 383, 449, 500, 511]
     sampled_layer_check(512, True, 21, sample)
+
+
+def test_prefill_8192_sampled():
+    """A long prefill: 32768 assignments through the token->expert sort, about
+    128 tokens per expert (several tiles each)."""
+    sample = [0, 1, 1000, 2047, 2048, 4095, 4096, 5555, 8000, 8191]
+    sampled_layer_check(8192, True, 23, sample)
 
 
 def test_decode_batch32_sampled():
