@@ -1,7 +1,7 @@
 // Decode-path kernels for gfx950: prologue, bf16 GEMVs with top-k, token to
 // expert sort/permute, and the int4 grouped GEMVs (gate/up + SwiGLU, down +
 // combine + shared expert + LoRA + residual).
-#include "device_common.h"
+#include "dec_common.h"
 #include "moe_internal.h"
 #include "topk.h"
 
@@ -88,30 +88,44 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Token to expert sort/permute, as a counting sort in one block: bucket sizes
-// by LDS atomics, their exclusive scan (the active experts, ascending, and
-// their offsets), placement into buckets, then each entry's rank among the
-// smaller assignment ids of its bucket, so that the order is by (expert,
-// assignment) whatever order the atomics took.
+// Token to expert sort/permute: a stable counting sort in one block. Each of
+// the 16 waves owns a contiguous chunk of the assignments and walks it 64 at
+// a time; lanes holding the same expert find each other with one ballot per
+// bit of the expert id, which gives each entry its rank among equal experts
+// in the step and the step's count per expert. Pass 1 counts per (wave,
+// expert); a scan over waves, then over experts, gives every (wave, expert)
+// its first position; pass 2 repeats the walk and places the entries. The
+// order is (expert, assignment id), and the active experts come out
+// ascending with their offsets.
 // ---------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
+constexpr int kSortWaves = kSortThreads / 64;
 
-size_t sort_lds_bytes(int n, int E) { return (size_t)(3 * E + n) * sizeof(int); }
+size_t sort_lds_bytes(int n, int E) { (void)n; return (size_t)(kSortWaves + 1) * E * sizeof(int); }
+
+// lanes (of the valid ones) whose expert equals this lane's; nbits covers E
+__device__ __forceinline__ unsigned long long match_expert(int e, bool valid, int nbits) {
+    unsigned long long m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long bb = __ballot(valid && bit);
+        m &= bit ? bb : ~bb;
+    }
+    return valid ? m : 0ull;
+}
 
 __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     extern __shared__ int sm[];
     const int n = a.n_tok * a.k, E = a.E;
-    int* cnt = sm;                 // [E] bucket sizes
-    int* fill = sm + E;            // [E] placement counters
-    int* off = sm + 2 * E;         // [E] bucket offsets
-    int* tmp = sm + 3 * E;         // [n] assignments in bucket order (unordered within a bucket)
-    const int32_t* ex = a.used_idx;  // expert of each assignment (-1: invalid), written below
-    __shared__ int wsum[kSortThreads / 64];
-    __shared__ int wact[kSortThreads / 64];
+    int* wcnt = sm;                          // [kSortWaves][E]: counts, then first positions
+    int* cnt = sm + kSortWaves * E;          // [E] bucket sizes
+    __shared__ int wsum[kSortWaves];
+    __shared__ int wact[kSortWaves];
     __shared__ int tot_valid, tot_active;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int e = tid; e < E; e += kSortThreads) { cnt[e] = 0; fill[e] = 0; }
-    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int i = tid; i < kSortWaves * E; i += kSortThreads) wcnt[i] = 0;
     for (int i = tid; i < n; i += kSortThreads) {
         const int t = i / a.k;
         const bool self = !a.route_idx || a.route_idx[(size_t)t * a.k] < 0;
@@ -121,14 +135,34 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
         a.used_idx[i] = e; a.used_w[i] = w;
         if (a.user_used_idx) a.user_used_idx[i] = e;
         if (a.user_used_w) a.user_used_w[i] = w;
-        if (e >= 0) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();                         // used_idx is read back below by other threads
+    const int chunk = ((n + kSortWaves - 1) / kSortWaves + 63) / 64 * 64;
+    const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
+    const unsigned long long lt = (1ull << lane) - 1;
+    // pass 1: counts per (wave, expert)
+    for (int base = c0; base < c1; base += 64) {
+        const int i = base + lane;
+        const int e = i < c1 ? a.used_idx[i] : -1;
+        const unsigned long long m = match_expert(e, e >= 0, nbits);
+        if (m && (m & lt) == 0) wcnt[wave * E + e] += __popcll(m);
     }
     __syncthreads();
-    // exclusive scan over the buckets: thread tid owns experts [e0, e1)
+    // scan over waves per expert, then over experts
     const int per = (E + kSortThreads - 1) / kSortThreads;
     const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
     int c = 0, na = 0;
-    for (int e = e0; e < e1; ++e) { c += cnt[e]; na += cnt[e] > 0; }
+    for (int e = e0; e < e1; ++e) {
+        int run = 0;
+        for (int w = 0; w < kSortWaves; ++w) {
+            const int v = wcnt[w * E + e];
+            wcnt[w * E + e] = run;
+            run += v;
+        }
+        cnt[e] = run;
+        c += run;
+        na += run > 0;
+    }
     int ic = c, ia = na;
     for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(ic, o, 64), u = __shfl_up(ia, o, 64);
@@ -138,7 +172,7 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     __syncthreads();
     if (tid == 0) {
         int s1 = 0, s2 = 0;
-        for (int w = 0; w < kSortThreads / 64; ++w) {
+        for (int w = 0; w < kSortWaves; ++w) {
             const int v = wsum[w], u = wact[w];
             wsum[w] = s1; wact[w] = s2; s1 += v; s2 += u;
         }
@@ -147,21 +181,23 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     __syncthreads();
     int o1 = wsum[wave] + ic - c, o2 = wact[wave] + ia - na;
     for (int e = e0; e < e1; ++e) {
-        off[e] = o1;
+        for (int w = 0; w < kSortWaves; ++w) wcnt[w * E + e] += o1;
         if (cnt[e] > 0) { a.active[o2] = e; a.act_off[o2] = o1; ++o2; }
         o1 += cnt[e];
     }
     __syncthreads();
-    for (int i = tid; i < n; i += kSortThreads) {
-        const int e = ex[i];
-        if (e >= 0) tmp[off[e] + atomicAdd(&fill[e], 1)] = i;
-    }
-    __syncthreads();
-    for (int s = tid; s < tot_valid; s += kSortThreads) {
-        const int i = tmp[s], e = ex[i], b0 = off[e], b1 = b0 + cnt[e];
-        int r = 0;
-        for (int q = b0; q < b1; ++q) r += tmp[q] < i;
-        a.perm[b0 + r] = i;
+    // pass 2: place
+    for (int base = c0; base < c1; base += 64) {
+        const int i = base + lane;
+        const int e = i < c1 ? a.used_idx[i] : -1;
+        const unsigned long long m = match_expert(e, e >= 0, nbits);
+        if (m) {
+            a.perm[wcnt[wave * E + e] + __popcll(m & lt)] = i;
+        }
+        // every lane has read its first position; the group's leader advances it
+        wave_lds_sync();
+        if (m && (m & lt) == 0) wcnt[wave * E + e] += __popcll(m);
+        wave_lds_sync();
     }
     if (tid == 0) {
         a.act_off[tot_active] = tot_valid;
@@ -174,7 +210,6 @@ hipError_t launch_sort(const SortArgs& a, hipStream_t s) {
     const size_t lds = sort_lds_bytes(a.n_tok * a.k, a.E);
     if (lds > 64 * 1024) {
         // above the default dynamic LDS limit: raise it to what this call needs
-        // (the kernel's static LDS is a few hundred bytes of the 160 KiB)
         static size_t raised = 0;
         if (lds > 159 * 1024) return hipErrorInvalidValue;
         if (lds > raised) {

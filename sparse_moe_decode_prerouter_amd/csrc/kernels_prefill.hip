@@ -55,18 +55,21 @@ __device__ __forceinline__ u32x4 nib4v(uint32_t w, uint32_t m, uint32_t c) {
     return r;
 }
 
-int prefill_max_tiles(int T, int K, int E) {
+constexpr int kTileBig = 64;      // assignments (tokens) per tile of the large-tile path
+
+int prefill_max_tiles(int T, int K, int E, int tm) {
     const int nk = T * K;
-    return (nk + kTileM - 1) / kTileM + (nk < E ? nk : E) + (T + kTileM - 1) / kTileM + 1;
+    return (nk + tm - 1) / tm + (nk < E ? nk : E) + (T + tm - 1) / tm + 1;
 }
 
 // ---------------------------------------------------------------------------
-// Tile list: the 16-row tiles of every active expert's sorted assignments,
-// then the 16-token tiles of the shared expert. Each record carries its blob,
-// resolved (and its staging checked) here once. meta[2] = tiles, meta[3] =
-// routed tiles. One block.
+// Tile list: the TM-row tiles of every active expert's sorted assignments,
+// then the TM-token tiles of the shared expert. Each record carries its blob,
+// resolved (and its staging checked) here once. Written to `tiles` with
+// meta[mi] = tiles, meta[mi + 1] = routed tiles. One block.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(1024) k_pf_tiles(PrefillArgs a) {
+template <int TM>
+__global__ void __launch_bounds__(1024) k_pf_tiles(PrefillArgs a, int32_t* tiles, int mi) {
     __shared__ int wsum[16];
     __shared__ int total;
     const GemvArgs& g = a.g;
@@ -77,7 +80,7 @@ __global__ void __launch_bounds__(1024) k_pf_tiles(PrefillArgs a) {
     if (tid < n_active) {
         off0 = g.act_off[tid];
         off1 = g.act_off[tid + 1];
-        cnt = (off1 - off0 + kTileM - 1) / kTileM;
+        cnt = (off1 - off0 + TM - 1) / TM;
         const int e = g.active[tid];
         if (!ev.slot_of) {
             blob = e;
@@ -102,18 +105,18 @@ __global__ void __launch_bounds__(1024) k_pf_tiles(PrefillArgs a) {
     __syncthreads();
     const int start = wsum[wave] + incl - cnt;
     for (int i = 0; i < cnt; ++i) {
-        const int p0 = off0 + i * kTileM;
-        *(int4*)(a.tiles + 4 * (start + i)) = make_int4(tid, p0, min(kTileM, off1 - p0), blob);
+        const int p0 = off0 + i * TM;
+        *(int4*)(tiles + 4 * (start + i)) = make_int4(tid, p0, min(TM, off1 - p0), blob);
     }
-    const int ns = g.fs ? (g.n_tok + kTileM - 1) / kTileM : 0;
+    const int ns = g.fs ? (g.n_tok + TM - 1) / TM : 0;
     int sblob = -1;
     if (ns && ev.shared) {
         if (ev.shared_tag && *ev.shared_tag != ev.E) { if (tid == 0) set_err(g.err, ERR_NOT_STAGED); }
         else sblob = -2;
     }
     for (int i = tid; i < ns; i += 1024)
-        *(int4*)(a.tiles + 4 * (total + i)) = make_int4(-1, i * kTileM, min(kTileM, g.n_tok - i * kTileM), sblob);
-    if (tid == 0) { a.meta_w[2] = total + ns; a.meta_w[3] = total; }
+        *(int4*)(tiles + 4 * (total + i)) = make_int4(-1, i * TM, min(TM, g.n_tok - i * TM), sblob);
+    if (tid == 0) { a.meta_w[mi] = total + ns; a.meta_w[mi + 1] = total; }
 }
 
 struct PfItem {
@@ -380,6 +383,31 @@ __device__ __forceinline__ void vm_wait() {
 }
 
 // wait until this wave's loads of the stage `ahead` stages before the newest
+// issued one have landed, for LN loads per stage per wave (LS for the waves
+// that also load the scales); any other load issued after that stage only
+// makes the wait longer
+template <int LN, int LS>
+__device__ __forceinline__ void ring_wait(int ahead, bool sc_wave) {
+    if (sc_wave) {
+        switch (ahead) {
+            case 0: vm_wait<0>(); break;
+            case 1: vm_wait<LS>(); break;
+            case 2: vm_wait<2 * LS>(); break;
+            case 3: vm_wait<3 * LS>(); break;
+            default: vm_wait<4 * LS>(); break;
+        }
+    } else {
+        switch (ahead) {
+            case 0: vm_wait<0>(); break;
+            case 1: vm_wait<LN>(); break;
+            case 2: vm_wait<2 * LN>(); break;
+            case 3: vm_wait<3 * LN>(); break;
+            default: vm_wait<4 * LN>(); break;
+        }
+    }
+}
+
+// wait until this wave's loads of the stage `ahead` stages before the newest
 // issued one have landed (2 loads per stage per wave, 3 for waves 0-1; any
 // other load issued after that stage only makes the wait longer)
 __device__ __forceinline__ void dn_wait(int ahead, bool sc_wave) {
@@ -642,6 +670,214 @@ __global__ void __launch_bounds__(kDnThreads) k_pf_down(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Gate/up + SwiGLU with 64-token tiles (many tokens per expert, long
+// prefills). Block = 64 tokens x 128 rows of W_g and the same rows of W_u;
+// wave w owns rows 32 w .. 32 w + 31 (2 row tiles) of both and all 64 tokens
+// (4 token tiles), so each unpacked B fragment feeds 4 MFMAs and each A
+// fragment 4 weight tiles. k walks in stages of GS groups (64 GS elements)
+// through a ring of NST LDS buffers filled NST - 1 stages ahead by
+// direct-to-LDS loads. The bias half of
+// the affine dequant, sum_g (b - 128 s)_g * sum_{k in g} u_k, is itself a bf16
+// MFMA over the group axis (hi/lo of both factors) evaluated before the k loop;
+// each group's scale s multiplies that group's fresh MFMA accumulator.
+// bf16 activations; d a multiple of 128 up to 2048 (at most 32 groups, one
+// MFMA k-step); f a multiple of 128.
+// ---------------------------------------------------------------------------
+constexpr int kBgRows = 128;                  // rows of W_g (and of W_u) per block
+constexpr int kBgGs = 2;                      // groups per stage
+constexpr int kBgNst = 2;                     // ring depth (two blocks per CU fit the LDS)
+
+// one stage of GS groups: PA = 8 GS 16-byte pieces of u per token row, PB =
+// 2 GS pieces of int4 per weight row
+template <int GS>
+struct BgStage {
+    static constexpr int PA = 8 * GS, PB = 2 * GS;
+    uint8_t a[kTileBig * PA * 16];            // piece c of token row m at slot c ^ (m mod PA)
+    uint8_t b[2 * kBgRows * PB * 16];         // 256 rows (gate, then up); piece p of row r at slot p ^ bsw(r)
+    uint32_t sc[2 * kBgRows][GS];             // (s, b) of the stage's groups per row
+    // slot swizzle of the weight rows: the 16 rows of one MFMA read spread
+    // over all bank groups
+    static __device__ __forceinline__ int bsw(int r) { return PB == 4 ? (r >> 2) & 3 : (r >> 3) & 1; }
+};
+
+// 4 bytes per lane from global memory straight into LDS (lane l at lds + 4 l)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma4(const void* gptr, const void* lds) {
+    const uint32_t off = (uint32_t)(uintptr_t)lds;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" : : "s"(off), "v"(gptr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int GS, int NST>
+__global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
+    using Stage = BgStage<GS>;
+    constexpr int PA = Stage::PA, PB = Stage::PB, KS = 64 * GS;
+    constexpr int LA = PA / 4, LB = PB, LN = LA + LB + GS;     // direct-to-LDS loads per stage per wave
+    const GemvArgs& g = a.g;
+    __shared__ __align__(16) Stage S[NST];
+    __shared__ __align__(16) uint16_t ush[kTileBig][32], usl[kTileBig][32];   // group sums of u, bf16 hi / lo
+    __shared__ int tok[kTileBig];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if ((int)blockIdx.x >= g.meta[4]) return;
+    const int4 ti = *(const int4*)(a.tiles64 + 4 * blockIdx.x);
+    const bool shared = ti.x < 0;
+    const int f = shared ? g.fs : g.f;
+    const int rb0 = blockIdx.y * kBgRows;
+    const int p0 = ti.y, M = ti.z;
+    if (rb0 >= f || M <= 0) return;
+    const uint8_t* blob = pf_blob(g, ti.w);
+    const uint8_t* wb = blob ? blob : g.ev.base;
+    const int d = g.d, G = d / 64, NS = d / KS;
+    const BlobLayout L = BlobLayout::make(d, f);
+    if (tid < kTileBig) {
+        const int p = p0 + (tid < M ? tid : M - 1);
+        tok[tid] = shared ? p : g.perm[p] / g.k;
+    }
+    __syncthreads();
+    // per-thread sources of a stage (direct-to-LDS, contiguous per wave instruction)
+    const uint32_t* asrc[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int pa = wave * 64 + 256 * i + lane, m = pa / PA, c = (pa % PA) ^ (m % PA);
+        asrc[i] = g.u_pk + (size_t)tok[m] * (d / 2) + 4 * c;
+    }
+    const uint8_t* bsrc[LB];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int pi = wave * 64 + 256 * i + lane, r = pi / PB, pg = (pi % PB) ^ Stage::bsw(r);
+        bsrc[i] = wb + (r < kBgRows ? L.gate_q : L.up_q) + (size_t)(rb0 + (r & (kBgRows - 1))) * (d / 2) + 16 * pg;
+    }
+    const uint8_t* ssrc[GS];
+#pragma unroll
+    for (int j = 0; j < GS; ++j) {
+        const int di = wave * 64 + 256 * j + lane, r = di / GS;
+        ssrc[j] = wb + (r < kBgRows ? L.gate_sb : L.up_sb) + (size_t)(rb0 + (r & (kBgRows - 1))) * (d / 16) + 4 * (di % GS);
+    }
+    auto stage_issue = [&](int kc, Stage& st) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i) lds_dma16(asrc[i] + kc * (KS / 2), &st.a[(wave * 64 + 256 * i) * 16]);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) lds_dma16(bsrc[i] + kc * (KS / 2), &st.b[(wave * 64 + 256 * i) * 16]);
+#pragma unroll
+        for (int j = 0; j < GS; ++j) lds_dma4(ssrc[j] + kc * 4 * GS, (const uint8_t*)&st.sc[0][0] + (wave * 64 + 256 * j) * 4);
+    };
+    for (int i = 0; i < NST - 1 && i < NS; ++i) stage_issue(i, S[i]);
+
+    // ---- bias term, as one MFMA k-step over the groups: A = group sums of u
+    // (tokens x groups), B = (b - 128 s) (groups x rows), both bf16 hi + lo
+    for (int i = tid; i < kTileBig * 32; i += 256) {
+        const int m = i >> 5, gg = i & 31;
+        float us = 0.f;
+        if (gg < G) us = g.usum[(size_t)tok[m] * (d / 32) + 2 * gg] + g.usum[(size_t)tok[m] * (d / 32) + 2 * gg + 1];
+        const uint32_t hi = f32_to_bf16(us);
+        ush[m][gg] = (uint16_t)hi;
+        usl[m][gg] = (uint16_t)f32_to_bf16(us - bf16_to_f32(hi));
+    }
+    const int ml = lane & 15, pc = lane >> 4;
+    f32x4 acc[4][2][2];                        // [token tile][row tile][gate / up]
+    {
+        u32x4 chi[2][2], clo[2][2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int gu = 0; gu < 2; ++gu) {
+                const int n = rb0 + 32 * wave + 16 * rt + ml;
+                const uint32_t* sbp = (const uint32_t*)(wb + (gu ? L.up_sb : L.gate_sb) + (size_t)n * (d / 16));
+                uint32_t h8[8], l8[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int gg = 8 * pc + j;
+                    float c = 0.f;
+                    if (gg < G) {
+                        const uint32_t sb = sbp[gg];
+                        c = f16_to_f32(sb >> 16) - 128.f * f16_to_f32(sb & 0xFFFF);
+                    }
+                    h8[j] = f32_to_bf16(c);
+                    l8[j] = f32_to_bf16(c - bf16_to_f32(h8[j]));
+                }
+                chi[rt][gu] = u32x4{h8[0] | (h8[1] << 16), h8[2] | (h8[3] << 16), h8[4] | (h8[5] << 16),
+                                    h8[6] | (h8[7] << 16)};
+                clo[rt][gu] = u32x4{l8[0] | (l8[1] << 16), l8[2] | (l8[3] << 16), l8[4] | (l8[5] << 16),
+                                    l8[6] | (l8[7] << 16)};
+            }
+        lds_barrier();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const u32x4 uh = *(const u32x4*)&ush[16 * mt + ml][8 * pc];
+            const u32x4 ul = *(const u32x4*)&usl[16 * mt + ml][8 * pc];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int gu = 0; gu < 2; ++gu) {
+                    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+                    c = mfma16(uh, chi[rt][gu], c);
+                    c = mfma16(uh, clo[rt][gu], c);
+                    c = mfma16(ul, chi[rt][gu], c);
+                    acc[mt][rt][gu] = c;
+                }
+        }
+    }
+
+    // ---- k loop: stages kc + 1 .. kc + NST - 1 load while stage kc is multiplied
+    uint32_t nm = 0x000F000Fu, nc = 0x43004300u;
+    asm volatile("" : "+v"(nm), "+v"(nc));
+    for (int kc = 0; kc < NS; ++kc) {
+        ring_wait<LN, LN>(min(NST - 2, NS - 1 - kc), false);
+        lds_barrier();                                  // stage kc landed everywhere; stage kc - 1 consumed
+        const Stage& st = S[kc % NST];
+        if (kc + NST - 1 < NS) stage_issue(kc + NST - 1, S[(kc + NST - 1) % NST]);
+#pragma unroll
+        for (int q = 0; q < GS; ++q) {
+            const int p = 2 * q + (pc >> 1);
+            u32x4 b0[2][2], b1[2][2];
+            float sv[2][2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int gu = 0; gu < 2; ++gu) {
+                    const int r = gu * kBgRows + 32 * wave + 16 * rt + ml;
+                    const u32x2 w = *(const u32x2*)&st.b[r * (PB * 16) + ((p ^ Stage::bsw(r)) << 4) + ((pc & 1) << 3)];
+                    b0[rt][gu] = nib4v(w.x, nm, nc);
+                    b1[rt][gu] = nib4v(w.y, nm, nc);
+                    sv[rt][gu] = f16_to_f32(st.sc[r][q] & 0xFFFF);
+                }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int m = 16 * mt + ml, gp = 8 * q + 2 * pc;        // pieces gp, gp + 1 of row m
+                const u32x4 a0 = *(const u32x4*)&st.a[m * (PA * 16) + ((gp ^ (m % PA)) << 4)];
+                const u32x4 a1 = *(const u32x4*)&st.a[m * (PA * 16) + (((gp + 1) ^ (m % PA)) << 4)];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int gu = 0; gu < 2; ++gu) {
+                        f32x4 pp = {0.f, 0.f, 0.f, 0.f};
+                        pp = mfma16(a0, b0[rt][gu], pp);
+                        pp = mfma16(a1, b1[rt][gu], pp);
+                        const float s1 = sv[rt][gu];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[mt][rt][gu][i] = __builtin_fmaf(s1, pp[i], acc[mt][rt][gu][i]);
+                    }
+            }
+        }
+    }
+    const bool ok = blob != nullptr;
+    float* hb = shared ? g.hs : g.h;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int n = rb0 + 32 * wave + 16 * rt + ml;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * mt + 4 * pc + i;
+                if (m < M && n < f) hb[(size_t)(p0 + m) * f + n] = ok ? silu_f32(acc[mt][rt][0][i]) * acc[mt][rt][1][i] : 0.f;
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Combine per (token, row): shared (gated), routed in routing order
 // (weighted), LoRA B, residual. A thread takes 4 consecutive rows of
 // kCombTok tokens; every load of a term is issued for all its tokens before
@@ -839,6 +1075,120 @@ __global__ void __launch_bounds__(256) k_route_mm(RouteMMArgs a) {
     }
 }
 
+// The same products for many tokens: block = 64 tokens x 64 rows staged
+// through LDS 64 elements of k at a time (the next stage's loads in flight
+// while the current one is multiplied); wave (wm, wn) computes tokens
+// 32 wm .. + 31 x rows 32 wn .. + 31. Same per-step fp32 / fp64 split.
+constexpr int kRmTile = 64;                  // tokens and rows per block
+constexpr int kRmK = 64;                     // hidden elements per stage (2 k-steps)
+
+__global__ void __launch_bounds__(256) k_route_mm_tiled(RouteMMArgs a) {
+    // [token or row][piece of 8 elements], padded by one piece against bank conflicts
+    __shared__ __align__(16) u32x4 sa[2][kRmTile][kRmK / 8 + 1], sl[2][kRmTile][kRmK / 8 + 1], sw[2][kRmTile][kRmK / 8 + 1];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ml = lane & 15, pc = lane >> 4;
+    const int d = a.d, T = a.n_tok;
+    const int nr_router = a.router ? a.E : 0, nr_head = a.head ? a.En : 0;
+    const int nr_lora = a.lora_a ? a.r : 0;
+    const int R = nr_router + nr_head + nr_lora + (a.sgate_w ? 1 : 0);
+    const int t0 = blockIdx.y * kRmTile, r0 = blockIdx.x * kRmTile;
+    const bool lo = a.u_pk_lo != nullptr;
+    // this thread's two load pieces of each stage: row/token q >> 3, piece q & 7
+    const uint32_t* ap[2];
+    const uint32_t* alp[2];
+    const uint16_t* wp[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = tid + 256 * j, rr = q >> 3, pcs = q & 7;
+        const int tok = t0 + rr < T ? t0 + rr : T - 1;
+        ap[j] = a.u_pk + (size_t)tok * (d / 2) + 4 * pcs;
+        alp[j] = lo ? a.u_pk_lo + (size_t)tok * (d / 2) + 4 * pcs : ap[j];
+        int row = r0 + rr < R ? r0 + rr : R - 1;
+        const uint16_t* w;
+        if (row < nr_router) w = a.router + (size_t)row * d;
+        else if (row < nr_router + nr_head) w = a.head + (size_t)(row - nr_router) * d;
+        else if (row < nr_router + nr_head + nr_lora) w = a.lora_a + (size_t)(row - nr_router - nr_head) * d;
+        else w = a.sgate_w;
+        wp[j] = w + 8 * pcs;
+    }
+    u32x4 ra[2], rl[2], rw[2];
+    auto load = [&](int st) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            ra[j] = *(const u32x4*)(ap[j] + st * (kRmK / 2));
+            rw[j] = *(const u32x4*)(wp[j] + st * kRmK);
+            rl[j] = lo ? *(const u32x4*)(alp[j] + st * (kRmK / 2)) : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store = [&](int b) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int q = tid + 256 * j, rr = q >> 3, pcs = q & 7;
+            sa[b][rr][pcs] = ra[j];
+            sw[b][rr][pcs] = bf16_pairs_p4(rw[j]);
+            if (lo) sl[b][rr][pcs] = rl[j];
+        }
+    };
+    // wave (wm, wn): tokens 32 wm + 16 i, rows 32 wn + 16 j
+    const int wm = wave & 1, wn = wave >> 1;
+    double acc[2][2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
+    const int NS = d / kRmK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int st = 0; st < NS; ++st) {
+        const int b = st & 1;
+        if (st + 1 < NS) load(st + 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 av[2], alv[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                av[i] = sa[b][32 * wm + 16 * i + ml][4 * ks + pc];
+                alv[i] = lo ? sl[b][32 * wm + 16 * i + ml][4 * ks + pc] : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bv[j] = sw[b][32 * wn + 16 * j + ml][4 * ks + pc];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+                    p = mfma16(av[i], bv[j], p);
+                    if (lo) p = mfma16(alv[i], bv[j], p);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[i][j][v] += (double)p[v];
+                }
+        }
+        if (st + 1 < NS) store((st + 1) & 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = r0 + 32 * wn + 16 * j + ml;
+        if (r >= R) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = t0 + 32 * wm + 16 * i + 4 * pc + v;
+                if (t >= T) continue;
+                const double z = acc[i][j][v];
+                if (r < nr_router) a.logits_r[(size_t)t * a.E + r] = z;
+                else if (r < nr_router + nr_head) a.logits_h[(size_t)t * a.En + (r - nr_router)] = z;
+                else if (r < nr_router + nr_head + nr_lora) a.au[(size_t)t * a.r + (r - nr_router - nr_head)] = (float)z;
+                else a.sgate[t] = (float)(1.0 / (1.0 + exp(-z)));
+            }
+    }
+}
+
 // top-k per token: blockIdx.y = 0 router (self-routed rows), 1 head
 __global__ void __launch_bounds__(256) k_route_topk(RouteMMArgs a) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -865,7 +1215,13 @@ hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s) {
     if (a.d % 128) return hipErrorInvalidValue;
     const int R = (a.router ? a.E : 0) + (a.head ? a.En : 0) + (a.lora_a ? a.r : 0) + (a.sgate_w ? 1 : 0);
     if (R > 0) {
-        hipLaunchKernelGGL(k_route_mm, dim3((R + 15) / 16, (a.n_tok + 15) / 16), dim3(256), 0, s, a);
+        // 64 x 64 LDS tiles once they alone fill the chip twice over
+        const long long big_blocks = (long long)((R + kRmTile - 1) / kRmTile) * ((a.n_tok + kRmTile - 1) / kRmTile);
+        if (big_blocks >= 512)
+            hipLaunchKernelGGL(k_route_mm_tiled, dim3((R + kRmTile - 1) / kRmTile, (a.n_tok + kRmTile - 1) / kRmTile),
+                               dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(k_route_mm, dim3((R + 15) / 16, (a.n_tok + 15) / 16), dim3(256), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -884,13 +1240,22 @@ bool prefill_mm_ok(int d, int f, int fs) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     const GemvArgs& g = a.g;
     if (!prefill_mm_ok(g.d, g.f, g.fs)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(k_pf_tiles<kTileM>, dim3(1), dim3(1024), 0, s, a, a.tiles, 2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int fmax = g.f > g.fs ? g.f : g.fs;
-    const dim3 ggrid(a.max_tiles, (fmax + kGuRows - 1) / kGuRows);
-    if (g.u_pk_lo) hipLaunchKernelGGL(k_pf_gateup<true>, ggrid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_pf_gateup<false>, ggrid, dim3(256), 0, s, a);
+    // many tokens per expert (on average 48 or more): 64-token tiles for gate/up
+    const bool big = !g.u_pk_lo && g.d <= 2048 && g.d % 128 == 0 && g.f % kBgRows == 0 &&
+                     (g.fs == 0 || g.fs % kBgRows == 0) && (long long)g.n_tok * g.k >= 48LL * g.max_active;
+    if (big) {
+        hipLaunchKernelGGL(k_pf_tiles<kTileBig>, dim3(1), dim3(1024), 0, s, a, a.tiles64, 4);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((k_pf_gateup_big<kBgGs, kBgNst>), dim3(a.max_tiles64, (fmax + kBgRows - 1) / kBgRows), dim3(256), 0, s, a);
+    } else {
+        const dim3 ggrid(a.max_tiles, (fmax + kGuRows - 1) / kGuRows);
+        if (g.u_pk_lo) hipLaunchKernelGGL(k_pf_gateup<true>, ggrid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(k_pf_gateup<false>, ggrid, dim3(256), 0, s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         // enough blocks that none spans more than kDnTiles tiles: a block

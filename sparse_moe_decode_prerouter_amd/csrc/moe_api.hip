@@ -88,7 +88,7 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.used_w = c.take<float>(T * K);
     S.au = c.take<float>(T * std::max(1, d->lora_rank));
     S.sgate = c.take<float>(std::max<size_t>(T, 64));
-    S.sort_meta = c.take<int32_t>(4);
+    S.sort_meta = c.take<int32_t>(8);
     // the digest arrays are at least one wavefront wide: the decode kernels
     // read 64 entries unconditionally and use the valid ones
     S.active = c.take<int32_t>(std::max<size_t>(nas + 1, 64));
@@ -98,6 +98,7 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.h = c.take<float>(T * K * d->d_ff);
     S.hs = c.take<float>(T * std::max(1, d->d_ff_shared));
     S.tiles = c.take<int32_t>(4 * (size_t)prefill_max_tiles((int)T, (int)K, (int)E));
+    S.tiles64 = c.take<int32_t>(4 * (size_t)prefill_max_tiles((int)T, (int)K, (int)E, 64));
     S.ob = c.take<float>(T * K * D);
     S.obs = c.take<float>(T * D);
     (void)Kn;
@@ -362,6 +363,8 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
         pf.g = ga;
         pf.tiles = L->s.tiles;
         pf.max_tiles = prefill_max_tiles(n_tok, D.top_k, D.n_experts);
+        pf.tiles64 = L->s.tiles64;
+        pf.max_tiles64 = prefill_max_tiles(n_tok, D.top_k, D.n_experts, 64);
         pf.meta_w = L->s.sort_meta;
         pf.n_cu = L->n_cu;
         pf.ob = L->s.ob; pf.obs = L->s.obs;

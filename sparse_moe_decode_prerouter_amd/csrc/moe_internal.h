@@ -80,7 +80,8 @@ struct Scratch {
     float* wsort;            // [T*k] routing weight of each sorted assignment
     float* h;                // [T*k][f] routed expert hidden (sorted order)
     float* hs;               // [T][fs] shared expert hidden
-    int32_t* tiles;          // prefill: grouped-GEMM work list, 4 ints per tile
+    int32_t* tiles;          // prefill: grouped-GEMM work list, 4 ints per tile (16-row tiles)
+    int32_t* tiles64;        // the same with 64-row tiles (many tokens per expert)
     float* ob;               // prefill: [T*k][d] routed expert outputs by assignment
     float* obs;              // prefill: [T][d] shared expert outputs
 };
@@ -194,12 +195,13 @@ struct PrefillArgs {
     // first position, rows (<= 16), blob (>= 0: index in the store or slab,
     // -2: shared blob, -1: not staged)}
     int32_t* tiles; int max_tiles;
-    int32_t* meta_w;                     // tile kernel writes meta[2] = tiles, meta[3] = routed tiles
+    int32_t* tiles64; int max_tiles64;   // 64-row tiles (large-tile gate/up)
+    int32_t* meta_w;                     // tile kernel writes meta[2] = tiles, meta[3] = routed tiles (meta[4], [5]: 64-row)
     int n_cu;                            // blocks of the persistent down projection
     float* ob; float* obs;               // down outputs: [T*k][d] by assignment, [T][d] shared
     const int32_t* used_idx; const float* used_w;
 };
-int prefill_max_tiles(int T, int K, int E);
+int prefill_max_tiles(int T, int K, int E, int tm = 16);
 bool prefill_mm_ok(int d, int f, int fs);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 

@@ -83,6 +83,13 @@ def test_prefill_8192_sampled():
     sampled_layer_check(8192, True, 23, sample)
 
 
+def test_prefill_ragged_long_sampled():
+    """A long prefill whose token count is not a multiple of 64: the 64 x 64
+    routing tiles and the 64-token gate/up tiles both end in a partial tile."""
+    sample = [0, 63, 64, 2500, 4095, 4096, 4132]
+    sampled_layer_check(4133, True, 24, sample)
+
+
 def test_decode_batch32_sampled():
     sample = [0, 1, 5, 13, 16, 22, 30, 31]
     sampled_layer_check(32, False, 22, sample)
