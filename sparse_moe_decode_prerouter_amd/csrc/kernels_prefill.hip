@@ -255,6 +255,8 @@ __global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
     f32x4 accg[NJ], accu[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) { accg[j] = f32x4{0.f, 0.f, 0.f, 0.f}; accu[j] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    uint32_t nm = 0x000F000Fu, nc = 0x43004300u;
+    asm volatile("" : "+v"(nm), "+v"(nc));
     for (int st = 0; st < NS; ++st) {
         const GuLds<LO>& C = S[st & 1];
         if (st + 1 < NS) gu_stage_load<LO>(R, st + 1, wb, L, d, f, rb0, tok, a);
@@ -276,7 +278,8 @@ __global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
                 const int rg = wave * (16 * NJ) + 16 * j + ml, ru = kGuRows + rg;
                 const u32x2 wg = gu_b_read<LO>(C, rg, q, pc), wu = gu_b_read<LO>(C, ru, q, pc);
                 const uint32_t sg = C.sc[rg][q], su = C.sc[ru][q];
-                const u32x4 bg0 = nib4(wg.x), bg1 = nib4(wg.y), bu0 = nib4(wu.x), bu1 = nib4(wu.y);
+                const u32x4 bg0 = nib4v(wg.x, nm, nc), bg1 = nib4v(wg.y, nm, nc);
+                const u32x4 bu0 = nib4v(wu.x, nm, nc), bu1 = nib4v(wu.y, nm, nc);
                 f32x4 pg = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
                 pg = mfma16(a0, bg0, pg);
                 pu = mfma16(a0, bu0, pu);
@@ -689,10 +692,10 @@ constexpr int kBgNst = 2;                     // ring depth (two blocks per CU f
 
 // one stage of GS groups: PA = 8 GS 16-byte pieces of u per token row, PB =
 // 2 GS pieces of int4 per weight row
-template <int GS>
+template <int GS, int TM>
 struct BgStage {
     static constexpr int PA = 8 * GS, PB = 2 * GS;
-    uint8_t a[kTileBig * PA * 16];            // piece c of token row m at slot c ^ (m mod PA)
+    uint8_t a[TM * PA * 16];                  // piece c of token row m at slot c ^ (m mod PA)
     uint8_t b[2 * kBgRows * PB * 16];         // 256 rows (gate, then up); piece p of row r at slot p ^ bsw(r)
     uint32_t sc[2 * kBgRows][GS];             // (s, b) of the stage's groups per row
     // slot swizzle of the weight rows: the 16 rows of one MFMA read spread
@@ -709,19 +712,20 @@ __device__ __forceinline__ void lds_dma4(const void* gptr, const void* lds) {
 }
 #pragma clang diagnostic pop
 
-template <int GS, int NST>
+template <int GS, int NST, int TM>
 __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
-    using Stage = BgStage<GS>;
-    constexpr int PA = Stage::PA, PB = Stage::PB, KS = 64 * GS;
-    constexpr int LA = PA / 4, LB = PB, LN = LA + LB + GS;     // direct-to-LDS loads per stage per wave
+    using Stage = BgStage<GS, TM>;
+    constexpr int PA = Stage::PA, PB = Stage::PB, KS = 64 * GS, MT = TM / 16;
+    constexpr int LA = TM * PA / 256, LB = PB, LN = LA + LB + GS;   // direct-to-LDS loads per stage per wave
+    static_assert(TM * PA >= 256, "one A piece per thread at least");
     const GemvArgs& g = a.g;
     __shared__ __align__(16) Stage S[NST];
-    __shared__ __align__(16) uint16_t ush[kTileBig][32], usl[kTileBig][32];   // group sums of u, bf16 hi / lo
-    __shared__ int tok[kTileBig];
+    __shared__ __align__(16) uint16_t ush[TM][32], usl[TM][32];   // group sums of u, bf16 hi / lo
+    __shared__ int tok[TM];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if ((int)blockIdx.x >= g.meta[4]) return;
-    const int4 ti = *(const int4*)(a.tiles64 + 4 * blockIdx.x);
+    if ((int)blockIdx.x >= g.meta[TM == kTileBig ? 4 : 2]) return;
+    const int4 ti = *(const int4*)((TM == kTileBig ? a.tiles64 : a.tiles) + 4 * blockIdx.x);
     const bool shared = ti.x < 0;
     const int f = shared ? g.fs : g.f;
     const int rb0 = blockIdx.y * kBgRows;
@@ -731,7 +735,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
     const uint8_t* wb = blob ? blob : g.ev.base;
     const int d = g.d, G = d / 64, NS = d / KS;
     const BlobLayout L = BlobLayout::make(d, f);
-    if (tid < kTileBig) {
+    if (tid < TM) {
         const int p = p0 + (tid < M ? tid : M - 1);
         tok[tid] = shared ? p : g.perm[p] / g.k;
     }
@@ -767,7 +771,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
 
     // ---- bias term, as one MFMA k-step over the groups: A = group sums of u
     // (tokens x groups), B = (b - 128 s) (groups x rows), both bf16 hi + lo
-    for (int i = tid; i < kTileBig * 32; i += 256) {
+    for (int i = tid; i < TM * 32; i += 256) {
         const int m = i >> 5, gg = i & 31;
         float us = 0.f;
         if (gg < G) us = g.usum[(size_t)tok[m] * (d / 32) + 2 * gg] + g.usum[(size_t)tok[m] * (d / 32) + 2 * gg + 1];
@@ -776,7 +780,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
         usl[m][gg] = (uint16_t)f32_to_bf16(us - bf16_to_f32(hi));
     }
     const int ml = lane & 15, pc = lane >> 4;
-    f32x4 acc[4][2][2];                        // [token tile][row tile][gate / up]
+    f32x4 acc[MT][2][2];                       // [token tile][row tile][gate / up]
     {
         u32x4 chi[2][2], clo[2][2];
 #pragma unroll
@@ -804,7 +808,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
             }
         lds_barrier();
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
             const u32x4 uh = *(const u32x4*)&ush[16 * mt + ml][8 * pc];
             const u32x4 ul = *(const u32x4*)&usl[16 * mt + ml][8 * pc];
 #pragma unroll
@@ -844,7 +848,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
                     sv[rt][gu] = f16_to_f32(st.sc[r][q] & 0xFFFF);
                 }
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
                 const int m = 16 * mt + ml, gp = 8 * q + 2 * pc;        // pieces gp, gp + 1 of row m
                 const u32x4 a0 = *(const u32x4*)&st.a[m * (PA * 16) + ((gp ^ (m % PA)) << 4)];
                 const u32x4 a1 = *(const u32x4*)&st.a[m * (PA * 16) + (((gp + 1) ^ (m % PA)) << 4)];
@@ -865,7 +869,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
     const bool ok = blob != nullptr;
     float* hb = shared ? g.hs : g.h;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int n = rb0 + 32 * wave + 16 * rt + ml;
@@ -990,8 +994,8 @@ __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
 // r | shared gate 1] x tokens. bf16 x bf16 products are exact in fp32; each
 // 32-wide k-step goes to a fresh fp32 accumulator and the steps are summed in
 // fp64, so a logit carries the rounding of at most one 32-term fp32 sum per
-// step. Grid: (16-row tiles, 16-token tiles); wave w takes the k-steps of
-// the w-th quarter of d and the quarters are summed in order.
+// step. Grid: (blocks of 16 RT rows, blocks of 16 TT tokens); the NW waves
+// of a block take consecutive slices of the k-steps, summed in slice order.
 // B (weights) pairs are reordered to the (p, p + 4) order of u_pk.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 bf16_pairs_p4(u32x4 v) {
@@ -1003,9 +1007,12 @@ __device__ __forceinline__ u32x4 bf16_pairs_p4(u32x4 v) {
     return r;
 }
 
-__global__ void __launch_bounds__(256) k_route_mm(RouteMMArgs a) {
-    constexpr int kMaxSteps = 16;              // 32-wide k-steps whose loads are issued together
-    __shared__ double red[3][64][4];
+// RT x TT 16 x 16 tiles (rows x tokens) per block; NW waves split the d / 32
+// k-steps into NW consecutive slices (a wave's loads issued kMaxSteps k-steps
+// at a time); LO: activations carry a bf16 lo part (two MFMAs per product)
+template <int RT, int TT, int NW, bool LO>
+__global__ void __launch_bounds__(64 * NW) k_route_mm(RouteMMArgs a) {
+    __shared__ double red[NW - 1][RT * TT * 4][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ml = lane & 15, pc = lane >> 4;
@@ -1013,65 +1020,106 @@ __global__ void __launch_bounds__(256) k_route_mm(RouteMMArgs a) {
     const int nr_router = a.router ? a.E : 0, nr_head = a.head ? a.En : 0;
     const int nr_lora = a.lora_a ? a.r : 0;
     const int R = nr_router + nr_head + nr_lora + (a.sgate_w ? 1 : 0);
-    const int t0 = blockIdx.y * 16;
-    // this lane's weight row (B side) and token (A side)
-    int row = blockIdx.x * 16 + ml;
-    const bool row_ok = row < R;
-    row = row_ok ? row : R - 1;
-    const uint16_t* w;
-    if (row < nr_router) w = a.router + (size_t)row * d;
-    else if (row < nr_router + nr_head) w = a.head + (size_t)(row - nr_router) * d;
-    else if (row < nr_router + nr_head + nr_lora) w = a.lora_a + (size_t)(row - nr_router - nr_head) * d;
-    else w = a.sgate_w;
-    const int tok = t0 + ml < T ? t0 + ml : T - 1;
-    // wave w takes k-steps [w * ns, (w + 1) * ns) of the d / 32
-    const int ns = d / 128, c0 = wave * ns;
-    const uint32_t* aq = a.u_pk + (size_t)tok * (d / 2) + 4 * pc;
-    const uint32_t* aql = a.u_pk_lo ? a.u_pk_lo + (size_t)tok * (d / 2) + 4 * pc : nullptr;
-    const u32x4* wq = (const u32x4*)(w + 8 * pc);
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    const int r0 = blockIdx.x * 16 * RT, t0 = blockIdx.y * 16 * TT;
+    // this lane's weight rows (B side) and tokens (A side), clamped into range
+    const u32x4* wq[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        int row = r0 + 16 * i + ml;
+        row = row < R ? row : R - 1;
+        const uint16_t* w;
+        if (row < nr_router) w = a.router + (size_t)row * d;
+        else if (row < nr_router + nr_head) w = a.head + (size_t)(row - nr_router) * d;
+        else if (row < nr_router + nr_head + nr_lora) w = a.lora_a + (size_t)(row - nr_router - nr_head) * d;
+        else w = a.sgate_w;
+        wq[i] = (const u32x4*)(w + 8 * pc);
+    }
+    const uint32_t* aq[TT];
+    const uint32_t* aql[TT];
+    constexpr bool lo = LO;
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+        const int tok = t0 + 16 * j + ml < T ? t0 + 16 * j + ml : T - 1;
+        aq[j] = a.u_pk + (size_t)tok * (d / 2) + 4 * pc;
+        aql[j] = lo ? a.u_pk_lo + (size_t)tok * (d / 2) + 4 * pc : aq[j];
+    }
+    // wave w takes k-steps [w * ns, (w + 1) * ns)
+    const int ns = d / (32 * NW), c0 = wave * ns;
+    constexpr int kMaxSteps = RT * TT > 1 ? (LO ? 4 : 8) : (LO ? 8 : 16);   // k-steps whose loads are issued together
+    double acc[RT][TT][4];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < TT; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
     for (int b0 = 0; b0 < ns; b0 += kMaxSteps) {
         const int nb = min(kMaxSteps, ns - b0);
-        u32x4 av[kMaxSteps], al[kMaxSteps], wv[kMaxSteps];
+        u32x4 wv[kMaxSteps][RT], av[kMaxSteps][TT], al[kMaxSteps][LO ? TT : 1];
         // unconditional loads (indices clamped into the slice), so that the
         // arrays stay in registers
 #pragma unroll
         for (int c = 0; c < kMaxSteps; ++c) {
             const int cc = c0 + b0 + (c < nb ? c : nb - 1);
-            av[c] = *(const u32x4*)(aq + 16 * cc);
-            wv[c] = wq[4 * cc];
-            al[c] = aql ? *(const u32x4*)(aql + 16 * cc) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < RT; ++i) wv[c][i] = wq[i][4 * cc];
+#pragma unroll
+            for (int j = 0; j < TT; ++j) {
+                av[c][j] = *(const u32x4*)(aq[j] + 16 * cc);
+                if constexpr (LO) al[c][j] = *(const u32x4*)(aql[j] + 16 * cc);
+            }
         }
 #pragma unroll
         for (int c = 0; c < kMaxSteps; ++c) {
             if (c >= nb) continue;
-            const u32x4 bv = bf16_pairs_p4(wv[c]);
-            f32x4 p = {0.f, 0.f, 0.f, 0.f};
-            p = mfma16(av[c], bv, p);
-            if (aql) p = mfma16(al[c], bv, p);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] += (double)p[i];
+            for (int i = 0; i < RT; ++i) {
+                const u32x4 bv = bf16_pairs_p4(wv[c][i]);
+#pragma unroll
+                for (int j = 0; j < TT; ++j) {
+                    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+                    p = mfma16(av[c][j], bv, p);
+                    if constexpr (LO) p = mfma16(al[c][j], bv, p);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[i][j][v] += (double)p[v];
+                }
+            }
         }
     }
-    // the four k-slices are summed in slice order
+    // the k-slices are summed in slice order
     if (wave > 0)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave - 1][lane][i] = acc[i];
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int j = 0; j < TT; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) red[wave - 1][(i * TT + j) * 4 + v][lane] = acc[i][j][v];
     __syncthreads();
-    if (wave > 0 || !row_ok) return;
+    if (wave > 0) return;
+#pragma unroll 1
+    for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
-    for (int s = 0; s < 3; ++s)
+        for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += red[s][lane][i];
-    const int r = blockIdx.x * 16 + ml;
+            for (int j = 0; j < TT; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * pc + i;
-        if (t >= T) continue;
-        if (r < nr_router) a.logits_r[(size_t)t * a.E + r] = acc[i];
-        else if (r < nr_router + nr_head) a.logits_h[(size_t)t * a.En + (r - nr_router)] = acc[i];
-        else if (r < nr_router + nr_head + nr_lora) a.au[(size_t)t * a.r + (r - nr_router - nr_head)] = (float)acc[i];
-        else a.sgate[t] = (float)(1.0 / (1.0 + exp(-acc[i])));
+                for (int v = 0; v < 4; ++v) acc[i][j][v] += red[w][(i * TT + j) * 4 + v][lane];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const int r = r0 + 16 * i + ml;
+        if (r >= R) continue;
+#pragma unroll
+        for (int j = 0; j < TT; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = t0 + 16 * j + 4 * pc + v;
+                if (t >= T) continue;
+                const double z = acc[i][j][v];
+                if (r < nr_router) a.logits_r[(size_t)t * a.E + r] = z;
+                else if (r < nr_router + nr_head) a.logits_h[(size_t)t * a.En + (r - nr_router)] = z;
+                else if (r < nr_router + nr_head + nr_lora) a.au[(size_t)t * a.r + (r - nr_router - nr_head)] = (float)z;
+                else a.sgate[t] = (float)(1.0 / (1.0 + exp(-z)));
+            }
     }
 }
 
@@ -1220,8 +1268,11 @@ hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s) {
         if (big_blocks >= 512)
             hipLaunchKernelGGL(k_route_mm_tiled, dim3((R + kRmTile - 1) / kRmTile, (a.n_tok + kRmTile - 1) / kRmTile),
                                dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL(k_route_mm, dim3((R + 15) / 16, (a.n_tok + 15) / 16), dim3(256), 0, s, a);
+        else {
+            const dim3 grid((R + 15) / 16, (a.n_tok + 15) / 16);
+            if (a.u_pk_lo) hipLaunchKernelGGL((k_route_mm<1, 1, 4, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_route_mm<1, 1, 4, false>), grid, dim3(256), 0, s, a);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1250,7 +1301,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     if (big) {
         hipLaunchKernelGGL(k_pf_tiles<kTileBig>, dim3(1), dim3(1024), 0, s, a, a.tiles64, 4);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((k_pf_gateup_big<kBgGs, kBgNst>), dim3(a.max_tiles64, (fmax + kBgRows - 1) / kBgRows), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_pf_gateup_big<kBgGs, kBgNst, kTileBig>), dim3(a.max_tiles64, (fmax + kBgRows - 1) / kBgRows), dim3(256), 0, s, a);
     } else {
         const dim3 ggrid(a.max_tiles, (fmax + kGuRows - 1) / kGuRows);
         if (g.u_pk_lo) hipLaunchKernelGGL(k_pf_gateup<true>, ggrid, dim3(256), 0, s, a);
