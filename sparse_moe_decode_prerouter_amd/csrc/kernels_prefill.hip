@@ -1007,6 +1007,15 @@ __device__ __forceinline__ u32x4 bf16_pairs_p4(u32x4 v) {
     return r;
 }
 
+// whether any of the tokens t0 .. t0 + n - 1 takes the layer's own router
+// (block-uniform; every thread of the block calls it)
+__device__ __forceinline__ bool route_tile_needed(const RouteMMArgs& a, int t0, int n) {
+    if (!a.route_idx) return true;
+    const int t = t0 + (int)threadIdx.x;
+    const int self = (int)threadIdx.x < n && t < a.n_tok && a.route_idx[(size_t)t * a.k] < 0;
+    return __syncthreads_or(self) != 0;
+}
+
 // RT x TT 16 x 16 tiles (rows x tokens) per block; NW waves split the d / 32
 // k-steps into NW consecutive slices (a wave's loads issued kMaxSteps k-steps
 // at a time); LO: activations carry a bf16 lo part (two MFMAs per product)
@@ -1021,6 +1030,8 @@ __global__ void __launch_bounds__(64 * NW) k_route_mm(RouteMMArgs a) {
     const int nr_lora = a.lora_a ? a.r : 0;
     const int R = nr_router + nr_head + nr_lora + (a.sgate_w ? 1 : 0);
     const int r0 = blockIdx.x * 16 * RT, t0 = blockIdx.y * 16 * TT;
+    // router rows are needed only for self-routed tokens
+    if (r0 + 16 * RT <= nr_router && !route_tile_needed(a, t0, 16 * TT)) return;
     // this lane's weight rows (B side) and tokens (A side), clamped into range
     const u32x4* wq[RT];
 #pragma unroll
@@ -1141,6 +1152,7 @@ __global__ void __launch_bounds__(256) k_route_mm_tiled(RouteMMArgs a) {
     const int nr_lora = a.lora_a ? a.r : 0;
     const int R = nr_router + nr_head + nr_lora + (a.sgate_w ? 1 : 0);
     const int t0 = blockIdx.y * kRmTile, r0 = blockIdx.x * kRmTile;
+    if (r0 + kRmTile <= nr_router && !route_tile_needed(a, t0, kRmTile)) return;
     const bool lo = a.u_pk_lo != nullptr;
     // this thread's two load pieces of each stage: row/token q >> 3, piece q & 7
     const uint32_t* ap[2];
