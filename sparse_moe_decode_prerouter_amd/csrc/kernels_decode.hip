@@ -119,10 +119,35 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     const int n = a.n_tok * a.k, E = a.E;
     int* wcnt = sm;                          // [kSortWaves][E]: counts, then first positions
     int* cnt = sm + kSortWaves * E;          // [E] bucket sizes
-    __shared__ int wsum[kSortWaves];
-    __shared__ int wact[kSortWaves];
-    __shared__ int tot_valid, tot_active;
+    __shared__ int wsum[kSortWaves], wact[kSortWaves], wt16[kSortWaves], wt64[kSortWaves];
+    __shared__ int tot_valid, tot_active, tot16, tot64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // blob of expert `tid` for the tile records (E <= kSortThreads), loaded early
+    int my_blob = -1;
+    if ((a.tiles16 || a.tiles64) && a.resolve_blobs && tid < E) {
+        if (!a.ev.slot_of) my_blob = tid;
+        else {
+            const int sl = a.ev.slot_of[tid];
+            my_blob = (sl < 0 || (a.ev.slot_tag && a.ev.slot_tag[sl] != tid)) ? -1 : sl;
+        }
+    }
+    if (a.self_topk && a.route_idx) {
+        // top-k of the self-routed rows: a wave checks 64 rows per load and
+        // takes each self-routed one in turn
+        for (int base = wave * 64; base < a.n_tok; base += kSortThreads) {
+            const int t = base + lane;
+            unsigned long long m = __ballot(t < a.n_tok && a.route_idx[(size_t)t * a.k] < 0);
+            while (m) {
+                const int tt = base + __ffsll((long long)m) - 1;
+                m &= m - 1;
+                if (E <= 64) topk_row<1>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
+                else if (E <= 128) topk_row<2>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
+                else topk_row<4>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
+            }
+        }
+        __threadfence_block();
+        __syncthreads();                     // self_idx / self_w are read below by other threads
+    }
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     for (int i = tid; i < kSortWaves * E; i += kSortThreads) wcnt[i] = 0;
@@ -151,7 +176,7 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     // scan over waves per expert, then over experts
     const int per = (E + kSortThreads - 1) / kSortThreads;
     const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-    int c = 0, na = 0;
+    int c = 0, na = 0, n16 = 0, n64 = 0;
     for (int e = e0; e < e1; ++e) {
         int run = 0;
         for (int w = 0; w < kSortWaves; ++w) {
@@ -162,28 +187,69 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
         cnt[e] = run;
         c += run;
         na += run > 0;
+        n16 += (run + 15) >> 4;
+        n64 += (run + 63) >> 6;
     }
-    int ic = c, ia = na;
+    int ic = c, ia = na, i16 = n16, i64 = n64;
     for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(ic, o, 64), u = __shfl_up(ia, o, 64);
-        if (lane >= o) { ic += v; ia += u; }
+        const int x16 = __shfl_up(i16, o, 64), x64 = __shfl_up(i64, o, 64);
+        if (lane >= o) { ic += v; ia += u; i16 += x16; i64 += x64; }
     }
-    if (lane == 63) { wsum[wave] = ic; wact[wave] = ia; }
+    if (lane == 63) { wsum[wave] = ic; wact[wave] = ia; wt16[wave] = i16; wt64[wave] = i64; }
     __syncthreads();
     if (tid == 0) {
-        int s1 = 0, s2 = 0;
+        int s1 = 0, s2 = 0, s3 = 0, s4 = 0;
         for (int w = 0; w < kSortWaves; ++w) {
-            const int v = wsum[w], u = wact[w];
-            wsum[w] = s1; wact[w] = s2; s1 += v; s2 += u;
+            const int v = wsum[w], u = wact[w], x16 = wt16[w], x64 = wt64[w];
+            wsum[w] = s1; wact[w] = s2; wt16[w] = s3; wt64[w] = s4;
+            s1 += v; s2 += u; s3 += x16; s4 += x64;
         }
-        tot_valid = s1; tot_active = s2;
+        tot_valid = s1; tot_active = s2; tot16 = s3; tot64 = s4;
     }
     __syncthreads();
     int o1 = wsum[wave] + ic - c, o2 = wact[wave] + ia - na;
+    int q16 = wt16[wave] + i16 - n16, q64 = wt64[wave] + i64 - n64;
     for (int e = e0; e < e1; ++e) {
         for (int w = 0; w < kSortWaves; ++w) wcnt[w * E + e] += o1;
-        if (cnt[e] > 0) { a.active[o2] = e; a.act_off[o2] = o1; ++o2; }
-        o1 += cnt[e];
+        const int ce = cnt[e];
+        if (ce > 0) {
+            a.active[o2] = e;
+            a.act_off[o2] = o1;
+            // tile records of this expert (my_blob belongs to expert tid == e)
+            if (a.tiles16 || a.tiles64) {
+                if (my_blob < 0 && a.resolve_blobs) set_err(a.err, ERR_NOT_STAGED);
+                if (a.tiles16)
+                    for (int i = 0; i * 16 < ce; ++i)
+                        *(int4*)(a.tiles16 + 4 * (q16 + i)) = make_int4(o2, o1 + 16 * i, min(16, ce - 16 * i), my_blob);
+                if (a.tiles64)
+                    for (int i = 0; i * 64 < ce; ++i)
+                        *(int4*)(a.tiles64 + 4 * (q64 + i)) = make_int4(o2, o1 + 64 * i, min(64, ce - 64 * i), my_blob);
+            }
+            ++o2;
+        }
+        o1 += ce;
+        q16 += (ce + 15) >> 4;
+        q64 += (ce + 63) >> 6;
+    }
+    if (a.tiles16 || a.tiles64) {
+        // the shared expert's token tiles follow the routed ones
+        int sblob = -1;
+        if (a.fs && a.ev.shared && a.resolve_blobs) {
+            if (a.ev.shared_tag && *a.ev.shared_tag != a.ev.E) { if (tid == 0) set_err(a.err, ERR_NOT_STAGED); }
+            else sblob = -2;
+        }
+        const int ns16 = a.fs ? (a.n_tok + 15) / 16 : 0, ns64 = a.fs ? (a.n_tok + 63) / 64 : 0;
+        if (a.tiles16)
+            for (int i = tid; i < ns16; i += kSortThreads)
+                *(int4*)(a.tiles16 + 4 * (tot16 + i)) = make_int4(-1, 16 * i, min(16, a.n_tok - 16 * i), sblob);
+        if (a.tiles64)
+            for (int i = tid; i < ns64; i += kSortThreads)
+                *(int4*)(a.tiles64 + 4 * (tot64 + i)) = make_int4(-1, 64 * i, min(64, a.n_tok - 64 * i), sblob);
+        if (tid == 0) {
+            a.meta[2] = tot16 + ns16; a.meta[3] = tot16;
+            a.meta[4] = tot64 + ns64; a.meta[5] = tot64;
+        }
     }
     __syncthreads();
     // pass 2: place
@@ -207,6 +273,7 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
 }
 
 hipError_t launch_sort(const SortArgs& a, hipStream_t s) {
+    if (a.E > kSortThreads || (a.self_topk && a.E > kSortTopkMaxE)) return hipErrorInvalidValue;
     const size_t lds = sort_lds_bytes(a.n_tok * a.k, a.E);
     if (lds > 64 * 1024) {
         // above the default dynamic LDS limit: raise it to what this call needs

@@ -63,60 +63,41 @@ int prefill_max_tiles(int T, int K, int E, int tm) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile list: the TM-row tiles of every active expert's sorted assignments,
-// then the TM-token tiles of the shared expert. Each record carries its blob,
-// resolved (and its staging checked) here once. Written to `tiles` with
-// meta[mi] = tiles, meta[mi + 1] = routed tiles. One block.
+// Blob of every tile record, resolved after a reactive staging (the sort
+// wrote the records before the routing was known on the host). One block.
 // ---------------------------------------------------------------------------
-template <int TM>
-__global__ void __launch_bounds__(1024) k_pf_tiles(PrefillArgs a, int32_t* tiles, int mi) {
-    __shared__ int wsum[16];
-    __shared__ int total;
+__global__ void __launch_bounds__(1024) k_tile_blobs(PrefillArgs a, int32_t* tiles, int mi) {
     const GemvArgs& g = a.g;
     const ExpertView& ev = g.ev;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n_active = g.meta[0];
-    int cnt = 0, off0 = 0, off1 = 0, blob = -1;
-    if (tid < n_active) {
-        off0 = g.act_off[tid];
-        off1 = g.act_off[tid + 1];
-        cnt = (off1 - off0 + TM - 1) / TM;
-        const int e = g.active[tid];
-        if (!ev.slot_of) {
-            blob = e;
-        } else {
-            const int sl = ev.slot_of[e];
-            blob = (sl < 0 || (ev.slot_tag && ev.slot_tag[sl] != e)) ? -1 : sl;
-        }
-        if (blob < 0) set_err(g.err, ERR_NOT_STAGED);
-    }
-    int incl = cnt;
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int w = 0; w < 16; ++w) { const int v = wsum[w]; wsum[w] = acc; acc += v; }
-        total = acc;
-    }
-    __syncthreads();
-    const int start = wsum[wave] + incl - cnt;
-    for (int i = 0; i < cnt; ++i) {
-        const int p0 = off0 + i * TM;
-        *(int4*)(tiles + 4 * (start + i)) = make_int4(tid, p0, min(TM, off1 - p0), blob);
-    }
-    const int ns = g.fs ? (g.n_tok + TM - 1) / TM : 0;
+    const int n = a.meta_w[mi], nr = a.meta_w[mi + 1];
     int sblob = -1;
-    if (ns && ev.shared) {
-        if (ev.shared_tag && *ev.shared_tag != ev.E) { if (tid == 0) set_err(g.err, ERR_NOT_STAGED); }
-        else sblob = -2;
+    if (ev.shared) sblob = (ev.shared_tag && *ev.shared_tag != ev.E) ? -1 : -2;
+    for (int i = threadIdx.x; i < n; i += 1024) {
+        int blob;
+        bool missing;
+        if (i < nr) {
+            const int e = g.active[tiles[4 * i]];
+            if (!ev.slot_of) blob = e;
+            else {
+                const int sl = ev.slot_of[e];
+                blob = (sl < 0 || (ev.slot_tag && ev.slot_tag[sl] != e)) ? -1 : sl;
+            }
+            missing = blob < 0;
+        } else {
+            blob = sblob;
+            missing = ev.shared && blob == -1;           // no shared blob at all is not an error
+        }
+        if (missing) set_err(g.err, ERR_NOT_STAGED);
+        tiles[4 * i + 3] = blob;
     }
-    for (int i = tid; i < ns; i += 1024)
-        *(int4*)(tiles + 4 * (total + i)) = make_int4(-1, i * TM, min(TM, g.n_tok - i * TM), sblob);
-    if (tid == 0) { a.meta_w[mi] = total + ns; a.meta_w[mi + 1] = total; }
+}
+
+hipError_t launch_tile_blobs(const PrefillArgs& a, bool big, hipStream_t s) {
+    hipLaunchKernelGGL(k_tile_blobs, dim3(1), dim3(1024), 0, s, a, a.tiles, 2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !big) return e;
+    hipLaunchKernelGGL(k_tile_blobs, dim3(1), dim3(1024), 0, s, a, a.tiles64, 4);
+    return hipGetLastError();
 }
 
 struct PfItem {
@@ -891,6 +872,19 @@ constexpr int kCombTok = 4;
 
 __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
     const GemvArgs& g = a.g;
+    const int gy = (g.n_tok + kCombTok - 1) / kCombTok;
+    if ((int)blockIdx.y >= gy) {
+        // the head's top-k for the next layer: one token per wave
+        const TopkJob& j = a.head;
+        const int t = (((int)blockIdx.y - gy) * (int)gridDim.x + (int)blockIdx.x) * 4 + (int)(threadIdx.x >> 6);
+        if (t >= g.n_tok) return;
+        if (j.En <= 64) topk_row<1>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+        else if (j.En <= 128) topk_row<2>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+        else if (j.En <= 256) topk_row<4>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+        else if (j.En <= 512) topk_row<8>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+        else topk_row<16>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+        return;
+    }
     const int d = g.d, n = (blockIdx.x * 256 + threadIdx.x) * 4;
     const int t0 = blockIdx.y * kCombTok;
     if (n >= d) return;
@@ -1249,11 +1243,11 @@ __global__ void __launch_bounds__(256) k_route_mm_tiled(RouteMMArgs a) {
     }
 }
 
-// top-k per token: blockIdx.y = 0 router (self-routed rows), 1 head
-__global__ void __launch_bounds__(256) k_route_topk(RouteMMArgs a) {
+// top-k per token: job (blockIdx.y + job0) 0 router (self-routed rows), 1 head
+__global__ void __launch_bounds__(256) k_route_topk(RouteMMArgs a, int job0) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.n_tok) return;
-    if (blockIdx.y == 0) {
+    if ((int)blockIdx.y + job0 == 0) {
         if (!a.router || (a.route_idx && a.route_idx[(size_t)t * a.k] >= 0)) return;
         if (a.E <= 64) topk_row<1>(false, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
         else if (a.E <= 128) topk_row<2>(false, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
@@ -1271,7 +1265,7 @@ __global__ void __launch_bounds__(256) k_route_topk(RouteMMArgs a) {
     }
 }
 
-hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s) {
+hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk) {
     if (a.d % 128) return hipErrorInvalidValue;
     const int R = (a.router ? a.E : 0) + (a.head ? a.En : 0) + (a.lora_a ? a.r : 0) + (a.sgate_w ? 1 : 0);
     if (R > 0) {
@@ -1288,8 +1282,11 @@ hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.router || (a.head && a.pred_idx)) {
-        hipLaunchKernelGGL(k_route_topk, dim3((a.n_tok + 3) / 4, 2), dim3(256), 0, s, a);
+    router_topk = router_topk && a.router;
+    head_topk = head_topk && a.head && a.pred_idx;
+    if (router_topk || head_topk) {
+        hipLaunchKernelGGL(k_route_topk, dim3((a.n_tok + 3) / 4, (router_topk ? 1 : 0) + (head_topk ? 1 : 0)), dim3(256), 0, s,
+                           a, router_topk ? 0 : 1);
         return hipGetLastError();
     }
     return hipSuccess;
@@ -1303,16 +1300,10 @@ bool prefill_mm_ok(int d, int f, int fs) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     const GemvArgs& g = a.g;
     if (!prefill_mm_ok(g.d, g.f, g.fs)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_pf_tiles<kTileM>, dim3(1), dim3(1024), 0, s, a, a.tiles, 2);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
     const int fmax = g.f > g.fs ? g.f : g.fs;
-    // many tokens per expert (on average 48 or more): 64-token tiles for gate/up
-    const bool big = !g.u_pk_lo && g.d <= 2048 && g.d % 128 == 0 && g.f % kBgRows == 0 &&
-                     (g.fs == 0 || g.fs % kBgRows == 0) && (long long)g.n_tok * g.k >= 48LL * g.max_active;
-    if (big) {
-        hipLaunchKernelGGL(k_pf_tiles<kTileBig>, dim3(1), dim3(1024), 0, s, a, a.tiles64, 4);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the tile lists were written by the sort (64-row ones when big)
+    if (prefill_big_tiles(g.d, g.f, g.fs, g.u_pk_lo != nullptr, g.n_tok, g.k, g.max_active)) {
         hipLaunchKernelGGL((k_pf_gateup_big<kBgGs, kBgNst, kTileBig>), dim3(a.max_tiles64, (fmax + kBgRows - 1) / kBgRows), dim3(256), 0, s, a);
     } else {
         const dim3 ggrid(a.max_tiles, (fmax + kGuRows - 1) / kGuRows);
@@ -1331,8 +1322,19 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(k_pf_down, dim3((unsigned)nb), dim3(kDnThreads), 0, s, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pf_combine, dim3((g.d + 1023) / 1024, (g.n_tok + kCombTok - 1) / kCombTok), dim3(256), 0, s, a);
+    {
+        // combine blocks, then the head top-k blocks (one token per wave)
+        const int gx = (g.d + 1023) / 1024, gy = (g.n_tok + kCombTok - 1) / kCombTok;
+        const int gt = a.head.pred_idx ? ((g.n_tok + 3) / 4 + gx - 1) / gx : 0;
+        hipLaunchKernelGGL(k_pf_combine, dim3(gx, gy + gt), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
+}
+
+bool prefill_big_tiles(int d, int f, int fs, bool act_lo, int n_tok, int k, int max_active) {
+    // many tokens per expert (on average 48 or more): 64-token tiles for gate/up
+    return !act_lo && d <= 2048 && d % 128 == 0 && f % kBgRows == 0 && (fs == 0 || fs % kBgRows == 0) &&
+           (long long)n_tok * k >= 48LL * max_active;
 }
 
 }  // namespace moe

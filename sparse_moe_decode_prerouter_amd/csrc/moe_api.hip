@@ -318,7 +318,16 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     ra.self_idx = L->s.self_idx; ra.self_w = L->s.self_w;
     ra.pred_idx = io->pred_idx; ra.pred_w = io->pred_w;
     ra.au = L->s.au; ra.sgate = L->s.sgate;
-    HIPCHK(launch_route_mm(ra, st));
+    const bool mm = prefill_mm_ok(D.d_model, D.d_ff, D.d_ff_shared);
+    const int max_active = std::min(D.n_experts, n_tok * D.top_k);
+    const bool big = mm && prefill_big_tiles(D.d_model, D.d_ff, D.d_ff_shared, D.act_dtype != MOE_ACT_BF16, n_tok,
+                                             D.top_k, max_active);
+    const bool reactive = !L->resident && (io->route_idx == nullptr || io->reactive || prefill);
+    // the router's top-k runs here when every row self-routes (or the expert
+    // count is large); otherwise the sort takes the few self-routed rows. The
+    // head's top-k runs beside the combine on the matrix-core path
+    const bool sort_topk = io->route_idx != nullptr && L->w.router != nullptr && D.n_experts <= kSortTopkMaxE;
+    HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm));
 
     SortArgs sa{};
     sa.route_idx = io->route_idx; sa.route_w = io->route_w;
@@ -328,9 +337,15 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     sa.user_used_idx = io->used_idx; sa.user_used_w = io->used_w;
     sa.meta = L->s.sort_meta; sa.active = L->s.active; sa.act_off = L->s.act_off; sa.perm = L->s.perm;
     sa.err = L->s.err;
+    sa.self_topk = sort_topk;
+    sa.logits_r = L->s.logits_r; sa.router_bias = L->w.router_bias;
+    sa.ev = view_of(L); sa.fs = D.d_ff_shared;
+    sa.tiles16 = mm ? L->s.tiles : nullptr;
+    sa.tiles64 = big ? L->s.tiles64 : nullptr;
+    sa.resolve_blobs = !reactive;
     HIPCHK(launch_sort(sa, st));
 
-    if (!L->resident && (io->route_idx == nullptr || io->reactive || prefill)) {
+    if (reactive) {
         // reactive: the routing exists only now; read it back and stage it
         const size_t nk = (size_t)n_tok * D.top_k;
         HIPCHK(hipMemcpyAsync(L->h_readback, L->s.used_idx, nk * sizeof(int32_t), hipMemcpyDeviceToHost, st));
@@ -356,8 +371,8 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     ga.lora_scale = D.lora_rank ? D.lora_alpha / (float)D.lora_rank : 0.f;
     ga.y = io->y_out;
     ga.err = L->s.err;
-    ga.max_active = std::min(D.n_experts, n_tok * D.top_k);
-    if (prefill_mm_ok(D.d_model, D.d_ff, D.d_ff_shared)) {
+    ga.max_active = max_active;
+    if (mm) {
         // grouped GEMM on the matrix cores (prefill and large decode batches)
         PrefillArgs pf{};
         pf.g = ga;
@@ -369,6 +384,10 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
         pf.n_cu = L->n_cu;
         pf.ob = L->s.ob; pf.obs = L->s.obs;
         pf.used_idx = L->s.used_idx; pf.used_w = L->s.used_w;
+        if (io->pred_idx && L->w.head)
+            pf.head = TopkJob{L->s.logits_h, D.next_n_experts, D.next_top_k, L->w.head_bias, L->w.hist_cur, io->hist_cur,
+                              L->w.hist_prev, io->hist_prev, io->pred_idx, io->pred_w};
+        if (reactive) HIPCHK(launch_tile_blobs(pf, big, st));
         HIPCHK(launch_prefill(pf, st));
     } else {
         HIPCHK(launch_gateup(ga, st));

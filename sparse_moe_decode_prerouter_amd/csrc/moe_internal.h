@@ -163,14 +163,34 @@ struct RouteMMArgs {
     int32_t* self_idx; float* self_w; int32_t* pred_idx; float* pred_w;
     float* au; float* sgate;
 };
-hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s);
+// router_topk: top-k of the self-routed rows here (else the sort does it);
+// head_topk: the head's top-k here (else the combine launch does it)
+hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk);
 
+// A head top-k run by a later launch than the one that wrote its logits
+// (only for E_next <= 64 * kDeferMaxPer; larger heads keep their own launch).
+constexpr int kDeferMaxPer = 4;
+struct TopkJob {
+    const double* logits; int En; int kn; const float* bias;
+    const float* mc; const int32_t* hc; const float* mp; const int32_t* hp;
+    int32_t* pred_idx; float* pred_w;
+};
+
+constexpr int kSortTopkMaxE = 256;
 struct SortArgs {
-    const int32_t* route_idx; const float* route_w; const int32_t* self_idx; const float* self_w;
+    const int32_t* route_idx; const float* route_w; int32_t* self_idx; float* self_w;
     int n_tok; int k; int E;
     int32_t* used_idx; float* used_w; int32_t* user_used_idx; float* user_used_w;
     int32_t* meta; int32_t* active; int32_t* act_off; int32_t* perm;
     int32_t* err;
+    // when set: the top-k of the self-routed rows (route_idx[t*k] < 0) from
+    // the router logits, written to self_idx / self_w before the sort reads them
+    bool self_topk; const double* logits_r; const float* router_bias;   // self_topk: E <= kSortTopkMaxE
+    // when set: the grouped GEMM's tile lists (16-row, and 64-row if tiles64),
+    // records {active slot or -1 (shared), first position, rows, blob}, with
+    // meta[2] = tiles, meta[3] = routed tiles (meta[4], meta[5]: 64-row)
+    ExpertView ev; int fs; int32_t* tiles16; int32_t* tiles64;
+    bool resolve_blobs;                 // false: blob fields left -1, resolved after staging (launch_tile_blobs)
 };
 hipError_t launch_sort(const SortArgs& a, hipStream_t s);
 
@@ -196,23 +216,20 @@ struct PrefillArgs {
     // -2: shared blob, -1: not staged)}
     int32_t* tiles; int max_tiles;
     int32_t* tiles64; int max_tiles64;   // 64-row tiles (large-tile gate/up)
-    int32_t* meta_w;                     // tile kernel writes meta[2] = tiles, meta[3] = routed tiles (meta[4], [5]: 64-row)
+    const int32_t* meta_w;               // meta[2] = tiles, meta[3] = routed tiles (meta[4], [5]: 64-row), from the sort
     int n_cu;                            // blocks of the persistent down projection
     float* ob; float* obs;               // down outputs: [T*k][d] by assignment, [T][d] shared
     const int32_t* used_idx; const float* used_w;
+    TopkJob head;                        // the head's top-k, run beside the combine (pred_idx null: none)
 };
 int prefill_max_tiles(int T, int K, int E, int tm = 16);
 bool prefill_mm_ok(int d, int f, int fs);
+// whether the gate/up projection takes 64-token tiles (many tokens per expert)
+bool prefill_big_tiles(int d, int f, int fs, bool act_lo, int n_tok, int k, int max_active);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+// resolve the blob field of the tile records once the experts are staged
+hipError_t launch_tile_blobs(const PrefillArgs& a, bool big, hipStream_t s);
 
-// A head top-k run by a later launch than the one that wrote its logits
-// (only for E_next <= 64 * kDeferMaxPer; larger heads keep their own launch).
-constexpr int kDeferMaxPer = 4;
-struct TopkJob {
-    const double* logits; int En; int kn; const float* bias;
-    const float* mc; const int32_t* hc; const float* mp; const int32_t* hp;
-    int32_t* pred_idx; float* pred_w;
-};
 
 struct DecAArgs {
     const void* x; int x_is_bf16; int fused; const float* gamma; float eps; int act_bf16; int d; int n_tok;

@@ -130,5 +130,12 @@ def test_prefill_small(n_tok):
     check_layer(synth.LAYER35B, n_tok, fused=True, given_route=True, prefill=True, seed=11)
 
 
+@pytest.mark.parametrize("given_route", [True, False])
+def test_prefill_streamed(given_route):
+    """Streamed store on the matrix-core path: the routing is read back and
+    staged inside the call, then the tile records get their slab slots."""
+    check_layer(synth.LAYER35B, 13, fused=True, given_route=given_route, prefill=True, resident=False, seed=13)
+
+
 def test_tiny_prefill():
     check_layer(synth.TINY, 9, fused=True, given_route=True, prefill=True, seed=12)
