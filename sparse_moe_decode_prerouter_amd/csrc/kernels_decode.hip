@@ -101,7 +101,14 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
 
-size_t sort_lds_bytes(int n, int E) { (void)n; return (size_t)(kSortWaves + 1) * E * sizeof(int); }
+constexpr size_t kSortLdsMax = 159 * 1024;
+// the assignments' experts stay in LDS between the passes when they fit
+__host__ __device__ inline bool sort_cache_e(int n, int E) {
+    return ((size_t)(kSortWaves + 1) * E + n) * sizeof(int) <= kSortLdsMax;
+}
+size_t sort_lds_bytes(int n, int E) {
+    return ((size_t)(kSortWaves + 1) * E + (sort_cache_e(n, E) ? n : 0)) * sizeof(int);
+}
 
 // lanes (of the valid ones) whose expert equals this lane's; nbits covers E
 __device__ __forceinline__ unsigned long long match_expert(int e, bool valid, int nbits) {
@@ -131,44 +138,57 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
             my_blob = (sl < 0 || (a.ev.slot_tag && a.ev.slot_tag[sl] != tid)) ? -1 : sl;
         }
     }
-    if (a.self_topk && a.route_idx) {
-        // top-k of the self-routed rows: a wave checks 64 rows per load and
-        // takes each self-routed one in turn
+    int* se = sm + (kSortWaves + 1) * E;     // [n] experts of the assignments (when cache_e)
+    const bool cache_e = sort_cache_e(n, E);
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int i = tid; i < kSortWaves * E; i += kSortThreads) wcnt[i] = 0;
+    const bool own_topk = a.self_topk && a.route_idx;
+    if (own_topk) {
+        // top-k of the self-routed rows, straight into the used routing: a
+        // wave checks 64 rows per load and takes each self-routed one in turn
         for (int base = wave * 64; base < a.n_tok; base += kSortThreads) {
             const int t = base + lane;
             unsigned long long m = __ballot(t < a.n_tok && a.route_idx[(size_t)t * a.k] < 0);
             while (m) {
                 const int tt = base + __ffsll((long long)m) - 1;
                 m &= m - 1;
-                if (E <= 64) topk_row<1>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
-                else if (E <= 128) topk_row<2>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
-                else topk_row<4>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
+                if (E <= 64) topk_row<1>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.used_idx, a.used_w);
+                else if (E <= 128) topk_row<2>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.used_idx, a.used_w);
+                else topk_row<4>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.used_idx, a.used_w);
+                if (lane < a.k) {
+                    // lane j wrote selection j just above
+                    const int i = tt * a.k + lane;
+                    const int e = a.used_idx[i];
+                    const float w = a.used_w[i];
+                    if (a.user_used_idx) a.user_used_idx[i] = e;
+                    if (a.user_used_w) a.user_used_w[i] = w;
+                    if (cache_e) se[i] = e;
+                }
             }
         }
-        __threadfence_block();
-        __syncthreads();                     // self_idx / self_w are read below by other threads
     }
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
-    for (int i = tid; i < kSortWaves * E; i += kSortThreads) wcnt[i] = 0;
     for (int i = tid; i < n; i += kSortThreads) {
         const int t = i / a.k;
         const bool self = !a.route_idx || a.route_idx[(size_t)t * a.k] < 0;
+        if (self && own_topk) continue;      // written by the top-k above
         int e = self ? a.self_idx[i] : a.route_idx[i];
         const float w = self ? a.self_w[i] : a.route_w[i];
         if (e < 0 || e >= E) { set_err(a.err, ERR_BAD_INDEX); e = -1; }
         a.used_idx[i] = e; a.used_w[i] = w;
         if (a.user_used_idx) a.user_used_idx[i] = e;
         if (a.user_used_w) a.user_used_w[i] = w;
+        if (cache_e) se[i] = e;
     }
-    __syncthreads();                         // used_idx is read back below by other threads
+    __threadfence_block();
+    __syncthreads();                         // the experts are read below by other threads
     const int chunk = ((n + kSortWaves - 1) / kSortWaves + 63) / 64 * 64;
     const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
     const unsigned long long lt = (1ull << lane) - 1;
     // pass 1: counts per (wave, expert)
     for (int base = c0; base < c1; base += 64) {
         const int i = base + lane;
-        const int e = i < c1 ? a.used_idx[i] : -1;
+        const int e = i < c1 ? (cache_e ? se[i] : a.used_idx[i]) : -1;
         const unsigned long long m = match_expert(e, e >= 0, nbits);
         if (m && (m & lt) == 0) wcnt[wave * E + e] += __popcll(m);
     }
@@ -255,7 +275,7 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     // pass 2: place
     for (int base = c0; base < c1; base += 64) {
         const int i = base + lane;
-        const int e = i < c1 ? a.used_idx[i] : -1;
+        const int e = i < c1 ? (cache_e ? se[i] : a.used_idx[i]) : -1;
         const unsigned long long m = match_expert(e, e >= 0, nbits);
         if (m) {
             a.perm[wcnt[wave * E + e] + __popcll(m & lt)] = i;
@@ -278,7 +298,7 @@ hipError_t launch_sort(const SortArgs& a, hipStream_t s) {
     if (lds > 64 * 1024) {
         // above the default dynamic LDS limit: raise it to what this call needs
         static size_t raised = 0;
-        if (lds > 159 * 1024) return hipErrorInvalidValue;
+        if (lds > kSortLdsMax) return hipErrorInvalidValue;
         if (lds > raised) {
             const hipError_t e = hipFuncSetAttribute((const void*)k_sort, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
