@@ -87,8 +87,7 @@ typedef struct moe_layer_desc {
     float lora_alpha;     /* alpha; the branch is scaled by alpha / r             */
     float rms_eps;        /* epsilon of RMSNorm (fused norm only)                 */
     int   act_dtype;      /* MOE_ACT_F32 or MOE_ACT_BF16                          */
-    int   max_tokens;     /* largest n_tok of any decode/prefill call: <= 8192 and
-                             max_tokens * top_k + 3 * n_experts <= 40704        */
+    int   max_tokens;     /* largest n_tok of any decode/prefill call: <= 8192  */
     int   slab_slots;     /* streamed mode: routed-expert slots (>= distinct experts per call) */
     int   next_n_experts; /* experts of the layer the head predicts (0 = no head) */
     int   next_top_k;     /* k of the layer the head predicts                     */

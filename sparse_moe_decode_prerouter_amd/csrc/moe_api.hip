@@ -51,9 +51,7 @@ int validate_desc(const moe_layer_desc* d) {
     if (d->next_n_experts < 0 || d->next_n_experts > kMaxExperts) return MOE_E_UNSUPPORTED;
     if (d->next_n_experts > 0 && (d->next_top_k <= 0 || d->next_top_k > kMaxTopK || d->next_top_k > d->next_n_experts))
         return MOE_E_UNSUPPORTED;
-    // the token->expert sort holds one int per assignment and three per expert in LDS (159 KiB)
-    if (d->max_tokens > 8192 || (size_t)d->max_tokens * d->top_k + 3 * (size_t)d->n_experts > 40704)
-        return MOE_E_UNSUPPORTED;
+    if (d->max_tokens > 8192) return MOE_E_UNSUPPORTED;
     const bool resident = d->flags & MOE_RESIDENT_STORE;
     if (!resident && (d->slab_slots < 1 || d->slab_slots > 64)) return MOE_E_UNSUPPORTED;
     if (d->flags & ~(MOE_FUSE_NORM_RESIDUAL | MOE_RESIDENT_STORE)) return MOE_E_INVALID;
