@@ -230,7 +230,7 @@ hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s, co
 // token, and each (token, row) output sums them in routing order, so the
 // result does not depend on how slots are spread over waves.
 // ---------------------------------------------------------------------------
-constexpr int kPassB = 8;
+constexpr int kPassB = 4;
 constexpr int kMaxTokB = 16;
 
 template <int F>

@@ -667,18 +667,20 @@ __global__ void __launch_bounds__(kDnThreads) k_pf_down(PrefillArgs a) {
 // bf16 activations; d a multiple of 128 up to 2048 (at most 32 groups, one
 // MFMA k-step); f a multiple of 128.
 // ---------------------------------------------------------------------------
-constexpr int kBgRows = 128;                  // rows of W_g (and of W_u) per block
+constexpr int kBgWaves = 8;                   // waves per block
+constexpr int kBgRt = 1;                      // 16-row tiles of W_g (and of W_u) per wave
+constexpr int kBgRows = 16 * kBgRt * kBgWaves;   // rows of W_g (and of W_u) per block
 constexpr int kBgGs = 2;                      // groups per stage
 constexpr int kBgNst = 2;                     // ring depth (two blocks per CU fit the LDS)
 
 // one stage of GS groups: PA = 8 GS 16-byte pieces of u per token row, PB =
 // 2 GS pieces of int4 per weight row
-template <int GS, int TM>
+template <int GS, int TM, int NR>
 struct BgStage {
     static constexpr int PA = 8 * GS, PB = 2 * GS;
     uint8_t a[TM * PA * 16];                  // piece c of token row m at slot c ^ (m mod PA)
-    uint8_t b[2 * kBgRows * PB * 16];         // 256 rows (gate, then up); piece p of row r at slot p ^ bsw(r)
-    uint32_t sc[2 * kBgRows][GS];             // (s, b) of the stage's groups per row
+    uint8_t b[2 * NR * PB * 16];              // 2 NR rows (gate, then up); piece p of row r at slot p ^ bsw(r)
+    uint32_t sc[2 * NR][GS];                  // (s, b) of the stage's groups per row
     // slot swizzle of the weight rows: the 16 rows of one MFMA read spread
     // over all bank groups
     static __device__ __forceinline__ int bsw(int r) { return PB == 4 ? (r >> 2) & 3 : (r >> 3) & 1; }
@@ -693,12 +695,18 @@ __device__ __forceinline__ void lds_dma4(const void* gptr, const void* lds) {
 }
 #pragma clang diagnostic pop
 
-template <int GS, int NST, int TM>
-__global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
-    using Stage = BgStage<GS, TM>;
+template <int GS, int NST, int TM, int RT, int NW>
+__global__ void __launch_bounds__(64 * NW) k_pf_gateup_big(PrefillArgs a) {
+    constexpr int NT = 64 * NW;               // threads
+    constexpr int NR = 16 * RT * NW;          // rows of W_g (and of W_u) per block
+    using Stage = BgStage<GS, TM, NR>;
     constexpr int PA = Stage::PA, PB = Stage::PB, KS = 64 * GS, MT = TM / 16;
-    constexpr int LA = TM * PA / 256, LB = PB, LN = LA + LB + GS;   // direct-to-LDS loads per stage per wave
-    static_assert(TM * PA >= 256, "one A piece per thread at least");
+    // direct-to-LDS loads per stage per wave: LA of u, LB of codes, LS of
+    // scales (fewer than one per thread: only the first SW waves load them)
+    constexpr int LA = TM * PA / NT, LB = 2 * NR * PB / NT;
+    constexpr int LS = 2 * NR * GS >= NT ? 2 * NR * GS / NT : 1, SW = 2 * NR * GS >= NT ? NW : 2 * NR * GS / 64;
+    constexpr int LN = LA + LB;
+    static_assert(TM * PA >= NT && 2 * NR * PB >= NT && 2 * NR * GS >= 64, "one piece per thread at least");
     const GemvArgs& g = a.g;
     __shared__ __align__(16) Stage S[NST];
     __shared__ __align__(16) uint16_t ush[TM][32], usl[TM][32];   // group sums of u, bf16 hi / lo
@@ -709,7 +717,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
     const int4 ti = *(const int4*)((TM == kTileBig ? a.tiles64 : a.tiles) + 4 * blockIdx.x);
     const bool shared = ti.x < 0;
     const int f = shared ? g.fs : g.f;
-    const int rb0 = blockIdx.y * kBgRows;
+    const int rb0 = blockIdx.y * NR;
     const int p0 = ti.y, M = ti.z;
     if (rb0 >= f || M <= 0) return;
     const uint8_t* blob = pf_blob(g, ti.w);
@@ -725,34 +733,35 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
     const uint32_t* asrc[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-        const int pa = wave * 64 + 256 * i + lane, m = pa / PA, c = (pa % PA) ^ (m % PA);
+        const int pa = wave * 64 + NT * i + lane, m = pa / PA, c = (pa % PA) ^ (m % PA);
         asrc[i] = g.u_pk + (size_t)tok[m] * (d / 2) + 4 * c;
     }
     const uint8_t* bsrc[LB];
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-        const int pi = wave * 64 + 256 * i + lane, r = pi / PB, pg = (pi % PB) ^ Stage::bsw(r);
-        bsrc[i] = wb + (r < kBgRows ? L.gate_q : L.up_q) + (size_t)(rb0 + (r & (kBgRows - 1))) * (d / 2) + 16 * pg;
+        const int pi = wave * 64 + NT * i + lane, r = pi / PB, pg = (pi % PB) ^ Stage::bsw(r);
+        bsrc[i] = wb + (r < NR ? L.gate_q : L.up_q) + (size_t)(rb0 + (r & (NR - 1))) * (d / 2) + 16 * pg;
     }
-    const uint8_t* ssrc[GS];
+    const uint8_t* ssrc[LS];
 #pragma unroll
-    for (int j = 0; j < GS; ++j) {
-        const int di = wave * 64 + 256 * j + lane, r = di / GS;
-        ssrc[j] = wb + (r < kBgRows ? L.gate_sb : L.up_sb) + (size_t)(rb0 + (r & (kBgRows - 1))) * (d / 16) + 4 * (di % GS);
+    for (int j = 0; j < LS; ++j) {
+        const int di = wave * 64 + NT * j + lane, r = di / GS;
+        ssrc[j] = wb + (r < NR ? L.gate_sb : L.up_sb) + (size_t)(rb0 + (r & (NR - 1))) * (d / 16) + 4 * (di % GS);
     }
     auto stage_issue = [&](int kc, Stage& st) {
 #pragma unroll
-        for (int i = 0; i < LA; ++i) lds_dma16(asrc[i] + kc * (KS / 2), &st.a[(wave * 64 + 256 * i) * 16]);
+        for (int i = 0; i < LA; ++i) lds_dma16(asrc[i] + kc * (KS / 2), &st.a[(wave * 64 + NT * i) * 16]);
 #pragma unroll
-        for (int i = 0; i < LB; ++i) lds_dma16(bsrc[i] + kc * (KS / 2), &st.b[(wave * 64 + 256 * i) * 16]);
+        for (int i = 0; i < LB; ++i) lds_dma16(bsrc[i] + kc * (KS / 2), &st.b[(wave * 64 + NT * i) * 16]);
 #pragma unroll
-        for (int j = 0; j < GS; ++j) lds_dma4(ssrc[j] + kc * 4 * GS, (const uint8_t*)&st.sc[0][0] + (wave * 64 + 256 * j) * 4);
+        for (int j = 0; j < LS; ++j)
+            if (wave < SW) lds_dma4(ssrc[j] + kc * 4 * GS, (const uint8_t*)&st.sc[0][0] + (wave * 64 + NT * j) * 4);
     };
     for (int i = 0; i < NST - 1 && i < NS; ++i) stage_issue(i, S[i]);
 
     // ---- bias term, as one MFMA k-step over the groups: A = group sums of u
     // (tokens x groups), B = (b - 128 s) (groups x rows), both bf16 hi + lo
-    for (int i = tid; i < TM * 32; i += 256) {
+    for (int i = tid; i < TM * 32; i += NT) {
         const int m = i >> 5, gg = i & 31;
         float us = 0.f;
         if (gg < G) us = g.usum[(size_t)tok[m] * (d / 32) + 2 * gg] + g.usum[(size_t)tok[m] * (d / 32) + 2 * gg + 1];
@@ -761,14 +770,14 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
         usl[m][gg] = (uint16_t)f32_to_bf16(us - bf16_to_f32(hi));
     }
     const int ml = lane & 15, pc = lane >> 4;
-    f32x4 acc[MT][2][2];                       // [token tile][row tile][gate / up]
+    f32x4 acc[MT][RT][2];                      // [token tile][row tile][gate / up]
     {
-        u32x4 chi[2][2], clo[2][2];
+        u32x4 chi[RT][2], clo[RT][2];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int gu = 0; gu < 2; ++gu) {
-                const int n = rb0 + 32 * wave + 16 * rt + ml;
+                const int n = rb0 + 16 * RT * wave + 16 * rt + ml;
                 const uint32_t* sbp = (const uint32_t*)(wb + (gu ? L.up_sb : L.gate_sb) + (size_t)n * (d / 16));
                 uint32_t h8[8], l8[8];
 #pragma unroll
@@ -793,7 +802,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
             const u32x4 uh = *(const u32x4*)&ush[16 * mt + ml][8 * pc];
             const u32x4 ul = *(const u32x4*)&usl[16 * mt + ml][8 * pc];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int gu = 0; gu < 2; ++gu) {
                     f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -809,20 +818,20 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
     uint32_t nm = 0x000F000Fu, nc = 0x43004300u;
     asm volatile("" : "+v"(nm), "+v"(nc));
     for (int kc = 0; kc < NS; ++kc) {
-        ring_wait<LN, LN>(min(NST - 2, NS - 1 - kc), false);
+        ring_wait<LN, LN + LS>(min(NST - 2, NS - 1 - kc), wave < SW);
         lds_barrier();                                  // stage kc landed everywhere; stage kc - 1 consumed
         const Stage& st = S[kc % NST];
         if (kc + NST - 1 < NS) stage_issue(kc + NST - 1, S[(kc + NST - 1) % NST]);
 #pragma unroll
         for (int q = 0; q < GS; ++q) {
             const int p = 2 * q + (pc >> 1);
-            u32x4 b0[2][2], b1[2][2];
-            float sv[2][2];
+            u32x4 b0[RT][2], b1[RT][2];
+            float sv[RT][2];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int gu = 0; gu < 2; ++gu) {
-                    const int r = gu * kBgRows + 32 * wave + 16 * rt + ml;
+                    const int r = gu * NR + 16 * RT * wave + 16 * rt + ml;
                     const u32x2 w = *(const u32x2*)&st.b[r * (PB * 16) + ((p ^ Stage::bsw(r)) << 4) + ((pc & 1) << 3)];
                     b0[rt][gu] = nib4v(w.x, nm, nc);
                     b1[rt][gu] = nib4v(w.y, nm, nc);
@@ -834,7 +843,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
                 const u32x4 a0 = *(const u32x4*)&st.a[m * (PA * 16) + ((gp ^ (m % PA)) << 4)];
                 const u32x4 a1 = *(const u32x4*)&st.a[m * (PA * 16) + (((gp + 1) ^ (m % PA)) << 4)];
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int gu = 0; gu < 2; ++gu) {
                         f32x4 pp = {0.f, 0.f, 0.f, 0.f};
@@ -852,8 +861,8 @@ __global__ void __launch_bounds__(256) k_pf_gateup_big(PrefillArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int n = rb0 + 32 * wave + 16 * rt + ml;
+        for (int rt = 0; rt < RT; ++rt) {
+            const int n = rb0 + 16 * RT * wave + 16 * rt + ml;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 16 * mt + 4 * pc + i;
@@ -1304,7 +1313,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     const int fmax = g.f > g.fs ? g.f : g.fs;
     // the tile lists were written by the sort (64-row ones when big)
     if (prefill_big_tiles(g.d, g.f, g.fs, g.u_pk_lo != nullptr, g.n_tok, g.k, g.max_active)) {
-        hipLaunchKernelGGL((k_pf_gateup_big<kBgGs, kBgNst, kTileBig>), dim3(a.max_tiles64, (fmax + kBgRows - 1) / kBgRows), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_pf_gateup_big<kBgGs, kBgNst, kTileBig, kBgRt, kBgWaves>), dim3(a.max_tiles64, (fmax + kBgRows - 1) / kBgRows),
+                           dim3(64 * kBgWaves), 0, s, a);
     } else {
         const dim3 ggrid(a.max_tiles, (fmax + kGuRows - 1) / kGuRows);
         if (g.u_pk_lo) hipLaunchKernelGGL(k_pf_gateup<true>, ggrid, dim3(256), 0, s, a);
