@@ -126,7 +126,7 @@ __device__ __forceinline__ const uint8_t* pf_blob(const GemvArgs& g, int blob) {
 // stored to LDS with piece p of line r at slot p ^ (r & 7), so the MFMA reads
 // (8 bytes per lane, 16 rows per instruction) hit at most 2 lanes per bank
 // group. The next stage is loaded into registers while the current one is
-// multiplied.
+// multiplied, then stored over it once every wave is done with it.
 // k-mapping inside a 64-group (8 pieces of 8 elements): MFMA q (0, 1) takes
 // piece 2*pc + q from lane group pc, so every MFMA stays inside one group and
 // its scale applies to the whole accumulator.
@@ -198,10 +198,12 @@ __device__ __forceinline__ u32x2 gu_b_read(const GuLds<LO>& S, int r, int q, int
     return *(const u32x2*)&S.b[r * 128 + ((p ^ (r & 7)) << 4) + ((pc & 1) << 3)];
 }
 
-template <bool LO>
+// NB LDS stage buffers: one keeps blocks small (three per CU) for calls with
+// many tiles; two save a barrier per stage when there are few
+template <bool LO, int NB>
 __global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
     const GemvArgs& g = a.g;
-    __shared__ __align__(16) GuLds<LO> S[2];
+    __shared__ __align__(16) GuLds<LO> S[NB];
     __shared__ float us64[kTileM][kMaxGroupsPf + 1];
     __shared__ int tok[kTileM];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -239,7 +241,7 @@ __global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
     uint32_t nm = 0x000F000Fu, nc = 0x43004300u;
     asm volatile("" : "+v"(nm), "+v"(nc));
     for (int st = 0; st < NS; ++st) {
-        const GuLds<LO>& C = S[st & 1];
+        const GuLds<LO>& C = S[st % NB];
         if (st + 1 < NS) gu_stage_load<LO>(R, st + 1, wb, L, d, f, rb0, tok, a);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -281,7 +283,8 @@ __global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
                 }
             }
         }
-        if (st + 1 < NS) gu_stage_store<LO>(R, S[(st + 1) & 1]);
+        if (NB == 1) __syncthreads();            // one buffer: every wave is done with it
+        if (st + 1 < NS) gu_stage_store<LO>(R, S[(st + 1) % NB]);
         __syncthreads();
     }
     const bool ok = blob != nullptr;
@@ -1317,8 +1320,15 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
                            dim3(64 * kBgWaves), 0, s, a);
     } else {
         const dim3 ggrid(a.max_tiles, (fmax + kGuRows - 1) / kGuRows);
-        if (g.u_pk_lo) hipLaunchKernelGGL(k_pf_gateup<true>, ggrid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(k_pf_gateup<false>, ggrid, dim3(256), 0, s, a);
+        // one stage buffer once the experts average 4 or more tokens
+        const bool many = (long long)g.n_tok * g.k >= 4LL * g.max_active;
+        if (g.u_pk_lo) {
+            if (many) hipLaunchKernelGGL((k_pf_gateup<true, 1>), ggrid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_pf_gateup<true, 2>), ggrid, dim3(256), 0, s, a);
+        } else {
+            if (many) hipLaunchKernelGGL((k_pf_gateup<false, 1>), ggrid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_pf_gateup<false, 2>), ggrid, dim3(256), 0, s, a);
+        }
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
