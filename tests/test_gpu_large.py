@@ -8,6 +8,7 @@ per-token), while the routing of every row is compared: indices bit-exact
 except certified near ties (oracle logit gap < 1e-3, counted), block outputs
 within rel-L2 2e-3 per row.
 """
+import dataclasses
 import json
 import os
 
@@ -29,8 +30,7 @@ NEAR_TIE = 1e-3
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def sampled_layer_check(n_tok, prefill, seed, sample):
-    shape = synth.LAYER35B
+def sampled_layer_check(n_tok, prefill, seed, sample, shape=synth.LAYER35B):
     say(f"{shape.name} n_tok={n_tok} prefill={prefill} sampled rows={len(sample)}")
     w = layer_tensors(shape, layer=seed, tag="large")
     lw = oracle_layer(shape, w)
@@ -88,6 +88,14 @@ def test_prefill_ragged_long_sampled():
     routing tiles and the 64-token gate/up tiles both end in a partial tile."""
     sample = [0, 63, 64, 2500, 4095, 4096, 4132]
     sampled_layer_check(4133, True, 24, sample)
+
+
+def test_prefill_f32_activations_sampled():
+    """fp32 block input on the matrix-core path: u enters every MFMA as a bf16
+    hi + lo pair (two products), both gate/up buffering modes."""
+    shape = dataclasses.replace(synth.LAYER35B, name="layer_d2048_e256_k4_f32", act="f32")
+    sampled_layer_check(300, True, 25, [0, 1, 150, 299], shape=shape)
+    sampled_layer_check(37, True, 26, [0, 5, 36], shape=shape)
 
 
 def test_decode_batch32_sampled():
