@@ -149,7 +149,8 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
         // wave checks 64 rows per load and takes each self-routed one in turn
         for (int base = wave * 64; base < a.n_tok; base += kSortThreads) {
             const int t = base + lane;
-            unsigned long long m = __ballot(t < a.n_tok && a.route_idx[(size_t)t * a.k] < 0);
+            unsigned long long m = __ballot(t < a.n_tok && (t < a.route_shift ||
+                                                              a.route_idx[(size_t)(t - a.route_shift) * a.k] < 0));
             while (m) {
                 const int tt = base + __ffsll((long long)m) - 1;
                 m &= m - 1;
@@ -170,10 +171,11 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     }
     for (int i = tid; i < n; i += kSortThreads) {
         const int t = i / a.k;
-        const bool self = !a.route_idx || a.route_idx[(size_t)t * a.k] < 0;
+        const size_t gi = (size_t)i - (size_t)a.route_shift * a.k;   // the given routing's entry (t >= shift)
+        const bool self = !a.route_idx || t < a.route_shift || a.route_idx[gi - (size_t)(i % a.k)] < 0;
         if (self && own_topk) continue;      // written by the top-k above
-        int e = self ? a.self_idx[i] : a.route_idx[i];
-        const float w = self ? a.self_w[i] : a.route_w[i];
+        int e = self ? a.self_idx[i] : a.route_idx[gi];
+        const float w = self ? a.self_w[i] : a.route_w[gi];
         if (e < 0 || e >= E) { set_err(a.err, ERR_BAD_INDEX); e = -1; }
         a.used_idx[i] = e; a.used_w[i] = w;
         if (a.user_used_idx) a.user_used_idx[i] = e;

@@ -1018,7 +1018,8 @@ __device__ __forceinline__ u32x4 bf16_pairs_p4(u32x4 v) {
 __device__ __forceinline__ bool route_tile_needed(const RouteMMArgs& a, int t0, int n) {
     if (!a.route_idx) return true;
     const int t = t0 + (int)threadIdx.x;
-    const int self = (int)threadIdx.x < n && t < a.n_tok && a.route_idx[(size_t)t * a.k] < 0;
+    const int self = (int)threadIdx.x < n && t < a.n_tok &&
+                     (t < a.route_shift || a.route_idx[(size_t)(t - a.route_shift) * a.k] < 0);
     return __syncthreads_or(self) != 0;
 }
 
@@ -1260,7 +1261,8 @@ __global__ void __launch_bounds__(256) k_route_topk(RouteMMArgs a, int job0) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.n_tok) return;
     if ((int)blockIdx.y + job0 == 0) {
-        if (!a.router || (a.route_idx && a.route_idx[(size_t)t * a.k] >= 0)) return;
+        if (!a.router || (a.route_idx && t >= a.route_shift && a.route_idx[(size_t)(t - a.route_shift) * a.k] >= 0))
+            return;
         if (a.E <= 64) topk_row<1>(false, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
         else if (a.E <= 128) topk_row<2>(false, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
         else if (a.E <= 256) topk_row<4>(false, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);

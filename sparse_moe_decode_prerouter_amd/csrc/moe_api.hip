@@ -192,7 +192,7 @@ __global__ void k_merge_route(const int32_t* ridx, const int32_t* sidx, int32_t*
     dst[i] = (ridx && ridx[(size_t)t * k] >= 0) ? ridx[i] : sidx[i];
 }
 
-int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill);
+int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill, int route_shift = 0);
 
 // defer_in: a previous layer's head top-k to run inside this layer's K_A.
 // defer_out (stack mode): this layer's head top-k is not run here but handed
@@ -286,7 +286,9 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
     return MOE_OK;
 }
 
-int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill) {
+// route_shift = 1: io->route_idx / route_w hold the previous layer's
+// predictions by token; token t takes row t - 1 and token 0 self-routes
+int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill, int route_shift) {
     const moe_layer_desc& D = L->desc;
     const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
     if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
@@ -306,7 +308,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     RouteMMArgs ra{};
     ra.u_pk = L->s.u_pk; ra.u_pk_lo = L->s.u_pk_lo; ra.d = D.d_model; ra.n_tok = n_tok;
     ra.router = L->w.router; ra.router_bias = L->w.router_bias; ra.E = D.n_experts; ra.k = D.top_k;
-    ra.route_idx = io->route_idx;
+    ra.route_idx = io->route_idx; ra.route_shift = route_shift;
     ra.head = io->pred_idx ? L->w.head : nullptr; ra.head_bias = L->w.head_bias;
     ra.En = D.next_n_experts; ra.kn = D.next_top_k;
     ra.hist_cur_m = L->w.hist_cur; ra.hist_prev_m = L->w.hist_prev; ra.hist_cur = io->hist_cur; ra.hist_prev = io->hist_prev;
@@ -328,7 +330,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm));
 
     SortArgs sa{};
-    sa.route_idx = io->route_idx; sa.route_w = io->route_w;
+    sa.route_idx = io->route_idx; sa.route_w = io->route_w; sa.route_shift = route_shift;
     sa.self_idx = L->w.router ? L->s.self_idx : nullptr; sa.self_w = L->s.self_w;
     sa.n_tok = n_tok; sa.k = D.top_k; sa.E = D.n_experts;
     sa.used_idx = L->s.used_idx; sa.used_w = L->s.used_w;
@@ -573,16 +575,15 @@ int moe_stack_create(moe_layer* const* layers, int n, moe_stack** out) {
     S->layers = new moe_layer*[n];
     for (int l = 0; l < n; ++l) S->layers[l] = layers[l];
     S->n = n;
-    // prefill scratch for the shifted routing, sized by the smallest max_tokens
+    // prefill scratch for the predictions passed between layers, sized by the
+    // smallest max_tokens
     int T = layers[0]->desc.max_tokens;
     for (int l = 1; l < n; ++l) T = std::min(T, layers[l]->desc.max_tokens);
     const size_t per = (size_t)T * layers[0]->desc.top_k;
-    hipError_t e = hipMalloc(&S->d_shift_idx, per * sizeof(int32_t));
-    if (e == hipSuccess) e = hipMalloc(&S->d_shift_w, per * sizeof(float));
-    if (e == hipSuccess) e = hipMalloc(&S->d_pred_idx, per * sizeof(int32_t));
+    hipError_t e = hipMalloc(&S->d_pred_idx, per * sizeof(int32_t));
     if (e == hipSuccess) e = hipMalloc(&S->d_pred_w, per * sizeof(float));
     if (e != hipSuccess) { g_last_hip = (int)e; moe_stack_destroy(S); return MOE_E_HIP; }
-    S->shift_cap = per;
+    S->pred_cap = per;
     *out = S;
     return MOE_OK;
 }
@@ -624,35 +625,24 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
     return MOE_OK;
 }
 
-// dst row i = src row i-1, row 0 = -1 (no prediction: self-route)
-__global__ void k_shift_rows(const int32_t* si, const float* sw, int32_t* di, float* dw, int n_tok, int k) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n_tok * k) return;
-    const int t = i / k;
-    di[i] = t == 0 ? -1 : si[i - k];
-    dw[i] = t == 0 ? 0.f : sw[i - k];
-}
-
 int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, float* used_w, int32_t* pred_idx,
                       float* pred_w, void* stream) {
     if (!S || !x || n_tok < 1) return MOE_E_INVALID;
     const int k = S->layers[0]->desc.top_k;
     const size_t per = (size_t)n_tok * k;
     hipStream_t st = (hipStream_t)stream;
-    if (per > S->shift_cap) return MOE_E_INVALID;
+    if (per > S->pred_cap) return MOE_E_INVALID;
     for (int l = 0; l < S->n; ++l) {
         moe_layer* L = S->layers[l];
         moe_io io{};
         io.x_in = x;
         io.y_out = x;
         if (l > 0) {
-            const int32_t* src_i = pred_idx ? pred_idx + l * per : S->d_pred_idx;
-            const float* src_w = pred_w ? pred_w + l * per : S->d_pred_w;
-            hipLaunchKernelGGL(k_shift_rows, dim3((per + 255) / 256), dim3(256), 0, st, src_i, src_w,
-                               S->d_shift_idx, S->d_shift_w, n_tok, k);
-            HIPCHK(hipGetLastError());
-            io.route_idx = S->d_shift_idx;
-            io.route_w = S->d_shift_w;
+            // the previous layer's predictions by token, shifted by one token
+            // inside the call (token 0 self-routes); they are read before this
+            // call's own predictions overwrite the shared buffer
+            io.route_idx = pred_idx ? pred_idx + l * per : S->d_pred_idx;
+            io.route_w = pred_w ? pred_w + l * per : S->d_pred_w;
         }
         io.used_idx = used_idx ? used_idx + l * per : nullptr;
         io.used_w = used_w ? used_w + l * per : nullptr;
@@ -660,7 +650,9 @@ int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, floa
             io.pred_idx = pred_idx ? pred_idx + (l + 1) * per : S->d_pred_idx;
             io.pred_w = pred_w ? pred_w + (l + 1) * per : S->d_pred_w;
         }
-        int rc = moe_prefill(L, &io, n_tok, stream);
+        int rc = check_io(L, &io, n_tok);
+        if (rc != MOE_OK) return rc;
+        rc = run_prefill(L, &io, n_tok, st, true, l > 0 ? 1 : 0);
         if (rc != MOE_OK) return rc;
     }
     return MOE_OK;
@@ -668,8 +660,6 @@ int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, floa
 
 void moe_stack_destroy(moe_stack* S) {
     if (!S) return;
-    if (S->d_shift_idx) (void)hipFree(S->d_shift_idx);
-    if (S->d_shift_w) (void)hipFree(S->d_shift_w);
     if (S->d_pred_idx) (void)hipFree(S->d_pred_idx);
     if (S->d_pred_w) (void)hipFree(S->d_pred_w);
     delete[] S->layers;

@@ -117,11 +117,9 @@ struct moe_stack {
     moe_layer** layers;
     int n;
     // prefill scratch: shifted routing and per-layer predictions (device)
-    int32_t* d_shift_idx;
-    float* d_shift_w;
     int32_t* d_pred_idx;
     float* d_pred_w;
-    size_t shift_cap;        // entries
+    size_t pred_cap;         // entries
 };
 
 // ---- kernel launchers (kernels_*.hip) -------------------------------------
@@ -140,6 +138,7 @@ struct RouteArgs {
     int d; int n_tok;
     const uint16_t* router; const float* router_bias; int E; int k;
     const int32_t* route_idx;           // rows to self-route: idx[t*k] < 0 or route_idx == nullptr
+    int route_shift;                    // 1: token t takes row t - 1 of route_idx, token 0 self-routes
     const uint16_t* head; const float* head_bias; int En; int kn;
     const float* hist_cur_m; const float* hist_prev_m; const int32_t* hist_cur; const int32_t* hist_prev;
     const uint16_t* lora_a; int r;
@@ -155,6 +154,7 @@ struct RouteMMArgs {
     const uint32_t* u_pk; const uint32_t* u_pk_lo; int d; int n_tok;
     const uint16_t* router; const float* router_bias; int E; int k;
     const int32_t* route_idx;           // rows to self-route: idx[t*k] < 0 or route_idx == nullptr
+    int route_shift;                    // 1: token t takes row t - 1 of route_idx, token 0 self-routes
     const uint16_t* head; const float* head_bias; int En; int kn;
     const float* hist_cur_m; const float* hist_prev_m; const int32_t* hist_cur; const int32_t* hist_prev;
     const uint16_t* lora_a; int r;
@@ -179,6 +179,7 @@ struct TopkJob {
 constexpr int kSortTopkMaxE = 256;
 struct SortArgs {
     const int32_t* route_idx; const float* route_w; int32_t* self_idx; float* self_w;
+    int route_shift;                    // 1: token t takes row t - 1 of the given routing, token 0 self-routes
     int n_tok; int k; int E;
     int32_t* used_idx; float* used_w; int32_t* user_used_idx; float* user_used_w;
     int32_t* meta; int32_t* active; int32_t* act_off; int32_t* perm;

@@ -134,3 +134,61 @@ def test_stack_free_running():
             compared += 1
     say(f"  compared {compared} (step, sequence) pairs; stopped sequences: {alive.count(False)}")
     assert compared >= steps * B // 2
+
+
+def test_stack_prefill():
+    """moe_stack_prefill through 3 layers at 37 tokens (the grouped-GEMM path):
+    layer 0 self-routes every token; layer l >= 1 routes token i by head l-1 on
+    token i-1 (shifted inside the call) and token 0 self-routes. The oracle is
+    fed the routing the GPU used, so every block output is compared; every
+    routing decision the GPU made (its self-routed rows and its predictions)
+    is checked against the oracle's logits (certified near ties counted)."""
+    shape = synth.LAYER35B
+    L_, T = 3, 37
+    say(f"stack prefill L={L_} T={T}")
+    ws = [layer_tensors(shape, layer=l, tag="spf") for l in range(L_)]
+    ora = [oracle_layer(shape, w) for w in ws]
+    gpus = [gpu_layer(shape, w, fused=True, max_tokens=T, head=(l + 1 < L_)) for l, w in enumerate(ws)]
+    import sparse_moe_decode_prerouter_amd as moe
+    stack = moe.MoeStack(gpus)
+    x0 = synth.activations(shape, T, ("spf",), dtype=torch.float32)
+    xg = x0.cuda().contiguous()
+    k = shape.k
+    used_i = torch.empty((L_, T, k), dtype=torch.int32, device="cuda")
+    used_w = torch.empty((L_, T, k), dtype=torch.float32, device="cuda")
+    pred_i = torch.full((L_, T, k), -7, dtype=torch.int32, device="cuda")
+    pred_w = torch.zeros((L_, T, k), dtype=torch.float32, device="cuda")
+    stack.prefill(xg, used_idx=used_i, used_w=used_w, pred_idx=pred_i, pred_w=pred_w)
+    torch.cuda.synchronize()
+    for Lr in gpus:
+        assert Lr.status() == 0
+    ui, uw = used_i.cpu().numpy(), used_w.cpu().numpy()
+    pi, pw = pred_i.cpu().numpy(), pred_w.cpu().numpy()
+    x = x0.double().numpy()
+    flips = 0
+    for l in range(L_):
+        if l > 0:
+            # token i of layer l took head l-1's prediction on token i-1
+            assert np.array_equal(ui[l][1:], pi[l][:-1]), l
+            assert np.array_equal(uw[l][1:], pw[l][:-1]), l
+        nk = shape.k if l + 1 < L_ else None
+        x_next, y, u, used, pred, z = oracle.decode_layer(ora[l], x, (ui[l].astype(np.int64), uw[l].astype(np.float64)),
+                                                          nk, fused_norm=True)
+        # the GPU's self-routed rows: every row of layer 0, row 0 of the others
+        for t in (range(T) if l == 0 else [0]):
+            zr = oracle.head_logits(ora[l].router, u[t], ora[l].router_bias)
+            ref, ref_w = oracle.route(zr, k)
+            if not np.array_equal(ui[l][t], ref):
+                assert logit_gap_ok(zr, k, ui[l][t], ref, NEAR_TIE), (l, t)
+                flips += 1
+            else:
+                assert np.allclose(uw[l][t], ref_w, rtol=1e-6, atol=1e-7), (l, t)
+        if nk:
+            for t in range(T):
+                if not np.array_equal(pi[l + 1][t], pred[0][t]):
+                    assert logit_gap_ok(z[t], k, pi[l + 1][t], pred[0][t], NEAR_TIE), (l, t)
+                    flips += 1
+        x = x_next
+    err = rel_l2_rows(xg.double().cpu().numpy(), x)
+    say(f"  stack output rel-L2 {err:.2e}; certified near-tie flips {flips}")
+    assert err <= STACK_TOL
