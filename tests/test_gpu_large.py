@@ -30,12 +30,16 @@ NEAR_TIE = 1e-3
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def sampled_layer_check(n_tok, prefill, seed, sample, shape=synth.LAYER35B):
-    say(f"{shape.name} n_tok={n_tok} prefill={prefill} sampled rows={len(sample)}")
+def sampled_layer_check(n_tok, prefill, seed, sample, shape=synth.LAYER35B, same_experts=None):
+    say(f"{shape.name} n_tok={n_tok} prefill={prefill} sampled rows={len(sample)} same_experts={same_experts}")
     w = layer_tensors(shape, layer=seed, tag="large")
     lw = oracle_layer(shape, w)
     x = synth.activations(shape, n_tok, ("large", seed, n_tok), dtype=torch.float32)
     ridx, rw = synth.random_routing(n_tok, shape.E, shape.k, ("large", seed, n_tok))
+    if same_experts is not None:
+        # every row routes to the same experts (in a row-dependent order)
+        base = torch.tensor(same_experts, dtype=torch.int32)
+        ridx = torch.stack([torch.roll(base, t % shape.k) for t in range(n_tok)])
     ridx[0] = -1                     # row 0 self-routes (as the first prefill row does)
     L = gpu_layer(shape, w, fused=True, max_tokens=n_tok)
     call = L.prefill if prefill else L.decode
@@ -96,6 +100,15 @@ def test_prefill_f32_activations_sampled():
     shape = dataclasses.replace(synth.LAYER35B, name="layer_d2048_e256_k4_f32", act="f32")
     sampled_layer_check(300, True, 25, [0, 1, 150, 299], shape=shape)
     sampled_layer_check(37, True, 26, [0, 5, 36], shape=shape)
+
+
+def test_prefill_one_hot_experts_sampled():
+    """Degenerate routing: all 511 given rows use the same 4 experts (511
+    assignments each: 32 tiles per expert, a down
+    projection block spanning one expert's tiles), plus a single-token
+    prefill."""
+    sampled_layer_check(512, True, 27, [0, 1, 63, 64, 255, 511], same_experts=[3, 200, 77, 255])
+    sampled_layer_check(1, True, 28, [0])
 
 
 def test_decode_batch32_sampled():
