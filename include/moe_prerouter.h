@@ -26,9 +26,13 @@
  *     pinned" pointers come from hipHostMalloc (or torch pin_memory). Streams
  *     are hipStream_t passed as void* (NULL = the default stream).
  *   - The caller owns every buffer it passes and keeps it alive until
- *     moe_layer_destroy. The library keeps pointers and copies no weight; it
- *     allocates only its host handle, HIP events and a small pinned host
- *     buffer for read-backs.
+ *     moe_layer_destroy. The library keeps pointers; it allocates only its
+ *     host handle, HIP events and a small pinned host buffer for read-backs.
+ *     One copy is made: with bf16 activations, moe_layer_create writes the
+ *     bf16 router, head, LoRA A and shared-gate rows into the workspace in
+ *     matrix-core fragment order (the prefill routing GEMM reads them there),
+ *     so those four arrays must not change after create; the expert store
+ *     and the other weights are read in place.
  *   - A layer handle is not thread-safe. Calls on one handle must not overlap
  *     on different streams; separate handles are independent.
  *   - Routing indices are int32, routing weights fp32, logits fp64 inside.
@@ -157,7 +161,8 @@ typedef struct moe_layer moe_layer;
 size_t moe_expert_blob_bytes(int d_model, int d_ff, int group_size);
 
 /* Device workspace bytes a layer needs (slab in streamed mode, slot table,
- * activations, routing and sort scratch for max_tokens); 0 on invalid desc. */
+ * activations, routing and sort scratch for max_tokens, the fragment-ordered
+ * routing rows); 0 on invalid desc. */
 size_t moe_layer_workspace_bytes(const moe_layer_desc* desc);
 
 /* Create a layer on the current device. d_workspace: device memory of at

@@ -13,14 +13,23 @@ namespace moe {
 // once to the activation dtype (RMSNorm prologue of the head input: the head
 // reads the post-norm hidden state -- reading guide, Method, prerouter head).
 // Writes the GEMV-ordered bf16 pairs (and the lo parts for fp32 activations)
-// and the per-32-chunk sums used by the int4 dot products.
+// and the per-32-chunk sums used by the int4 dot products; with u_frag, the
+// same pairs again in MFMA fragment order for the routing GEMM: per 16
+// tokens and 32 elements one 1 KB block, whose 16 bytes at 16 l are the
+// 8 elements 8 (l / 16) .. of token l mod 16. Blocks are dealt to the 8 XCDs
+// round robin, so block b takes token (b mod 8) * per + b / 8 with per a
+// multiple of 8: the 8 tokens that share a line of u_frag are written on one
+// XCD, and their lines reach memory whole.
 // GEMV order of a 32-element chunk c: dword 4*i + p holds elements
 // (32c + 8i + p, 32c + 8i + p + 4), matching the nibble pairs that one
 // masked shift of a packed dword yields.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_prologue(PrologueArgs a) {
     __shared__ double red[4];
-    const int t = blockIdx.x, d = a.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (((a.n_tok + 7) / 8) + 7) / 8 * 8;
+    const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (t >= a.n_tok) return;                 // the grid is 8 per blocks
+    const int d = a.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // thread tid takes the 8-element pieces tid, tid + 256, ...; piece pc is
     // (chunk pc / 4, sub-block pc % 4), whose four pairs are dwords 4 pc .. + 3
     auto load8 = [&](int pc, double* v) {
@@ -69,6 +78,10 @@ __global__ void __launch_bounds__(256) k_prologue(PrologueArgs a) {
         if (a.u_pk_lo)
             *(u32x4*)(a.u_pk_lo + (size_t)t * (d / 2) + 4 * pc) =
                 u32x4{lo[0] | (lo[4] << 16), lo[1] | (lo[5] << 16), lo[2] | (lo[6] << 16), lo[3] | (lo[7] << 16)};
+        if (a.u_frag)
+            // block (t / 16, pc / 4), lane 16 (pc mod 4) + t mod 16
+            *(u32x4*)(a.u_frag + ((size_t)(t >> 4) * (d / 32) + (pc >> 2)) * 256 + ((pc & 3) * 16 + (t & 15)) * 4) =
+                u32x4{hi[0] | (hi[4] << 16), hi[1] | (hi[5] << 16), hi[2] | (hi[6] << 16), hi[3] | (hi[7] << 16)};
         // the chunk's 4 pieces are 4 consecutive lanes
         sh += __shfl_xor(sh, 1, 64);
         sh += __shfl_xor(sh, 2, 64);
@@ -82,8 +95,9 @@ __global__ void __launch_bounds__(256) k_prologue(PrologueArgs a) {
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
-    if (a.d % 64) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_prologue, dim3(a.n_tok), dim3(256), 0, s, a);
+    if (a.d % 64 || a.n_tok <= 0) return hipErrorInvalidValue;
+    const int per = ((a.n_tok + 7) / 8 + 7) / 8 * 8;
+    hipLaunchKernelGGL(k_prologue, dim3(8 * per), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

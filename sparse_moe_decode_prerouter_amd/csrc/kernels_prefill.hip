@@ -1141,6 +1141,108 @@ __global__ void __launch_bounds__(64 * NW) k_route_mm(RouteMMArgs a) {
     }
 }
 
+// The same products on operands stored in MFMA fragment order: for 16 rows
+// (or tokens) and 32 hidden elements, one 1 KB block whose 16 bytes at 16 l
+// are the 8 elements 8 (l / 16) .. of row l mod 16, so every load
+// instruction reads 1 KB of contiguous memory (the row-major form makes each
+// instruction touch 16 rows 4 KB apart, and the loads run at about half the
+// rate). u comes so from the prologue; router, head, LoRA A and shared-gate
+// rows are packed at layer creation, each set in tiles of its own 16 rows,
+// pairs already in u's (p, p + 4) order. Block = one row tile x 16 tokens;
+// the 4 waves take consecutive quarters of the k-steps, summed in order.
+constexpr int kFrWaves = 4;
+
+__global__ void __launch_bounds__(256) k_pack_rows(const uint16_t* w, int n, int d, uint32_t* out) {
+    const int S = d / 32;
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;        // one 16-byte piece
+    const long long total = (long long)((n + 15) / 16) * S * 64;
+    if (i >= total) return;
+    const int l = (int)(i & 63);
+    const long long blk = i >> 6;
+    const int c = (int)(blk % S), rt = (int)(blk / S);
+    const int row = rt * 16 + (l & 15);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < n) v = bf16_pairs_p4(*(const u32x4*)(w + (size_t)row * d + 32 * c + 8 * (l >> 4)));
+    *(u32x4*)(out + 4 * i) = v;
+}
+
+hipError_t launch_pack_rows(const uint16_t* w, int n, int d, uint32_t* out, hipStream_t s) {
+    if (n <= 0 || d % 32) return hipErrorInvalidValue;
+    const long long total = (long long)((n + 15) / 16) * (d / 32) * 64;
+    hipLaunchKernelGGL(k_pack_rows, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w, n, d, out);
+    return hipGetLastError();
+}
+
+// row tiles of the four sets, in order: router, head, LoRA A, shared gate
+struct FrSets {
+    int n0, n1, n2, n3;
+    __device__ __host__ int rows(int i) const { return i == 0 ? n0 : i == 1 ? n1 : i == 2 ? n2 : n3; }
+    __device__ __host__ int tiles(int i) const { return (rows(i) + 15) / 16; }
+    __device__ __host__ int total() const { return tiles(0) + tiles(1) + tiles(2) + tiles(3); }
+};
+__device__ __host__ __forceinline__ FrSets fr_sets(const RouteMMArgs& a) {
+    return FrSets{a.router ? a.E : 0, a.head ? a.En : 0, a.lora_a ? a.r : 0, a.sgate_w ? 1 : 0};
+}
+
+__global__ void __launch_bounds__(64 * kFrWaves) k_route_mm_fr(RouteMMArgs a) {
+    __shared__ double red[kFrWaves - 1][4][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pc = lane >> 4, ml = lane & 15;
+    const int d = a.d, T = a.n_tok, S = d / 32;
+    const FrSets fs = fr_sets(a);
+    int rt = blockIdx.x, set = 0;
+    while (set < 3 && rt >= fs.tiles(set)) { rt -= fs.tiles(set); ++set; }
+    const int t0 = blockIdx.y * 16;
+    // router rows are needed only for self-routed tokens
+    if (set == 0 && !route_tile_needed(a, t0, 16)) return;
+    const uint32_t* wf = set == 0 ? a.wf_router : set == 1 ? a.wf_head : set == 2 ? a.wf_lora : a.wf_sgate;
+    const u32x4* wq = (const u32x4*)wf + (size_t)rt * S * 64 + lane;
+    const u32x4* aq = (const u32x4*)a.u_frag + (size_t)blockIdx.y * S * 64 + lane;
+    // wave w takes k-steps [w * ns, (w + 1) * ns), loads issued 16 steps at a time
+    const int ns = S / kFrWaves, c0 = wave * ns;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int b0 = 0; b0 < ns; b0 += 16) {
+        const int nb = min(16, ns - b0);
+        u32x4 wv[16], av[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int cc = c0 + b0 + (c < nb ? c : nb - 1);
+            wv[c] = wq[64 * cc];
+            av[c] = aq[64 * cc];
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            if (c >= nb) continue;
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+            p = mfma16(av[c], wv[c], p);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] += (double)p[v];
+        }
+    }
+    if (wave > 0)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll 1
+    for (int w = 0; w < kFrWaves - 1; ++w)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] += red[w][v][lane];
+    const int r = 16 * rt + ml;                          // row within its set
+    if (r >= fs.rows(set)) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int t = t0 + 4 * pc + v;
+        if (t >= T) continue;
+        const double z = acc[v];
+        if (set == 0) a.logits_r[(size_t)t * a.E + r] = z;
+        else if (set == 1) a.logits_h[(size_t)t * a.En + r] = z;
+        else if (set == 2) a.au[(size_t)t * a.r + r] = (float)z;
+        else a.sgate[t] = (float)(1.0 / (1.0 + exp(-z)));
+    }
+}
+
 // The same products for many tokens: block = 64 tokens x 64 rows staged
 // through LDS 64 elements of k at a time (the next stage's loads in flight
 // while the current one is multiplied); wave (wm, wn) computes tokens
@@ -1288,7 +1390,10 @@ hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s, bool router_topk
         if (big_blocks >= 512)
             hipLaunchKernelGGL(k_route_mm_tiled, dim3((R + kRmTile - 1) / kRmTile, (a.n_tok + kRmTile - 1) / kRmTile),
                                dim3(256), 0, s, a);
-        else {
+        else if (a.u_frag && !a.u_pk_lo && a.d % (32 * kFrWaves) == 0 && (!a.router || a.wf_router) &&
+                 (!a.head || a.wf_head) && (!a.lora_a || a.wf_lora) && (!a.sgate_w || a.wf_sgate)) {
+            hipLaunchKernelGGL(k_route_mm_fr, dim3(fr_sets(a).total(), (a.n_tok + 15) / 16), dim3(64 * kFrWaves), 0, s, a);
+        } else {
             const dim3 grid((R + 15) / 16, (a.n_tok + 15) / 16);
             if (a.u_pk_lo) hipLaunchKernelGGL((k_route_mm<1, 1, 4, true>), grid, dim3(256), 0, s, a);
             else hipLaunchKernelGGL((k_route_mm<1, 1, 4, false>), grid, dim3(256), 0, s, a);

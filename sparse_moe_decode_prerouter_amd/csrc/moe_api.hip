@@ -76,6 +76,13 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.slab = resident ? nullptr : c.take<uint8_t>((slots + (d->d_ff_shared ? 1 : 0)) * blob);
     S.u_pk = c.take<uint32_t>(T * D / 2);
     S.u_pk_lo = f32 ? c.take<uint32_t>(T * D / 2) : nullptr;
+    // the routing GEMM's fragment-ordered operands (bf16 activations)
+    const size_t T16 = (T + 15) / 16 * 16;
+    S.u_frag = f32 ? nullptr : c.take<uint32_t>(T16 * D / 2);
+    S.wf_router = f32 ? nullptr : c.take<uint32_t>(frag_rows_words((int)E, (int)D));
+    S.wf_head = f32 || d->next_n_experts <= 0 ? nullptr : c.take<uint32_t>(frag_rows_words((int)En, (int)D));
+    S.wf_lora = f32 || d->lora_rank <= 0 ? nullptr : c.take<uint32_t>(frag_rows_words(d->lora_rank, (int)D));
+    S.wf_sgate = f32 || d->d_ff_shared <= 0 ? nullptr : c.take<uint32_t>(frag_rows_words(1, (int)D));
     S.usum = c.take<float>(T * D / 32);
     S.usum_lo = f32 ? c.take<float>(T * D / 32) : nullptr;
     S.logits_r = c.take<double>(T * E);
@@ -303,6 +310,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     pa.d = D.d_model;
     pa.n_tok = n_tok;
     pa.u_pk = L->s.u_pk; pa.u_pk_lo = L->s.u_pk_lo; pa.usum = L->s.usum; pa.usum_lo = L->s.usum_lo;
+    pa.u_frag = L->s.u_frag;
     HIPCHK(launch_prologue(pa, st));
 
     RouteMMArgs ra{};
@@ -318,6 +326,8 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     ra.self_idx = L->s.self_idx; ra.self_w = L->s.self_w;
     ra.pred_idx = io->pred_idx; ra.pred_w = io->pred_w;
     ra.au = L->s.au; ra.sgate = L->s.sgate;
+    ra.u_frag = L->s.u_frag;
+    ra.wf_router = L->s.wf_router; ra.wf_head = L->s.wf_head; ra.wf_lora = L->s.wf_lora; ra.wf_sgate = L->s.wf_sgate;
     const bool mm = prefill_mm_ok(D.d_model, D.d_ff, D.d_ff_shared);
     const int max_active = std::min(D.n_experts, n_tok * D.top_k);
     const bool big = mm && prefill_big_tiles(D.d_model, D.d_ff, D.d_ff_shared, D.act_dtype != MOE_ACT_BF16, n_tok,
@@ -461,6 +471,20 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w, voi
     if ((e = hipMemset(L->s.counters, 0, 16 * sizeof(uint32_t))) != hipSuccess) return fail(e);
     if ((e = hipMemset(L->s.slot_of, 0xFF, sizeof(int32_t) * desc->n_experts)) != hipSuccess) return fail(e);
     if ((e = hipMemset(L->s.slot_tag, 0xFF, sizeof(int32_t) * (L->slots + 1))) != hipSuccess) return fail(e);
+    {
+        // tile-ordered copies of the routing-side rows for the prefill routing
+        // GEMM (contiguous 1 KB loads); a set without its rows is not used
+        const int D = desc->d_model;
+        auto pack = [&](const uint16_t* w, int n, uint32_t*& out) -> hipError_t {
+            if (!out) return hipSuccess;
+            if (!w) { out = nullptr; return hipSuccess; }
+            return launch_pack_rows(w, n, D, out, nullptr);
+        };
+        if ((e = pack(w->router, desc->n_experts, L->s.wf_router)) != hipSuccess) return fail(e);
+        if ((e = pack(w->head, desc->next_n_experts, L->s.wf_head)) != hipSuccess) return fail(e);
+        if ((e = pack(w->lora_a, desc->lora_rank, L->s.wf_lora)) != hipSuccess) return fail(e);
+        if ((e = pack(w->shared_gate, 1, L->s.wf_sgate)) != hipSuccess) return fail(e);
+    }
     if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e);
     *out = L;
     return MOE_OK;

@@ -63,6 +63,11 @@ struct Scratch {
     uint8_t* slab;           // [(slots + 1) * blob] (streamed); shared slot last
     uint32_t* u_pk;          // [T][d/2] bf16 pairs, GEMV order (hi part)
     uint32_t* u_pk_lo;       // [T][d/2] lo part (f32 act) or nullptr
+    uint32_t* u_frag;        // [T/16][d/32][64 lanes][4]: u_pk in MFMA fragment order (bf16 act), or nullptr
+    uint32_t* wf_router;     // routing-side bf16 rows in MFMA fragment order (packed at create):
+    uint32_t* wf_head;       //   [rows/16][d/32][64 lanes][4], rows padded to 16 with zeros
+    uint32_t* wf_lora;
+    uint32_t* wf_sgate;
     float* usum;             // [T][d/32] sums of hi part per 32-chunk
     float* usum_lo;          // [T][d/32] or nullptr
     double* logits_r;        // [T][E] router logits
@@ -129,6 +134,7 @@ struct PrologueArgs {
     const void* x; int x_is_bf16; int fused; const float* gamma; float eps;
     int act_bf16; int d; int n_tok;
     uint32_t* u_pk; uint32_t* u_pk_lo; float* usum; float* usum_lo;
+    uint32_t* u_frag;                   // or nullptr
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 
@@ -162,7 +168,15 @@ struct RouteMMArgs {
     double* logits_r; double* logits_h;
     int32_t* self_idx; float* self_w; int32_t* pred_idx; float* pred_w;
     float* au; float* sgate;
+    // fragment-ordered operands (both or neither; bf16 activations): u, and
+    // the packed rows of router / head / LoRA A / shared gate (non-null where
+    // the plain pointer above is)
+    const uint32_t* u_frag;
+    const uint32_t* wf_router; const uint32_t* wf_head; const uint32_t* wf_lora; const uint32_t* wf_sgate;
 };
+// pack n bf16 rows of length d into MFMA fragment order (rows padded to 16)
+hipError_t launch_pack_rows(const uint16_t* w, int n, int d, uint32_t* out, hipStream_t s);
+inline size_t frag_rows_words(int n, int d) { return (size_t)((n + 15) / 16) * 16 * d / 2; }
 // router_topk: top-k of the self-routed rows here (else the sort does it);
 // head_topk: the head's top-k here (else the combine launch does it)
 hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk);
