@@ -24,64 +24,76 @@ namespace moe {
 // (32c + 8i + p, 32c + 8i + p + 4), matching the nibble pairs that one
 // masked shift of a packed dword yields.
 // ---------------------------------------------------------------------------
+constexpr int kProPieces = 4;                 // 8-element pieces per thread: d <= 8192
 __global__ void __launch_bounds__(256) k_prologue(PrologueArgs a) {
     __shared__ double red[4];
     const int per = (((a.n_tok + 7) / 8) + 7) / 8 * 8;
     const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
     if (t >= a.n_tok) return;                 // the grid is 8 per blocks
     const int d = a.d, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // thread tid takes the 8-element pieces tid, tid + 256, ...; piece pc is
-    // (chunk pc / 4, sub-block pc % 4), whose four pairs are dwords 4 pc .. + 3
-    auto load8 = [&](int pc, double* v) {
+    // thread tid takes the 8-element pieces tid, tid + 256, ... (at most
+    // kProPieces); piece pc is (chunk pc / 4, sub-block pc % 4), whose four
+    // pairs are dwords 4 pc .. + 3. x and gamma are loaded once, together.
+    float xv[kProPieces][8], gv[kProPieces][8];
+#pragma unroll
+    for (int j = 0; j < kProPieces; ++j) {
+        const int pc = tid + 256 * j;
+        if (pc >= d / 8) break;
         if (a.x_is_bf16) {
             const u32x4 w = *(const u32x4*)((const uint16_t*)a.x + (size_t)t * d + 8 * pc);
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                v[2 * i] = (double)bf16_to_f32(ws[i] & 0xFFFF);
-                v[2 * i + 1] = (double)bf16_to_f32(ws[i] >> 16);
+                xv[j][2 * i] = bf16_to_f32(ws[i] & 0xFFFF);
+                xv[j][2 * i + 1] = bf16_to_f32(ws[i] >> 16);
             }
         } else {
             const float4 x0 = *(const float4*)((const float*)a.x + (size_t)t * d + 8 * pc);
             const float4 x1 = *(const float4*)((const float*)a.x + (size_t)t * d + 8 * pc + 4);
-            v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-            v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+            xv[j][0] = x0.x; xv[j][1] = x0.y; xv[j][2] = x0.z; xv[j][3] = x0.w;
+            xv[j][4] = x1.x; xv[j][5] = x1.y; xv[j][6] = x1.z; xv[j][7] = x1.w;
         }
-    };
+        if (a.fused) {
+            const float4 g0 = *(const float4*)(a.gamma + 8 * pc), g1 = *(const float4*)(a.gamma + 8 * pc + 4);
+            gv[j][0] = g0.x; gv[j][1] = g0.y; gv[j][2] = g0.z; gv[j][3] = g0.w;
+            gv[j][4] = g1.x; gv[j][5] = g1.y; gv[j][6] = g1.z; gv[j][7] = g1.w;
+        }
+    }
     double ss = 0.0;
-    for (int pc = tid; pc < d / 8; pc += 256) {
-        double v[8];
-        load8(pc, v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+    for (int j = 0; j < kProPieces; ++j) {
+        if (tid + 256 * j >= d / 8) break;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += (double)xv[j][i] * (double)xv[j][i];
     }
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
     if (lane == 0) red[wave] = ss;
     __syncthreads();
     const double den = sqrt((red[0] + red[1] + red[2] + red[3]) / (double)d + (double)a.eps);
-    for (int pc = tid; pc < d / 8; pc += 256) {
-        double v[8];
-        load8(pc, v);
+#pragma unroll
+    for (int j = 0; j < kProPieces; ++j) {
+        const int pc = tid + 256 * j;
+        if (pc >= d / 8) break;
         uint32_t hi[8], lo[8];
         float sh = 0.f, sl = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const double uv = a.fused ? (v[i] / den) * (double)a.gamma[8 * pc + i] : v[i];
+            const double v = (double)xv[j][i];
+            const double uv = a.fused ? (v / den) * (double)gv[j][i] : v;
             const float uf = a.act_bf16 ? bf16_to_f32(f64_to_bf16(uv)) : (float)uv;
             hi[i] = f32_to_bf16(uf);
             lo[i] = f32_to_bf16(uf - bf16_to_f32(hi[i]));
             sh += bf16_to_f32(hi[i]);
             sl += bf16_to_f32(lo[i]);
         }
-        *(u32x4*)(a.u_pk + (size_t)t * (d / 2) + 4 * pc) =
-            u32x4{hi[0] | (hi[4] << 16), hi[1] | (hi[5] << 16), hi[2] | (hi[6] << 16), hi[3] | (hi[7] << 16)};
+        const u32x4 hv = u32x4{hi[0] | (hi[4] << 16), hi[1] | (hi[5] << 16), hi[2] | (hi[6] << 16), hi[3] | (hi[7] << 16)};
+        *(u32x4*)(a.u_pk + (size_t)t * (d / 2) + 4 * pc) = hv;
         if (a.u_pk_lo)
             *(u32x4*)(a.u_pk_lo + (size_t)t * (d / 2) + 4 * pc) =
                 u32x4{lo[0] | (lo[4] << 16), lo[1] | (lo[5] << 16), lo[2] | (lo[6] << 16), lo[3] | (lo[7] << 16)};
         if (a.u_frag)
             // block (t / 16, pc / 4), lane 16 (pc mod 4) + t mod 16
-            *(u32x4*)(a.u_frag + ((size_t)(t >> 4) * (d / 32) + (pc >> 2)) * 256 + ((pc & 3) * 16 + (t & 15)) * 4) =
-                u32x4{hi[0] | (hi[4] << 16), hi[1] | (hi[5] << 16), hi[2] | (hi[6] << 16), hi[3] | (hi[7] << 16)};
+            *(u32x4*)(a.u_frag + ((size_t)(t >> 4) * (d / 32) + (pc >> 2)) * 256 + ((pc & 3) * 16 + (t & 15)) * 4) = hv;
         // the chunk's 4 pieces are 4 consecutive lanes
         sh += __shfl_xor(sh, 1, 64);
         sh += __shfl_xor(sh, 2, 64);
@@ -95,7 +107,7 @@ __global__ void __launch_bounds__(256) k_prologue(PrologueArgs a) {
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
-    if (a.d % 64 || a.n_tok <= 0) return hipErrorInvalidValue;
+    if (a.d % 64 || a.d > 8 * 256 * kProPieces || a.n_tok <= 0) return hipErrorInvalidValue;
     const int per = ((a.n_tok + 7) / 8 + 7) / 8 * 8;
     hipLaunchKernelGGL(k_prologue, dim3(8 * per), dim3(256), 0, s, a);
     return hipGetLastError();
