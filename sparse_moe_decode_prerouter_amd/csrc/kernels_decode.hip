@@ -126,6 +126,7 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
+constexpr int kSortPre = 2;                   // assignments per thread whose routing is loaded up front
 
 constexpr size_t kSortLdsMax = 159 * 1024;
 // the assignments' experts stay in LDS between the passes when they fit
@@ -170,43 +171,86 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     while ((1 << nbits) < E) ++nbits;
     for (int i = tid; i < kSortWaves * E; i += kSortThreads) wcnt[i] = 0;
     const bool own_topk = a.self_topk && a.route_idx;
-    if (own_topk) {
-        // top-k of the self-routed rows, straight into the used routing: a
-        // wave checks 64 rows per load and takes each self-routed one in turn
-        for (int base = wave * 64; base < a.n_tok; base += kSortThreads) {
-            const int t = base + lane;
-            unsigned long long m = __ballot(t < a.n_tok && (t < a.route_shift ||
-                                                              a.route_idx[(size_t)(t - a.route_shift) * a.k] < 0));
-            while (m) {
-                const int tt = base + __ffsll((long long)m) - 1;
-                m &= m - 1;
-                if (E <= 64) topk_row<1>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.used_idx, a.used_w);
-                else if (E <= 128) topk_row<2>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.used_idx, a.used_w);
-                else topk_row<4>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.used_idx, a.used_w);
-                if (lane < a.k) {
-                    // lane j wrote selection j just above
-                    const int i = tt * a.k + lane;
-                    const int e = a.used_idx[i];
-                    const float w = a.used_w[i];
-                    if (a.user_used_idx) a.user_used_idx[i] = e;
-                    if (a.user_used_w) a.user_used_w[i] = w;
-                    if (cache_e) se[i] = e;
-                }
+    // Loads first, waits later. This thread's first kSortPre assignments: the
+    // given routing entry and weight, the row's first entry (negative: the
+    // row self-routes), and the self-routing result of an earlier launch.
+    int pe[kSortPre], pf[kSortPre], ps[kSortPre];
+    float pw[kSortPre], psw[kSortPre];
+#pragma unroll
+    for (int j = 0; j < kSortPre; ++j) {
+        const int i = tid + kSortThreads * j;
+        pe[j] = -1; pf[j] = -1; ps[j] = -1; pw[j] = 0.f; psw[j] = 0.f;
+        if (i < n) {
+            const int t = i / a.k;
+            if (a.route_idx && t >= a.route_shift) {
+                const size_t gi = (size_t)i - (size_t)a.route_shift * a.k;
+                pe[j] = a.route_idx[gi];
+                pw[j] = a.route_w[gi];
+                pf[j] = a.route_idx[gi - (size_t)(i % a.k)];
             }
+            if (!own_topk && a.self_idx) { ps[j] = a.self_idx[i]; psw[j] = a.self_w[i]; }
         }
     }
-    for (int i = tid; i < n; i += kSortThreads) {
-        const int t = i / a.k;
-        const size_t gi = (size_t)i - (size_t)a.route_shift * a.k;   // the given routing's entry (t >= shift)
-        const bool self = !a.route_idx || t < a.route_shift || a.route_idx[gi - (size_t)(i % a.k)] < 0;
-        if (self && own_topk) continue;      // written by the top-k above
-        int e = self ? a.self_idx[i] : a.route_idx[gi];
-        const float w = self ? a.self_w[i] : a.route_w[gi];
+    // the first 64-row window's row entries for this wave's own top-k
+    int wf0 = 0;
+    if (own_topk) {
+        const int t = wave * 64 + lane;
+        if (t >= a.route_shift && t < a.n_tok) wf0 = a.route_idx[(size_t)(t - a.route_shift) * a.k];
+    }
+    auto place = [&](int i, int e, float w) {
         if (e < 0 || e >= E) { set_err(a.err, ERR_BAD_INDEX); e = -1; }
         a.used_idx[i] = e; a.used_w[i] = w;
         if (a.user_used_idx) a.user_used_idx[i] = e;
         if (a.user_used_w) a.user_used_w[i] = w;
         if (cache_e) se[i] = e;
+    };
+    if (own_topk) {
+        // top-k of the self-routed rows, straight into the used routing (the
+        // selection stays in lanes 0 .. k-1)
+        auto own_row = [&](int tt) {
+            TopkSel sel;
+            if (E <= 64) sel = topk_row<1>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.used_idx, a.used_w);
+            else if (E <= 128) sel = topk_row<2>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.used_idx, a.used_w);
+            else sel = topk_row<4>(false, a.logits_r, E, a.k, tt, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.used_idx, a.used_w);
+            if (lane < a.k) {
+                const int i = tt * a.k + lane;
+                if (a.user_used_idx) a.user_used_idx[i] = sel.idx;
+                if (a.user_used_w) a.user_used_w[i] = sel.w;
+                if (cache_e) se[i] = sel.idx;
+            }
+        };
+        // rows before the shift have no given routing: no read to wait for
+        const int nsh = min(a.route_shift, a.n_tok);
+        for (int tt = wave; tt < nsh; tt += kSortWaves) own_row(tt);
+        // the others: a wave checks 64 rows at a time and takes each
+        // self-routed one in turn
+        for (int base = wave * 64; base < a.n_tok; base += kSortThreads) {
+            const int t = base + lane;
+            int f = wf0;
+            if (base != wave * 64) f = t >= a.route_shift && t < a.n_tok ? a.route_idx[(size_t)(t - a.route_shift) * a.k] : 0;
+            unsigned long long m = __ballot(t >= a.route_shift && t < a.n_tok && f < 0);
+            while (m) {
+                const int tt = base + __ffsll((long long)m) - 1;
+                m &= m - 1;
+                own_row(tt);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kSortPre; ++j) {
+        const int i = tid + kSortThreads * j;
+        if (i >= n) break;
+        const int t = i / a.k;
+        const bool self = !a.route_idx || t < a.route_shift || pf[j] < 0;
+        if (self && own_topk) continue;      // written by the top-k above
+        place(i, self ? ps[j] : pe[j], self ? psw[j] : pw[j]);
+    }
+    for (int i = tid + kSortThreads * kSortPre; i < n; i += kSortThreads) {
+        const int t = i / a.k;
+        const size_t gi = (size_t)i - (size_t)a.route_shift * a.k;   // the given routing's entry (t >= shift)
+        const bool self = !a.route_idx || t < a.route_shift || a.route_idx[gi - (size_t)(i % a.k)] < 0;
+        if (self && own_topk) continue;      // written by the top-k above
+        place(i, self ? a.self_idx[i] : a.route_idx[gi], self ? a.self_w[i] : a.route_w[gi]);
     }
     __threadfence_block();
     __syncthreads();                         // the experts are read below by other threads

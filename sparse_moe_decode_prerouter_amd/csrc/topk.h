@@ -6,9 +6,44 @@
 
 namespace moe {
 
+// (v, i) becomes the best of (v, i) and the pair of lane l - S (mod 16)
+// in this lane's row of 16 (a DPP row rotation: no trip through the LDS
+// crossbar, which every other lane shuffle takes)
+template <int S>
+__device__ __forceinline__ void best_row_ror(double& v, int& i) {
+    constexpr int kCtrl = 0x120 + S;          // row_ror:S
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, kCtrl, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), kCtrl, 0xF, 0xF, false);
+    const int oi = __builtin_amdgcn_update_dpp(0, i, kCtrl, 0xF, 0xF, false);
+    const double ov = __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// every lane ends with the best (v, i) of the wave: rotations by 1, 2, 4
+// and 8 cover each row of 16 lanes, two shuffles join the four rows
+__device__ __forceinline__ void wave_best(double& v, int& i) {
+    best_row_ror<1>(v, i);
+    best_row_ror<2>(v, i);
+    best_row_ror<4>(v, i);
+    best_row_ror<8>(v, i);
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+        const double ov = __shfl_xor(v, o, 64);
+        const int oi = __shfl_xor(i, o, 64);
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+}
+
+// lane j < k: the j-th selection and its weight (as also written out)
+struct TopkSel {
+    int idx;
+    float w;
+};
+
 // PER logits per lane (E <= 64 * PER), held in registers with fixed indices.
 template <int PER>
-__device__ __forceinline__ void topk_row(bool coherent, const double* logits, int E, int k, int t, const float* bias,
+__device__ __forceinline__ TopkSel topk_row(bool coherent, const double* logits, int E, int k, int t, const float* bias,
                                 const float* mc, const int32_t* hc, const float* mp, const int32_t* hp,
                                 int32_t* out_idx, float* out_w) {
     const int lane = threadIdx.x & 63;
@@ -57,11 +92,7 @@ __device__ __forceinline__ void topk_row(bool coherent, const double* logits, in
             const int e = lane + 64 * m;
             if (e < E && better(v[m], e, bv, bi)) { bv = v[m]; bi = e; }
         }
-        for (int o = 32; o > 0; o >>= 1) {
-            const double ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
+        wave_best(bv, bi);
         if (lane == j) { my_v = bv; my_i = bi; }
 #pragma unroll
         for (int m = 0; m < PER; ++m)
@@ -72,10 +103,12 @@ __device__ __forceinline__ void topk_row(bool coherent, const double* logits, in
     const double ex = lane < k ? exp(my_v - top) : 0.0;
     double ssum = 0.0;
     for (int j = 0; j < k; ++j) ssum += __shfl(ex, j, 64);
+    const float wsel = (float)(ex / ssum);
     if (lane < k) {
         out_idx[(size_t)t * k + lane] = my_i;
-        out_w[(size_t)t * k + lane] = (float)(ex / ssum);
+        out_w[(size_t)t * k + lane] = wsel;
     }
+    return TopkSel{my_i, wsel};
 }
 
 // MAXPER bounds the register arrays instantiated (E <= 64 * MAXPER).
