@@ -127,6 +127,7 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kSortPre = 2;                   // assignments per thread whose routing is loaded up front
+constexpr int kSortMC = 4;                    // 64-assignment steps per wave whose expert matches pass 2 reuses
 
 constexpr size_t kSortLdsMax = 159 * 1024;
 // the assignments' experts stay in LDS between the passes when they fit
@@ -156,13 +157,17 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     __shared__ int wsum[kSortWaves], wact[kSortWaves], wt16[kSortWaves], wt64[kSortWaves];
     __shared__ int tot_valid, tot_active, tot16, tot64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // blob of expert `tid` for the tile records (E <= kSortThreads), loaded early
+    // up to 256 experts, four threads per expert (thread 4 e + q takes waves
+    // 4 q .. 4 q + 3 of expert e) in the scan below; else one per expert
+    const bool quad = 4 * E <= kSortThreads;
+    const int my_e = quad ? tid >> 2 : tid;
+    // blob of expert my_e for the tile records, loaded early
     int my_blob = -1;
-    if ((a.tiles16 || a.tiles64) && a.resolve_blobs && tid < E) {
-        if (!a.ev.slot_of) my_blob = tid;
+    if ((a.tiles16 || a.tiles64) && a.resolve_blobs && my_e < E) {
+        if (!a.ev.slot_of) my_blob = my_e;
         else {
-            const int sl = a.ev.slot_of[tid];
-            my_blob = (sl < 0 || (a.ev.slot_tag && a.ev.slot_tag[sl] != tid)) ? -1 : sl;
+            const int sl = a.ev.slot_of[my_e];
+            my_blob = (sl < 0 || (a.ev.slot_tag && a.ev.slot_tag[sl] != my_e)) ? -1 : sl;
         }
     }
     int* se = sm + (kSortWaves + 1) * E;     // [n] experts of the assignments (when cache_e)
@@ -188,7 +193,7 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
                 pw[j] = a.route_w[gi];
                 pf[j] = a.route_idx[gi - (size_t)(i % a.k)];
             }
-            if (!own_topk && a.self_idx) { ps[j] = a.self_idx[i]; psw[j] = a.self_w[i]; }
+            if ((!own_topk || t < a.pre_rows) && a.self_idx) { ps[j] = a.self_idx[i]; psw[j] = a.self_w[i]; }
         }
     }
     // the first 64-row window's row entries for this wave's own top-k
@@ -220,8 +225,9 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
             }
         };
         // rows before the shift have no given routing: no read to wait for
+        // (the first pre_rows of them came with the routing GEMM)
         const int nsh = min(a.route_shift, a.n_tok);
-        for (int tt = wave; tt < nsh; tt += kSortWaves) own_row(tt);
+        for (int tt = a.pre_rows + wave; tt < nsh; tt += kSortWaves) own_row(tt);
         // the others: a wave checks 64 rows at a time and takes each
         // self-routed one in turn
         for (int base = wave * 64; base < a.n_tok; base += kSortThreads) {
@@ -242,14 +248,14 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
         if (i >= n) break;
         const int t = i / a.k;
         const bool self = !a.route_idx || t < a.route_shift || pf[j] < 0;
-        if (self && own_topk) continue;      // written by the top-k above
+        if (self && own_topk && t >= a.pre_rows) continue;      // written by the top-k above
         place(i, self ? ps[j] : pe[j], self ? psw[j] : pw[j]);
     }
     for (int i = tid + kSortThreads * kSortPre; i < n; i += kSortThreads) {
         const int t = i / a.k;
         const size_t gi = (size_t)i - (size_t)a.route_shift * a.k;   // the given routing's entry (t >= shift)
         const bool self = !a.route_idx || t < a.route_shift || a.route_idx[gi - (size_t)(i % a.k)] < 0;
-        if (self && own_topk) continue;      // written by the top-k above
+        if (self && own_topk && t >= a.pre_rows) continue;      // written by the top-k above
         place(i, self ? a.self_idx[i] : a.route_idx[gi], self ? a.self_w[i] : a.route_w[gi]);
     }
     __threadfence_block();
@@ -257,30 +263,61 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     const int chunk = ((n + kSortWaves - 1) / kSortWaves + 63) / 64 * 64;
     const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
     const unsigned long long lt = (1ull << lane) - 1;
-    // pass 1: counts per (wave, expert)
-    for (int base = c0; base < c1; base += 64) {
+    // pass 1: counts per (wave, expert); the first kSortMC steps' matches
+    // are kept for pass 2
+    unsigned long long mcache[kSortMC];
+    int ecache[kSortMC];
+    for (int base = c0, it = 0; base < c1; base += 64, ++it) {
         const int i = base + lane;
         const int e = i < c1 ? (cache_e ? se[i] : a.used_idx[i]) : -1;
         const unsigned long long m = match_expert(e, e >= 0, nbits);
+#pragma unroll
+        for (int j = 0; j < kSortMC; ++j)
+            if (it == j) { mcache[j] = m; ecache[j] = e; }
         if (m && (m & lt) == 0) wcnt[wave * E + e] += __popcll(m);
     }
     __syncthreads();
     // scan over waves per expert, then over experts
+    static_assert(kSortWaves == 16, "four quarters of four waves");
+    const int qq = tid & 3;                   // quad: this thread's quarter of the waves
+    int qv[4] = {0, 0, 0, 0}, xs = 0;         // quad: counts of its waves, its quarter's offset in the expert
     const int per = (E + kSortThreads - 1) / kSortThreads;
     const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
     int c = 0, na = 0, n16 = 0, n64 = 0;
-    for (int e = e0; e < e1; ++e) {
-        int run = 0;
-        for (int w = 0; w < kSortWaves; ++w) {
-            const int v = wcnt[w * E + e];
-            wcnt[w * E + e] = run;
-            run += v;
+    if (quad) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qv[j] = my_e < E ? wcnt[(4 * qq + j) * E + my_e] : 0;
+        const int run = qv[0] + qv[1] + qv[2] + qv[3];
+        int inc = run;                        // inclusive scan over the quad
+        {
+            const int t1 = __shfl_up(inc, 1, 4);
+            if (qq >= 1) inc += t1;
+            const int t2 = __shfl_up(inc, 2, 4);
+            if (qq >= 2) inc += t2;
         }
-        cnt[e] = run;
-        c += run;
-        na += run > 0;
-        n16 += (run + 15) >> 4;
-        n64 += (run + 63) >> 6;
+        xs = inc - run;
+        const int tot_e = __shfl(inc, (lane & ~3) | 3, 64);
+        if (qq == 0) {
+            c = tot_e;
+            na = tot_e > 0;
+            n16 = (tot_e + 15) >> 4;
+            n64 = (tot_e + 63) >> 6;
+            if (my_e < E) cnt[my_e] = tot_e;
+        }
+    } else {
+        for (int e = e0; e < e1; ++e) {
+            int run = 0;
+            for (int w = 0; w < kSortWaves; ++w) {
+                const int v = wcnt[w * E + e];
+                wcnt[w * E + e] = run;
+                run += v;
+            }
+            cnt[e] = run;
+            c += run;
+            na += run > 0;
+            n16 += (run + 15) >> 4;
+            n64 += (run + 63) >> 6;
+        }
     }
     int ic = c, ia = na, i16 = n16, i64 = n64;
     for (int o = 1; o < 64; o <<= 1) {
@@ -302,27 +339,44 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     __syncthreads();
     int o1 = wsum[wave] + ic - c, o2 = wact[wave] + ia - na;
     int q16 = wt16[wave] + i16 - n16, q64 = wt64[wave] + i64 - n64;
-    for (int e = e0; e < e1; ++e) {
-        for (int w = 0; w < kSortWaves; ++w) wcnt[w * E + e] += o1;
-        const int ce = cnt[e];
-        if (ce > 0) {
-            a.active[o2] = e;
-            a.act_off[o2] = o1;
-            // tile records of this expert (my_blob belongs to expert tid == e)
-            if (a.tiles16 || a.tiles64) {
-                if (my_blob < 0 && a.resolve_blobs) set_err(a.err, ERR_NOT_STAGED);
-                if (a.tiles16)
-                    for (int i = 0; i * 16 < ce; ++i)
-                        *(int4*)(a.tiles16 + 4 * (q16 + i)) = make_int4(o2, o1 + 16 * i, min(16, ce - 16 * i), my_blob);
-                if (a.tiles64)
-                    for (int i = 0; i * 64 < ce; ++i)
-                        *(int4*)(a.tiles64 + 4 * (q64 + i)) = make_int4(o2, o1 + 64 * i, min(64, ce - 64 * i), my_blob);
-            }
-            ++o2;
+    // the tile records of expert e (my_blob belongs to it), first position o1
+    auto expert_records = [&](int e, int ce, int o1e, int o2e, int q16e, int q64e) {
+        a.active[o2e] = e;
+        a.act_off[o2e] = o1e;
+        if (a.tiles16 || a.tiles64) {
+            if (my_blob < 0 && a.resolve_blobs) set_err(a.err, ERR_NOT_STAGED);
+            if (a.tiles16)
+                for (int i = 0; i * 16 < ce; ++i)
+                    *(int4*)(a.tiles16 + 4 * (q16e + i)) = make_int4(o2e, o1e + 16 * i, min(16, ce - 16 * i), my_blob);
+            if (a.tiles64)
+                for (int i = 0; i * 64 < ce; ++i)
+                    *(int4*)(a.tiles64 + 4 * (q64e + i)) = make_int4(o2e, o1e + 64 * i, min(64, ce - 64 * i), my_blob);
         }
-        o1 += ce;
-        q16 += (ce + 15) >> 4;
-        q64 += (ce + 63) >> 6;
+    };
+    if (quad) {
+        // the expert's first position comes from its q = 0 thread
+        const int base = __shfl(o1, lane & ~3, 64) + xs;
+        if (my_e < E) {
+            int run = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                wcnt[(4 * qq + j) * E + my_e] = base + run;
+                run += qv[j];
+            }
+            if (qq == 0 && c > 0) expert_records(my_e, c, o1, o2, q16, q64);
+        }
+    } else {
+        for (int e = e0; e < e1; ++e) {
+            for (int w = 0; w < kSortWaves; ++w) wcnt[w * E + e] += o1;
+            const int ce = cnt[e];
+            if (ce > 0) {
+                expert_records(e, ce, o1, o2, q16, q64);
+                ++o2;
+            }
+            o1 += ce;
+            q16 += (ce + 15) >> 4;
+            q64 += (ce + 63) >> 6;
+        }
     }
     if (a.tiles16 || a.tiles64) {
         // the shared expert's token tiles follow the routed ones
@@ -345,10 +399,18 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
     }
     __syncthreads();
     // pass 2: place
-    for (int base = c0; base < c1; base += 64) {
+    for (int base = c0, it = 0; base < c1; base += 64, ++it) {
         const int i = base + lane;
-        const int e = i < c1 ? (cache_e ? se[i] : a.used_idx[i]) : -1;
-        const unsigned long long m = match_expert(e, e >= 0, nbits);
+        int e = -1;
+        unsigned long long m = 0;
+        bool hit = false;
+#pragma unroll
+        for (int j = 0; j < kSortMC; ++j)
+            if (it == j) { e = ecache[j]; m = mcache[j]; hit = true; }
+        if (!hit) {
+            e = i < c1 ? (cache_e ? se[i] : a.used_idx[i]) : -1;
+            m = match_expert(e, e >= 0, nbits);
+        }
         if (m) {
             a.perm[wcnt[wave * E + e] + __popcll(m & lt)] = i;
         }

@@ -1224,22 +1224,45 @@ __global__ void __launch_bounds__(64 * kFrWaves) k_route_mm_fr(RouteMMArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
     __syncthreads();
-    if (wave > 0) return;
-#pragma unroll 1
-    for (int w = 0; w < kFrWaves - 1; ++w)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] += red[w][v][lane];
+    // router rows of the first token tile when it holds rows before the shift
+    const bool pre = set == 0 && blockIdx.y == 0 && a.pre_rows > 0;
     const int r = 16 * rt + ml;                          // row within its set
-    if (r >= fs.rows(set)) return;
+    if (wave == 0 && r < fs.rows(set)) {
+#pragma unroll 1
+        for (int w = 0; w < kFrWaves - 1; ++w)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int t = t0 + 4 * pc + v;
-        if (t >= T) continue;
-        const double z = acc[v];
-        if (set == 0) a.logits_r[(size_t)t * a.E + r] = z;
-        else if (set == 1) a.logits_h[(size_t)t * a.En + r] = z;
-        else if (set == 2) a.au[(size_t)t * a.r + r] = (float)z;
-        else a.sgate[t] = (float)(1.0 / (1.0 + exp(-z)));
+            for (int v = 0; v < 4; ++v) acc[v] += red[w][v][lane];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int t = t0 + 4 * pc + v;
+            if (t >= T) continue;
+            const double z = acc[v];
+            if (set == 0) {
+                if (pre) st_dev(a.logits_r + (size_t)t * a.E + r, z);   // read by another block below
+                else a.logits_r[(size_t)t * a.E + r] = z;
+            } else if (set == 1) a.logits_h[(size_t)t * a.En + r] = z;
+            else if (set == 2) a.au[(size_t)t * a.r + r] = (float)z;
+            else a.sgate[t] = (float)(1.0 / (1.0 + exp(-z)));
+        }
+    }
+    if (!pre) return;
+    // the last of these blocks to finish takes the top-k of rows 0 .. pre_rows-1
+    // (device-scope stores, waited for, then a relaxed device-scope count:
+    // the last block reads every block's logits with coherent loads)
+    __shared__ int is_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = old == (unsigned)fs.tiles(0) - 1;
+        if (is_last) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!is_last) return;
+    for (int t = wave; t < a.pre_rows; t += kFrWaves) {
+        if (a.E <= 64) topk_row<1>(true, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
+        else if (a.E <= 128) topk_row<2>(true, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
+        else topk_row<4>(true, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
     }
 }
 
@@ -1381,7 +1404,9 @@ __global__ void __launch_bounds__(256) k_route_topk(RouteMMArgs a, int job0) {
     }
 }
 
-hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk) {
+hipError_t launch_route_mm(const RouteMMArgs& a_in, hipStream_t s, bool router_topk, bool head_topk, int* pre_done) {
+    RouteMMArgs a = a_in;
+    if (pre_done) *pre_done = 0;
     if (a.d % 128) return hipErrorInvalidValue;
     const int R = (a.router ? a.E : 0) + (a.head ? a.En : 0) + (a.lora_a ? a.r : 0) + (a.sgate_w ? 1 : 0);
     if (R > 0) {
@@ -1392,8 +1417,13 @@ hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s, bool router_topk
                                dim3(256), 0, s, a);
         else if (a.u_frag && !a.u_pk_lo && a.d % (32 * kFrWaves) == 0 && (!a.router || a.wf_router) &&
                  (!a.head || a.wf_head) && (!a.lora_a || a.wf_lora) && (!a.sgate_w || a.wf_sgate)) {
+            // the top-k of the rows before the shift, when asked for and possible
+            if (!(a.pre_rows > 0 && a.pre_rows <= 16 && a.router && a.E <= 256 && a.counter && a.self_idx)) a.pre_rows = 0;
+            if (a.pre_rows > a.n_tok) a.pre_rows = a.n_tok;
             hipLaunchKernelGGL(k_route_mm_fr, dim3(fr_sets(a).total(), (a.n_tok + 15) / 16), dim3(64 * kFrWaves), 0, s, a);
+            if (pre_done) *pre_done = a.pre_rows;
         } else {
+            a.pre_rows = 0;
             const dim3 grid((R + 15) / 16, (a.n_tok + 15) / 16);
             if (a.u_pk_lo) hipLaunchKernelGGL((k_route_mm<1, 1, 4, true>), grid, dim3(256), 0, s, a);
             else hipLaunchKernelGGL((k_route_mm<1, 1, 4, false>), grid, dim3(256), 0, s, a);

@@ -337,10 +337,14 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     // count is large); otherwise the sort takes the few self-routed rows. The
     // head's top-k runs beside the combine on the matrix-core path
     const bool sort_topk = io->route_idx != nullptr && L->w.router != nullptr && D.n_experts <= kSortTopkMaxE;
-    HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm));
+    // rows before the shift self-route: their top-k rides on the routing GEMM
+    ra.pre_rows = sort_topk ? std::min(route_shift, n_tok) : 0;
+    ra.counter = L->s.counters + 3;
+    int pre_done = 0;
+    HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm, &pre_done));
 
     SortArgs sa{};
-    sa.route_idx = io->route_idx; sa.route_w = io->route_w; sa.route_shift = route_shift;
+    sa.route_idx = io->route_idx; sa.route_w = io->route_w; sa.route_shift = route_shift; sa.pre_rows = pre_done;
     sa.self_idx = L->w.router ? L->s.self_idx : nullptr; sa.self_w = L->s.self_w;
     sa.n_tok = n_tok; sa.k = D.top_k; sa.E = D.n_experts;
     sa.used_idx = L->s.used_idx; sa.used_w = L->s.used_w;

@@ -173,13 +173,18 @@ struct RouteMMArgs {
     // the plain pointer above is)
     const uint32_t* u_frag;
     const uint32_t* wf_router; const uint32_t* wf_head; const uint32_t* wf_lora; const uint32_t* wf_sgate;
+    // rows 0 .. pre_rows-1 (before the routing shift; at most 16, E <= 256):
+    // the last router block of the first token tile takes their top-k into
+    // self_idx / self_w (fragment-order kernel only); counter: zero between calls
+    int pre_rows; uint32_t* counter;
 };
 // pack n bf16 rows of length d into MFMA fragment order (rows padded to 16)
 hipError_t launch_pack_rows(const uint16_t* w, int n, int d, uint32_t* out, hipStream_t s);
 inline size_t frag_rows_words(int n, int d) { return (size_t)((n + 15) / 16) * 16 * d / 2; }
 // router_topk: top-k of the self-routed rows here (else the sort does it);
 // head_topk: the head's top-k here (else the combine launch does it)
-hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk);
+// *pre_done: how many of the requested a.pre_rows rows got their top-k here
+hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk, int* pre_done);
 
 // A head top-k run by a later launch than the one that wrote its logits
 // (only for E_next <= 64 * kDeferMaxPer; larger heads keep their own launch).
@@ -194,6 +199,7 @@ constexpr int kSortTopkMaxE = 256;
 struct SortArgs {
     const int32_t* route_idx; const float* route_w; int32_t* self_idx; float* self_w;
     int route_shift;                    // 1: token t takes row t - 1 of the given routing, token 0 self-routes
+    int pre_rows;                       // rows whose top-k an earlier launch wrote to self_idx / self_w
     int n_tok; int k; int E;
     int32_t* used_idx; float* used_w; int32_t* user_used_idx; float* user_used_w;
     int32_t* meta; int32_t* active; int32_t* act_off; int32_t* perm;

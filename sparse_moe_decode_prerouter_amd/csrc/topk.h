@@ -41,25 +41,30 @@ struct TopkSel {
     float w;
 };
 
-// PER logits per lane (E <= 64 * PER), held in registers with fixed indices.
+// PER logits per lane (E <= 64 * PER), held in registers with fixed indices:
+// lane l holds experts l + 64 m. topk_load issues the loads (logits and
+// bias) and topk_select waits for them, so a caller can issue them early.
 template <int PER>
-__device__ __forceinline__ TopkSel topk_row(bool coherent, const double* logits, int E, int k, int t, const float* bias,
-                                const float* mc, const int32_t* hc, const float* mp, const int32_t* hp,
-                                int32_t* out_idx, float* out_w) {
+__device__ __forceinline__ void topk_load(bool coherent, const double* logits, int E, int t, const float* bias,
+                                          double (&v)[PER], float (&b)[PER]) {
     const int lane = threadIdx.x & 63;
-    double v[PER];
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
         const int e = lane + 64 * m;
         const int ec = e < E ? e : 0;
         v[m] = coherent ? ld_dev(logits + (size_t)t * E + ec) : logits[(size_t)t * E + ec];
+        b[m] = bias ? bias[ec] : 0.f;
     }
+}
+
+template <int PER>
+__device__ __forceinline__ TopkSel topk_select(double (&v)[PER], const float (&b)[PER], int E, int k, int t,
+                                               const float* bias, const float* mc, const int32_t* hc, const float* mp,
+                                               const int32_t* hp, int32_t* out_idx, float* out_w) {
+    const int lane = threadIdx.x & 63;
     if (bias) {
 #pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            const int e = lane + 64 * m;
-            v[m] += (double)bias[e < E ? e : 0];
-        }
+        for (int m = 0; m < PER; ++m) v[m] += (double)b[m];
     }
     // history terms: each distinct valid expert of the previous routings adds its row
     for (int src = 0; src < 2; ++src) {
@@ -109,6 +114,16 @@ __device__ __forceinline__ TopkSel topk_row(bool coherent, const double* logits,
         out_w[(size_t)t * k + lane] = wsel;
     }
     return TopkSel{my_i, wsel};
+}
+
+template <int PER>
+__device__ __forceinline__ TopkSel topk_row(bool coherent, const double* logits, int E, int k, int t, const float* bias,
+                                const float* mc, const int32_t* hc, const float* mp, const int32_t* hp,
+                                int32_t* out_idx, float* out_w) {
+    double v[PER];
+    float b[PER];
+    topk_load<PER>(coherent, logits, E, t, bias, v, b);
+    return topk_select<PER>(v, b, E, k, t, bias, mc, hc, mp, hp, out_idx, out_w);
 }
 
 // MAXPER bounds the register arrays instantiated (E <= 64 * MAXPER).
