@@ -6,6 +6,8 @@ batch 1 and 4, resident and streamed (pinned host store -> HBM slab), plus a
 ragged prefill. Routing indices must match exactly (ties: lowest index);
 block outputs within max rel-L2 2e-3 per token.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -25,9 +27,12 @@ def run_oracle(lw, x, route, fused, pred=True):
     return oracle.decode_layer(lw, x, route, lw.k if pred else None, fused_norm=fused)
 
 
-def check_layer(shape, n_tok, *, fused, given_route, resident=True, seed=0, prefill=False):
-    say(f"{shape.name} n_tok={n_tok} fused={fused} given_route={given_route} resident={resident} prefill={prefill}")
+def check_layer(shape, n_tok, *, fused, given_route, resident=True, seed=0, prefill=False, gate_fixed=False):
+    say(f"{shape.name} n_tok={n_tok} fused={fused} given_route={given_route} resident={resident} prefill={prefill}"
+        f" gate_fixed={gate_fixed}")
     w = layer_tensors(shape, layer=seed)
+    if gate_fixed:
+        w["shared_gate"] = None      # the shared expert's gate is fixed at 1
     lw = oracle_layer(shape, w)
     x = synth.activations(shape, n_tok, ("layer", seed, n_tok), dtype=torch.float32 if fused else None)
     route = None
@@ -139,3 +144,18 @@ def test_prefill_streamed(given_route):
 
 def test_tiny_prefill():
     check_layer(synth.TINY, 9, fused=True, given_route=True, prefill=True, seed=12)
+
+
+@pytest.mark.parametrize("prefill", [True, False])
+@pytest.mark.parametrize("variant", ["no_lora", "no_shared", "gate_fixed"])
+def test_layer_without_branch(variant, prefill):
+    """A layer without LoRA, without a shared expert, or with the shared
+    gate fixed at 1: prefill (the routing GEMM packs each row set in tiles of
+    its own 16 rows, one of them now empty) and a 4-token decode."""
+    shape = synth.LAYER35B
+    if variant == "no_lora":
+        shape = dataclasses.replace(shape, name="layer_d2048_e256_k4_nolora", r=0)
+    elif variant == "no_shared":
+        shape = dataclasses.replace(shape, name="layer_d2048_e256_k4_noshared", fs=0)
+    check_layer(shape, 21 if prefill else 4, fused=True, given_route=True, prefill=prefill, seed=14,
+                gate_fixed=variant == "gate_fixed")
