@@ -58,7 +58,9 @@ def kernel_b_bytes(shape, k):
 
 KA_SOURCES = ("sparse_moe_decode_prerouter_amd/csrc/kernels_deca.hip",
               "sparse_moe_decode_prerouter_amd/csrc/dec_common.h",
-              "sparse_moe_decode_prerouter_amd/csrc/device_common.h")
+              "sparse_moe_decode_prerouter_amd/csrc/device_common.h",
+              "sparse_moe_decode_prerouter_amd/csrc/moe_internal.h",
+              "sparse_moe_decode_prerouter_amd/csrc/topk.h")
 KA_TRAFFIC = "profiles/k_dec_a_hbm_traffic_40layer_decode_bs1.txt"
 
 
