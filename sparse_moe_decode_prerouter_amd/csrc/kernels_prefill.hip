@@ -882,29 +882,25 @@ __global__ void __launch_bounds__(64 * NW) k_pf_gateup_big(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kCombTok = 4;
 
-__global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
+// the head's top-k of token t (one wave)
+__device__ __forceinline__ void head_topk_wave(const PrefillArgs& a, int t) {
+    const TopkJob& j = a.head;
+    if (j.En <= 64) topk_row<1>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+    else if (j.En <= 128) topk_row<2>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+    else if (j.En <= 256) topk_row<4>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+    else if (j.En <= 512) topk_row<8>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+    else topk_row<16>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
+}
+
+// y of tokens t0 .. t0 + nt - 1 at columns n .. n + 3: gated shared expert, the
+// routed outputs in routing order, LoRA B, residual
+template <int NT>
+__device__ __forceinline__ void combine_cols(const PrefillArgs& a, int t0, int nt, int n, float4 (&y)[NT]) {
     const GemvArgs& g = a.g;
-    const int gy = (g.n_tok + kCombTok - 1) / kCombTok;
-    if ((int)blockIdx.y >= gy) {
-        // the head's top-k for the next layer: one token per wave
-        const TopkJob& j = a.head;
-        const int t = (((int)blockIdx.y - gy) * (int)gridDim.x + (int)blockIdx.x) * 4 + (int)(threadIdx.x >> 6);
-        if (t >= g.n_tok) return;
-        if (j.En <= 64) topk_row<1>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
-        else if (j.En <= 128) topk_row<2>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
-        else if (j.En <= 256) topk_row<4>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
-        else if (j.En <= 512) topk_row<8>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
-        else topk_row<16>(false, j.logits, j.En, j.kn, t, j.bias, j.mc, j.hc, j.mp, j.hp, j.pred_idx, j.pred_w);
-        return;
-    }
-    const int d = g.d, n = (blockIdx.x * 256 + threadIdx.x) * 4;
-    const int t0 = blockIdx.y * kCombTok;
-    if (n >= d) return;
-    const int nt = min(kCombTok, g.n_tok - t0);
-    float4 y[kCombTok];
+    const int d = g.d;
     const bool sh = g.fs && g.ev.shared;
 #pragma unroll
-    for (int tt = 0; tt < kCombTok; ++tt) {
+    for (int tt = 0; tt < NT; ++tt) {
         const int t = t0 + (tt < nt ? tt : 0);
         y[tt] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (sh) {
@@ -914,18 +910,18 @@ __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
         }
     }
     for (int j = 0; j < g.k; ++j) {
-        float4 o[kCombTok];
-        float w[kCombTok];
-        bool v[kCombTok];
+        float4 o[NT];
+        float w[NT];
+        bool v[NT];
 #pragma unroll
-        for (int tt = 0; tt < kCombTok; ++tt) {
+        for (int tt = 0; tt < NT; ++tt) {
             const int aid = (t0 + (tt < nt ? tt : 0)) * g.k + j;
             v[tt] = a.used_idx[aid] >= 0;            // an invalid entry's row was never written
             w[tt] = a.used_w[aid];
             o[tt] = *(const float4*)(a.ob + (size_t)aid * d + n);
         }
 #pragma unroll
-        for (int tt = 0; tt < kCombTok; ++tt) {
+        for (int tt = 0; tt < NT; ++tt) {
             if (!v[tt]) continue;
             y[tt].x += w[tt] * o[tt].x; y[tt].y += w[tt] * o[tt].y;
             y[tt].z += w[tt] * o[tt].z; y[tt].w += w[tt] * o[tt].w;
@@ -933,9 +929,9 @@ __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
     }
     if (g.lora_b && g.r) {
         const int r = g.r;
-        float l[kCombTok][4];
+        float l[NT][4];
 #pragma unroll
-        for (int tt = 0; tt < kCombTok; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) l[tt][i] = 0.f;
         if (r % 8 == 0 && r <= 32) {
@@ -949,7 +945,7 @@ __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
             for (int c = 0; c < 4; ++c) {
                 if (8 * c >= r) break;
 #pragma unroll
-                for (int tt = 0; tt < kCombTok; ++tt) {
+                for (int tt = 0; tt < NT; ++tt) {
                     const float* au = g.au + (size_t)(t0 + (tt < nt ? tt : 0)) * r + 8 * c;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -968,7 +964,7 @@ __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) wq[i] = bf16_to_f32(g.lora_b[(size_t)(n + i) * r + q]);
 #pragma unroll
-                for (int tt = 0; tt < kCombTok; ++tt) {
+                for (int tt = 0; tt < NT; ++tt) {
                     const float u = g.au[(size_t)(t0 + (tt < nt ? tt : 0)) * r + q];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) l[tt][i] += wq[i] * u;
@@ -976,23 +972,142 @@ __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
             }
         }
 #pragma unroll
-        for (int tt = 0; tt < kCombTok; ++tt) {
+        for (int tt = 0; tt < NT; ++tt) {
             y[tt].x += g.lora_scale * l[tt][0]; y[tt].y += g.lora_scale * l[tt][1];
             y[tt].z += g.lora_scale * l[tt][2]; y[tt].w += g.lora_scale * l[tt][3];
         }
     }
     if (g.fused) {
-        float4 x[kCombTok];
+        float4 x[NT];
 #pragma unroll
-        for (int tt = 0; tt < kCombTok; ++tt) x[tt] = *(const float4*)(g.x + (size_t)(t0 + (tt < nt ? tt : 0)) * d + n);
+        for (int tt = 0; tt < NT; ++tt) x[tt] = *(const float4*)(g.x + (size_t)(t0 + (tt < nt ? tt : 0)) * d + n);
 #pragma unroll
-        for (int tt = 0; tt < kCombTok; ++tt) {
+        for (int tt = 0; tt < NT; ++tt) {
             y[tt].x += x[tt].x; y[tt].y += x[tt].y; y[tt].z += x[tt].z; y[tt].w += x[tt].w;
         }
     }
+}
+
+__global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
+    const GemvArgs& g = a.g;
+    const int gy = (g.n_tok + kCombTok - 1) / kCombTok;
+    if ((int)blockIdx.y >= gy) {
+        // the head's top-k for the next layer: one token per wave
+        const int t = (((int)blockIdx.y - gy) * (int)gridDim.x + (int)blockIdx.x) * 4 + (int)(threadIdx.x >> 6);
+        if (t >= g.n_tok) return;
+        head_topk_wave(a, t);
+        return;
+    }
+    const int d = g.d, n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int t0 = blockIdx.y * kCombTok;
+    if (n >= d) return;
+    const int nt = min(kCombTok, g.n_tok - t0);
+    float4 y[kCombTok];
+    combine_cols<kCombTok>(a, t0, nt, n, y);
 #pragma unroll
     for (int tt = 0; tt < kCombTok; ++tt)
         if (tt < nt) *(float4*)(g.y + (size_t)(t0 + tt) * d + n) = y[tt];
+}
+
+// ---------------------------------------------------------------------------
+// The combine with the next stacked layer's prologue: a block holds whole rows
+// (d <= 4 kCnThreads) of kCnTok tokens, so once it has x + y it also takes
+// that layer's RMSNorm (fp64 sum of squares over the block, u rounded once)
+// and writes its u in the prologue's three forms (GEMV-order pairs with their
+// lo parts, fragment order, 32-chunk sums, each piece summed in element
+// order), and the next layer launches no prologue. Head top-k blocks (one
+// token per wave) follow the combine blocks.
+// ---------------------------------------------------------------------------
+constexpr int kCnThreads = 512;
+constexpr int kCnTok = 1;                     // tokens per block
+constexpr int kCnMaxTok = 128;                // calls of at most this many tokens take the fused form
+
+__global__ void __launch_bounds__(kCnThreads) k_pf_combine_norm(PrefillArgs a) {
+    const GemvArgs& g = a.g;
+    const PrologueArgs& p = a.nxt;
+    __shared__ double red[kCnTok][kCnThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gy = (g.n_tok + kCnTok - 1) / kCnTok;
+    if ((int)blockIdx.x >= gy) {
+        const int t = ((int)blockIdx.x - gy) * (kCnThreads / 64) + wave;
+        if (t < g.n_tok) head_topk_wave(a, t);
+        return;
+    }
+    const int d = g.d, n = tid * 4;
+    const int t0 = blockIdx.x * kCnTok;
+    const int nt = min(kCnTok, g.n_tok - t0);
+    const bool act = n < d;                   // threads past d only take part in the reductions
+    float4 y[kCnTok];
+#pragma unroll
+    for (int tt = 0; tt < kCnTok; ++tt) y[tt] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (act) {
+        combine_cols<kCnTok>(a, t0, nt, n, y);
+#pragma unroll
+        for (int tt = 0; tt < kCnTok; ++tt)
+            if (tt < nt) *(float4*)(g.y + (size_t)(t0 + tt) * d + n) = y[tt];
+    }
+    float4 gm = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (act) gm = *(const float4*)(p.gamma + n);
+#pragma unroll
+    for (int tt = 0; tt < kCnTok; ++tt) {
+        double ss = (double)y[tt].x * y[tt].x;
+        ss += (double)y[tt].y * y[tt].y;
+        ss += (double)y[tt].z * y[tt].z;
+        ss += (double)y[tt].w * y[tt].w;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        if (lane == 0) red[tt][wave] = ss;
+    }
+    __syncthreads();
+    const int pc = n >> 3;                    // 8-element piece; even threads hold its first half
+#pragma unroll
+    for (int tt = 0; tt < kCnTok; ++tt) {
+        if (tt >= nt) break;                  // block-uniform
+        const int t = t0 + tt;
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < kCnThreads / 64; ++w) tot += red[tt][w];
+        const double den = sqrt(tot / (double)d + (double)p.eps);
+        const float xv[4] = {y[tt].x, y[tt].y, y[tt].z, y[tt].w};
+        const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double uv = ((double)xv[i] / den) * (double)gv[i];
+            const float uf = p.act_bf16 ? bf16_to_f32(f64_to_bf16(uv)) : (float)uv;
+            hi[i] = f32_to_bf16(uf);
+            lo[i] = f32_to_bf16(uf - bf16_to_f32(hi[i]));
+        }
+        uint32_t ho[4], lw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ho[i] = (uint32_t)__shfl_xor((int)hi[i], 1, 64);
+            lw[i] = (uint32_t)__shfl_xor((int)lo[i], 1, 64);
+        }
+        // the piece's sums in element order, then over the chunk's 4 pieces
+        float sh = 0.f, sl = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sh += bf16_to_f32(hi[i]); sl += bf16_to_f32(lo[i]); }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sh += bf16_to_f32(ho[i]); sl += bf16_to_f32(lw[i]); }
+        sh += __shfl_xor(sh, 2, 64);
+        sh += __shfl_xor(sh, 4, 64);
+        sl += __shfl_xor(sl, 2, 64);
+        sl += __shfl_xor(sl, 4, 64);
+        if (act && (tid & 1) == 0) {
+            const u32x4 hv = u32x4{hi[0] | (ho[0] << 16), hi[1] | (ho[1] << 16), hi[2] | (ho[2] << 16), hi[3] | (ho[3] << 16)};
+            *(u32x4*)(p.u_pk + (size_t)t * (d / 2) + 4 * pc) = hv;
+            if (p.u_pk_lo)
+                *(u32x4*)(p.u_pk_lo + (size_t)t * (d / 2) + 4 * pc) =
+                    u32x4{lo[0] | (lw[0] << 16), lo[1] | (lw[1] << 16), lo[2] | (lw[2] << 16), lo[3] | (lw[3] << 16)};
+            if (p.u_frag)
+                *(u32x4*)(p.u_frag + ((size_t)(t >> 4) * (d / 32) + (pc >> 2)) * 256 + ((pc & 3) * 16 + (t & 15)) * 4) = hv;
+            if ((n & 31) == 0) {
+                p.usum[(size_t)t * (d / 32) + (n >> 5)] = sh;
+                if (p.usum_lo) p.usum_lo[(size_t)t * (d / 32) + (n >> 5)] = sl;
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1481,11 +1596,26 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         // combine blocks, then the head top-k blocks (one token per wave)
-        const int gx = (g.d + 1023) / 1024, gy = (g.n_tok + kCombTok - 1) / kCombTok;
-        const int gt = a.head.pred_idx ? ((g.n_tok + 3) / 4 + gx - 1) / gx : 0;
-        hipLaunchKernelGGL(k_pf_combine, dim3(gx, gy + gt), dim3(256), 0, s, a);
+        if (combine_norm_ok(a)) {
+            const int gy = (g.n_tok + kCnTok - 1) / kCnTok;
+            const int gt = a.head.pred_idx ? (g.n_tok + kCnThreads / 64 - 1) / (kCnThreads / 64) : 0;
+            hipLaunchKernelGGL(k_pf_combine_norm, dim3(gy + gt), dim3(kCnThreads), 0, s, a);
+        } else {
+            const int gy = (g.n_tok + kCombTok - 1) / kCombTok;
+            const int gx = (g.d + 1023) / 1024;
+            const int gt = a.head.pred_idx ? ((g.n_tok + 3) / 4 + gx - 1) / gx : 0;
+            hipLaunchKernelGGL(k_pf_combine, dim3(gx, gy + gt), dim3(256), 0, s, a);
+        }
     }
     return hipGetLastError();
+}
+
+bool combine_norm_ok(const PrefillArgs& a) {
+    const PrologueArgs& p = a.nxt;
+    // measured: one launch instead of two pays for 32 tokens (batched decode
+    // 2.37 against 2.48 ms per 40-layer step), not for 512 (6.86 against 6.77 ms)
+    return p.u_pk && p.usum && p.gamma && p.fused && a.g.fused && p.d == a.g.d && p.n_tok == a.g.n_tok &&
+           a.g.d % 32 == 0 && a.g.d <= 4 * kCnThreads && a.g.n_tok <= kCnMaxTok;
 }
 
 bool prefill_big_tiles(int d, int f, int fs, bool act_lo, int n_tok, int k, int max_active) {

@@ -199,19 +199,25 @@ __global__ void k_merge_route(const int32_t* ridx, const int32_t* sidx, int32_t*
     dst[i] = (ridx && ridx[(size_t)t * k] >= 0) ? ridx[i] : sidx[i];
 }
 
-int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill, int route_shift = 0);
+// nxt: the next stacked layer's prologue for this call's combine to take
+// (*took_nxt tells whether it did); skip_pro: this layer's prologue was taken
+// by the previous layer's combine
+int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill, int route_shift = 0,
+                const PrologueArgs* nxt = nullptr, bool skip_pro = false, bool* took_nxt = nullptr);
 
 // defer_in: a previous layer's head top-k to run inside this layer's K_A.
 // defer_out (stack mode): this layer's head top-k is not run here but handed
 // back, for the next layer's K_A to run (its prediction is for the next step).
 int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const TopkJob* defer_in = nullptr,
-               TopkJob* defer_out = nullptr) {
+               TopkJob* defer_out = nullptr, const PrologueArgs* nxt = nullptr, bool skip_pro = false,
+               bool* took_nxt = nullptr) {
     const moe_layer_desc& D = L->desc;
     if (defer_out) defer_out->pred_idx = nullptr;
+    if (took_nxt) *took_nxt = false;
     // shapes outside the fused two-kernel path take the general grouped-GEMM path
     if (!dec_fast_path_ok(D.d_model, D.d_ff, D.d_ff_shared, n_tok, D.top_k)) {
         if (defer_in && defer_in->pred_idx) HIPCHK(launch_topk_job(*defer_in, n_tok, st));
-        return run_prefill(L, io, n_tok, st, false);
+        return run_prefill(L, io, n_tok, st, false, 0, nxt, skip_pro, took_nxt);
     }
     const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
     if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
@@ -295,13 +301,11 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
 
 // route_shift = 1: io->route_idx / route_w hold the previous layer's
 // predictions by token; token t takes row t - 1 and token 0 self-routes
-int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill, int route_shift) {
+PrologueArgs prologue_args(const moe_layer* L, const void* x, int n_tok) {
     const moe_layer_desc& D = L->desc;
     const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
-    if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
-
     PrologueArgs pa{};
-    pa.x = io->x_in;
+    pa.x = x;
     pa.x_is_bf16 = (!fused && D.act_dtype == MOE_ACT_BF16) ? 1 : 0;
     pa.fused = fused;
     pa.gamma = L->w.norm_gamma;
@@ -311,7 +315,17 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     pa.n_tok = n_tok;
     pa.u_pk = L->s.u_pk; pa.u_pk_lo = L->s.u_pk_lo; pa.usum = L->s.usum; pa.usum_lo = L->s.usum_lo;
     pa.u_frag = L->s.u_frag;
-    HIPCHK(launch_prologue(pa, st));
+    return pa;
+}
+
+int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill, int route_shift,
+                const PrologueArgs* nxt, bool skip_pro, bool* took_nxt) {
+    const moe_layer_desc& D = L->desc;
+    const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
+    if (took_nxt) *took_nxt = false;
+    if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
+
+    if (!skip_pro) HIPCHK(launch_prologue(prologue_args(L, io->x_in, n_tok), st));
 
     RouteMMArgs ra{};
     ra.u_pk = L->s.u_pk; ra.u_pk_lo = L->s.u_pk_lo; ra.d = D.d_model; ra.n_tok = n_tok;
@@ -401,6 +415,11 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
         if (io->pred_idx && L->w.head)
             pf.head = TopkJob{L->s.logits_h, D.next_n_experts, D.next_top_k, L->w.head_bias, L->w.hist_cur, io->hist_cur,
                               L->w.hist_prev, io->hist_prev, io->pred_idx, io->pred_w};
+        if (nxt) {
+            pf.nxt = *nxt;
+            if (!combine_norm_ok(pf)) pf.nxt = PrologueArgs{};
+            else if (took_nxt) *took_nxt = true;
+        }
         if (reactive) HIPCHK(launch_tile_blobs(pf, big, st));
         HIPCHK(launch_prefill(pf, st));
     } else {
@@ -625,6 +644,7 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
     const size_t per = (size_t)n_tok * k;
     if (n_tok * k > 4096 || n_tok > 256) return MOE_E_UNSUPPORTED;
     TopkJob pend{};
+    bool pro_done = false;                   // this layer's prologue was taken by the previous combine
     for (int l = 0; l < S->n; ++l) {
         moe_layer* L = S->layers[l];
         moe_io io{};
@@ -644,10 +664,14 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
         int rc = check_io(L, &io, n_tok);
         if (rc != MOE_OK) return rc;
         TopkJob out{};
+        PrologueArgs nxt{};
+        if (l + 1 < S->n) nxt = prologue_args(S->layers[l + 1], x_out, n_tok);
+        bool took = false;
         rc = run_decode(L, &io, n_tok, (hipStream_t)stream, pend.pred_idx ? &pend : nullptr,
-                        l + 1 < S->n ? &out : nullptr);
+                        l + 1 < S->n ? &out : nullptr, l + 1 < S->n ? &nxt : nullptr, pro_done, &took);
         if (rc != MOE_OK) return rc;
         pend = out;
+        pro_done = took;
     }
     if (pend.pred_idx) HIPCHK(launch_topk_job(pend, n_tok, (hipStream_t)stream));
     return MOE_OK;
@@ -660,6 +684,7 @@ int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, floa
     const size_t per = (size_t)n_tok * k;
     hipStream_t st = (hipStream_t)stream;
     if (per > S->pred_cap) return MOE_E_INVALID;
+    bool pro_done = false;                   // this layer's prologue was taken by the previous combine
     for (int l = 0; l < S->n; ++l) {
         moe_layer* L = S->layers[l];
         moe_io io{};
@@ -680,8 +705,12 @@ int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, floa
         }
         int rc = check_io(L, &io, n_tok);
         if (rc != MOE_OK) return rc;
-        rc = run_prefill(L, &io, n_tok, st, true, l > 0 ? 1 : 0);
+        PrologueArgs nxt{};
+        if (l + 1 < S->n) nxt = prologue_args(S->layers[l + 1], x, n_tok);
+        bool took = false;
+        rc = run_prefill(L, &io, n_tok, st, true, l > 0 ? 1 : 0, l + 1 < S->n ? &nxt : nullptr, pro_done, &took);
         if (rc != MOE_OK) return rc;
+        pro_done = took;
     }
     return MOE_OK;
 }

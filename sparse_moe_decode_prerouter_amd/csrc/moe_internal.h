@@ -242,7 +242,10 @@ struct PrefillArgs {
     float* ob; float* obs;               // down outputs: [T*k][d] by assignment, [T][d] shared
     const int32_t* used_idx; const float* used_w;
     TopkJob head;                        // the head's top-k, run beside the combine (pred_idx null: none)
+    PrologueArgs nxt;                    // the next stacked layer's prologue, taken by the combine (u_pk null: none)
 };
+// whether the combine takes a.nxt (the next layer then launches no prologue)
+bool combine_norm_ok(const PrefillArgs& a);
 int prefill_max_tiles(int T, int K, int E, int tm = 16);
 bool prefill_mm_ok(int d, int f, int fs);
 // whether the gate/up projection takes 64-token tiles (many tokens per expert)

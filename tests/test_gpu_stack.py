@@ -136,15 +136,18 @@ def test_stack_free_running():
     assert compared >= steps * B // 2
 
 
-def test_stack_prefill():
-    """moe_stack_prefill through 3 layers at 37 tokens (the grouped-GEMM path):
-    layer 0 self-routes every token; layer l >= 1 routes token i by head l-1 on
-    token i-1 (shifted inside the call) and token 0 self-routes. The oracle is
-    fed the routing the GPU used, so every block output is compared; every
-    routing decision the GPU made (its self-routed rows and its predictions)
-    is checked against the oracle's logits (certified near ties counted)."""
+@pytest.mark.parametrize("T", [37, 150])
+def test_stack_prefill(T):
+    """moe_stack_prefill through 3 layers (the grouped-GEMM path): layer 0
+    self-routes every token; layer l >= 1 routes token i by head l-1 on token
+    i-1 (shifted inside the call) and token 0 self-routes. At 37 tokens each
+    combine also takes the next layer's RMSNorm prologue; at 150 the layers
+    run their own. The oracle is fed the routing the GPU used, so every block
+    output is compared; every routing decision the GPU made (its self-routed
+    rows and its predictions) is checked against the oracle's logits
+    (certified near ties counted)."""
     shape = synth.LAYER35B
-    L_, T = 3, 37
+    L_ = 3
     say(f"stack prefill L={L_} T={T}")
     ws = [layer_tensors(shape, layer=l, tag="spf") for l in range(L_)]
     ora = [oracle_layer(shape, w) for w in ws]
