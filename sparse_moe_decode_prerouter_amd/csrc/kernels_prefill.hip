@@ -1016,7 +1016,7 @@ __global__ void __launch_bounds__(256) k_pf_combine(PrefillArgs a) {
 // and writes its u in the prologue's three forms (GEMV-order pairs with their
 // lo parts, fragment order, 32-chunk sums, each piece summed in element
 // order), and the next layer launches no prologue. Head top-k blocks (one
-// token per wave) follow the combine blocks.
+// token per wave) come before the combine blocks.
 // ---------------------------------------------------------------------------
 constexpr int kCnThreads = 512;
 constexpr int kCnTok = 1;                     // tokens per block
@@ -1027,14 +1027,15 @@ __global__ void __launch_bounds__(kCnThreads) k_pf_combine_norm(PrefillArgs a) {
     const PrologueArgs& p = a.nxt;
     __shared__ double red[kCnTok][kCnThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int gy = (g.n_tok + kCnTok - 1) / kCnTok;
-    if ((int)blockIdx.x >= gy) {
-        const int t = ((int)blockIdx.x - gy) * (kCnThreads / 64) + wave;
+    // head top-k blocks first (they run longest), then the combine blocks
+    const int gt = a.head.pred_idx ? (g.n_tok + kCnThreads / 64 - 1) / (kCnThreads / 64) : 0;
+    if ((int)blockIdx.x < gt) {
+        const int t = (int)blockIdx.x * (kCnThreads / 64) + wave;
         if (t < g.n_tok) head_topk_wave(a, t);
         return;
     }
     const int d = g.d, n = tid * 4;
-    const int t0 = blockIdx.x * kCnTok;
+    const int t0 = ((int)blockIdx.x - gt) * kCnTok;
     const int nt = min(kCnTok, g.n_tok - t0);
     const bool act = n < d;                   // threads past d only take part in the reductions
     float4 y[kCnTok];
@@ -1613,7 +1614,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
 bool combine_norm_ok(const PrefillArgs& a) {
     const PrologueArgs& p = a.nxt;
     // measured: one launch instead of two pays for 32 tokens (batched decode
-    // 2.37 against 2.48 ms per 40-layer step), not for 512 (6.86 against 6.77 ms)
+    // 2.36 against 2.48 ms per 40-layer step); at 512 tokens the two forms tie
     return p.u_pk && p.usum && p.gamma && p.fused && a.g.fused && p.d == a.g.d && p.n_tok == a.g.n_tok &&
            a.g.d % 32 == 0 && a.g.d <= 4 * kCnThreads && a.g.n_tok <= kCnMaxTok;
 }
