@@ -177,6 +177,18 @@ class _BlobsOnDemand:
         return self.cache[e]
 
 
+def _oracle_layer_dev(shape, w, has_head):
+    """Oracle weights of a layer whose tensors live on the GPU (expert blobs
+    copied on demand)."""
+    return oracle.LayerWeights(
+        d=shape.d, E=shape.E, k=shape.k, f=shape.f, fs=shape.fs, r=shape.r, alpha=shape.alpha, eps=shape.eps,
+        act=shape.act, store=_BlobsOnDemand(w["store"].view(shape.E, shape.blob_bytes)),
+        shared=w["shared"].cpu().numpy(), shared_gate=synth.bf16_bits(w["shared_gate"].cpu()),
+        lora_a=synth.bf16_bits(w["lora_a"].cpu()), lora_b=synth.bf16_bits(w["lora_b"].cpu()),
+        gamma=w["gamma"].double().cpu().numpy(),
+        head=synth.bf16_bits(w["head"].cpu()) if has_head else None, router=synth.bf16_bits(w["router"].cpu()))
+
+
 def test_decode_stack_40_layers():
     """The benchmarked configuration at full size: 40 layers of the 35B shape
     (16.9 GiB of int4 experts resident), batch 1, the stack decode the bench
@@ -194,15 +206,7 @@ def test_decode_stack_40_layers():
     ws = [synth.layer_weights(shape, l, device="cuda", tag="full40") for l in range(L_)]
     gpus = [gpu_layer(shape, w, fused=True, max_tokens=B, head=(l + 1 < L_))
             for l, w in enumerate(ws)]
-    ora = []
-    for l, w in enumerate(ws):
-        ora.append(oracle.LayerWeights(
-            d=shape.d, E=shape.E, k=shape.k, f=shape.f, fs=shape.fs, r=shape.r, alpha=shape.alpha, eps=shape.eps,
-            act=shape.act, store=_BlobsOnDemand(w["store"].view(shape.E, shape.blob_bytes)),
-            shared=w["shared"].cpu().numpy(), shared_gate=synth.bf16_bits(w["shared_gate"].cpu()),
-            lora_a=synth.bf16_bits(w["lora_a"].cpu()), lora_b=synth.bf16_bits(w["lora_b"].cpu()),
-            gamma=w["gamma"].double().cpu().numpy(),
-            head=synth.bf16_bits(w["head"].cpu()) if l + 1 < L_ else None, router=synth.bf16_bits(w["router"].cpu())))
+    ora = [_oracle_layer_dev(shape, w, l + 1 < L_) for l, w in enumerate(ws)]
     stack = moe.MoeStack(gpus)
     xs = np.stack([synth.activations(shape, B, ("full40", t), dtype=torch.float32).double().numpy()
                    for t in range(steps)])
@@ -240,6 +244,74 @@ def test_decode_stack_40_layers():
         compared += 1
     assert compared >= 1
     say(f"  certified near-tie flips: {flips}")
+    stack.close()
+    for Lr in gpus:
+        Lr.close()
+
+
+def test_stack_prefill_40_layers_sampled():
+    """The benchmarked prefill at full size: 512 tokens through the 40-layer
+    stack (layer l >= 1 routes token i by head l-1 on token i-1, token 0
+    self-routes; layer 0 self-routes every token). Sampled tokens go through
+    the oracle with the routing the GPU used (a token's trajectory depends on
+    no other token then); every self-routed row and prediction of theirs is
+    checked against the oracle's logits (certified near ties counted), and
+    their outputs after 40 layers within rel-L2 1e-2. The one-token shift is
+    checked on every token."""
+    import sparse_moe_decode_prerouter_amd as moe
+    shape = synth.LAYER35B
+    L_, T, k = 40, 512, synth.LAYER35B.k
+    sample = [0, 1, 77, 255, 256, 511]
+    say(f"40-layer stack prefill T={T} sampled tokens {sample}")
+    ws = [synth.layer_weights(shape, l, device="cuda", tag="pf40") for l in range(L_)]
+    gpus = [gpu_layer(shape, w, fused=True, max_tokens=T, head=(l + 1 < L_)) for l, w in enumerate(ws)]
+    stack = moe.MoeStack(gpus)
+    x0 = synth.activations(shape, T, ("pf40",), dtype=torch.float32)
+    xg = x0.cuda().contiguous()
+    used_i = torch.empty((L_, T, k), dtype=torch.int32, device="cuda")
+    used_w = torch.empty((L_, T, k), dtype=torch.float32, device="cuda")
+    pred_i = torch.full((L_, T, k), -7, dtype=torch.int32, device="cuda")
+    pred_w = torch.zeros((L_, T, k), dtype=torch.float32, device="cuda")
+    stack.prefill(xg, used_idx=used_i, used_w=used_w, pred_idx=pred_i, pred_w=pred_w)
+    torch.cuda.synchronize()
+    for Lr in gpus:
+        assert Lr.status() == 0
+    ui, uw = used_i.cpu().numpy(), used_w.cpu().numpy()
+    pi, pw = pred_i.cpu().numpy(), pred_w.cpu().numpy()
+    x = x0.double().numpy()[sample]
+    flips, wdev = 0, 0.0
+    for l in range(L_):
+        if l > 0:
+            assert np.array_equal(ui[l][1:], pi[l][:-1]), l
+            assert np.array_equal(uw[l][1:], pw[l][:-1]), l
+        lw = _oracle_layer_dev(shape, ws[l], l + 1 < L_)
+        nk = k if l + 1 < L_ else None
+        x_next, y, u, used, pred, z = oracle.decode_layer(
+            lw, x, (ui[l][sample].astype(np.int64), uw[l][sample].astype(np.float64)), nk, fused_norm=True)
+        for i, t in enumerate(sample):
+            if l == 0 or t == 0:
+                zr = oracle.head_logits(lw.router, u[i], lw.router_bias)
+                ref, ref_w = oracle.route(zr, k)
+                if not np.array_equal(ui[l][t], ref):
+                    assert logit_gap_ok(zr, k, ui[l][t], ref, NEAR_TIE), (l, t)
+                    flips += 1
+                elif l == 0:
+                    # the same input on both sides
+                    assert np.allclose(uw[l][t], ref_w, rtol=1e-6, atol=1e-7), (l, t)
+                else:
+                    # from each side's own residual stream, which drift apart by up to
+                    # the stack tolerance over depth: the weights agree to that bound
+                    dev = float(np.max(np.abs(uw[l][t] - ref_w) / np.maximum(np.abs(ref_w), 1e-3)))
+                    wdev = max(wdev, dev)
+                    assert dev <= STACK_TOL, (l, t, dev)
+            if nk and not np.array_equal(pi[l + 1][t], pred[0][i]):
+                assert logit_gap_ok(z[i], k, pi[l + 1][t], pred[0][i], NEAR_TIE), (l, t)
+                flips += 1
+        x = x_next
+    err = rel_l2_rows(xg.double().cpu().numpy()[sample], x)
+    say(f"  sampled outputs after {L_} layers rel-L2 {err:.2e}; certified near-tie flips {flips}; "
+        f"self-routed weights past layer 0 within {wdev:.1e}")
+    assert err <= STACK_TOL
     stack.close()
     for Lr in gpus:
         Lr.close()
