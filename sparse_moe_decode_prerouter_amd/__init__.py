@@ -62,7 +62,7 @@ class MoeError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m sparse_moe_decode_prerouter_amd.build` "
+            f"{LIB_PATH} is not built; run `python sparse_moe_decode_prerouter_amd/build.py` "
             "(or __graft_entry__.build()) first. There is no non-HIP path.")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
