@@ -165,7 +165,11 @@ size_t moe_expert_blob_bytes(int d_model, int d_ff, int group_size);
  * routing rows); 0 on invalid desc. */
 size_t moe_layer_workspace_bytes(const moe_layer_desc* desc);
 
-/* Create a layer on the current device. d_workspace: device memory of at
+/* Create a layer on the current device (one layer of the per-layer MoE block:
+ * 256 routed experts plus one shared expert, int4 affine group-64 weights --
+ * ai.info news article, section on the 35B version; the unmerged adapter of
+ * the guide's Method section, unmerged adapter execution; the prerouter head
+ * of the guide's Method section, prerouter head architecture). d_workspace: device memory of at
  * least moe_layer_workspace_bytes(desc), 256-byte aligned, owned by the
  * caller. The struct contents are copied; the pointers inside are kept.
  * Errors: MOE_E_INVALID (null/size), MOE_E_UNSUPPORTED (shape),
@@ -194,14 +198,17 @@ int moe_layer_slots(const moe_layer* layer, int32_t* h_slot_expert, int n_slots,
                     uint64_t* staged_bytes);
 
 /* Decode call for n_tok (1..max_tokens) independent tokens: grouped GEMV
- * path. Asynchronous on `stream` except the reactive read-back.
+ * path. The routing used is the prediction passed in (prediction-as-routing:
+ * guide, Key ideas and Key terms); the head's output is the next layer's
+ * routing at the next token (guide, Q&A: why one token ahead). Asynchronous on `stream` except the reactive read-back.
  * Errors (returned): MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_HIP. Device
  * errors (NOT_STAGED, BAD_INDEX) set a sticky flag read by
  * moe_layer_sync_status; the affected expert's contribution is dropped.    */
 int moe_decode_step(moe_layer* layer, const moe_io* io, int n_tok, void* stream);
 
 /* Prefill call for n_tok tokens of one sequence (or any rows): token-to-
- * expert sort/permute and int4->bf16 MFMA grouped GEMM. Same io contract;
+ * expert sort/permute and int4->bf16 MFMA grouped GEMM (the prefill of the
+ * ai.info news article's 35B section; the routing and head as in decode). Same io contract;
  * pred row i is the head on token i, i.e. the routing of the next layer for
  * token i+1 (the caller shifts it down by one row).                         */
 int moe_prefill(moe_layer* layer, const moe_io* io, int n_tok, void* stream);
@@ -221,10 +228,15 @@ void moe_layer_destroy(moe_layer* layer);
  * token t predicts the routing of layer l+1 at token t+1, and that
  * prediction is the routing. Launches only (no host synchronisation, no
  * allocation; in streamed mode the reactive layer-0 staging reads back), so
- * resident-mode calls can be captured into a HIP graph. moe_stack_create
- * allocates the prefill routing scratch (max_tokens * k entries); destroy
- * frees it.
+ * resident-mode calls can be captured into a HIP graph.
  *
+ * moe_stack_workspace_bytes: device scratch the stack needs (two prediction
+ *   buffers of min(max_tokens) * k entries for stack prefill calls without
+ *   caller prediction buffers); 0 if the layers do not form a valid stack.
+ * moe_stack_create: d_workspace is caller-owned device memory of at least
+ *   that size, 256-byte aligned, kept until destroy. The library allocates
+ *   only the host handle. Errors: MOE_E_INVALID (null, misaligned, layers
+ *   not chainable), MOE_E_CAPACITY (workspace too small).
  * moe_stack_decode: one decode step for n_tok independent sequences.
  *   x_in       device fp32 [n_tok][d]: step input (may equal x_out)
  *   x_out      device fp32 [n_tok][d]: residual stream after the last layer
@@ -240,14 +252,22 @@ void moe_layer_destroy(moe_layer* layer);
  * moe_stack_prefill: n_tok tokens of one sequence. Token i >= 1 at layer
  *   l >= 1 uses head l-1's prediction on token i-1 (shifted on the device);
  *   token 0 and layer 0 self-route. x is updated in place; used_* as above;
- *   pred_* (optional) receive each head's unshifted predictions.            */
+ *   pred_* (optional) receive each head's unshifted predictions; without
+ *   them the predictions pass through the stack's workspace.
+ * moe_stack_set_trace: with d_x_trace non-NULL (device fp32, n_floats), every
+ *   later stack call first copies layer l's input residual stream [n_tok][d]
+ *   to d_x_trace + l * n_tok * d (a device-to-device copy per layer, for
+ *   checking each layer on the input it saw); calls whose trace would not
+ *   fit return MOE_E_CAPACITY. NULL / 0 turns the trace off.              */
 typedef struct moe_stack moe_stack;
-int moe_stack_create(moe_layer* const* layers, int n_layers, moe_stack** out);
+size_t moe_stack_workspace_bytes(moe_layer* const* layers, int n_layers);
+int moe_stack_create(moe_layer* const* layers, int n_layers, void* d_workspace, size_t ws_bytes, moe_stack** out);
 int moe_stack_decode(moe_stack* st, const float* x_in, float* x_out, int n_tok,
                      const int32_t* route_idx, const float* route_w, int32_t* pred_idx, float* pred_w,
                      int32_t* used_idx, float* used_w, const int32_t* hist_prev, int first_step, void* stream);
 int moe_stack_prefill(moe_stack* st, float* x, int n_tok, int32_t* used_idx, float* used_w,
                       int32_t* pred_idx, float* pred_w, void* stream);
+int moe_stack_set_trace(moe_stack* st, float* d_x_trace, size_t n_floats);
 void moe_stack_destroy(moe_stack* st);
 
 /* ---- measurement --------------------------------------------------------

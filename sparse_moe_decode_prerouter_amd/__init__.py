@@ -79,7 +79,9 @@ def _load():
         "moe_status_str": (ctypes.c_char_p, [I]),
         "moe_last_hip_error": (I, []),
         "moe_plan_slots": (I, [P, I, P, I, I, P, P, P]),
-        "moe_stack_create": (I, [P, I, ctypes.POINTER(P)]),
+        "moe_stack_workspace_bytes": (Z, [P, I]),
+        "moe_stack_create": (I, [P, I, P, Z, ctypes.POINTER(P)]),
+        "moe_stack_set_trace": (I, [P, P, Z]),
         "moe_stack_decode": (I, [P, P, P, I, P, P, P, P, P, P, P, I, P]),
         "moe_stack_prefill": (I, [P, P, I, P, P, P, P, P]),
         "moe_stack_destroy": (None, [P]),
@@ -96,7 +98,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_expert_blob_bytes", "moe_layer_workspace_bytes", "moe_layer_create", "moe_stage_experts",
             "moe_layer_slots", "moe_decode_step", "moe_prefill", "moe_layer_sync_status", "moe_layer_destroy",
-            "moe_status_str", "moe_last_hip_error", "moe_plan_slots", "moe_stack_create", "moe_stack_decode",
+            "moe_status_str", "moe_last_hip_error", "moe_plan_slots", "moe_stack_workspace_bytes",
+            "moe_stack_create", "moe_stack_set_trace", "moe_stack_decode",
             "moe_stack_prefill", "moe_stack_destroy", "moe_layer_set_profiling", "moe_layer_kernel_ms")
 
 
@@ -178,13 +181,24 @@ def moe_plan_slots(resident: Sequence[int], wanted: Sequence[int], n_experts: in
     return list(res)[:n], [(cs[i], ce[i]) for i in range(nc.value)]
 
 
-def moe_stack_create(handles: Sequence[int]) -> int:
+def moe_stack_workspace_bytes(handles: Sequence[int]) -> int:
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    return _lib.moe_stack_workspace_bytes(arr, len(handles))
+
+
+def moe_stack_create(handles: Sequence[int], ws_ptr: int, ws_bytes: int) -> int:
     arr = (ctypes.c_void_p * len(handles))(*handles)
     h = ctypes.c_void_p()
-    rc = _lib.moe_stack_create(arr, len(handles), ctypes.byref(h))
+    rc = _lib.moe_stack_create(arr, len(handles), ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.byref(h))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_stack_create")
     return h.value
+
+
+def moe_stack_set_trace(stack: int, trace_ptr: Optional[int], n_floats: int) -> None:
+    rc = _lib.moe_stack_set_trace(stack, trace_ptr, n_floats)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stack_set_trace")
 
 
 def moe_stack_decode(stack: int, x_in: int, x_out: int, n_tok: int, route_idx: Optional[int],
@@ -329,10 +343,23 @@ class MoeStack:
     (moe_stack_decode). Routing buffers are [L][n_tok][k] device tensors; the
     step's predictions feed the next step, so callers rotate two buffers."""
 
-    def __init__(self, layers):
+    def __init__(self, layers, device="cuda"):
+        import torch
         self.layers = list(layers)
-        self.handle = moe_stack_create([L.handle for L in self.layers])
+        hs = [L.handle for L in self.layers]
+        nbytes = moe_stack_workspace_bytes(hs)
+        if nbytes == 0:
+            raise MoeError(MOE_E_INVALID, "moe_stack_workspace_bytes")
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        self.handle = moe_stack_create(hs, (self.workspace.data_ptr() + 255) // 256 * 256, nbytes)
         self.k = self.layers[0].top_k
+        self.trace = None
+
+    def set_trace(self, trace):
+        """trace: device fp32 tensor [n_layers, n_tok, d] receiving each layer's
+        input residual stream on later calls (None turns it off)."""
+        self.trace = trace
+        moe_stack_set_trace(self.handle, _ptr(trace), 0 if trace is None else trace.numel())
 
     def decode(self, x, route_idx, route_w, pred_idx, pred_w, *, x_out=None, used_idx=None, used_w=None,
                hist_prev=None, first_step=False, stream=None):

@@ -604,9 +604,8 @@ int moe_layer_kernel_ms(moe_layer* L, float* ms_router, float* ms_a, float* ms_b
     return MOE_OK;
 }
 
-int moe_stack_create(moe_layer* const* layers, int n, moe_stack** out) {
-    if (!out || !layers || n < 1) return MOE_E_INVALID;
-    *out = nullptr;
+static int validate_stack(moe_layer* const* layers, int n) {
+    if (!layers || n < 1) return MOE_E_INVALID;
     for (int l = 0; l < n; ++l) {
         const moe_layer* L = layers[l];
         if (!L) return MOE_E_INVALID;
@@ -617,21 +616,63 @@ int moe_stack_create(moe_layer* const* layers, int n, moe_stack** out) {
             return MOE_E_INVALID;
         if (!L->w.router) return MOE_E_INVALID;
     }
-    moe_stack* S = new (std::nothrow) moe_stack();
-    if (!S) return MOE_E_INVALID;
-    S->layers = new moe_layer*[n];
-    for (int l = 0; l < n; ++l) S->layers[l] = layers[l];
-    S->n = n;
-    // prefill scratch for the predictions passed between layers, sized by the
-    // smallest max_tokens
+    return MOE_OK;
+}
+
+// prediction entries per buffer: the smallest max_tokens times k
+static size_t stack_pred_entries(moe_layer* const* layers, int n) {
     int T = layers[0]->desc.max_tokens;
     for (int l = 1; l < n; ++l) T = std::min(T, layers[l]->desc.max_tokens);
-    const size_t per = (size_t)T * layers[0]->desc.top_k;
-    hipError_t e = hipMalloc(&S->d_pred_idx, per * sizeof(int32_t));
-    if (e == hipSuccess) e = hipMalloc(&S->d_pred_w, per * sizeof(float));
-    if (e != hipSuccess) { g_last_hip = (int)e; moe_stack_destroy(S); return MOE_E_HIP; }
-    S->pred_cap = per;
+    return (size_t)T * layers[0]->desc.top_k;
+}
+
+static size_t stack_carve(moe_layer* const* layers, int n, uint8_t* base, moe_stack* S) {
+    Carver c{base};
+    const size_t per = stack_pred_entries(layers, n);
+    for (int b = 0; b < 2; ++b) {
+        int32_t* pi = c.take<int32_t>(per);
+        float* pw = c.take<float>(per);
+        if (S) { S->d_pred_idx[b] = pi; S->d_pred_w[b] = pw; }
+    }
+    if (S) S->pred_cap = per;
+    return align_up(c.off, 256);
+}
+
+size_t moe_stack_workspace_bytes(moe_layer* const* layers, int n) {
+    if (validate_stack(layers, n) != MOE_OK) return 0;
+    return stack_carve(layers, n, nullptr, nullptr);
+}
+
+int moe_stack_create(moe_layer* const* layers, int n, void* d_workspace, size_t ws_bytes, moe_stack** out) {
+    if (!out) return MOE_E_INVALID;
+    *out = nullptr;
+    int rc = validate_stack(layers, n);
+    if (rc != MOE_OK) return rc;
+    if (!d_workspace || ((uintptr_t)d_workspace & 255)) return MOE_E_INVALID;
+    if (ws_bytes < stack_carve(layers, n, nullptr, nullptr)) return MOE_E_CAPACITY;
+    moe_stack* S = new (std::nothrow) moe_stack();
+    if (!S) return MOE_E_INVALID;
+    S->layers = new (std::nothrow) moe_layer*[n];
+    if (!S->layers) { delete S; return MOE_E_INVALID; }
+    for (int l = 0; l < n; ++l) S->layers[l] = layers[l];
+    S->n = n;
+    stack_carve(layers, n, (uint8_t*)d_workspace, S);
     *out = S;
+    return MOE_OK;
+}
+
+int moe_stack_set_trace(moe_stack* S, float* d_x_trace, size_t n_floats) {
+    if (!S || (n_floats && !d_x_trace)) return MOE_E_INVALID;
+    S->x_trace = n_floats ? d_x_trace : nullptr;
+    S->trace_cap = n_floats;
+    return MOE_OK;
+}
+
+// copy layer l's input residual stream into the trace (when one is set)
+static int trace_layer(moe_stack* S, int l, const void* x, int n_tok, hipStream_t st) {
+    if (!S->x_trace) return MOE_OK;
+    const size_t per = (size_t)n_tok * S->layers[0]->desc.d_model;
+    HIPCHK(hipMemcpyAsync(S->x_trace + (size_t)l * per, x, per * sizeof(float), hipMemcpyDeviceToDevice, st));
     return MOE_OK;
 }
 
@@ -642,7 +683,8 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
     if (!first_step && (!route_idx || !route_w)) return MOE_E_INVALID;
     const int k = S->layers[0]->desc.top_k;
     const size_t per = (size_t)n_tok * k;
-    if (n_tok * k > 4096 || n_tok > 256) return MOE_E_UNSUPPORTED;
+    if (n_tok < 1 || n_tok * k > 4096 || n_tok > 256) return MOE_E_UNSUPPORTED;
+    if (S->x_trace && (size_t)S->n * n_tok * S->layers[0]->desc.d_model > S->trace_cap) return MOE_E_CAPACITY;
     TopkJob pend{};
     bool pro_done = false;                   // this layer's prologue was taken by the previous combine
     for (int l = 0; l < S->n; ++l) {
@@ -662,6 +704,8 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
             io.hist_prev = hist_prev ? hist_prev + (l + 1) * per : nullptr;
         }
         int rc = check_io(L, &io, n_tok);
+        if (rc != MOE_OK) return rc;
+        rc = trace_layer(S, l, io.x_in, n_tok, (hipStream_t)stream);
         if (rc != MOE_OK) return rc;
         TopkJob out{};
         PrologueArgs nxt{};
@@ -684,6 +728,7 @@ int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, floa
     const size_t per = (size_t)n_tok * k;
     hipStream_t st = (hipStream_t)stream;
     if (per > S->pred_cap) return MOE_E_INVALID;
+    if (S->x_trace && (size_t)S->n * n_tok * S->layers[0]->desc.d_model > S->trace_cap) return MOE_E_CAPACITY;
     bool pro_done = false;                   // this layer's prologue was taken by the previous combine
     for (int l = 0; l < S->n; ++l) {
         moe_layer* L = S->layers[l];
@@ -692,18 +737,21 @@ int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, floa
         io.y_out = x;
         if (l > 0) {
             // the previous layer's predictions by token, shifted by one token
-            // inside the call (token 0 self-routes); they are read before this
-            // call's own predictions overwrite the shared buffer
-            io.route_idx = pred_idx ? pred_idx + l * per : S->d_pred_idx;
-            io.route_w = pred_w ? pred_w + l * per : S->d_pred_w;
+            // inside the call (token 0 self-routes); without caller buffers
+            // they sit in scratch buffer (l - 1) & 1 while this layer writes
+            // its own into the other one
+            io.route_idx = pred_idx ? pred_idx + l * per : S->d_pred_idx[(l - 1) & 1];
+            io.route_w = pred_w ? pred_w + l * per : S->d_pred_w[(l - 1) & 1];
         }
         io.used_idx = used_idx ? used_idx + l * per : nullptr;
         io.used_w = used_w ? used_w + l * per : nullptr;
         if (l + 1 < S->n) {
-            io.pred_idx = pred_idx ? pred_idx + (l + 1) * per : S->d_pred_idx;
-            io.pred_w = pred_w ? pred_w + (l + 1) * per : S->d_pred_w;
+            io.pred_idx = pred_idx ? pred_idx + (l + 1) * per : S->d_pred_idx[l & 1];
+            io.pred_w = pred_w ? pred_w + (l + 1) * per : S->d_pred_w[l & 1];
         }
         int rc = check_io(L, &io, n_tok);
+        if (rc != MOE_OK) return rc;
+        rc = trace_layer(S, l, x, n_tok, st);
         if (rc != MOE_OK) return rc;
         PrologueArgs nxt{};
         if (l + 1 < S->n) nxt = prologue_args(S->layers[l + 1], x, n_tok);
@@ -717,8 +765,6 @@ int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, floa
 
 void moe_stack_destroy(moe_stack* S) {
     if (!S) return;
-    if (S->d_pred_idx) (void)hipFree(S->d_pred_idx);
-    if (S->d_pred_w) (void)hipFree(S->d_pred_w);
     delete[] S->layers;
     delete S;
 }

@@ -121,10 +121,14 @@ struct moe_layer {
 struct moe_stack {
     moe_layer** layers;
     int n;
-    // prefill scratch: shifted routing and per-layer predictions (device)
-    int32_t* d_pred_idx;
-    float* d_pred_w;
-    size_t pred_cap;         // entries
+    // prefill scratch (caller's workspace): two prediction buffers, layer l
+    // writing buffer l & 1 while it reads layer l-1's from the other one
+    int32_t* d_pred_idx[2];
+    float* d_pred_w[2];
+    size_t pred_cap;         // entries per buffer
+    // optional trace of every layer's input residual stream (device fp32)
+    float* x_trace;
+    size_t trace_cap;        // floats
 };
 
 // ---- kernel launchers (kernels_*.hip) -------------------------------------

@@ -437,3 +437,181 @@ def test_plan_slots_capacity():
 def test_head_input_width_from_pages():
     g = json.load(open(os.path.join(GOLDEN, "pages_figures.json")))["head_input_width_35b"]
     assert g["d_model"] + 2 * g["experts"] == g["value"]
+
+
+# ----------------------------------------------------------------------------
+# Pins of the shared gate's sign and input, the LoRA scale at r > 1, the
+# residual, and the stack's history wiring. Each is a closed form or a
+# hand-derived trajectory that a plausible slip changes.
+# ----------------------------------------------------------------------------
+def zero_blob(d, f):
+    """An expert whose three matrices are exactly zero (codes 0, s = b = 0)."""
+    return np.zeros(oracle.blob_bytes(d, f), dtype=np.uint8)
+
+
+def test_shared_gate_three_quarters_on_normalised_input():
+    """sigma(g . u) with g . u = ln 3 is 3/4 exactly (1 / (1 + 1/3)). Here the
+    input x is all ones, the norm has eps = 0, so u = gamma (in fp32) and
+    g = e_0 picks u_0 = fp32(ln 3). A gate with the opposite sign gives 1/4;
+    a gate taken on x instead of u gives sigma(1) = 0.731."""
+    lw = tiny_layer(r=0)
+    d = lw.d
+    lw.eps = 0.0
+    lw.gamma = np.ones(d)
+    lw.gamma[0] = math.log(3.0)
+    g = np.zeros(d); g[0] = 1.0
+    lw.shared_gate = oracle.bf16_bits_of(g)
+    x = np.ones((1, d))
+    route = (np.array([[2, 5]]), np.array([[0.5, 0.5]]))
+    xo, y, u, used, pred, z = oracle.decode_layer(lw, x, route, None, fused_norm=True)
+    u0 = u[0]
+    assert u0[0] == float(np.float32(math.log(3.0))) and np.all(u0[1:] == 1.0)
+    routed = 0.5 * oracle.expert_ffn(lw.expert(2), u0) + 0.5 * oracle.expert_ffn(lw.expert(5), u0)
+    shared = oracle.expert_ffn(lw.shared_expert(), u0)
+    ratio = (y[0] - routed) / shared
+    assert np.allclose(ratio, 0.75, rtol=0, atol=1e-7)
+
+
+def test_lora_scale_alpha_over_r_at_rank4():
+    """Rank 4, alpha 8: the branch is scaled by alpha / r = 2 (a scale of alpha
+    would give 8, alpha / sqrt(r) would give 4). A = the first four unit rows
+    and B[7, i] = (i + 1) / 4 make (B A u)_7 = sum_i (i + 1) u_i / 4, with every
+    other output zero; the experts are zero so y is the branch alone."""
+    d, r = 128, 4
+    lw = tiny_layer(fs=0, r=r)
+    assert lw.alpha == 8.0 and lw.r == 4
+    lw.store = np.stack([zero_blob(d, lw.f)] * lw.E)
+    A = np.zeros((r, d)); A[np.arange(r), np.arange(r)] = 1.0
+    Bm = np.zeros((d, r)); Bm[7, :] = (np.arange(r) + 1) / 4.0
+    lw.lora_a = oracle.bf16_bits_of(A)
+    lw.lora_b = oracle.bf16_bits_of(Bm)
+    u = np.random.default_rng(21).standard_normal(d)
+    y = oracle.moe_block(lw, u, [0, 1], [0.5, 0.5])
+    expect = np.zeros(d)
+    expect[7] = 2.0 * (1 * u[0] + 2 * u[1] + 3 * u[2] + 4 * u[3]) / 4.0
+    assert np.allclose(y, expect, rtol=1e-14, atol=1e-15)
+
+
+def test_residual_adds_block_output_to_x():
+    """x_out = x + y. With zero experts, no shared expert and a rank-1 branch
+    of closed form, y = 8 * b (a . u) at one coordinate, so x_out - x is that
+    value there and exactly zero elsewhere. A residual taken from u (the
+    normalised input) or a dropped residual fails."""
+    d = 128
+    lw = tiny_layer(fs=0, r=1)
+    lw.store = np.stack([zero_blob(d, lw.f)] * lw.E)
+    a = np.zeros(d); a[5] = 1.0
+    bvec = np.zeros(d); bvec[9] = 0.5
+    lw.lora_a = oracle.bf16_bits_of(a)[None, :]
+    lw.lora_b = oracle.bf16_bits_of(bvec)[:, None]
+    x = np.random.default_rng(22).standard_normal((2, d)) * 3.0
+    route = (np.array([[0, 1], [3, 2]]), np.array([[0.5, 0.5], [0.9, 0.1]]))
+    xo, y, u, used, pred, z = oracle.decode_layer(lw, x, route, None, fused_norm=True)
+    for b in range(2):
+        un = float(np.float32(x[b, 5] / math.sqrt(np.mean(x[b] ** 2) + lw.eps) * lw.gamma[5]))
+        delta = np.zeros(d); delta[9] = lw.alpha * 0.5 * un
+        assert np.allclose(xo[b] - x[b], delta, rtol=1e-13, atol=1e-14)
+        assert np.array_equal(xo[b][np.arange(d) != 9], x[b][np.arange(d) != 9])
+
+
+# The history wiring of the stack. Head l predicts layer l+1 at the next step;
+# its one-hot inputs are layer l+1's routing at this step (cur) and at the
+# previous step (prev). In the hand-built stack below every expert is zero, so
+# x never changes, every head and router matrix is zero, and the logits are
+# bias + history only:
+#   routers (self-routing, layer 0 every step and all layers at step 0):
+#     layer 0 -> {0, 1}, layer 1 -> {2, 3}, layer 2 -> {4, 5}
+#   head 0 bias (.2 on 6, .1 on 7); head 1 bias (.2 on 0, .1 on 1)
+#   Mc = 10 I (an expert in cur gains 10)
+#   Mp[j, (j + 1) mod 8] = 10 (an expert j in prev lifts expert j + 1 by 10)
+# Step 0: no history; head 0 predicts layer 1 = [6, 7], head 1 predicts
+#   layer 2 = [0, 1].
+# Step 1: layer 1 uses [6, 7], layer 2 uses [0, 1].
+#   head 0: cur = {6, 7}, prev = layer 1 at step 0 = {2, 3} lifts {3, 4};
+#     z6 = 10.2, z7 = 10.1, z3 = z4 = 10 -> [6, 7]
+#   head 1: cur = {0, 1}, prev = layer 2 at step 0 = {4, 5} lifts {5, 6};
+#     z0 = 10.2, z1 = 10.1, z5 = z6 = 10 -> [0, 1]
+# Step 2: layer 1 uses [6, 7], layer 2 uses [0, 1].
+#   head 0: cur = {6, 7}, prev = {6, 7} lifts {7, 0}; z7 = 20.1, z6 = 10.2,
+#     z0 = 10 -> [7, 6]
+#   head 1: cur = {0, 1}, prev = {0, 1} lifts {1, 2}; z1 = 20.1, z0 = 10.2,
+#     z2 = 10 -> [1, 0]
+# Taking cur or prev from layer l, or cur from step t-1, or prev from step t,
+# changes at least one of these predictions (checked below; e.g. cur from
+# step t-1 gives head 0 at step 1 cur = {2, 3}, so z3 = 20 and [3, 2]).
+HIST_EXPECT = {            # step -> (head 0 prediction, head 1 prediction)
+    0: ([6, 7], [0, 1]),
+    1: ([6, 7], [0, 1]),
+    2: ([7, 6], [1, 0]),
+}
+
+
+def history_stack():
+    E, k, d, f = 8, 2, 64, 64
+    layers = []
+    router_bias = [np.array([2, 1, 0, 0, 0, 0, 0, 0.]), np.array([0, 0, 2, 1, 0, 0, 0, 0.]),
+                   np.array([0, 0, 0, 0, 2, 1, 0, 0.])]
+    head_bias = [np.array([0, 0, 0, 0, 0, 0, .2, .1]), np.array([.2, .1, 0, 0, 0, 0, 0, 0])]
+    Mp = np.zeros((E, E))
+    for j in range(E):
+        Mp[j, (j + 1) % E] = 10.0
+    for l in range(3):
+        lw = oracle.LayerWeights(
+            d=d, E=E, k=k, f=f, fs=0, r=0, alpha=0.0, eps=1e-6, act="bf16",
+            store=np.stack([zero_blob(d, f)] * E), shared=None, shared_gate=None, lora_a=None, lora_b=None,
+            gamma=np.ones(d), head=np.zeros((E, d), np.uint16) if l < 2 else None,
+            router=np.zeros((E, d), np.uint16), router_bias=router_bias[l],
+            head_bias=head_bias[l] if l < 2 else None,
+            hist_cur=10.0 * np.eye(E) if l < 2 else None, hist_prev=Mp if l < 2 else None)
+        layers.append(lw)
+    return layers
+
+
+def simulate_routing(wiring):
+    """Routing-only replay of the hand-built stack under a given reading of
+    which routing feeds the history one-hots (the test's own derivation; the
+    correct reading must reproduce HIST_EXPECT)."""
+    E = 8
+    b0 = [np.array([0, 0, 0, 0, 0, 0, .2, .1]), np.array([.2, .1, 0, 0, 0, 0, 0, 0])]
+    selfr = {0: [0, 1], 1: [2, 3], 2: [4, 5]}
+    used = {}          # (layer, step) -> list
+    preds = {}
+    for t in range(3):
+        for l in range(3):
+            used[(l, t)] = selfr[l] if (t == 0 or l == 0) else preds[(l - 1, t - 1)]
+        for l in range(2):
+            cur, prev = wiring(used, l, t)
+            z = b0[l].copy()
+            for e in (cur or []):
+                z[e] += 10.0
+            for e in (prev or []):
+                z[(e + 1) % E] += 10.0
+            order = sorted(range(E), key=lambda e: (-z[e], e))
+            preds[(l, t)] = order[:2]
+    return {t: (preds[(0, t)], preds[(1, t)]) for t in range(3)}
+
+
+def _w_correct(used, l, t):
+    return (used[(l + 1, t)] if t > 0 else None), (used[(l + 1, t - 1)] if t > 0 else None)
+
+
+def test_stack_history_wiring_hand_derived():
+    layers = history_stack()
+    xs = np.random.default_rng(23).standard_normal((3, 1, layers[0].d))
+    recs = oracle.stack_decode(layers, xs, 3)
+    for t, (p0, p1) in HIST_EXPECT.items():
+        assert list(recs[t].preds[0][0][0]) == p0, (t, recs[t].preds[0][0][0])
+        assert list(recs[t].preds[1][0][0]) == p1, (t, recs[t].preds[1][0][0])
+        if t >= 1:
+            # the routing really is the prediction of the step before
+            assert list(recs[t].routes[1][0][0]) == HIST_EXPECT[t - 1][0]
+            assert list(recs[t].routes[2][0][0]) == HIST_EXPECT[t - 1][1]
+    assert simulate_routing(_w_correct) == HIST_EXPECT
+    mutations = {
+        "cur from layer l": lambda u, l, t: ((u[(l, t)] if t > 0 else None), _w_correct(u, l, t)[1]),
+        "prev from layer l": lambda u, l, t: (_w_correct(u, l, t)[0], (u[(l, t - 1)] if t > 0 else None)),
+        "cur from step t-1": lambda u, l, t: ((u[(l + 1, t - 1)] if t > 0 else None), _w_correct(u, l, t)[1]),
+        "prev from step t": lambda u, l, t: (_w_correct(u, l, t)[0], (u[(l + 1, t)] if t > 0 else None)),
+    }
+    for name, wiring in mutations.items():
+        assert simulate_routing(wiring) != HIST_EXPECT, name
