@@ -206,6 +206,26 @@ int moe_layer_slots(const moe_layer* layer, int32_t* h_slot_expert, int n_slots,
  * moe_layer_sync_status; the affected expert's contribution is dropped.    */
 int moe_decode_step(moe_layer* layer, const moe_io* io, int n_tok, void* stream);
 
+/* moe_decode_noalloc: the decode call for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). No layer handle and no workspace: desc and w as for
+ * moe_layer_create (MOE_RESIDENT_STORE required: the store is device
+ * memory and is read in place), io as for moe_decode_step. The per-call
+ * scratch (logits, routing digest, hidden activations, flags) lives in a
+ * 256 KiB array of device memory that the library holds per GPU for the
+ * life of the process; the call allocates nothing. Every call on one GPU
+ * shares that array and the last call's contents stay in it, so calls that
+ * overlap on one GPU race (issue them on one stream or order them). Only
+ * the fused two-kernel decode path is served: 1..16 tokens, n_tok * k <= 64,
+ * d and f powers of two (d in 256..2048, f in 64..512, f_s 0 or f).
+ * d_status (optional, device int32): receives this call's device flag as a
+ * status code (MOE_OK, MOE_E_BAD_INDEX, MOE_E_NOT_STAGED). Asynchronous on
+ * `stream`. Errors (returned): MOE_E_INVALID, MOE_E_UNSUPPORTED (shape or
+ * path not served, streamed store), MOE_E_CAPACITY (the call's scratch
+ * exceeds 256 KiB, e.g. 16 tokens over 1024 experts), MOE_E_HIP.            */
+int moe_decode_noalloc(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_io* io, int n_tok,
+                       int32_t* d_status, void* stream);
+
 /* Prefill call for n_tok tokens of one sequence (or any rows): token-to-
  * expert sort/permute and int4->bf16 MFMA grouped GEMM (the prefill of the
  * ai.info news article's 35B section; the routing and head as in decode). Same io contract;

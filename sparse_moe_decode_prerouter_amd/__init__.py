@@ -73,6 +73,7 @@ def _load():
         "moe_stage_experts": (I, [P, P, I, P]),
         "moe_layer_slots": (I, [P, P, I, P]),
         "moe_decode_step": (I, [P, P, I, P]),
+        "moe_decode_noalloc": (I, [P, P, P, I, P, P]),
         "moe_prefill": (I, [P, P, I, P]),
         "moe_layer_sync_status": (I, [P]),
         "moe_layer_destroy": (None, [P]),
@@ -97,7 +98,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("moe_expert_blob_bytes", "moe_layer_workspace_bytes", "moe_layer_create", "moe_stage_experts",
-            "moe_layer_slots", "moe_decode_step", "moe_prefill", "moe_layer_sync_status", "moe_layer_destroy",
+            "moe_layer_slots", "moe_decode_step", "moe_decode_noalloc", "moe_prefill", "moe_layer_sync_status", "moe_layer_destroy",
             "moe_status_str", "moe_last_hip_error", "moe_plan_slots", "moe_stack_workspace_bytes",
             "moe_stack_create", "moe_stack_set_trace", "moe_stack_decode",
             "moe_stack_prefill", "moe_stack_destroy", "moe_layer_set_profiling", "moe_layer_kernel_ms")
@@ -143,6 +144,14 @@ def moe_decode_step(handle: int, io: moe_io, n_tok: int, stream: int = 0) -> Non
     rc = _lib.moe_decode_step(handle, ctypes.byref(io), n_tok, ctypes.c_void_p(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_decode_step")
+
+
+def moe_decode_noalloc(desc: moe_layer_desc, w: moe_layer_weights, io: moe_io, n_tok: int,
+                       status_ptr: Optional[int] = None, stream: int = 0) -> None:
+    rc = _lib.moe_decode_noalloc(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(io), n_tok, status_ptr,
+                                 ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_decode_noalloc")
 
 
 def moe_prefill(handle: int, io: moe_io, n_tok: int, stream: int = 0) -> None:

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -294,8 +295,10 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
     const KTime tb{L->profiling ? L->ev_t[4] : nullptr, L->profiling ? L->ev_t[5] : nullptr};
     HIPCHK(launch_dec_b(b, st, &tb));
     if (L->profiling) L->ev_t_used[2] = true;
-    HIPCHK(hipEventRecord(L->ev_done, st));
-    L->done_recorded = true;
+    if (L->ev_done) {
+        HIPCHK(hipEventRecord(L->ev_done, st));
+        L->done_recorded = true;
+    }
     return MOE_OK;
 }
 
@@ -431,6 +434,70 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     return MOE_OK;
 }
 
+// ---- scratch of the entry point that allocates nothing ---------------------
+// A file-scope device array per GPU (it lives as long as the process). Host
+// code never passes its name to a kernel: it looks the array's device
+// address up once per device and uses that address.
+constexpr size_t kNoallocScratchBytes = 256u << 10;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+constexpr int kNoallocMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kNoallocMaxDevices] = {};
+
+int noalloc_scratch(uint8_t** out) {
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kNoallocMaxDevices) return MOE_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return MOE_E_HIP;
+        g_scratch_ptr[dev] = (uint8_t*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+// the per-call scratch of a fused-path decode call of n_tok tokens
+size_t carve_decode(const moe_layer_desc* d, int n_tok, uint8_t* base, Scratch* s) {
+    Carver c{base};
+    Scratch tmp{};
+    Scratch& S = s ? *s : tmp;
+    const size_t T = (size_t)n_tok, E = d->n_experts, K = d->top_k;
+    const size_t En = d->next_n_experts > 0 ? d->next_n_experts : 1;
+    S.err = c.take<int32_t>(64);
+    S.counters = c.take<uint32_t>(16);
+    S.logits_r = c.take<double>(T * E);
+    S.logits_h = c.take<double>(T * En);
+    S.self_idx = c.take<int32_t>(T * K);
+    S.self_w = c.take<float>(T * K);
+    S.used_idx = c.take<int32_t>(T * K);
+    S.used_w = c.take<float>(T * K);
+    S.au = c.take<float>(T * std::max(1, d->lora_rank));
+    S.sgate = c.take<float>(std::max<size_t>(T, 64));
+    S.sort_meta = c.take<int32_t>(8);
+    S.active = c.take<int32_t>(std::max<size_t>(std::min(E, T * K) + 1, 64));
+    S.act_off = c.take<int32_t>(std::max<size_t>(std::min(E, T * K) + 1, 64));
+    S.perm = c.take<int32_t>(std::max<size_t>(T * K, 64));
+    S.wsort = c.take<float>(std::max<size_t>(T * K, 64));
+    S.h = c.take<float>(T * K * d->d_ff);
+    S.hs = c.take<float>(T * std::max(1, d->d_ff_shared));
+    return align_up(c.off, 256);
+}
+
+__global__ void k_noalloc_begin(int32_t* err, uint32_t* counters) {
+    const int i = threadIdx.x;
+    if (i < 64) err[i] = 0;
+    if (i < 16) counters[i] = 0u;
+}
+
+__global__ void k_noalloc_status(const int32_t* err, int32_t* status) {
+    const int e = err[0];
+    status[0] = (e & ERR_TIMEOUT) ? MOE_E_TIMEOUT : (e & ERR_BAD_INDEX) ? MOE_E_BAD_INDEX
+                : (e & ERR_NOT_STAGED) ? MOE_E_NOT_STAGED : MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -547,6 +614,47 @@ int moe_decode_step(moe_layer* L, const moe_io* io, int n_tok, void* stream) {
     if (rc != MOE_OK) return rc;
     if (n_tok * L->desc.top_k > 4096 || n_tok > 256) return MOE_E_UNSUPPORTED;
     return run_decode(L, io, n_tok, (hipStream_t)stream);
+}
+
+int moe_decode_noalloc(const moe_layer_desc* desc, const moe_layer_weights* w, const moe_io* io, int n_tok,
+                       int32_t* d_status, void* stream) {
+    int rc = validate_desc(desc);
+    if (rc != MOE_OK) return rc;
+    if (!w || !w->expert_store) return MOE_E_INVALID;
+    if (!(desc->flags & MOE_RESIDENT_STORE)) return MOE_E_UNSUPPORTED;
+    if ((desc->d_ff_shared != 0) != (w->shared_blob != nullptr)) return MOE_E_INVALID;
+    if ((desc->flags & MOE_FUSE_NORM_RESIDUAL) && !w->norm_gamma) return MOE_E_INVALID;
+    if (desc->lora_rank && (!w->lora_a || !w->lora_b)) return MOE_E_INVALID;
+    if (desc->next_n_experts > 0 && !w->head) return MOE_E_INVALID;
+    if ((w->hist_cur || w->hist_prev) && desc->next_n_experts <= 0) return MOE_E_INVALID;
+    if (n_tok < 1 || n_tok > desc->max_tokens) return MOE_E_INVALID;
+    if (!dec_fast_path_ok(desc->d_model, desc->d_ff, desc->d_ff_shared, n_tok, desc->top_k))
+        return MOE_E_UNSUPPORTED;
+    if (carve_decode(desc, n_tok, nullptr, nullptr) > kNoallocScratchBytes) return MOE_E_CAPACITY;
+    uint8_t* base = nullptr;
+    rc = noalloc_scratch(&base);
+    if (rc != MOE_OK) return rc;
+    moe_layer L{};
+    L.desc = *desc;
+    L.w = *w;
+    carve_decode(desc, n_tok, base, &L.s);
+    L.L = BlobLayout::make(desc->d_model, desc->d_ff);
+    L.Ls = BlobLayout::make(desc->d_model, desc->d_ff_shared ? desc->d_ff_shared : desc->d_ff);
+    L.blob = L.L.total;
+    L.sblob = desc->d_ff_shared ? L.Ls.total : 0;
+    L.resident = true;
+    rc = check_io(&L, io, n_tok);
+    if (rc != MOE_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_noalloc_begin, dim3(1), dim3(64), 0, st, L.s.err, L.s.counters);
+    HIPCHK(hipGetLastError());
+    rc = run_decode(&L, io, n_tok, st);
+    if (rc != MOE_OK) return rc;
+    if (d_status) {
+        hipLaunchKernelGGL(k_noalloc_status, dim3(1), dim3(1), 0, st, (const int32_t*)L.s.err, d_status);
+        HIPCHK(hipGetLastError());
+    }
+    return MOE_OK;
 }
 
 int moe_prefill(moe_layer* L, const moe_io* io, int n_tok, void* stream) {
