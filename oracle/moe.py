@@ -13,15 +13,23 @@ Pins (tests/test_oracle_pins.py, marked "not gpu"):
   round_bf16       exhaustive neighbours of bf16 values, ties to even
   topk / weights   brute force over all k-subsets, exact ties, k = E,
                    shift invariance, sum to one
+  head_mlp         erf-GELU at textbook normal-CDF values (and against the
+                   tanh form), one-hot wiring of fc1 (current block vs
+                   previous block), fc2 orientation, W2 = 0 gives the linear
+                   head, l + MLP composed in predict_next
   expert_ffn       permutation-structured experts with closed-form outputs
-  moe_block        identical experts, k = 1, sigmoid(0) gate, LoRA rank 1
-                   closed form, expert relabelling invariance
+  moe_block        identical experts, k = 1, sigmoid(0) gate and
+                   sigmoid(ln 3) = 3/4 on the normalised input, LoRA rank 1
+                   and rank 4 (alpha / r) closed forms, residual x + y,
+                   expert relabelling invariance
   stack dataflow   prefill == sequential per-token decode with the same
-                   shifted routing; batch rows == separate batch-1 runs
+                   shifted routing; batch rows == separate batch-1 runs;
+                   history one-hots of head l = layer l+1's routing at this
+                   step and the previous one (hand-derived 3-layer run)
   plan_slots       brute-force minimal-copy / sticky-slot properties
-Parity unpinned: the prediction *quality* of heads (no trained heads exist),
-the pages' absolute throughputs, and the head's MLP branch (its fc1 width is
-not on the pages); none of these is computed here.
+Parity unpinned: the prediction *quality* of heads (no trained heads exist)
+and the pages' absolute throughputs; neither is computed here. The MLP
+branch's fc1 width is not on the pages: it is a parameter.
 """
 from __future__ import annotations
 
@@ -132,10 +140,10 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # O3-O5: head logits, top-k, renormalised softmax weights
 # [Guide] Method, prerouter head architecture: the head reads the hidden state
-# plus top-k one-hot routing vectors of the current and previous token; its
-# linear path l(x) is what is evaluated here (head(x) = fc2(gelu(fc1(x))) + l(x);
-# the MLP branch is not part of this block). [Guide] Key terms,
-# prediction-as-routing: the predicted set is the routing itself.
+# plus top-k one-hot routing vectors of the current and previous token;
+# head(x) = fc2(gelu(fc1(x))) + l(x), and head_logits is the linear path l(x)
+# (the MLP branch is head_mlp below). [Guide] Key terms, prediction-as-routing:
+# the predicted set is the routing itself.
 # ----------------------------------------------------------------------------
 def head_logits(H_bits: np.ndarray, u: np.ndarray, bias: Optional[np.ndarray] = None,
                 hist_cur_mat: Optional[np.ndarray] = None, hist_cur: Optional[Sequence[int]] = None,
@@ -181,6 +189,47 @@ def route_weights(z: np.ndarray, idx: np.ndarray) -> np.ndarray:
 def route(z: np.ndarray, k: int):
     idx = topk(z, k)
     return idx, route_weights(z, idx)
+
+
+# ----------------------------------------------------------------------------
+# O3b: the head's MLP branch. [Guide] Method, prerouter head architecture: the
+# head computes fc2(erf-GELU(fc1(x))) + l(x) on x = [hidden state, top-k
+# one-hot of the current token's routing, top-k one-hot of the previous
+# token's], of width d + 2E. l(x) is head_logits above (H u + bias + the
+# one-hot rows). fc1 is stored as its hidden-state columns W1u [H1, d] and
+# its one-hot columns W1oh [2E, H1] (row j < E: column d + j, the current
+# token's expert j; row E + j: column d + E + j, the previous token's).
+# ----------------------------------------------------------------------------
+def gelu_erf(a):
+    """GELU with the exact normal CDF: a * Phi(a) = a / 2 * (1 + erf(a / sqrt 2))."""
+    a = np.asarray(a, dtype=np.float64)
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * a * (1.0 + erf(a / math.sqrt(2.0)))
+
+
+def onehot_input(E: int, cur: Optional[Sequence[int]], prev: Optional[Sequence[int]]) -> np.ndarray:
+    """The 2E one-hot part of the head input: 1 at j for expert j in cur, at
+    E + j for expert j in prev (indices < 0 are absent)."""
+    v = np.zeros(2 * E, dtype=np.float64)
+    for j in (cur if cur is not None else []):
+        if j >= 0:
+            v[int(j)] = 1.0
+    for j in (prev if prev is not None else []):
+        if j >= 0:
+            v[E + int(j)] = 1.0
+    return v
+
+
+def head_mlp(W1u_bits, W1oh_bits, b1, W2_bits, u, E: int, cur=None, prev=None) -> np.ndarray:
+    """fc2(gelu(fc1(x))): fc1(x) = [W1u | W1oh^T] x + b1 with x = [u, onehot];
+    fc2 is W2 [E, H1] (its bias is the head bias, added with l(x))."""
+    W1u = bf16_to_f64(W1u_bits)
+    W1oh = bf16_to_f64(W1oh_bits)
+    x_oh = onehot_input(E, cur, prev)
+    a1 = W1u @ np.asarray(u, dtype=np.float64) + W1oh.T @ x_oh
+    if b1 is not None:
+        a1 = a1 + np.asarray(b1, dtype=np.float64)
+    return bf16_to_f64(W2_bits) @ gelu_erf(a1)
 
 
 # ----------------------------------------------------------------------------
@@ -230,6 +279,10 @@ class LayerWeights:
     router_bias: Optional[np.ndarray] = None
     hist_cur: Optional[np.ndarray] = None    # float [E, E]
     hist_prev: Optional[np.ndarray] = None   # float [E, E]
+    head_fc1: Optional[np.ndarray] = None      # bf16 bits [H1, d]: fc1's hidden-state columns
+    head_fc1_oh: Optional[np.ndarray] = None   # bf16 bits [2E, H1]: fc1's one-hot columns
+    head_fc1_bias: Optional[np.ndarray] = None  # float [H1]
+    head_fc2: Optional[np.ndarray] = None      # bf16 bits [E, H1]
     max_cache: int = 8                       # dequantised experts kept (memory bound)
     _cache: dict = field(default_factory=dict, repr=False)
 
@@ -291,7 +344,12 @@ def self_route(lw: LayerWeights, u: np.ndarray):
 
 
 def predict_next(lw: LayerWeights, u: np.ndarray, k_next: int, cur=None, prev=None):
+    """head(x) = l(x) + fc2(gelu(fc1(x))) (the MLP branch when the layer has one),
+    then top-k and the renormalised weights."""
     z = head_logits(lw.head, u, lw.head_bias, lw.hist_cur, cur, lw.hist_prev, prev)
+    if lw.head_fc1 is not None:
+        E = z.shape[0]
+        z = z + head_mlp(lw.head_fc1, lw.head_fc1_oh, lw.head_fc1_bias, lw.head_fc2, u, E, cur, prev)
     idx, w = route(z, k_next)
     return idx, w, z
 

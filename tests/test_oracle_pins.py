@@ -615,3 +615,81 @@ def test_stack_history_wiring_hand_derived():
     }
     for name, wiring in mutations.items():
         assert simulate_routing(wiring) != HIST_EXPECT, name
+
+
+# ----------------------------------------------------------------------------
+# O3b the head's MLP branch: fc2(erf-GELU(fc1([u, onehot cur, onehot prev])))
+# ----------------------------------------------------------------------------
+PHI_1 = 0.8413447460685429      # standard normal CDF at 1 (textbook table value)
+PHI_2 = 0.9772498680518208      # at 2
+
+
+def test_gelu_erf_normal_cdf_values():
+    """erf-GELU(a) = a Phi(a): Phi(1), Phi(2) and Phi(0) = 1/2 from the normal
+    table; GELU(a) - GELU(-a) = a; the tanh approximation of GELU differs at
+    1 by 1.5e-4, so a tanh form would fail."""
+    g = oracle.gelu_erf(np.array([1.0, -1.0, 2.0, 0.0, 0.5]))
+    assert abs(g[0] - PHI_1) < 1e-15
+    assert abs(g[1] - (-(1.0 - PHI_1))) < 1e-15
+    assert abs(g[2] - 2.0 * PHI_2) < 1e-15
+    assert g[3] == 0.0
+    a = np.linspace(-4, 4, 17)
+    assert np.allclose(oracle.gelu_erf(a) - oracle.gelu_erf(-a), a, atol=1e-15)
+    tanh_form = 0.5 * (1 + math.tanh(math.sqrt(2 / math.pi) * (1 + 0.044715)))
+    assert abs(g[0] - tanh_form) > 1e-4
+
+
+def mlp_case():
+    """E = 6 experts, H1 = 3 hidden units, d = 64. W1u = 0. The one-hot
+    columns: current expert j adds v_j to unit 0; previous expert j adds
+    -2 v_j to unit 1 (v = 1/2, 1/4, 3/4, 1/8, 3/8, 5/8, exact in bf16); unit
+    2 sees only its bias. W2 [6, 3]: rows 0, 1, 2 pick units 0, 1, 2; rows
+    3..5 are zero."""
+    E, H1, d = 6, 3, 64
+    W1u = np.zeros((H1, d), np.uint16)
+    vals = [0.5, 0.25, 0.75, 0.125, 0.375, 0.625]
+    W1oh = np.zeros((2 * E, H1))
+    for j in range(E):
+        W1oh[j, 0] = vals[j]
+        W1oh[E + j, 1] = -2.0 * vals[j]
+    W2 = np.zeros((E, H1))
+    W2[0, 0] = W2[1, 1] = W2[2, 2] = 1.0
+    return E, H1, d, W1u, oracle.bf16_bits_of(W1oh), oracle.bf16_bits_of(W2)
+
+
+def test_head_mlp_onehot_wiring_closed_form():
+    """cur = {1, 2} gives unit 0 the value 1/4 + 3/4 = 1; prev = {0} gives
+    unit 1 -2 (1/2) = -1; unit 2 has bias 2. The logits are then the table
+    values [Phi(1), -(1 - Phi(1)), 2 Phi(2), 0, 0, 0]. Swapping cur and prev
+    (unit 0 = 1/2, unit 1 = -2), reading prev at column j instead of E + j
+    (unit 1 = 0), or a transposed W2 gives other values."""
+    E, H1, d, W1u, W1oh, W2 = mlp_case()
+    u = np.random.default_rng(31).standard_normal(d)
+    b1 = np.array([0.0, 0.0, 2.0])
+    z = oracle.head_mlp(W1u, W1oh, b1, W2, u, E, cur=[1, 2, -1], prev=[0])
+    assert np.allclose(z, [PHI_1, -(1.0 - PHI_1), 2.0 * PHI_2, 0, 0, 0], rtol=0, atol=1e-15)
+    # duplicates in a routing list set the one-hot once
+    z2 = oracle.head_mlp(W1u, W1oh, b1, W2, u, E, cur=[1, 2, 2], prev=[0, 0])
+    assert np.array_equal(z, z2)
+
+
+def test_head_mlp_hidden_columns_and_zero_fc2():
+    """The hidden-state columns: W1u row 0 picks 2 u_5, so unit 0 = 2 u_5; with
+    u_5 = 1/2 that is GELU(1) = Phi(1). W2 = 0 leaves the linear head alone in
+    predict_next, and a nonzero W2 adds exactly head_mlp to it."""
+    E, H1, d, W1u, W1oh, W2 = mlp_case()
+    W1u = np.zeros((H1, d)); W1u[0, 5] = 2.0
+    W1u = oracle.bf16_bits_of(W1u)
+    u = np.zeros(d); u[5] = 0.5
+    z = oracle.head_mlp(W1u, W1oh, None, W2, u, E)
+    assert abs(z[0] - PHI_1) < 1e-15 and np.all(z[1:] == 0.0)
+    lw = tiny_layer(E=E, k=2, d=d, f=64, fs=0, r=0)
+    H = np.zeros((E, d)); H[4, 5] = 1.0                      # l(x)_4 = u_5
+    lw.head = oracle.bf16_bits_of(H)
+    lw.head_fc1, lw.head_fc1_oh, lw.head_fc1_bias = W1u, W1oh, None
+    lw.head_fc2 = np.zeros((E, H1), np.uint16)
+    idx0, w0, z0 = oracle.predict_next(lw, u, 2)
+    assert np.array_equal(z0, oracle.head_logits(lw.head, u))
+    lw.head_fc2 = W2
+    idx1, w1, z1 = oracle.predict_next(lw, u, 2)
+    assert abs(z1[0] - PHI_1) < 1e-15 and z1[4] == 0.5 and list(idx1) == [0, 4]
