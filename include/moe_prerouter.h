@@ -96,6 +96,11 @@ typedef struct moe_layer_desc {
     int   next_n_experts; /* experts of the layer the head predicts (0 = no head) */
     int   next_top_k;     /* k of the layer the head predicts                     */
     unsigned flags;       /* MOE_FUSE_NORM_RESIDUAL | MOE_RESIDENT_STORE          */
+    /* H1: hidden width of the head's MLP branch (guide, Method: prerouter head
+     * architecture: head(x) = fc2(erf-GELU(fc1(x))) + l(x) on x = [u, top-k
+     * one-hot of the current token, of the previous token]); 0 = the linear
+     * path l(x) alone. 0..1024, a multiple of 8; needs a head.              */
+    int   head_hidden;
 } moe_layer_desc;
 
 typedef struct moe_layer_weights {
@@ -119,6 +124,18 @@ typedef struct moe_layer_weights {
     const uint16_t* lora_a;       /* device bf16 [r][d]                      */
     const uint16_t* lora_b;       /* device bf16 [d][r]                      */
     const float*    norm_gamma;   /* device fp32 [d]; needed with FUSE_NORM_RESIDUAL */
+    /* the head's MLP branch (head_hidden = H1 > 0; all NULL otherwise):
+     * fc1 = [head_fc1 | head_fc1_onehot^T] acting on [u, one-hot] plus
+     * head_fc1_bias; fc2 = head_fc2. Its output adds to l(x) (whose bias
+     * head_bias also serves as fc2's). The one-hot inputs are the history
+     * routings of moe_io (hist_cur, hist_prev), each distinct valid expert
+     * once.                                                                */
+    const uint16_t* head_fc1;         /* device bf16 [H1][d]                 */
+    const uint16_t* head_fc1_onehot;  /* device bf16 [2 E_next][H1]: row j is fc1's column
+                                         for expert j in the current token's routing, row
+                                         E_next + j for expert j in the previous token's */
+    const float*    head_fc1_bias;    /* device fp32 [H1] or NULL            */
+    const uint16_t* head_fc2;         /* device bf16 [E_next][H1]            */
 } moe_layer_weights;
 
 /* Per-call inputs and outputs (all device memory). */
@@ -218,6 +235,7 @@ int moe_decode_step(moe_layer* layer, const moe_io* io, int n_tok, void* stream)
  * overlap on one GPU race (issue them on one stream or order them). Only
  * the fused two-kernel decode path is served: 1..16 tokens, n_tok * k <= 64,
  * d and f powers of two (d in 256..2048, f in 64..512, f_s 0 or f).
+ * The head's MLP branch (head_hidden > 0) is not served here.
  * d_status (optional, device int32): receives this call's device flag as a
  * status code (MOE_OK, MOE_E_BAD_INDEX, MOE_E_NOT_STAGED). Asynchronous on
  * `stream`. Errors (returned): MOE_E_INVALID, MOE_E_UNSUPPORTED (shape or

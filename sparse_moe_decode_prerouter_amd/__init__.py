@@ -37,13 +37,15 @@ class moe_layer_desc(ctypes.Structure):
         ("lora_rank", ctypes.c_int), ("lora_alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
         ("act_dtype", ctypes.c_int), ("max_tokens", ctypes.c_int), ("slab_slots", ctypes.c_int),
         ("next_n_experts", ctypes.c_int), ("next_top_k", ctypes.c_int), ("flags", ctypes.c_uint),
+        ("head_hidden", ctypes.c_int),
     ]
 
 
 class moe_layer_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "expert_store", "shared_blob", "shared_gate", "router", "router_bias", "head", "head_bias",
-        "hist_cur", "hist_prev", "lora_a", "lora_b", "norm_gamma")]
+        "hist_cur", "hist_prev", "lora_a", "lora_b", "norm_gamma", "head_fc1", "head_fc1_onehot", "head_fc1_bias",
+        "head_fc2")]
 
 
 class moe_io(ctypes.Structure):
@@ -265,14 +267,16 @@ class MoeLayer:
                  max_tokens, expert_store, shared_blob=None, shared_gate=None, router=None, router_bias=None,
                  head=None, head_bias=None, next_n_experts=0, next_top_k=0, hist_cur=None, hist_prev=None,
                  lora_a=None, lora_b=None, norm_gamma=None, rms_eps=1e-6, fuse_norm_residual=False,
-                 resident=True, slab_slots=0, device="cuda"):
+                 resident=True, slab_slots=0, head_fc1=None, head_fc1_onehot=None, head_fc1_bias=None,
+                 head_fc2=None, device="cuda"):
         import torch
         self._keep = [expert_store, shared_blob, shared_gate, router, router_bias, head, head_bias, hist_cur,
-                      hist_prev, lora_a, lora_b, norm_gamma]
+                      hist_prev, lora_a, lora_b, norm_gamma, head_fc1, head_fc1_onehot, head_fc1_bias, head_fc2]
         flags = (MOE_FUSE_NORM_RESIDUAL if fuse_norm_residual else 0) | (MOE_RESIDENT_STORE if resident else 0)
+        head_hidden = 0 if head_fc1 is None else int(head_fc1.shape[0])
         self.desc = moe_layer_desc(d_model, n_experts, top_k, d_ff, d_ff_shared, 64, lora_rank, float(lora_alpha),
                                    float(rms_eps), act_dtype, max_tokens, slab_slots, next_n_experts, next_top_k,
-                                   flags)
+                                   flags, head_hidden)
         self.weights = moe_layer_weights(*[_ptr(t) for t in self._keep])
         nbytes = moe_layer_workspace_bytes(self.desc)
         if nbytes == 0:

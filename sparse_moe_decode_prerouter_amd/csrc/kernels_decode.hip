@@ -678,6 +678,70 @@ hipError_t launch_down(const GemvArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Slot-table update after staging copies (queued on the copy stream).
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// The head's MLP branch, after fc1's hidden-state part: kMlpTok tokens per
+// block. For each token: a = a1 + fc1's one-hot columns of its current and
+// previous routing (each distinct valid expert once) + bias, g = erf-GELU(a)
+// in fp64 (LDS); then every thread takes logits rows e = tid, tid + 256, ...
+// and adds W2[e] . g for the block's tokens (each W2 row is read once for
+// all of them). bf16 weights times fp64 activations, fp64 sums.
+// ---------------------------------------------------------------------------
+constexpr int kMlpTok = 4;
+
+__global__ void __launch_bounds__(256) k_head_mlp_out(HeadMlpArgs a) {
+    __shared__ double g[kMlpTok][kMaxHeadHidden];
+    __shared__ int ids[kMlpTok][2 * kMaxTopK];
+    const int tid = threadIdx.x, t0 = blockIdx.x * kMlpTok;
+    const int H1 = a.H1, En = a.En, kn = a.kn;
+    const int nt = min(kMlpTok, a.n_tok - t0);
+    if (tid < kMlpTok * 2 * kMaxTopK) {
+        const int q = tid / (2 * kMaxTopK), i = tid % (2 * kMaxTopK);
+        const int src = i / kMaxTopK, j = i % kMaxTopK;      // src 0: current, 1: previous
+        const int32_t* H = src ? a.hp : a.hc;
+        int e = -1;
+        if (q < nt && j < kn && H) e = H[(size_t)(t0 + q) * kn + j];
+        ids[q][i] = (e >= 0 && e < En) ? e : -1;
+    }
+    __syncthreads();
+    for (int q = 0; q < nt; ++q) {
+        const int t = t0 + q;
+        for (int j = tid; j < H1; j += 256) {
+            double v = a.a1[(size_t)t * H1 + j] + (a.b1 ? (double)a.b1[j] : 0.0);
+            for (int src = 0; src < 2; ++src)
+                for (int i = 0; i < kn; ++i) {
+                    const int e = ids[q][src * kMaxTopK + i];
+                    bool dup = false;
+                    for (int i2 = 0; i2 < i; ++i2) dup |= ids[q][src * kMaxTopK + i2] == e;
+                    if (e < 0 || dup) continue;
+                    v += (double)bf16_to_f32(a.w1oh[(size_t)(src * En + e) * H1 + j]);
+                }
+            g[q][j] = 0.5 * v * (1.0 + erf(v * M_SQRT1_2));
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < En; e += 256) {
+        const uint16_t* w = a.w2 + (size_t)e * H1;
+        double acc[kMlpTok] = {};
+        for (int j = 0; j < H1; j += 8) {
+            const u32x4 wv = *(const u32x4*)(w + j);
+            const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double w0 = (double)bf16_to_f32(ws[i] & 0xFFFF), w1 = (double)bf16_to_f32(ws[i] >> 16);
+#pragma unroll
+                for (int q = 0; q < kMlpTok; ++q) acc[q] += w0 * g[q][j + 2 * i] + w1 * g[q][j + 2 * i + 1];
+            }
+        }
+        for (int q = 0; q < nt; ++q) a.logits[(size_t)(t0 + q) * En + e] += acc[q];
+    }
+}
+
+hipError_t launch_head_mlp_out(const HeadMlpArgs& a, hipStream_t s) {
+    if (a.H1 <= 0 || a.H1 > kMaxHeadHidden || a.H1 % 8 || a.kn > kMaxTopK || a.n_tok <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_head_mlp_out, dim3((a.n_tok + kMlpTok - 1) / kMlpTok), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 __global__ void k_slot_update(int32_t* slot_of, int32_t* slot_tag, SlotUpdate u) {
     if (threadIdx.x != 0) return;
     for (int i = 0; i < u.n; ++i)

@@ -1547,6 +1547,10 @@ hipError_t launch_route_mm(const RouteMMArgs& a_in, hipStream_t s, bool router_t
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    return launch_route_topk(a, s, router_topk, head_topk);
+}
+
+hipError_t launch_route_topk(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk) {
     router_topk = router_topk && a.router;
     head_topk = head_topk && a.head && a.pred_idx;
     if (router_topk || head_topk) {

@@ -53,6 +53,8 @@ int validate_desc(const moe_layer_desc* d) {
     if (d->next_n_experts > 0 && (d->next_top_k <= 0 || d->next_top_k > kMaxTopK || d->next_top_k > d->next_n_experts))
         return MOE_E_UNSUPPORTED;
     if (d->max_tokens > 8192) return MOE_E_UNSUPPORTED;
+    if (d->head_hidden < 0 || d->head_hidden > kMaxHeadHidden || d->head_hidden % 8) return MOE_E_UNSUPPORTED;
+    if (d->head_hidden > 0 && d->next_n_experts <= 0) return MOE_E_INVALID;
     const bool resident = d->flags & MOE_RESIDENT_STORE;
     if (!resident && (d->slab_slots < 1 || d->slab_slots > 64)) return MOE_E_UNSUPPORTED;
     if (d->flags & ~(MOE_FUSE_NORM_RESIDUAL | MOE_RESIDENT_STORE)) return MOE_E_INVALID;
@@ -107,6 +109,8 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.tiles64 = c.take<int32_t>(4 * (size_t)prefill_max_tiles((int)T, (int)K, (int)E, 64));
     S.ob = c.take<float>(T * K * D);
     S.obs = c.take<float>(T * D);
+    S.a1 = d->head_hidden > 0 ? c.take<double>(T * d->head_hidden) : nullptr;
+    S.wf_fc1 = (d->head_hidden > 0 && !f32) ? c.take<uint32_t>(frag_rows_words(d->head_hidden, (int)D)) : nullptr;
     (void)Kn;
     return align_up(c.off, 256);
 }
@@ -206,6 +210,29 @@ __global__ void k_merge_route(const int32_t* ridx, const int32_t* sidx, int32_t*
 int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool prefill, int route_shift = 0,
                 const PrologueArgs* nxt = nullptr, bool skip_pro = false, bool* took_nxt = nullptr);
 
+PrologueArgs prologue_args(const moe_layer* L, const void* x, int n_tok);
+
+// The head's MLP branch: fc1's hidden-state part on the routing GEMM (u from
+// the prologue, run here when the call has not), then one-hot columns, bias,
+// erf-GELU and fc2 added into the head logits, before any head top-k reads them.
+int run_head_mlp(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool run_prologue) {
+    const moe_layer_desc& D = L->desc;
+    if (run_prologue) HIPCHK(launch_prologue(prologue_args(L, io->x_in, n_tok), st));
+    RouteMMArgs ra{};
+    ra.u_pk = L->s.u_pk; ra.u_pk_lo = L->s.u_pk_lo; ra.d = D.d_model; ra.n_tok = n_tok;
+    ra.head = L->w.head_fc1; ra.En = D.head_hidden; ra.kn = 0;
+    ra.logits_h = L->s.a1;
+    ra.u_frag = L->s.u_frag; ra.wf_head = L->s.wf_fc1;
+    HIPCHK(launch_route_mm(ra, st, false, false, nullptr));
+    HeadMlpArgs m{};
+    m.a1 = L->s.a1; m.H1 = D.head_hidden;
+    m.w1oh = L->w.head_fc1_onehot; m.b1 = L->w.head_fc1_bias; m.w2 = L->w.head_fc2;
+    m.hc = io->hist_cur; m.hp = io->hist_prev; m.kn = D.next_top_k; m.En = D.next_n_experts;
+    m.logits = L->s.logits_h; m.n_tok = n_tok;
+    HIPCHK(launch_head_mlp_out(m, st));
+    return MOE_OK;
+}
+
 // defer_in: a previous layer's head top-k to run inside this layer's K_A.
 // defer_out (stack mode): this layer's head top-k is not run here but handed
 // back, for the next layer's K_A to run (its prediction is for the next step).
@@ -270,6 +297,10 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
     const KTime ta{L->profiling ? L->ev_t[2] : nullptr, L->profiling ? L->ev_t[3] : nullptr};
     HIPCHK(launch_dec_a(a, st, &ta));
     if (L->profiling) L->ev_t_used[1] = true;
+    if (io->pred_idx && D.head_hidden > 0) {
+        const int rc = run_head_mlp(L, io, n_tok, st, true);
+        if (rc != MOE_OK) return rc;
+    }
 
     DecBArgs b{};
     b.ev = a.ev; b.d = D.d_model; b.f = D.d_ff; b.fs = D.d_ff_shared; b.k = D.top_k; b.n_tok = n_tok;
@@ -358,7 +389,14 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     ra.pre_rows = sort_topk ? std::min(route_shift, n_tok) : 0;
     ra.counter = L->s.counters + 3;
     int pre_done = 0;
-    HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm, &pre_done));
+    const bool mlp = io->pred_idx && L->w.head && D.head_hidden > 0;
+    HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm && !mlp, &pre_done));
+    if (mlp) {
+        int rc = run_head_mlp(L, io, n_tok, st, false);
+        if (rc != MOE_OK) return rc;
+        // off the matrix-core path the head's top-k has its own launch
+        if (!mm) HIPCHK(launch_route_topk(ra, st, false, true));
+    }
 
     SortArgs sa{};
     sa.route_idx = io->route_idx; sa.route_w = io->route_w; sa.route_shift = route_shift; sa.pre_rows = pre_done;
@@ -526,6 +564,9 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w, voi
     if (desc->lora_rank && (!w->lora_a || !w->lora_b)) return MOE_E_INVALID;
     if (desc->next_n_experts > 0 && !w->head) return MOE_E_INVALID;
     if ((w->hist_cur || w->hist_prev) && desc->next_n_experts <= 0) return MOE_E_INVALID;
+    if ((desc->head_hidden > 0) != (w->head_fc1 != nullptr) || (desc->head_hidden > 0) != (w->head_fc1_onehot != nullptr) ||
+        (desc->head_hidden > 0) != (w->head_fc2 != nullptr) || (w->head_fc1_bias && desc->head_hidden <= 0))
+        return MOE_E_INVALID;
     const size_t need = carve(desc, nullptr, nullptr);
     if (ws_bytes < need) return MOE_E_CAPACITY;
 
@@ -574,6 +615,7 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w, voi
         if ((e = pack(w->head, desc->next_n_experts, L->s.wf_head)) != hipSuccess) return fail(e);
         if ((e = pack(w->lora_a, desc->lora_rank, L->s.wf_lora)) != hipSuccess) return fail(e);
         if ((e = pack(w->shared_gate, 1, L->s.wf_sgate)) != hipSuccess) return fail(e);
+        if ((e = pack(w->head_fc1, desc->head_hidden, L->s.wf_fc1)) != hipSuccess) return fail(e);
     }
     if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e);
     *out = L;
@@ -628,6 +670,7 @@ int moe_decode_noalloc(const moe_layer_desc* desc, const moe_layer_weights* w, c
     if (desc->next_n_experts > 0 && !w->head) return MOE_E_INVALID;
     if ((w->hist_cur || w->hist_prev) && desc->next_n_experts <= 0) return MOE_E_INVALID;
     if (n_tok < 1 || n_tok > desc->max_tokens) return MOE_E_INVALID;
+    if (desc->head_hidden > 0) return MOE_E_UNSUPPORTED;
     if (!dec_fast_path_ok(desc->d_model, desc->d_ff, desc->d_ff_shared, n_tok, desc->top_k))
         return MOE_E_UNSUPPORTED;
     if (carve_decode(desc, n_tok, nullptr, nullptr) > kNoallocScratchBytes) return MOE_E_CAPACITY;

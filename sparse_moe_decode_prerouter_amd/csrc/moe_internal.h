@@ -89,6 +89,8 @@ struct Scratch {
     int32_t* tiles64;        // the same with 64-row tiles (many tokens per expert)
     float* ob;               // prefill: [T*k][d] routed expert outputs by assignment
     float* obs;              // prefill: [T][d] shared expert outputs
+    double* a1;              // head MLP: [T][H1] fc1 hidden-state part
+    uint32_t* wf_fc1;        // head MLP: fc1 hidden-state rows in MFMA fragment order (bf16 act)
 };
 
 }  // namespace moe
@@ -189,6 +191,20 @@ inline size_t frag_rows_words(int n, int d) { return (size_t)((n + 15) / 16) * 1
 // head_topk: the head's top-k here (else the combine launch does it)
 // *pre_done: how many of the requested a.pre_rows rows got their top-k here
 hipError_t launch_route_mm(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk, int* pre_done);
+
+// The head's MLP branch after fc1's hidden-state part (a1, from the routing
+// GEMM): per token, add fc1's one-hot columns and bias, erf-GELU, then fc2
+// into the head logits (which then hold l(x) + fc2(gelu(fc1(x)))).
+constexpr int kMaxHeadHidden = 1024;
+struct HeadMlpArgs {
+    const double* a1; int H1;
+    const uint16_t* w1oh; const float* b1; const uint16_t* w2;
+    const int32_t* hc; const int32_t* hp; int kn; int En;
+    double* logits; int n_tok;
+};
+hipError_t launch_head_mlp_out(const HeadMlpArgs& a, hipStream_t s);
+// the routing GEMM's per-token top-k launch alone (router and / or head)
+hipError_t launch_route_topk(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk);
 
 // A head top-k run by a later launch than the one that wrote its logits
 // (only for E_next <= 64 * kDeferMaxPer; larger heads keep their own launch).

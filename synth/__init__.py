@@ -177,6 +177,22 @@ def layer_weights(shape: Shape, layer: int, device="cpu", with_head=True, with_r
     return w
 
 
+def head_mlp_weights(shape: Shape, layer: int, hidden: int, device="cpu", tag: str = "w") -> dict:
+    """The head's MLP branch of one layer, every entry ~ N(0, std) (the
+    matrices rounded to bf16): fc1's hidden-state columns [H1, d], its
+    one-hot columns [2E, H1] (current token's experts, then the previous
+    token's), fc1's bias fp32 [H1], fc2 [E, H1]."""
+    d, E = shape.d, shape.E
+    key = (tag, shape.name, layer, "mlp", hidden)
+    sd = shape.std
+    return {
+        "head_fc1": gaussian((hidden, d), sd, key + ("fc1",), device).bfloat16(),
+        "head_fc1_onehot": gaussian((2 * E, hidden), sd * 10, key + ("fc1oh",), device).bfloat16(),
+        "head_fc1_bias": gaussian((hidden,), sd * 10, key + ("b1",), device),
+        "head_fc2": gaussian((E, hidden), sd * 5, key + ("fc2",), device).bfloat16(),
+    }
+
+
 def activations(shape: Shape, n_tok: int, key, device="cpu", dtype=None) -> torch.Tensor:
     """x ~ N(0, 1), [n_tok, d]; dtype defaults to the shape's act dtype."""
     x = gaussian((n_tok, shape.d), 1.0, ("act", shape.name) + tuple(key), device)

@@ -40,6 +40,10 @@ def oracle_layer(shape: synth.Shape, w: dict, act=None) -> oracle.LayerWeights:
         head_bias=w["head_bias"].double().numpy() if w.get("head_bias") is not None else None,
         hist_cur=w["hist_cur"].double().numpy() if w.get("hist_cur") is not None else None,
         hist_prev=w["hist_prev"].double().numpy() if w.get("hist_prev") is not None else None,
+        head_fc1=b(w["head_fc1"]) if w.get("head_fc1") is not None else None,
+        head_fc1_oh=b(w["head_fc1_onehot"]) if w.get("head_fc1_onehot") is not None else None,
+        head_fc1_bias=w["head_fc1_bias"].double().cpu().numpy() if w.get("head_fc1_bias") is not None else None,
+        head_fc2=b(w["head_fc2"]) if w.get("head_fc2") is not None else None,
     )
 
 
@@ -66,7 +70,9 @@ def gpu_layer(shape: synth.Shape, w: dict, *, fused: bool, resident: bool = True
         next_n_experts=shape.E if head else 0, next_top_k=shape.k if head else 0,
         hist_cur=dv(w.get("hist_cur")) if head else None, hist_prev=dv(w.get("hist_prev")) if head else None,
         lora_a=dv(w["lora_a"]), lora_b=dv(w["lora_b"]), norm_gamma=dv(w["gamma"]), rms_eps=shape.eps,
-        fuse_norm_residual=fused, resident=resident, slab_slots=slab_slots)
+        fuse_norm_residual=fused, resident=resident, slab_slots=slab_slots,
+        head_fc1=dv(w.get("head_fc1")) if head else None, head_fc1_onehot=dv(w.get("head_fc1_onehot")) if head else None,
+        head_fc1_bias=dv(w.get("head_fc1_bias")) if head else None, head_fc2=dv(w.get("head_fc2")) if head else None)
 
 
 def rel_l2_rows(got: np.ndarray, ref: np.ndarray) -> float:
@@ -199,6 +205,31 @@ def batched_logits(H_bits, u, mode, bias=None):
     return z, delta
 
 
+GELU_SLOPE = 1.13     # max |d/da a Phi(a)| = Phi(sqrt 2) + sqrt 2 phi(sqrt 2) = 1.1289
+
+
+def mlp_logits_and_delta(lw, u, cur, prev, mode):
+    """The head's MLP branch on u (oracle) and a bound on the GPU's deviation
+    from it: fc1's hidden part through the routing GEMM (mode), its one-hot
+    columns and bias added in fp64, erf-GELU in fp64 (|GELU'| <= 1.13, erf
+    within a few ulps), fc2 in fp64."""
+    E = lw.head.shape[0]
+    W1u = oracle.bf16_to_f64(lw.head_fc1)
+    W1oh = oracle.bf16_to_f64(lw.head_fc1_oh)
+    W2 = oracle.bf16_to_f64(lw.head_fc2)
+    x_oh = oracle.onehot_input(E, cur, prev)
+    b1 = np.zeros(W1u.shape[0]) if lw.head_fc1_bias is None else np.asarray(lw.head_fc1_bias, np.float64)
+    a1 = W1u @ u + W1oh.T @ x_oh + b1
+    d = u.shape[-1]
+    da1 = (gpu_error_factor(mode, d) + gamma_n(d, U53)) * (np.abs(W1u) @ np.abs(u)) \
+        + 8 * U53 * (np.abs(a1) + np.abs(W1oh).T @ x_oh + np.abs(b1))
+    g = oracle.gelu_erf(a1)
+    dg = GELU_SLOPE * da1 + 8 * U53 * (np.abs(g) + np.abs(a1))
+    z = W2 @ g
+    dz = np.abs(W2) @ dg + 2 * gamma_n(W2.shape[1], U53) * (np.abs(W2) @ np.abs(g))
+    return z, dz
+
+
 def layer_same_input_check(lw, x, mode, *, got_used, got_used_w, route_in, got_y=None, got_pred=None,
                            got_pred_w=None, cur=None, prev=None, tol=2e-3, rows=None, what=""):
     """Check one layer call on the input the GPU saw (x: fp64 [n, d], the fp32
@@ -236,6 +267,11 @@ def layer_same_input_check(lw, x, mode, *, got_used, got_used_w, route_in, got_y
                 z = z + hist
                 if mode != "exact":
                     dz = dz + 8 * U53 * (np.abs(z) + np.abs(hist))
+            if lw.head_fc1 is not None:
+                # the MLP branch's fc1 always takes the routing GEMM
+                zm, dm = mlp_logits_and_delta(lw, u[t], ct, pt, "mfma_split" if lw.act == "f32" else "mfma")
+                z = z + zm
+                dz = dz + dm + 8 * U53 * np.abs(z)
             ref_i, ref_w = oracle.route(z, len(got_pred[t]))
             c = check_routing(z, got_pred[t], ref_i, dz, f"{what} prediction row {t}")
             flips += c
