@@ -22,6 +22,9 @@ Pins (tests/test_oracle_pins.py, marked "not gpu"):
                    sigmoid(ln 3) = 3/4 on the normalised input, LoRA rank 1
                    and rank 4 (alpha / r) closed forms, residual x + y,
                    expert relabelling invariance
+  shared_ffn       the shared expert's adapter on gate, up and down in
+                   closed form (each projection's A and B picking known
+                   entries), B = 0 reduces to the plain shared expert
   stack dataflow   prefill == sequential per-token decode with the same
                    shifted routing; batch rows == separate batch-1 runs;
                    history one-hots of head l = layer l+1's routing at this
@@ -283,6 +286,13 @@ class LayerWeights:
     head_fc1_oh: Optional[np.ndarray] = None   # bf16 bits [2E, H1]: fc1's one-hot columns
     head_fc1_bias: Optional[np.ndarray] = None  # float [H1]
     head_fc2: Optional[np.ndarray] = None      # bf16 bits [E, H1]
+    # recovery LoRA on the shared expert's projections (rank rs, alpha as):
+    shared_lora_rank: int = 0
+    shared_lora_alpha: float = 0.0
+    shared_lora_a: Optional[np.ndarray] = None    # bf16 bits [2 rs, d]: A of gate, then A of up
+    shared_lora_b: Optional[np.ndarray] = None    # bf16 bits [2 fs, rs]: B of gate, then B of up
+    shared_lora_ad: Optional[np.ndarray] = None   # bf16 bits [rs, fs]: A of down
+    shared_lora_bd: Optional[np.ndarray] = None   # bf16 bits [d, rs]: B of down
     max_cache: int = 8                       # dequantised experts kept (memory bound)
     _cache: dict = field(default_factory=dict, repr=False)
 
@@ -298,6 +308,33 @@ class LayerWeights:
         if "shared" not in self._cache:
             self._cache["shared"] = unpack_blob(self.shared, self.d, self.fs)
         return self._cache["shared"]
+
+
+def shared_ffn(lw: LayerWeights, u: np.ndarray) -> np.ndarray:
+    """The shared expert, with the recovery LoRA on its gate, up and down
+    projections when the layer has one ([Guide] Method, three-stage training:
+    the adapter sits on the attention, linear-attention and shared-expert
+    projections, not on the streamed experts; unmerged adapter execution:
+    each projection is W_int4 x + (alpha / r) B A x):
+        a = Wg u + s Bg Ag u,  c = Wu u + s Bu Au u,  h = silu(a) * c,
+        o = Wd h + s Bd Ad h,  s = alpha / r."""
+    Wg, Wu, Wd = lw.shared_expert()
+    u = np.asarray(u, dtype=np.float64)
+    a = Wg @ u
+    c = Wu @ u
+    rs = lw.shared_lora_rank
+    if rs:
+        sc = lw.shared_lora_alpha / rs
+        A = bf16_to_f64(lw.shared_lora_a)
+        B = bf16_to_f64(lw.shared_lora_b)
+        fs = Wg.shape[0]
+        a = a + sc * (B[:fs] @ (A[:rs] @ u))
+        c = c + sc * (B[fs:] @ (A[rs:] @ u))
+    h = silu(a) * c
+    o = Wd @ h
+    if rs:
+        o = o + sc * (bf16_to_f64(lw.shared_lora_bd) @ (bf16_to_f64(lw.shared_lora_ad) @ h))
+    return o
 
 
 def lora_delta(lw: LayerWeights, u: np.ndarray) -> np.ndarray:
@@ -322,7 +359,7 @@ def moe_block(lw: LayerWeights, u: np.ndarray, idx: Sequence[int], w: Sequence[f
     for e, wj in zip(idx, w):
         y += float(wj) * expert_ffn(lw.expert(int(e)), u)
     if lw.fs and lw.shared is not None:
-        y += shared_gate_value(lw, u) * expert_ffn(lw.shared_expert(), u)
+        y += shared_gate_value(lw, u) * shared_ffn(lw, u)
     y += lora_delta(lw, u)
     return y
 

@@ -693,3 +693,58 @@ def test_head_mlp_hidden_columns_and_zero_fc2():
     lw.head_fc2 = W2
     idx1, w1, z1 = oracle.predict_next(lw, u, 2)
     assert abs(z1[0] - PHI_1) < 1e-15 and z1[4] == 0.5 and list(idx1) == [0, 4]
+
+
+# ----------------------------------------------------------------------------
+# O8b the recovery LoRA on the shared expert's projections
+# ----------------------------------------------------------------------------
+def shared_lora_case():
+    """A layer whose shared expert is zero (W = 0 exactly), with a rank-2
+    adapter of alpha 4 (scale 2) on its projections: A of gate picks u_0,
+    u_1; B of gate sends the first to unit 3 with weight 1/2; A of up picks
+    u_2, u_3, B of up sends the second to unit 3 with weight 1/4; A of down
+    reads unit 3 of h, B of down writes it to output 7."""
+    d, f, rs = 64, 64, 2
+    lw = tiny_layer(d=d, f=f, fs=f, r=0, shared_gate=False)
+    lw.shared = zero_blob(d, f)
+    lw._cache.clear()
+    A = np.zeros((2 * rs, d)); A[0, 0] = A[1, 1] = 1.0; A[2, 2] = A[3, 3] = 1.0
+    B = np.zeros((2 * f, rs)); B[3, 0] = 0.5; B[f + 3, 1] = 0.25
+    Ad = np.zeros((rs, f)); Ad[0, 3] = 1.0
+    Bd = np.zeros((d, rs)); Bd[7, 0] = 1.0
+    lw.shared_lora_rank, lw.shared_lora_alpha = rs, 4.0
+    lw.shared_lora_a, lw.shared_lora_b = oracle.bf16_bits_of(A), oracle.bf16_bits_of(B)
+    lw.shared_lora_ad, lw.shared_lora_bd = oracle.bf16_bits_of(Ad), oracle.bf16_bits_of(Bd)
+    return lw
+
+
+def test_shared_lora_closed_form():
+    """a_3 = 2 (1/2) u_0 = u_0, c_3 = 2 (1/4) u_3 = u_3 / 2, h_3 = silu(u_0) u_3 / 2
+    and o_7 = 2 h_3 = silu(u_0) u_3; with u_0 = 40 (silu(40) = 40 to 1e-16)
+    the shared output is 40 u_3 at 7 and zero elsewhere. A scale of alpha
+    (4x), swapped gate / up adapters, or a down adapter reading u instead of
+    h all give other values."""
+    lw = shared_lora_case()
+    u = np.random.default_rng(41).standard_normal(lw.d)
+    u[0] = 40.0
+    o = oracle.shared_ffn(lw, u)
+    expect = np.zeros(lw.d); expect[7] = 40.0 * u[3]
+    assert np.allclose(o, expect, rtol=1e-14, atol=1e-14)
+    # inside the block, with the gate fixed at 1 and zero routed experts
+    lw.store = np.stack([zero_blob(lw.d, lw.f)] * lw.E)
+    lw._cache.clear()
+    y = oracle.moe_block(lw, u, [0, 1], [0.5, 0.5])
+    assert np.allclose(y, expect, rtol=1e-14, atol=1e-14)
+
+
+def test_shared_lora_zero_b_is_plain_shared():
+    lw = tiny_layer(r=0)
+    u = np.random.default_rng(42).standard_normal(lw.d)
+    plain = oracle.expert_ffn(lw.shared_expert(), u)
+    rs = 4
+    lw.shared_lora_rank, lw.shared_lora_alpha = rs, 8.0
+    lw.shared_lora_a = oracle.bf16_bits_of(np.random.default_rng(43).standard_normal((2 * rs, lw.d)))
+    lw.shared_lora_b = np.zeros((2 * lw.fs, rs), np.uint16)
+    lw.shared_lora_ad = oracle.bf16_bits_of(np.random.default_rng(44).standard_normal((rs, lw.fs)))
+    lw.shared_lora_bd = np.zeros((lw.d, rs), np.uint16)
+    assert np.array_equal(oracle.shared_ffn(lw, u), plain)
