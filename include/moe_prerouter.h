@@ -101,6 +101,12 @@ typedef struct moe_layer_desc {
      * one-hot of the current token, of the previous token]); 0 = the linear
      * path l(x) alone. 0..1024, a multiple of 8; needs a head.              */
     int   head_hidden;
+    /* recovery LoRA on the shared expert's gate, up and down projections
+     * (guide, Method: three-stage training, the adapter on the shared-expert
+     * projections; unmerged adapter execution): rank r_s (0 = none; 1..64,
+     * needs a shared expert) and alpha_s (scale alpha_s / r_s).          */
+    int   shared_lora_rank;
+    float shared_lora_alpha;
 } moe_layer_desc;
 
 typedef struct moe_layer_weights {
@@ -136,6 +142,12 @@ typedef struct moe_layer_weights {
                                          E_next + j for expert j in the previous token's */
     const float*    head_fc1_bias;    /* device fp32 [H1] or NULL            */
     const uint16_t* head_fc2;         /* device bf16 [E_next][H1]            */
+    /* the shared expert's adapter (shared_lora_rank = r_s > 0; else NULL):
+     * gate = Wg u + s Bg Ag u, up = Wu u + s Bu Au u, down = Wd h + s Bd Ad h */
+    const uint16_t* shared_lora_a;    /* device bf16 [2 r_s][d]: Ag, then Au   */
+    const uint16_t* shared_lora_b;    /* device bf16 [2 f_s][r_s]: Bg, then Bu */
+    const uint16_t* shared_lora_ad;   /* device bf16 [r_s][f_s]                */
+    const uint16_t* shared_lora_bd;   /* device bf16 [d][r_s]                  */
 } moe_layer_weights;
 
 /* Per-call inputs and outputs (all device memory). */
@@ -235,7 +247,8 @@ int moe_decode_step(moe_layer* layer, const moe_io* io, int n_tok, void* stream)
  * overlap on one GPU race (issue them on one stream or order them). Only
  * the fused two-kernel decode path is served: 1..16 tokens, n_tok * k <= 64,
  * d and f powers of two (d in 256..2048, f in 64..512, f_s 0 or f).
- * The head's MLP branch (head_hidden > 0) is not served here.
+ * The head's MLP branch (head_hidden > 0) and the shared expert's adapter
+ * (shared_lora_rank > 0) are not served here.
  * d_status (optional, device int32): receives this call's device flag as a
  * status code (MOE_OK, MOE_E_BAD_INDEX, MOE_E_NOT_STAGED). Asynchronous on
  * `stream`. Errors (returned): MOE_E_INVALID, MOE_E_UNSUPPORTED (shape or

@@ -37,7 +37,7 @@ class moe_layer_desc(ctypes.Structure):
         ("lora_rank", ctypes.c_int), ("lora_alpha", ctypes.c_float), ("rms_eps", ctypes.c_float),
         ("act_dtype", ctypes.c_int), ("max_tokens", ctypes.c_int), ("slab_slots", ctypes.c_int),
         ("next_n_experts", ctypes.c_int), ("next_top_k", ctypes.c_int), ("flags", ctypes.c_uint),
-        ("head_hidden", ctypes.c_int),
+        ("head_hidden", ctypes.c_int), ("shared_lora_rank", ctypes.c_int), ("shared_lora_alpha", ctypes.c_float),
     ]
 
 
@@ -45,7 +45,7 @@ class moe_layer_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "expert_store", "shared_blob", "shared_gate", "router", "router_bias", "head", "head_bias",
         "hist_cur", "hist_prev", "lora_a", "lora_b", "norm_gamma", "head_fc1", "head_fc1_onehot", "head_fc1_bias",
-        "head_fc2")]
+        "head_fc2", "shared_lora_a", "shared_lora_b", "shared_lora_ad", "shared_lora_bd")]
 
 
 class moe_io(ctypes.Structure):
@@ -268,15 +268,18 @@ class MoeLayer:
                  head=None, head_bias=None, next_n_experts=0, next_top_k=0, hist_cur=None, hist_prev=None,
                  lora_a=None, lora_b=None, norm_gamma=None, rms_eps=1e-6, fuse_norm_residual=False,
                  resident=True, slab_slots=0, head_fc1=None, head_fc1_onehot=None, head_fc1_bias=None,
-                 head_fc2=None, device="cuda"):
+                 head_fc2=None, shared_lora_a=None, shared_lora_b=None, shared_lora_ad=None, shared_lora_bd=None,
+                 shared_lora_alpha=0.0, device="cuda"):
         import torch
         self._keep = [expert_store, shared_blob, shared_gate, router, router_bias, head, head_bias, hist_cur,
-                      hist_prev, lora_a, lora_b, norm_gamma, head_fc1, head_fc1_onehot, head_fc1_bias, head_fc2]
+                      hist_prev, lora_a, lora_b, norm_gamma, head_fc1, head_fc1_onehot, head_fc1_bias, head_fc2,
+                      shared_lora_a, shared_lora_b, shared_lora_ad, shared_lora_bd]
+        shared_lora_rank = 0 if shared_lora_a is None else int(shared_lora_a.shape[0]) // 2
         flags = (MOE_FUSE_NORM_RESIDUAL if fuse_norm_residual else 0) | (MOE_RESIDENT_STORE if resident else 0)
         head_hidden = 0 if head_fc1 is None else int(head_fc1.shape[0])
         self.desc = moe_layer_desc(d_model, n_experts, top_k, d_ff, d_ff_shared, 64, lora_rank, float(lora_alpha),
                                    float(rms_eps), act_dtype, max_tokens, slab_slots, next_n_experts, next_top_k,
-                                   flags, head_hidden)
+                                   flags, head_hidden, shared_lora_rank, float(shared_lora_alpha))
         self.weights = moe_layer_weights(*[_ptr(t) for t in self._keep])
         nbytes = moe_layer_workspace_bytes(self.desc)
         if nbytes == 0:

@@ -55,6 +55,8 @@ int validate_desc(const moe_layer_desc* d) {
     if (d->max_tokens > 8192) return MOE_E_UNSUPPORTED;
     if (d->head_hidden < 0 || d->head_hidden > kMaxHeadHidden || d->head_hidden % 8) return MOE_E_UNSUPPORTED;
     if (d->head_hidden > 0 && d->next_n_experts <= 0) return MOE_E_INVALID;
+    if (d->shared_lora_rank < 0 || d->shared_lora_rank > 64) return MOE_E_UNSUPPORTED;
+    if (d->shared_lora_rank > 0 && d->d_ff_shared <= 0) return MOE_E_INVALID;
     const bool resident = d->flags & MOE_RESIDENT_STORE;
     if (!resident && (d->slab_slots < 1 || d->slab_slots > 64)) return MOE_E_UNSUPPORTED;
     if (d->flags & ~(MOE_FUSE_NORM_RESIDUAL | MOE_RESIDENT_STORE)) return MOE_E_INVALID;
@@ -109,11 +111,19 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     S.tiles64 = c.take<int32_t>(4 * (size_t)prefill_max_tiles((int)T, (int)K, (int)E, 64));
     S.ob = c.take<float>(T * K * D);
     S.obs = c.take<float>(T * D);
+    S.sau = d->shared_lora_rank > 0 ? c.take<float>(T * 2 * d->shared_lora_rank) : nullptr;
+    S.wf_slora = (d->shared_lora_rank > 0 && !f32) ? c.take<uint32_t>(frag_rows_words(2 * d->shared_lora_rank, (int)D))
+                                                   : nullptr;
     S.a1 = d->head_hidden > 0 ? c.take<double>(T * d->head_hidden) : nullptr;
     S.wf_fc1 = (d->head_hidden > 0 && !f32) ? c.take<uint32_t>(frag_rows_words(d->head_hidden, (int)D)) : nullptr;
     (void)Kn;
     return align_up(c.off, 256);
 }
+
+// With an adapter on the shared expert, the main kernels run without the
+// shared expert (the adapter path adds it); this is the shared width they see.
+inline bool has_shared_lora(const moe_layer* L) { return L->desc.shared_lora_rank > 0; }
+inline int fs_main(const moe_layer* L) { return has_shared_lora(L) ? 0 : L->desc.d_ff_shared; }
 
 ExpertView view_of(const moe_layer* L) {
     ExpertView ev{};
@@ -132,6 +142,11 @@ ExpertView view_of(const moe_layer* L) {
         ev.slot_tag = L->s.slot_tag;
         ev.shared = L->desc.d_ff_shared ? L->s.slab + (size_t)L->slots * L->blob : nullptr;
         ev.shared_tag = L->desc.d_ff_shared ? L->s.slot_tag + L->slots : nullptr;
+    }
+    if (has_shared_lora(L)) {
+        ev.shared = nullptr;
+        ev.shared_tag = nullptr;
+        ev.shared_blob = 0;
     }
     return ev;
 }
@@ -233,6 +248,46 @@ int run_head_mlp(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool
     return MOE_OK;
 }
 
+// The shared expert with its adapter. part 1 (needs u only): A_g u, A_u u and
+// the shared gate on the routing GEMM, then gate/up + SwiGLU; part 2 (after
+// the main path wrote y): down with its adapter, gated, added into y.
+SharedLoraArgs shared_lora_args(const moe_layer* L, const moe_io* io, int n_tok) {
+    const moe_layer_desc& D = L->desc;
+    SharedLoraArgs a{};
+    if (L->resident) {
+        a.blob = (const uint8_t*)L->w.shared_blob;
+    } else {
+        a.blob = L->s.slab + (size_t)L->slots * L->blob;
+        a.tag = L->s.slot_tag + L->slots;
+        a.tag_want = D.n_experts;
+    }
+    a.d = D.d_model; a.f = D.d_ff_shared; a.rs = D.shared_lora_rank;
+    a.scale = D.shared_lora_alpha / (float)D.shared_lora_rank;
+    a.u_pk = L->s.u_pk; a.u_pk_lo = L->s.u_pk_lo;
+    a.sau = L->s.sau;
+    a.b_gu = L->w.shared_lora_b; a.ad = L->w.shared_lora_ad; a.bd = L->w.shared_lora_bd;
+    a.sgate = L->w.shared_gate ? L->s.sgate : nullptr;
+    a.hs = L->s.hs; a.y = io->y_out; a.n_tok = n_tok; a.err = L->s.err;
+    return a;
+}
+
+int run_shared_lora_part1(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
+    const moe_layer_desc& D = L->desc;
+    RouteMMArgs ra{};
+    ra.u_pk = L->s.u_pk; ra.u_pk_lo = L->s.u_pk_lo; ra.d = D.d_model; ra.n_tok = n_tok;
+    ra.lora_a = L->w.shared_lora_a; ra.r = 2 * D.shared_lora_rank; ra.au = L->s.sau;
+    ra.sgate_w = L->w.shared_gate; ra.sgate = L->s.sgate;
+    ra.u_frag = L->s.u_frag; ra.wf_lora = L->s.wf_slora; ra.wf_sgate = L->s.wf_sgate;
+    HIPCHK(launch_route_mm(ra, st, false, false, nullptr));
+    HIPCHK(launch_shared_lora(shared_lora_args(L, io, n_tok), st, true, false));
+    return MOE_OK;
+}
+
+int run_shared_lora_part2(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st) {
+    HIPCHK(launch_shared_lora(shared_lora_args(L, io, n_tok), st, false, true));
+    return MOE_OK;
+}
+
 // defer_in: a previous layer's head top-k to run inside this layer's K_A.
 // defer_out (stack mode): this layer's head top-k is not run here but handed
 // back, for the next layer's K_A to run (its prediction is for the next step).
@@ -243,7 +298,7 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
     if (defer_out) defer_out->pred_idx = nullptr;
     if (took_nxt) *took_nxt = false;
     // shapes outside the fused two-kernel path take the general grouped-GEMM path
-    if (!dec_fast_path_ok(D.d_model, D.d_ff, D.d_ff_shared, n_tok, D.top_k)) {
+    if (!dec_fast_path_ok(D.d_model, D.d_ff, fs_main(L), n_tok, D.top_k)) {
         if (defer_in && defer_in->pred_idx) HIPCHK(launch_topk_job(*defer_in, n_tok, st));
         return run_prefill(L, io, n_tok, st, false, 0, nxt, skip_pro, took_nxt);
     }
@@ -260,16 +315,16 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
     a.route_idx = io->route_idx; a.route_w = io->route_w;
     a.self_idx = need_router ? L->s.self_idx : nullptr; a.self_w = need_router ? L->s.self_w : nullptr;
     a.k = D.top_k; a.E = D.n_experts;
-    a.ev = view_of(L); a.f = D.d_ff; a.fs = D.d_ff_shared;
+    a.ev = view_of(L); a.f = D.d_ff; a.fs = fs_main(L);
     a.head = io->pred_idx ? L->w.head : nullptr; a.En = io->pred_idx ? D.next_n_experts : 0;
     a.lora_a = D.lora_rank ? L->w.lora_a : nullptr; a.r = D.lora_rank;
-    a.sgate_w = D.d_ff_shared ? L->w.shared_gate : nullptr;
+    a.sgate_w = fs_main(L) ? L->w.shared_gate : nullptr;
     a.h = L->s.h; a.hs = L->s.hs; a.logits_h = L->s.logits_h; a.au = L->s.au; a.sgate = L->s.sgate;
     a.meta = L->s.sort_meta; a.active = L->s.active; a.act_off = L->s.act_off; a.perm = L->s.perm;
     a.wsort = L->s.wsort;
     a.used_idx = L->s.used_idx; a.used_w = L->s.used_w; a.user_used_idx = io->used_idx; a.user_used_w = io->used_w;
     a.err = L->s.err;
-    dec_a_blocks(D.d_model, D.d_ff, D.d_ff_shared, n_tok, D.top_k, D.n_experts, a.En, D.lora_rank,
+    dec_a_blocks(D.d_model, D.d_ff, fs_main(L), n_tok, D.top_k, D.n_experts, a.En, D.lora_rank,
                  a.sgate_w != nullptr, &a.nb_h, &a.nb_head, &a.nb_misc);
     if (defer_in && defer_in->pred_idx) a.topk = *defer_in;
 
@@ -297,16 +352,24 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
     const KTime ta{L->profiling ? L->ev_t[2] : nullptr, L->profiling ? L->ev_t[3] : nullptr};
     HIPCHK(launch_dec_a(a, st, &ta));
     if (L->profiling) L->ev_t_used[1] = true;
-    if (io->pred_idx && D.head_hidden > 0) {
-        const int rc = run_head_mlp(L, io, n_tok, st, true);
+    // the prologue (u for the routing GEMM) runs before K_B, which may
+    // overwrite x in place
+    const bool mlp = io->pred_idx && D.head_hidden > 0;
+    if (mlp || has_shared_lora(L)) HIPCHK(launch_prologue(prologue_args(L, io->x_in, n_tok), st));
+    if (mlp) {
+        const int rc = run_head_mlp(L, io, n_tok, st, false);
+        if (rc != MOE_OK) return rc;
+    }
+    if (has_shared_lora(L)) {
+        const int rc = run_shared_lora_part1(L, io, n_tok, st);
         if (rc != MOE_OK) return rc;
     }
 
     DecBArgs b{};
-    b.ev = a.ev; b.d = D.d_model; b.f = D.d_ff; b.fs = D.d_ff_shared; b.k = D.top_k; b.n_tok = n_tok;
+    b.ev = a.ev; b.d = D.d_model; b.f = D.d_ff; b.fs = fs_main(L); b.k = D.top_k; b.n_tok = n_tok;
     b.E = D.n_experts;
     b.route_idx = a.route_idx; b.route_w = a.route_w; b.self_idx = a.self_idx; b.self_w = a.self_w;
-    b.sgate = (D.d_ff_shared && L->w.shared_gate) ? L->s.sgate : nullptr;
+    b.sgate = (fs_main(L) && L->w.shared_gate) ? L->s.sgate : nullptr;
     b.h = L->s.h; b.hs = L->s.hs;
     b.x = (const float*)io->x_in; b.fused = fused;
     b.au = L->s.au; b.lora_b = D.lora_rank ? L->w.lora_b : nullptr; b.r = D.lora_rank;
@@ -326,6 +389,10 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
     const KTime tb{L->profiling ? L->ev_t[4] : nullptr, L->profiling ? L->ev_t[5] : nullptr};
     HIPCHK(launch_dec_b(b, st, &tb));
     if (L->profiling) L->ev_t_used[2] = true;
+    if (has_shared_lora(L)) {
+        const int rc = run_shared_lora_part2(L, io, n_tok, st);
+        if (rc != MOE_OK) return rc;
+    }
     if (L->ev_done) {
         HIPCHK(hipEventRecord(L->ev_done, st));
         L->done_recorded = true;
@@ -369,16 +436,16 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     ra.En = D.next_n_experts; ra.kn = D.next_top_k;
     ra.hist_cur_m = L->w.hist_cur; ra.hist_prev_m = L->w.hist_prev; ra.hist_cur = io->hist_cur; ra.hist_prev = io->hist_prev;
     ra.lora_a = D.lora_rank ? L->w.lora_a : nullptr; ra.r = D.lora_rank;
-    ra.sgate_w = D.d_ff_shared ? L->w.shared_gate : nullptr;
+    ra.sgate_w = fs_main(L) ? L->w.shared_gate : nullptr;
     ra.logits_r = L->s.logits_r; ra.logits_h = L->s.logits_h;
     ra.self_idx = L->s.self_idx; ra.self_w = L->s.self_w;
     ra.pred_idx = io->pred_idx; ra.pred_w = io->pred_w;
     ra.au = L->s.au; ra.sgate = L->s.sgate;
     ra.u_frag = L->s.u_frag;
     ra.wf_router = L->s.wf_router; ra.wf_head = L->s.wf_head; ra.wf_lora = L->s.wf_lora; ra.wf_sgate = L->s.wf_sgate;
-    const bool mm = prefill_mm_ok(D.d_model, D.d_ff, D.d_ff_shared);
+    const bool mm = prefill_mm_ok(D.d_model, D.d_ff, fs_main(L));
     const int max_active = std::min(D.n_experts, n_tok * D.top_k);
-    const bool big = mm && prefill_big_tiles(D.d_model, D.d_ff, D.d_ff_shared, D.act_dtype != MOE_ACT_BF16, n_tok,
+    const bool big = mm && prefill_big_tiles(D.d_model, D.d_ff, fs_main(L), D.act_dtype != MOE_ACT_BF16, n_tok,
                                              D.top_k, max_active);
     const bool reactive = !L->resident && (io->route_idx == nullptr || io->reactive || prefill);
     // the router's top-k runs here when every row self-routes (or the expert
@@ -397,6 +464,10 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
         // off the matrix-core path the head's top-k has its own launch
         if (!mm) HIPCHK(launch_route_topk(ra, st, false, true));
     }
+    if (has_shared_lora(L)) {
+        int rc = run_shared_lora_part1(L, io, n_tok, st);
+        if (rc != MOE_OK) return rc;
+    }
 
     SortArgs sa{};
     sa.route_idx = io->route_idx; sa.route_w = io->route_w; sa.route_shift = route_shift; sa.pre_rows = pre_done;
@@ -408,7 +479,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     sa.err = L->s.err;
     sa.self_topk = sort_topk;
     sa.logits_r = L->s.logits_r; sa.router_bias = L->w.router_bias;
-    sa.ev = view_of(L); sa.fs = D.d_ff_shared;
+    sa.ev = view_of(L); sa.fs = fs_main(L);
     sa.tiles16 = mm ? L->s.tiles : nullptr;
     sa.tiles64 = big ? L->s.tiles64 : nullptr;
     sa.resolve_blobs = !reactive;
@@ -430,9 +501,9 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
 
     GemvArgs ga{};
     ga.ev = view_of(L);
-    ga.d = D.d_model; ga.f = D.d_ff; ga.fs = D.d_ff_shared; ga.k = D.top_k; ga.n_tok = n_tok;
+    ga.d = D.d_model; ga.f = D.d_ff; ga.fs = fs_main(L); ga.k = D.top_k; ga.n_tok = n_tok;
     ga.meta = L->s.sort_meta; ga.active = L->s.active; ga.act_off = L->s.act_off; ga.perm = L->s.perm;
-    ga.used_w = L->s.used_w; ga.sgate = (D.d_ff_shared && L->w.shared_gate) ? L->s.sgate : nullptr;
+    ga.used_w = L->s.used_w; ga.sgate = (fs_main(L) && L->w.shared_gate) ? L->s.sgate : nullptr;
     ga.u_pk = L->s.u_pk; ga.u_pk_lo = L->s.u_pk_lo; ga.usum = L->s.usum; ga.usum_lo = L->s.usum_lo;
     ga.h = L->s.h; ga.hs = L->s.hs;
     ga.x = (const float*)io->x_in; ga.fused = fused;
@@ -456,7 +527,9 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
         if (io->pred_idx && L->w.head)
             pf.head = TopkJob{L->s.logits_h, D.next_n_experts, D.next_top_k, L->w.head_bias, L->w.hist_cur, io->hist_cur,
                               L->w.hist_prev, io->hist_prev, io->pred_idx, io->pred_w};
-        if (nxt) {
+        if (nxt && !has_shared_lora(L)) {
+            // (with the shared adapter the layer's output is complete only
+            // after its own down kernel, so the next norm runs on its own)
             pf.nxt = *nxt;
             if (!combine_norm_ok(pf)) pf.nxt = PrologueArgs{};
             else if (took_nxt) *took_nxt = true;
@@ -466,6 +539,10 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     } else {
         HIPCHK(launch_gateup(ga, st));
         HIPCHK(launch_down(ga, st));
+    }
+    if (has_shared_lora(L)) {
+        int rc = run_shared_lora_part2(L, io, n_tok, st);
+        if (rc != MOE_OK) return rc;
     }
     HIPCHK(hipEventRecord(L->ev_done, st));
     L->done_recorded = true;
@@ -567,6 +644,10 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w, voi
     if ((desc->head_hidden > 0) != (w->head_fc1 != nullptr) || (desc->head_hidden > 0) != (w->head_fc1_onehot != nullptr) ||
         (desc->head_hidden > 0) != (w->head_fc2 != nullptr) || (w->head_fc1_bias && desc->head_hidden <= 0))
         return MOE_E_INVALID;
+    const bool sl = desc->shared_lora_rank > 0;
+    if (sl != (w->shared_lora_a != nullptr) || sl != (w->shared_lora_b != nullptr) ||
+        sl != (w->shared_lora_ad != nullptr) || sl != (w->shared_lora_bd != nullptr))
+        return MOE_E_INVALID;
     const size_t need = carve(desc, nullptr, nullptr);
     if (ws_bytes < need) return MOE_E_CAPACITY;
 
@@ -616,6 +697,7 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w, voi
         if ((e = pack(w->lora_a, desc->lora_rank, L->s.wf_lora)) != hipSuccess) return fail(e);
         if ((e = pack(w->shared_gate, 1, L->s.wf_sgate)) != hipSuccess) return fail(e);
         if ((e = pack(w->head_fc1, desc->head_hidden, L->s.wf_fc1)) != hipSuccess) return fail(e);
+        if ((e = pack(w->shared_lora_a, 2 * desc->shared_lora_rank, L->s.wf_slora)) != hipSuccess) return fail(e);
     }
     if ((e = hipDeviceSynchronize()) != hipSuccess) return fail(e);
     *out = L;
@@ -670,7 +752,7 @@ int moe_decode_noalloc(const moe_layer_desc* desc, const moe_layer_weights* w, c
     if (desc->next_n_experts > 0 && !w->head) return MOE_E_INVALID;
     if ((w->hist_cur || w->hist_prev) && desc->next_n_experts <= 0) return MOE_E_INVALID;
     if (n_tok < 1 || n_tok > desc->max_tokens) return MOE_E_INVALID;
-    if (desc->head_hidden > 0) return MOE_E_UNSUPPORTED;
+    if (desc->head_hidden > 0 || desc->shared_lora_rank > 0) return MOE_E_UNSUPPORTED;
     if (!dec_fast_path_ok(desc->d_model, desc->d_ff, desc->d_ff_shared, n_tok, desc->top_k))
         return MOE_E_UNSUPPORTED;
     if (carve_decode(desc, n_tok, nullptr, nullptr) > kNoallocScratchBytes) return MOE_E_CAPACITY;

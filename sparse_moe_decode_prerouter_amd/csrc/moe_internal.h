@@ -89,6 +89,8 @@ struct Scratch {
     int32_t* tiles64;        // the same with 64-row tiles (many tokens per expert)
     float* ob;               // prefill: [T*k][d] routed expert outputs by assignment
     float* obs;              // prefill: [T][d] shared expert outputs
+    float* sau;              // shared-expert LoRA: [T][2 rs] A_g u, A_u u
+    uint32_t* wf_slora;      // shared-expert LoRA: A rows in MFMA fragment order (bf16 act)
     double* a1;              // head MLP: [T][H1] fc1 hidden-state part
     uint32_t* wf_fc1;        // head MLP: fc1 hidden-state rows in MFMA fragment order (bf16 act)
 };
@@ -203,6 +205,24 @@ struct HeadMlpArgs {
     double* logits; int n_tok;
 };
 hipError_t launch_head_mlp_out(const HeadMlpArgs& a, hipStream_t s);
+// The shared expert with the recovery LoRA on its projections.
+struct SharedLoraArgs {
+    const uint8_t* blob;                 // shared expert blob (device)
+    const int32_t* tag; int tag_want;    // streamed: the shared slot's tag must equal tag_want; nullptr: no check
+    int d; int f; int rs; float scale;
+    const uint32_t* u_pk; const uint32_t* u_pk_lo;   // the prologue's u (pair order), lo part or nullptr
+    const float* sau;                    // [T][2 rs]: A_g u, then A_u u
+    const uint16_t* b_gu;                // [2 f][rs]: B of gate, then B of up
+    const uint16_t* ad;                  // [rs][f]
+    const uint16_t* bd;                  // [d][rs]
+    const float* sgate;                  // [T] or nullptr (gate 1)
+    float* hs;                           // [T][f]
+    float* y;                            // [T][d], added to
+    int n_tok;
+    int32_t* err;
+};
+hipError_t launch_shared_lora(const SharedLoraArgs& a, hipStream_t s, bool gateup, bool down);
+
 // the routing GEMM's per-token top-k launch alone (router and / or head)
 hipError_t launch_route_topk(const RouteMMArgs& a, hipStream_t s, bool router_topk, bool head_topk);
 

@@ -193,6 +193,24 @@ def head_mlp_weights(shape: Shape, layer: int, hidden: int, device="cpu", tag: s
     }
 
 
+def shared_adapter(shape: Shape, layer: int, rank: int, delta_rms: float = 1e-3, device="cpu", tag: str = "w") -> dict:
+    """A and B of a recovery adapter on the shared expert's gate, up and down
+    projections, bf16, entries ~ N(0, sigma) with sigma^2 = delta_rms / sqrt(r):
+    with alpha = r (scale 1) each projection's delta B A then has an RMS of
+    about delta_rms (the pages put the adapter's delta near 1e-3, below the
+    int4 step)."""
+    d, fs = shape.d, shape.fs
+    sig = math.sqrt(delta_rms / math.sqrt(rank))
+    key = (tag, shape.name, layer, "sadapter", rank)
+    return {
+        "shared_lora_a": gaussian((2 * rank, d), sig, key + ("a",), device).bfloat16(),
+        "shared_lora_b": gaussian((2 * fs, rank), sig, key + ("b",), device).bfloat16(),
+        "shared_lora_ad": gaussian((rank, fs), sig, key + ("ad",), device).bfloat16(),
+        "shared_lora_bd": gaussian((d, rank), sig, key + ("bd",), device).bfloat16(),
+        "shared_lora_alpha": float(rank),
+    }
+
+
 def activations(shape: Shape, n_tok: int, key, device="cpu", dtype=None) -> torch.Tensor:
     """x ~ N(0, 1), [n_tok, d]; dtype defaults to the shape's act dtype."""
     x = gaussian((n_tok, shape.d), 1.0, ("act", shape.name) + tuple(key), device)

@@ -44,6 +44,12 @@ def oracle_layer(shape: synth.Shape, w: dict, act=None) -> oracle.LayerWeights:
         head_fc1_oh=b(w["head_fc1_onehot"]) if w.get("head_fc1_onehot") is not None else None,
         head_fc1_bias=w["head_fc1_bias"].double().cpu().numpy() if w.get("head_fc1_bias") is not None else None,
         head_fc2=b(w["head_fc2"]) if w.get("head_fc2") is not None else None,
+        shared_lora_rank=int(w["shared_lora_a"].shape[0]) // 2 if w.get("shared_lora_a") is not None else 0,
+        shared_lora_alpha=float(w.get("shared_lora_alpha", 0.0)),
+        shared_lora_a=b(w["shared_lora_a"]) if w.get("shared_lora_a") is not None else None,
+        shared_lora_b=b(w["shared_lora_b"]) if w.get("shared_lora_b") is not None else None,
+        shared_lora_ad=b(w["shared_lora_ad"]) if w.get("shared_lora_ad") is not None else None,
+        shared_lora_bd=b(w["shared_lora_bd"]) if w.get("shared_lora_bd") is not None else None,
     )
 
 
@@ -72,7 +78,10 @@ def gpu_layer(shape: synth.Shape, w: dict, *, fused: bool, resident: bool = True
         lora_a=dv(w["lora_a"]), lora_b=dv(w["lora_b"]), norm_gamma=dv(w["gamma"]), rms_eps=shape.eps,
         fuse_norm_residual=fused, resident=resident, slab_slots=slab_slots,
         head_fc1=dv(w.get("head_fc1")) if head else None, head_fc1_onehot=dv(w.get("head_fc1_onehot")) if head else None,
-        head_fc1_bias=dv(w.get("head_fc1_bias")) if head else None, head_fc2=dv(w.get("head_fc2")) if head else None)
+        head_fc1_bias=dv(w.get("head_fc1_bias")) if head else None, head_fc2=dv(w.get("head_fc2")) if head else None,
+        shared_lora_a=dv(w.get("shared_lora_a")), shared_lora_b=dv(w.get("shared_lora_b")),
+        shared_lora_ad=dv(w.get("shared_lora_ad")), shared_lora_bd=dv(w.get("shared_lora_bd")),
+        shared_lora_alpha=w.get("shared_lora_alpha", 0.0))
 
 
 def rel_l2_rows(got: np.ndarray, ref: np.ndarray) -> float:

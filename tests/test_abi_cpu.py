@@ -43,7 +43,8 @@ def desc(**kw):
     import sparse_moe_decode_prerouter_amd as moe
     base = dict(d_model=2048, n_experts=256, top_k=4, d_ff=512, d_ff_shared=512, group_size=64, lora_rank=16,
                 lora_alpha=16.0, rms_eps=1e-6, act_dtype=moe.MOE_ACT_BF16, max_tokens=4, slab_slots=5,
-                next_n_experts=256, next_top_k=4, flags=moe.MOE_FUSE_NORM_RESIDUAL, head_hidden=0)
+                next_n_experts=256, next_top_k=4, flags=moe.MOE_FUSE_NORM_RESIDUAL, head_hidden=0,
+                shared_lora_rank=0, shared_lora_alpha=0.0)
     base.update(kw)
     return moe.moe_layer_desc(*[base[f] for f, _ in moe.moe_layer_desc._fields_])
 
@@ -58,7 +59,8 @@ def test_workspace_bytes_and_validation():
     for bad in (dict(group_size=32), dict(d_model=100), dict(top_k=9), dict(top_k=0), dict(d_ff_shared=256),
                 dict(n_experts=2000), dict(act_dtype=7), dict(slab_slots=0), dict(next_top_k=0),
                 dict(flags=0x80), dict(max_tokens=0), dict(head_hidden=12), dict(head_hidden=2048),
-                dict(head_hidden=256, next_n_experts=0, next_top_k=0)):
+                dict(head_hidden=256, next_n_experts=0, next_top_k=0), dict(shared_lora_rank=65),
+                dict(shared_lora_rank=8, d_ff_shared=0)):
         assert moe.moe_layer_workspace_bytes(desc(**bad)) == 0, bad
 
 
