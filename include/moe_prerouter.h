@@ -79,6 +79,23 @@ extern "C" {
 /* expert_store / shared_blob are device memory holding every expert: no
  * slab, no copies; moe_stage_experts only validates ids.                   */
 #define MOE_RESIDENT_STORE      0x2u
+/* streamed mode: staging runs on the device. The pinned store is mapped into
+ * the device's address space; the routing on the device drives a plan kernel
+ * (the sticky-slot plan of moe_plan_slots on the GPU slot table) and a copy
+ * kernel, with no host read-back (moe_stage_experts_device; calls that route
+ * themselves stage this way inside the call).                              */
+#define MOE_DEVICE_STAGING      0x4u
+/* with MOE_DEVICE_STAGING: two slab buffers (the guide's Key terms describe
+ * staged decode with fixed slots in two alternating buffers): calls read the
+ * buffer chosen by moe_layer_use_buffer while the other one is staged for
+ * the next step.                                                          */
+#define MOE_DOUBLE_SLAB         0x8u
+
+/* staging modes of a stack (moe_stack_set_staging) */
+#define MOE_STAGE_OFF           0
+#define MOE_STAGE_PREROUTED     1   /* one token ahead: layer l's experts for step t+1 are copied on the
+                                       copy stream as soon as head l-1's prediction at step t is final */
+#define MOE_STAGE_ON_DEMAND     2   /* reactive: every layer routes itself and stages before it computes */
 
 typedef struct moe_layer_desc {
     int   d_model;        /* d: multiple of 256, <= 8192                          */
@@ -221,8 +238,27 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w,
 int moe_stage_experts(moe_layer* layer, const int32_t* h_expert_ids, int n_ids,
                       void* copy_stream);
 
+/* Device-initiated staging (layers created with MOE_DEVICE_STAGING): the
+ * n_ids routing entries at d_ids (device int32, duplicates allowed, negative
+ * entries absent) name the experts slab buffer `buffer` must hold. A plan
+ * kernel applies the sticky-slot plan to that buffer's GPU slot table and a
+ * copy kernel copies the changed blobs from the mapped pinned store, both on
+ * `stream`, with no host synchronisation ("staged decode" and "incr_stack",
+ * guide, Key terms); the next call reading `buffer` waits for them. Single
+ * slab: the copies wait for the layer's last call. Double slab: the caller
+ * orders `stream` after the last call that read `buffer`. More distinct
+ * experts than slots sets the NOT_STAGED flag and stages nothing.
+ * Errors: MOE_E_INVALID (null, buffer out of range), MOE_E_UNSUPPORTED
+ * (layer without device staging), MOE_E_HIP.                               */
+int moe_stage_experts_device(moe_layer* layer, const int32_t* d_ids, int n_ids, int buffer, void* stream);
+
+/* The slab buffer later calls read (0, or 0/1 with MOE_DOUBLE_SLAB).        */
+int moe_layer_use_buffer(moe_layer* layer, int buffer);
+
 /* Host copy of the current slot table (expert id per routed slot, -1 empty;
- * n_slots entries) and the number of bytes copied by staging so far.        */
+ * n_slots entries) and the number of bytes copied by staging so far. Layers
+ * with device staging: the table of the current buffer, read from the device
+ * after a device synchronisation.                                           */
 int moe_layer_slots(const moe_layer* layer, int32_t* h_slot_expert, int n_slots,
                     uint64_t* staged_bytes);
 
@@ -305,6 +341,15 @@ void moe_layer_destroy(moe_layer* layer);
  *   token 0 and layer 0 self-route. x is updated in place; used_* as above;
  *   pred_* (optional) receive each head's unshifted predictions; without
  *   them the predictions pass through the stack's workspace.
+ * moe_stack_set_staging: for stacks of streamed layers with device staging:
+ *   mode MOE_STAGE_PREROUTED stages, during decode step t, each layer l >= 1's
+ *   routing for step t+1 on copy_stream into the buffer step t+1 reads (with
+ *   double slabs the other one, so the copies overlap the rest of step t;
+ *   with one slab after layer l's call finished), and layer l at step t+1
+ *   waits for it; layer 0 and every layer of the first step route themselves
+ *   and stage inside the call. MOE_STAGE_ON_DEMAND: every layer routes itself
+ *   at every step and stages before it computes (the route_* inputs are
+ *   ignored). MOE_STAGE_OFF: the caller stages (moe_stage_experts).
  * moe_stack_set_trace: with d_x_trace non-NULL (device fp32, n_floats), every
  *   later stack call first copies layer l's input residual stream [n_tok][d]
  *   to d_x_trace + l * n_tok * d (a device-to-device copy per layer, for
@@ -319,6 +364,7 @@ int moe_stack_decode(moe_stack* st, const float* x_in, float* x_out, int n_tok,
 int moe_stack_prefill(moe_stack* st, float* x, int n_tok, int32_t* used_idx, float* used_w,
                       int32_t* pred_idx, float* pred_w, void* stream);
 int moe_stack_set_trace(moe_stack* st, float* d_x_trace, size_t n_floats);
+int moe_stack_set_staging(moe_stack* st, void* copy_stream, int mode);
 void moe_stack_destroy(moe_stack* st);
 
 /* ---- measurement --------------------------------------------------------

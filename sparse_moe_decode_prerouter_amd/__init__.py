@@ -28,6 +28,11 @@ MOE_ACT_F32 = 0
 MOE_ACT_BF16 = 1
 MOE_FUSE_NORM_RESIDUAL = 0x1
 MOE_RESIDENT_STORE = 0x2
+MOE_DEVICE_STAGING = 0x4
+MOE_DOUBLE_SLAB = 0x8
+MOE_STAGE_OFF = 0
+MOE_STAGE_PREROUTED = 1
+MOE_STAGE_ON_DEMAND = 2
 
 
 class moe_layer_desc(ctypes.Structure):
@@ -73,6 +78,9 @@ def _load():
         "moe_layer_workspace_bytes": (Z, [P]),
         "moe_layer_create": (I, [P, P, P, Z, ctypes.POINTER(P)]),
         "moe_stage_experts": (I, [P, P, I, P]),
+        "moe_stage_experts_device": (I, [P, P, I, I, P]),
+        "moe_layer_use_buffer": (I, [P, I]),
+        "moe_stack_set_staging": (I, [P, P, I]),
         "moe_layer_slots": (I, [P, P, I, P]),
         "moe_decode_step": (I, [P, P, I, P]),
         "moe_decode_noalloc": (I, [P, P, P, I, P, P]),
@@ -100,6 +108,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("moe_expert_blob_bytes", "moe_layer_workspace_bytes", "moe_layer_create", "moe_stage_experts",
+            "moe_stage_experts_device", "moe_layer_use_buffer", "moe_stack_set_staging",
             "moe_layer_slots", "moe_decode_step", "moe_decode_noalloc", "moe_prefill", "moe_layer_sync_status", "moe_layer_destroy",
             "moe_status_str", "moe_last_hip_error", "moe_plan_slots", "moe_stack_workspace_bytes",
             "moe_stack_create", "moe_stack_set_trace", "moe_stack_decode",
@@ -131,6 +140,24 @@ def moe_stage_experts(handle: int, ids: Sequence[int], copy_stream: int = 0) -> 
     rc = _lib.moe_stage_experts(handle, arr, len(ids), ctypes.c_void_p(copy_stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_stage_experts")
+
+
+def moe_stage_experts_device(handle: int, ids_ptr: int, n_ids: int, buffer: int, stream: int = 0) -> None:
+    rc = _lib.moe_stage_experts_device(handle, ids_ptr, n_ids, buffer, ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stage_experts_device")
+
+
+def moe_layer_use_buffer(handle: int, buffer: int) -> None:
+    rc = _lib.moe_layer_use_buffer(handle, buffer)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layer_use_buffer")
+
+
+def moe_stack_set_staging(stack: int, copy_stream: int, mode: int) -> None:
+    rc = _lib.moe_stack_set_staging(stack, ctypes.c_void_p(copy_stream), mode)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stack_set_staging")
 
 
 def moe_layer_slots(handle: int, n_slots: int):
@@ -269,13 +296,14 @@ class MoeLayer:
                  lora_a=None, lora_b=None, norm_gamma=None, rms_eps=1e-6, fuse_norm_residual=False,
                  resident=True, slab_slots=0, head_fc1=None, head_fc1_onehot=None, head_fc1_bias=None,
                  head_fc2=None, shared_lora_a=None, shared_lora_b=None, shared_lora_ad=None, shared_lora_bd=None,
-                 shared_lora_alpha=0.0, device="cuda"):
+                 shared_lora_alpha=0.0, device_staging=False, double_slab=False, device="cuda"):
         import torch
         self._keep = [expert_store, shared_blob, shared_gate, router, router_bias, head, head_bias, hist_cur,
                       hist_prev, lora_a, lora_b, norm_gamma, head_fc1, head_fc1_onehot, head_fc1_bias, head_fc2,
                       shared_lora_a, shared_lora_b, shared_lora_ad, shared_lora_bd]
         shared_lora_rank = 0 if shared_lora_a is None else int(shared_lora_a.shape[0]) // 2
-        flags = (MOE_FUSE_NORM_RESIDUAL if fuse_norm_residual else 0) | (MOE_RESIDENT_STORE if resident else 0)
+        flags = (MOE_FUSE_NORM_RESIDUAL if fuse_norm_residual else 0) | (MOE_RESIDENT_STORE if resident else 0) \
+            | (MOE_DEVICE_STAGING if device_staging else 0) | (MOE_DOUBLE_SLAB if double_slab else 0)
         head_hidden = 0 if head_fc1 is None else int(head_fc1.shape[0])
         self.desc = moe_layer_desc(d_model, n_experts, top_k, d_ff, d_ff_shared, 64, lora_rank, float(lora_alpha),
                                    float(rms_eps), act_dtype, max_tokens, slab_slots, next_n_experts, next_top_k,
@@ -298,6 +326,13 @@ class MoeLayer:
 
     def slots(self):
         return moe_layer_slots(self.handle, self.slab_slots)
+
+    def stage_device(self, ids, buffer=0, stream=None):
+        """ids: device int32 tensor of routing entries."""
+        moe_stage_experts_device(self.handle, ids.data_ptr(), ids.numel(), buffer, _stream_ptr(stream))
+
+    def use_buffer(self, buffer):
+        moe_layer_use_buffer(self.handle, buffer)
 
     def _io(self, x, y, route_idx, route_w, used, pred, hist_cur, hist_prev, reactive, self_rows=0):
         import torch
@@ -370,6 +405,11 @@ class MoeStack:
         self.handle = moe_stack_create(hs, (self.workspace.data_ptr() + 255) // 256 * 256, nbytes)
         self.k = self.layers[0].top_k
         self.trace = None
+
+    def set_staging(self, mode, copy_stream=None):
+        """Device staging driven by the stack (MOE_STAGE_PREROUTED / _ON_DEMAND / _OFF)."""
+        self.copy_stream = copy_stream
+        moe_stack_set_staging(self.handle, 0 if copy_stream is None else copy_stream.cuda_stream, mode)
 
     def set_trace(self, trace):
         """trace: device fp32 tensor [n_layers, n_tok, d] receiving each layer's

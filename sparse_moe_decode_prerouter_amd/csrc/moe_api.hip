@@ -25,6 +25,8 @@ thread_local int g_last_hip = 0;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+constexpr int kStageCopyBlocks = 32;     // blocks of a device staging copy (PCIe-bound)
+
 struct Carver {
     uint8_t* base;
     size_t off = 0;
@@ -58,8 +60,13 @@ int validate_desc(const moe_layer_desc* d) {
     if (d->shared_lora_rank < 0 || d->shared_lora_rank > 64) return MOE_E_UNSUPPORTED;
     if (d->shared_lora_rank > 0 && d->d_ff_shared <= 0) return MOE_E_INVALID;
     const bool resident = d->flags & MOE_RESIDENT_STORE;
-    if (!resident && (d->slab_slots < 1 || d->slab_slots > 64)) return MOE_E_UNSUPPORTED;
-    if (d->flags & ~(MOE_FUSE_NORM_RESIDUAL | MOE_RESIDENT_STORE)) return MOE_E_INVALID;
+    // host staging plans up to 64 slots per call; device staging up to kMaxStageSlots
+    const int max_slots = (d->flags & MOE_DEVICE_STAGING) ? kMaxStageSlots : 64;
+    if (!resident && (d->slab_slots < 1 || d->slab_slots > max_slots)) return MOE_E_UNSUPPORTED;
+    if (d->flags & ~(MOE_FUSE_NORM_RESIDUAL | MOE_RESIDENT_STORE | MOE_DEVICE_STAGING | MOE_DOUBLE_SLAB))
+        return MOE_E_INVALID;
+    if ((d->flags & (MOE_DEVICE_STAGING | MOE_DOUBLE_SLAB)) && resident) return MOE_E_INVALID;
+    if ((d->flags & MOE_DOUBLE_SLAB) && !(d->flags & MOE_DEVICE_STAGING)) return MOE_E_INVALID;
     return MOE_OK;
 }
 
@@ -74,11 +81,14 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
     const size_t slots = resident ? 0 : (size_t)d->slab_slots;
     const bool f32 = d->act_dtype == MOE_ACT_F32;
     const size_t nas = std::min(E, T * K);
+    const size_t nbuf = (d->flags & MOE_DOUBLE_SLAB) ? 2 : 1;
     S.err = c.take<int32_t>(64);
     S.counters = c.take<uint32_t>(16);
-    S.slot_of = c.take<int32_t>(E);
-    S.slot_tag = c.take<int32_t>(slots + 1);
-    S.slab = resident ? nullptr : c.take<uint8_t>((slots + (d->d_ff_shared ? 1 : 0)) * blob);
+    S.slot_of = c.take<int32_t>(nbuf * E);
+    S.slot_tag = c.take<int32_t>(nbuf * (slots + 1));
+    S.slab = resident ? nullptr : c.take<uint8_t>(nbuf * (slots + (d->d_ff_shared ? 1 : 0)) * blob);
+    S.stage_plan = c.take<int32_t>(nbuf * stage_plan_ints((int)slots));
+    S.stage_bytes = c.take<unsigned long long>(1);
     S.u_pk = c.take<uint32_t>(T * D / 2);
     S.u_pk_lo = f32 ? c.take<uint32_t>(T * D / 2) : nullptr;
     // the routing GEMM's fragment-ordered operands (bf16 activations)
@@ -125,6 +135,13 @@ size_t carve(const moe_layer_desc* d, uint8_t* base, Scratch* s) {
 inline bool has_shared_lora(const moe_layer* L) { return L->desc.shared_lora_rank > 0; }
 inline int fs_main(const moe_layer* L) { return has_shared_lora(L) ? 0 : L->desc.d_ff_shared; }
 
+// slab buffer b of a streamed layer: its blobs and its slot tables
+inline uint8_t* buf_slab(const moe_layer* L, int b) {
+    return L->s.slab + (size_t)b * (L->slots + (L->desc.d_ff_shared ? 1 : 0)) * L->blob;
+}
+inline int32_t* buf_slot_of(const moe_layer* L, int b) { return L->s.slot_of + (size_t)b * L->desc.n_experts; }
+inline int32_t* buf_slot_tag(const moe_layer* L, int b) { return L->s.slot_tag + (size_t)b * (L->slots + 1); }
+
 ExpertView view_of(const moe_layer* L) {
     ExpertView ev{};
     ev.E = L->desc.n_experts;
@@ -137,11 +154,12 @@ ExpertView view_of(const moe_layer* L) {
         ev.shared = (const uint8_t*)L->w.shared_blob;
         ev.shared_tag = nullptr;
     } else {
-        ev.base = L->s.slab;
-        ev.slot_of = L->s.slot_of;
-        ev.slot_tag = L->s.slot_tag;
-        ev.shared = L->desc.d_ff_shared ? L->s.slab + (size_t)L->slots * L->blob : nullptr;
-        ev.shared_tag = L->desc.d_ff_shared ? L->s.slot_tag + L->slots : nullptr;
+        const int b = L->cur_buf;
+        ev.base = buf_slab(L, b);
+        ev.slot_of = buf_slot_of(L, b);
+        ev.slot_tag = buf_slot_tag(L, b);
+        ev.shared = L->desc.d_ff_shared ? buf_slab(L, b) + (size_t)L->slots * L->blob : nullptr;
+        ev.shared_tag = L->desc.d_ff_shared ? buf_slot_tag(L, b) + L->slots : nullptr;
     }
     if (has_shared_lora(L)) {
         ev.shared = nullptr;
@@ -209,6 +227,18 @@ int reactive_stage(moe_layer* L, const int32_t* d_idx, int n_tok, hipStream_t st
     std::sort(want.begin(), want.end());
     want.erase(std::unique(want.begin(), want.end()), want.end());
     return stage_set(L, want, st);
+}
+
+// device-initiated staging of buffer b from routing entries on the device
+int stage_device(moe_layer* L, const int32_t* d_ids, int n_ids, int b, hipStream_t st) {
+    DevStageArgs a{};
+    a.ids = d_ids; a.n_ids = n_ids; a.E = L->desc.n_experts; a.slots = L->slots;
+    a.slot_of = buf_slot_of(L, b); a.slot_tag = buf_slot_tag(L, b);
+    a.store = L->store_dev; a.shared = L->desc.d_ff_shared ? L->shared_dev : nullptr;
+    a.slab = buf_slab(L, b); a.blob = L->blob; a.sblob = L->sblob;
+    a.plan = L->s.stage_plan + (size_t)b * stage_plan_ints(L->slots); a.bytes = L->s.stage_bytes; a.err = L->s.err;
+    HIPCHK(launch_stage_device(a, kStageCopyBlocks, st));
+    return MOE_OK;
 }
 
 // merged routing (given rows + self rows) into `dst`, for the reactive read-back
@@ -291,19 +321,22 @@ int run_shared_lora_part2(moe_layer* L, const moe_io* io, int n_tok, hipStream_t
 // defer_in: a previous layer's head top-k to run inside this layer's K_A.
 // defer_out (stack mode): this layer's head top-k is not run here but handed
 // back, for the next layer's K_A to run (its prediction is for the next step).
+// pred_ready (stack staging): recorded once the prediction of the previous
+// layer's head (run inside this call's first launch) is final
 int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const TopkJob* defer_in = nullptr,
                TopkJob* defer_out = nullptr, const PrologueArgs* nxt = nullptr, bool skip_pro = false,
-               bool* took_nxt = nullptr) {
+               bool* took_nxt = nullptr, hipEvent_t pred_ready = nullptr) {
     const moe_layer_desc& D = L->desc;
     if (defer_out) defer_out->pred_idx = nullptr;
     if (took_nxt) *took_nxt = false;
     // shapes outside the fused two-kernel path take the general grouped-GEMM path
     if (!dec_fast_path_ok(D.d_model, D.d_ff, fs_main(L), n_tok, D.top_k)) {
         if (defer_in && defer_in->pred_idx) HIPCHK(launch_topk_job(*defer_in, n_tok, st));
+        if (pred_ready) HIPCHK(hipEventRecord(pred_ready, st));
         return run_prefill(L, io, n_tok, st, false, 0, nxt, skip_pro, took_nxt);
     }
     const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
-    if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
+    if (L->staged_pending_buf[L->cur_buf]) HIPCHK(hipStreamWaitEvent(st, L->ev_staged_buf[L->cur_buf], 0));
     const bool need_router = io->route_idx == nullptr || io->self_rows;
     if (need_router && !L->w.router) return MOE_E_INVALID;
 
@@ -346,12 +379,13 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
             HIPCHK(hipGetLastError());
             src = L->s.used_idx;
         }
-        int rc = reactive_stage(L, src, n_tok, st);
+        int rc = L->dev_staging ? stage_device(L, src, n, L->cur_buf, st) : reactive_stage(L, src, n_tok, st);
         if (rc != MOE_OK) return rc;
     }
     const KTime ta{L->profiling ? L->ev_t[2] : nullptr, L->profiling ? L->ev_t[3] : nullptr};
     HIPCHK(launch_dec_a(a, st, &ta));
     if (L->profiling) L->ev_t_used[1] = true;
+    if (pred_ready) HIPCHK(hipEventRecord(pred_ready, st));
     // the prologue (u for the routing GEMM) runs before K_B, which may
     // overwrite x in place
     const bool mlp = io->pred_idx && D.head_hidden > 0;
@@ -424,7 +458,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     const moe_layer_desc& D = L->desc;
     const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
     if (took_nxt) *took_nxt = false;
-    if (L->staged_pending) HIPCHK(hipStreamWaitEvent(st, L->ev_staged, 0));
+    if (L->staged_pending_buf[L->cur_buf]) HIPCHK(hipStreamWaitEvent(st, L->ev_staged_buf[L->cur_buf], 0));
 
     if (!skip_pro) HIPCHK(launch_prologue(prologue_args(L, io->x_in, n_tok), st));
 
@@ -485,7 +519,11 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     sa.resolve_blobs = !reactive;
     HIPCHK(launch_sort(sa, st));
 
-    if (reactive) {
+    if (reactive && L->dev_staging) {
+        // reactive on the device: the sorted routing drives the staging
+        int rc = stage_device(L, L->s.used_idx, n_tok * D.top_k, L->cur_buf, st);
+        if (rc != MOE_OK) return rc;
+    } else if (reactive) {
         // reactive: the routing exists only now; read it back and stage it
         const size_t nk = (size_t)n_tok * D.top_k;
         HIPCHK(hipMemcpyAsync(L->h_readback, L->s.used_idx, nk * sizeof(int32_t), hipMemcpyDeviceToHost, st));
@@ -668,6 +706,9 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w, voi
         L->n_cu = ncu;
     }
     L->slots = L->resident ? 0 : desc->slab_slots;
+    L->nbuf = (desc->flags & MOE_DOUBLE_SLAB) ? 2 : 1;
+    L->cur_buf = 0;
+    L->dev_staging = desc->flags & MOE_DEVICE_STAGING;
     L->h_slot_expert = new int32_t[std::max(1, L->slots)];
     L->h_last_staged = new int32_t[std::max(1, L->slots)];
     std::fill(L->h_slot_expert, L->h_slot_expert + std::max(1, L->slots), -1);
@@ -677,12 +718,26 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w, voi
     if ((e = hipGetDevice(&L->dev)) != hipSuccess) return fail(e);
     if ((e = hipEventCreateWithFlags(&L->ev_staged, hipEventDisableTiming)) != hipSuccess) return fail(e);
     if ((e = hipEventCreateWithFlags(&L->ev_done, hipEventDisableTiming)) != hipSuccess) return fail(e);
+    L->ev_staged_buf[0] = L->ev_staged;
+    if ((e = hipEventCreateWithFlags(&L->ev_staged_buf[1], hipEventDisableTiming)) != hipSuccess) return fail(e);
+    if ((e = hipEventCreateWithFlags(&L->ev_pred, hipEventDisableTiming)) != hipSuccess) return fail(e);
+    if (L->dev_staging) {
+        // the pinned store (and shared blob) as the device sees them
+        void* p = nullptr;
+        if ((e = hipHostGetDevicePointer(&p, const_cast<void*>(w->expert_store), 0)) != hipSuccess) return fail(e);
+        L->store_dev = (const uint8_t*)p;
+        if (w->shared_blob) {
+            if ((e = hipHostGetDevicePointer(&p, const_cast<void*>(w->shared_blob), 0)) != hipSuccess) return fail(e);
+            L->shared_dev = (const uint8_t*)p;
+        }
+    }
     if ((e = hipHostMalloc((void**)&L->h_readback, sizeof(int32_t) * desc->max_tokens * desc->top_k, 0)) != hipSuccess)
         return fail(e);
     if ((e = hipMemset(L->s.err, 0, 64 * sizeof(int32_t))) != hipSuccess) return fail(e);
     if ((e = hipMemset(L->s.counters, 0, 16 * sizeof(uint32_t))) != hipSuccess) return fail(e);
-    if ((e = hipMemset(L->s.slot_of, 0xFF, sizeof(int32_t) * desc->n_experts)) != hipSuccess) return fail(e);
-    if ((e = hipMemset(L->s.slot_tag, 0xFF, sizeof(int32_t) * (L->slots + 1))) != hipSuccess) return fail(e);
+    if ((e = hipMemset(L->s.slot_of, 0xFF, sizeof(int32_t) * desc->n_experts * L->nbuf)) != hipSuccess) return fail(e);
+    if ((e = hipMemset(L->s.slot_tag, 0xFF, sizeof(int32_t) * (L->slots + 1) * L->nbuf)) != hipSuccess) return fail(e);
+    if ((e = hipMemset(L->s.stage_bytes, 0, sizeof(unsigned long long))) != hipSuccess) return fail(e);
     {
         // tile-ordered copies of the routing-side rows for the prefill routing
         // GEMM (contiguous 1 KB loads); a set without its rows is not used
@@ -714,18 +769,49 @@ int moe_stage_experts(moe_layer* L, const int32_t* ids, int n_ids, void* copy_st
     std::sort(want.begin(), want.end());
     want.erase(std::unique(want.begin(), want.end()), want.end());
     if (L->resident) return MOE_OK;
+    if (L->dev_staging) return MOE_E_UNSUPPORTED;      // one staging mode per layer
     if ((int)want.size() > L->slots) return MOE_E_CAPACITY;
     hipStream_t cs = (hipStream_t)copy_stream;
     if (L->done_recorded) HIPCHK(hipStreamWaitEvent(cs, L->ev_done, 0));
     int rc = stage_set(L, want, cs);
     if (rc != MOE_OK) return rc;
     HIPCHK(hipEventRecord(L->ev_staged, cs));
-    L->staged_pending = true;
+    L->staged_pending_buf[0] = true;
+    return MOE_OK;
+}
+
+int moe_stage_experts_device(moe_layer* L, const int32_t* d_ids, int n_ids, int buffer, void* stream) {
+    if (!L || n_ids < 0 || (n_ids > 0 && !d_ids) || buffer < 0) return MOE_E_INVALID;
+    if (!L->dev_staging || !L->store_dev) return MOE_E_UNSUPPORTED;
+    if (buffer >= L->nbuf) return MOE_E_INVALID;
+    hipStream_t cs = (hipStream_t)stream;
+    if (L->nbuf == 1 && L->done_recorded) HIPCHK(hipStreamWaitEvent(cs, L->ev_done, 0));
+    int rc = stage_device(L, d_ids, n_ids, buffer, cs);
+    if (rc != MOE_OK) return rc;
+    HIPCHK(hipEventRecord(L->ev_staged_buf[buffer], cs));
+    L->staged_pending_buf[buffer] = true;
+    return MOE_OK;
+}
+
+int moe_layer_use_buffer(moe_layer* L, int buffer) {
+    if (!L || buffer < 0 || buffer >= std::max(1, L->nbuf)) return MOE_E_INVALID;
+    L->cur_buf = buffer;
     return MOE_OK;
 }
 
 int moe_layer_slots(const moe_layer* L, int32_t* h_slot_expert, int n_slots, uint64_t* staged_bytes) {
     if (!L) return MOE_E_INVALID;
+    if (L->dev_staging) {
+        std::vector<int32_t> tags(std::max(1, L->slots), -1);
+        unsigned long long dev_bytes = 0;
+        HIPCHK(hipDeviceSynchronize());
+        HIPCHK(hipMemcpy(tags.data(), buf_slot_tag(L, L->cur_buf), sizeof(int32_t) * L->slots, hipMemcpyDeviceToHost));
+        HIPCHK(hipMemcpy(&dev_bytes, L->s.stage_bytes, sizeof(dev_bytes), hipMemcpyDeviceToHost));
+        if (h_slot_expert)
+            for (int i = 0; i < n_slots; ++i) h_slot_expert[i] = i < L->slots ? tags[i] : -1;
+        if (staged_bytes) *staged_bytes = dev_bytes;
+        return MOE_OK;
+    }
     if (h_slot_expert) {
         for (int i = 0; i < n_slots; ++i) h_slot_expert[i] = i < L->slots ? L->h_slot_expert[i] : -1;
     }
@@ -806,6 +892,8 @@ void moe_layer_destroy(moe_layer* L) {
     for (int i = 0; i < 6; ++i)
         if (L->ev_t[i]) (void)hipEventDestroy(L->ev_t[i]);
     if (L->ev_staged) (void)hipEventDestroy(L->ev_staged);
+    if (L->ev_staged_buf[1]) (void)hipEventDestroy(L->ev_staged_buf[1]);
+    if (L->ev_pred) (void)hipEventDestroy(L->ev_pred);
     if (L->ev_done) (void)hipEventDestroy(L->ev_done);
     if (L->h_readback) (void)hipHostFree(L->h_readback);
     delete[] L->h_slot_expert;
@@ -894,6 +982,16 @@ int moe_stack_create(moe_layer* const* layers, int n, void* d_workspace, size_t 
     return MOE_OK;
 }
 
+int moe_stack_set_staging(moe_stack* S, void* copy_stream, int mode) {
+    if (!S || mode < MOE_STAGE_OFF || mode > MOE_STAGE_ON_DEMAND) return MOE_E_INVALID;
+    if (mode != MOE_STAGE_OFF)
+        for (int l = 0; l < S->n; ++l)
+            if (!S->layers[l]->dev_staging) return MOE_E_UNSUPPORTED;
+    S->stage_mode = mode;
+    S->copy_stream = (hipStream_t)copy_stream;
+    return MOE_OK;
+}
+
 int moe_stack_set_trace(moe_stack* S, float* d_x_trace, size_t n_floats) {
     if (!S || (n_floats && !d_x_trace)) return MOE_E_INVALID;
     S->x_trace = n_floats ? d_x_trace : nullptr;
@@ -918,6 +1016,9 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
     const size_t per = (size_t)n_tok * k;
     if (n_tok < 1 || n_tok * k > 4096 || n_tok > 256) return MOE_E_UNSUPPORTED;
     if (S->x_trace && (size_t)S->n * n_tok * S->layers[0]->desc.d_model > S->trace_cap) return MOE_E_CAPACITY;
+    if (first_step) S->step = 0;
+    const bool on_demand = S->stage_mode == MOE_STAGE_ON_DEMAND;
+    const bool prerouted = S->stage_mode == MOE_STAGE_PREROUTED;
     TopkJob pend{};
     bool pro_done = false;                   // this layer's prologue was taken by the previous combine
     for (int l = 0; l < S->n; ++l) {
@@ -925,7 +1026,8 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
         moe_io io{};
         io.x_in = l == 0 ? x_in : x_out;
         io.y_out = x_out;
-        const bool self = first_step || l == 0;
+        const bool self = first_step || l == 0 || on_demand;
+        if (S->stage_mode != MOE_STAGE_OFF) L->cur_buf = L->nbuf == 2 ? (int)(S->step & 1) : 0;
         io.route_idx = self ? nullptr : route_idx + l * per;
         io.route_w = self ? nullptr : route_w + l * per;
         io.used_idx = used_idx ? used_idx + l * per : nullptr;
@@ -933,7 +1035,7 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
         if (l + 1 < S->n) {
             io.pred_idx = pred_idx + (l + 1) * per;
             io.pred_w = pred_w + (l + 1) * per;
-            io.hist_cur = first_step ? nullptr : route_idx + (l + 1) * per;
+            io.hist_cur = (first_step || on_demand) ? nullptr : route_idx + (l + 1) * per;
             io.hist_prev = hist_prev ? hist_prev + (l + 1) * per : nullptr;
         }
         int rc = check_io(L, &io, n_tok);
@@ -944,12 +1046,26 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
         PrologueArgs nxt{};
         if (l + 1 < S->n) nxt = prologue_args(S->layers[l + 1], x_out, n_tok);
         bool took = false;
+        const bool stage_next = prerouted && l >= 1;
         rc = run_decode(L, &io, n_tok, (hipStream_t)stream, pend.pred_idx ? &pend : nullptr,
-                        l + 1 < S->n ? &out : nullptr, l + 1 < S->n ? &nxt : nullptr, pro_done, &took);
+                        l + 1 < S->n ? &out : nullptr, l + 1 < S->n ? &nxt : nullptr, pro_done, &took,
+                        stage_next ? L->ev_pred : nullptr);
         if (rc != MOE_OK) return rc;
         pend = out;
         pro_done = took;
+        if (stage_next) {
+            // layer l's routing for the next step (head l-1's prediction, final
+            // after this call's first launch) goes to the buffer the next step
+            // reads; one slab: after this call is done with it
+            const int nb = L->nbuf == 2 ? (L->cur_buf ^ 1) : 0;
+            HIPCHK(hipStreamWaitEvent(S->copy_stream, L->nbuf == 2 ? L->ev_pred : L->ev_done, 0));
+            rc = stage_device(L, pred_idx + l * per, (int)per, nb, S->copy_stream);
+            if (rc != MOE_OK) return rc;
+            HIPCHK(hipEventRecord(L->ev_staged_buf[nb], S->copy_stream));
+            L->staged_pending_buf[nb] = true;
+        }
     }
+    S->step++;
     if (pend.pred_idx) HIPCHK(launch_topk_job(pend, n_tok, (hipStream_t)stream));
     return MOE_OK;
 }

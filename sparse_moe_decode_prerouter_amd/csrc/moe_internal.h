@@ -58,9 +58,11 @@ struct BlobLayout {
 struct Scratch {
     int32_t* err;            // [1] sticky error flag
     uint32_t* counters;      // [16] last-block counters (self-resetting)
-    int32_t* slot_of;        // [E]
-    int32_t* slot_tag;       // [slots + 1]; entry `slots` is the shared slot
-    uint8_t* slab;           // [(slots + 1) * blob] (streamed); shared slot last
+    int32_t* slot_of;        // [nbuf][E]
+    int32_t* slot_tag;       // [nbuf][slots + 1]; entry `slots` is the shared slot
+    uint8_t* slab;           // [nbuf][(slots + 1) * blob] (streamed); shared slot last
+    int32_t* stage_plan;     // [nbuf][stage_plan_ints(slots)]: device staging scratch
+    unsigned long long* stage_bytes;   // [1]: bytes staged by device staging
     uint32_t* u_pk;          // [T][d/2] bf16 pairs, GEMV order (hi part)
     uint32_t* u_pk_lo;       // [T][d/2] lo part (f32 act) or nullptr
     uint32_t* u_frag;        // [T/16][d/32][64 lanes][4]: u_pk in MFMA fragment order (bf16 act), or nullptr
@@ -114,7 +116,15 @@ struct moe_layer {
     bool shared_staged;
     uint64_t staged_bytes;
     hipEvent_t ev_staged, ev_done;
-    bool staged_pending, done_recorded;
+    bool done_recorded;
+    // slab buffers (2 with MOE_DOUBLE_SLAB), the one calls read, device staging
+    int nbuf, cur_buf;
+    hipEvent_t ev_staged_buf[2];
+    bool staged_pending_buf[2];
+    bool dev_staging;          // MOE_DEVICE_STAGING: reactive staging runs on the device
+    const uint8_t* store_dev;  // device address of the pinned store (streamed), or nullptr
+    const uint8_t* shared_dev;
+    hipEvent_t ev_pred;        // recorded once this call's predictions are final (stack staging)
     int32_t* h_readback;       // pinned [max_tokens * k]
     // kernel timing (profiling mode)
     bool profiling;
@@ -125,6 +135,10 @@ struct moe_layer {
 struct moe_stack {
     moe_layer** layers;
     int n;
+    // device staging driven by the stack (moe_stack_set_staging)
+    int stage_mode;          // 0 off, MOE_STAGE_PREROUTED, MOE_STAGE_ON_DEMAND
+    hipStream_t copy_stream;
+    long long step;
     // prefill scratch (caller's workspace): two prediction buffers, layer l
     // writing buffer l & 1 while it reads layer l-1's from the other one
     int32_t* d_pred_idx[2];
@@ -341,5 +355,22 @@ struct SlotUpdate {
     int shared_slot;
 };
 hipError_t launch_slot_update(int32_t* slot_of, int32_t* slot_tag, const SlotUpdate& u, hipStream_t s);
+
+// Device-initiated staging of one slab buffer (kernels_stage.hip).
+constexpr int kMaxStageSlots = 1024;            // slab slots a device-staged layer may have
+// plan: [0] copies, then (slot, expert) pairs, then the shared flag
+__host__ __device__ inline int stage_plan_shared(int slots) { return 1 + 2 * slots; }
+__host__ __device__ inline int stage_plan_ints(int slots) { return 2 + 2 * slots; }
+struct DevStageArgs {
+    const int32_t* ids; int n_ids;               // routing entries on the device (any order, duplicates, < 0 absent)
+    int E; int slots;
+    int32_t* slot_of; int32_t* slot_tag;         // this buffer's tables: [E], [slots + 1] (entry `slots`: shared)
+    const uint8_t* store; const uint8_t* shared; // device addresses of the mapped pinned store / shared blob
+    uint8_t* slab; size_t blob; size_t sblob;    // this buffer's slab: slots blobs, then the shared slot
+    int32_t* plan;                               // [stage_plan_ints(slots)] scratch
+    unsigned long long* bytes;                   // staged-bytes counter
+    int32_t* err;
+};
+hipError_t launch_stage_device(const DevStageArgs& a, int blocks, hipStream_t s);
 
 }  // namespace moe

@@ -54,7 +54,8 @@ def oracle_layer(shape: synth.Shape, w: dict, act=None) -> oracle.LayerWeights:
 
 
 def gpu_layer(shape: synth.Shape, w: dict, *, fused: bool, resident: bool = True, slab_slots: int = 0,
-              max_tokens: int = 8, head: bool = True, act=None, keep_host: bool = False):
+              max_tokens: int = 8, head: bool = True, act=None, keep_host: bool = False, device_staging=False,
+              double_slab=False, pinned=None):
     import sparse_moe_decode_prerouter_amd as moe
     dev = "cuda"
 
@@ -63,6 +64,8 @@ def gpu_layer(shape: synth.Shape, w: dict, *, fused: bool, resident: bool = True
 
     if resident:
         store, shared = dv(w["store"]), dv(w["shared"])
+    elif pinned is not None:
+        store, shared = pinned
     else:
         store = w["store"].contiguous().pin_memory()
         shared = w["shared"].contiguous().pin_memory() if w["shared"] is not None else None
@@ -81,7 +84,7 @@ def gpu_layer(shape: synth.Shape, w: dict, *, fused: bool, resident: bool = True
         head_fc1_bias=dv(w.get("head_fc1_bias")) if head else None, head_fc2=dv(w.get("head_fc2")) if head else None,
         shared_lora_a=dv(w.get("shared_lora_a")), shared_lora_b=dv(w.get("shared_lora_b")),
         shared_lora_ad=dv(w.get("shared_lora_ad")), shared_lora_bd=dv(w.get("shared_lora_bd")),
-        shared_lora_alpha=w.get("shared_lora_alpha", 0.0))
+        shared_lora_alpha=w.get("shared_lora_alpha", 0.0), device_staging=device_staging, double_slab=double_slab)
 
 
 def rel_l2_rows(got: np.ndarray, ref: np.ndarray) -> float:
