@@ -109,8 +109,8 @@ class LazyStore:
 
 
 def make_layer(moe, shape, w, l, L, *, max_tokens, resident=True, store=None, shared=None, slab_slots=0,
-               head_bias=None, hist_cur=None):
-    return moe.MoeLayer(
+               head_bias=None, hist_cur=None, **extra):
+    return moe.MoeLayer(**extra,
         d_model=shape.d, n_experts=shape.E, top_k=shape.k, d_ff=shape.f, d_ff_shared=shape.fs,
         lora_rank=shape.r, lora_alpha=shape.alpha, act_dtype=moe.MOE_ACT_BF16, max_tokens=max_tokens,
         expert_store=w["store"] if store is None else store, shared_blob=w["shared"] if shared is None else shared,
@@ -155,11 +155,203 @@ def time_stack_steps(torch, stack, L, B, k, d, steps, warm, key, synth, shape, u
     return e0.elapsed_time(e1) / steps, pidx[(warm + steps) % 2]
 
 
+def streamed_layer(moe, shape, w, l, L, k, store, shared, slots, double=True, max_tokens=1):
+    """A streamed layer with device staging (top-k k) over the shared pinned store."""
+    return moe.MoeLayer(
+        d_model=shape.d, n_experts=shape.E, top_k=k, d_ff=shape.f, d_ff_shared=shape.fs, lora_rank=shape.r,
+        lora_alpha=shape.alpha, act_dtype=moe.MOE_ACT_BF16, max_tokens=max_tokens, expert_store=store,
+        shared_blob=shared, shared_gate=w["shared_gate"], router=w["router"], head=w["head"] if l + 1 < L else None,
+        next_n_experts=shape.E if l + 1 < L else 0, next_top_k=k if l + 1 < L else 0, lora_a=w["lora_a"],
+        lora_b=w["lora_b"], norm_gamma=w["gamma"], rms_eps=shape.eps, fuse_norm_residual=True, resident=False,
+        slab_slots=slots, device_staging=True, double_slab=double)
+
+
+def measure_h2d(torch, moe, synth, shape, ws, pstore, pshared):
+    """Pinned host -> HBM rate: the copy engine (a 453 MB pinned tensor copied
+    to the device) and the device-staging copy kernel (64 experts staged into
+    an empty 64-slot slab)."""
+    dst = torch.empty(pstore.shape, dtype=pstore.dtype, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 1e9
+    for _ in range(3):
+        e0.record()
+        dst.copy_(pstore, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    sdma = pstore.numel() / (best * 1e-3) / 1e9
+    del dst
+    rates = []
+    for rep in range(3):
+        lay = streamed_layer(moe, shape, ws[1], 1, 2, shape.k, pstore, pshared, 64, double=False)
+        ids = torch.arange(64 * rep, 64 * rep + 64, dtype=torch.int32, device="cuda") % shape.E
+        torch.cuda.synchronize()
+        e0.record()
+        lay.stage_device(ids)
+        e1.record()
+        torch.cuda.synchronize()
+        nbytes = lay.slots()[1]
+        rates.append(nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        assert lay.status() == 0
+        lay.close()
+    res = {"copy_engine_GBs": round(sdma, 1), "copy_kernel_GBs": round(max(rates), 1),
+           "note": "pinned host memory -> HBM; copy engine: one 453 MB copy; copy kernel: 64 experts "
+                   "(113 MB) staged by the device-staging kernels; best of 3"}
+    log(f"pinned H2D: copy engine {sdma:.1f} GB/s, device-staging copy kernel {max(rates):.1f} GB/s")
+    return res
+
+
+def streamed_sweep(torch, np, moe, synth, shape, ws, pstore, pshared, copy_GBs):
+    """Batch-1 decode through 40 streamed layers at top-k K = 2, 4, 8, with
+    the experts staged on the device into two slab buffers of K + 1 slots:
+    one token ahead (layer l's experts for step t+1 copied on a side stream
+    during step t) against on demand (each layer routes itself and stages
+    before it computes). Blocked time per step = step - the same stack's
+    compute-only step (experts resident, same eager launches)."""
+    L, d = len(ws), shape.d
+    res = {}
+    steps, warm = 16, 4
+    for K in (2, 4, 8):
+        # compute-only reference: the same layers with the experts resident
+        rl = [moe.MoeLayer(
+            d_model=shape.d, n_experts=shape.E, top_k=K, d_ff=shape.f, d_ff_shared=shape.fs, lora_rank=shape.r,
+            lora_alpha=shape.alpha, act_dtype=moe.MOE_ACT_BF16, max_tokens=1, expert_store=w["store"],
+            shared_blob=w["shared"], shared_gate=w["shared_gate"], router=w["router"],
+            head=w["head"] if l + 1 < L else None, next_n_experts=shape.E if l + 1 < L else 0,
+            next_top_k=K if l + 1 < L else 0, lora_a=w["lora_a"], lora_b=w["lora_b"], norm_gamma=w["gamma"],
+            rms_eps=shape.eps, fuse_norm_residual=True, resident=True) for l, w in enumerate(ws)]
+        rs = moe.MoeStack(rl)
+        comp_ms = eager_steps(torch, rs, L, K, d, synth, shape, steps, warm, ("bench_str", K))
+        rs.close()
+        for Lr in rl:
+            Lr.close()
+        sl = [streamed_layer(moe, shape, w, l, L, K, pstore, pshared, K) for l, w in enumerate(ws)]
+        ss = moe.MoeStack(sl)
+        cs = torch.cuda.Stream()
+        row = {"compute_only_ms_per_step": round(comp_ms, 3)}
+        for mode, name in ((moe.MOE_STAGE_PREROUTED, "prerouted"), (moe.MOE_STAGE_ON_DEMAND, "on_demand")):
+            ss.set_staging(mode, cs)
+            b0 = None
+            ms = eager_steps(torch, ss, L, K, d, synth, shape, steps, warm, ("bench_str", K),
+                             on_warm=lambda: sum(Lr.slots()[1] for Lr in sl))
+            moved = sum(Lr.slots()[1] for Lr in sl)
+            assert all(Lr.status() == 0 for Lr in sl), [Lr.status() for Lr in sl]
+            moved_step = (moved - eager_steps.last_warm_value) / steps
+            copy_ms = moved_step / (copy_GBs * 1e9) * 1e3
+            blocked = max(0.0, ms - comp_ms)
+            hidden = max(0.0, copy_ms + comp_ms - ms)
+            row[name] = {"tok_s": round(1e3 / ms, 1), "ms_per_step": round(ms, 3),
+                         "blocked_ms_per_step": round(blocked, 3),
+                         "staged_MiB_per_step": round(moved_step / 2**20, 1),
+                         "copy_ms_per_step_at_kernel_rate": round(copy_ms, 3),
+                         "overlap_frac_of_compute": round(min(1.0, hidden / comp_ms), 3)}
+            log(f"streamed decode K={K} {name}: {ms:.2f} ms/step, {1e3 / ms:.1f} tok/s, blocked {blocked:.2f} ms, "
+                f"{moved_step / 2**20:.1f} MiB staged/step, copies {copy_ms:.2f} ms at the kernel rate")
+        row["prerouted_speedup"] = round(row["on_demand"]["ms_per_step"] / row["prerouted"]["ms_per_step"] - 1, 3)
+        res[f"K{K}"] = row
+        ss.set_staging(moe.MOE_STAGE_OFF, None)
+        ss.close()
+        for Lr in sl:
+            Lr.close()
+    return res
+
+
+def eager_steps(torch, stack, L, K, d, synth, shape, steps, warm, key, on_warm=None):
+    """ms per decode step over `steps` eager steps after `warm` (the first of
+    which self-routes); on_warm() is evaluated after the warm-up (its value is
+    kept in eager_steps.last_warm_value)."""
+    dev = "cuda"
+    xs = [synth.activations(shape, 1, key + (t,), device=dev, dtype=torch.float32) for t in range(warm + steps)]
+    xo = torch.empty((1, d), dtype=torch.float32, device=dev)
+    pidx = [torch.full((L, 1, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+    pw = [torch.zeros((L, 1, K), dtype=torch.float32, device=dev) for _ in range(2)]
+    for t in range(warm):
+        stack.decode(xs[t], pidx[t % 2], pw[t % 2], pidx[(t + 1) % 2], pw[(t + 1) % 2], x_out=xo, first_step=(t == 0))
+    torch.cuda.synchronize()
+    eager_steps.last_warm_value = on_warm() if on_warm else None
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(warm, warm + steps):
+        stack.decode(xs[t], pidx[t % 2], pw[t % 2], pidx[(t + 1) % 2], pw[(t + 1) % 2], x_out=xo, first_step=False)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cold_prefill(torch, moe, synth, shape, ws, pstore, pshared, T):
+    """Prefill of T tokens through the 40-layer stack with every expert in
+    pinned host memory: each layer's slab (all E experts + shared) starts
+    empty and the call stages on the device what its tokens route to, between
+    the sort and the grouped GEMMs (cold); the same stack again finds them
+    staged (slab warm); the resident stack is the fully warm case."""
+    L = len(ws)
+    sl = [streamed_layer(moe, shape, w, l, L, shape.k, pstore, pshared, shape.E, double=False, max_tokens=T)
+          for l, w in enumerate(ws)]
+    st = moe.MoeStack(sl)
+    xp = synth.activations(shape, T, ("bench_prefill",), device="cuda", dtype=torch.float32)
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name in ("cold", "slab_warm"):
+        xw = xp.clone()
+        torch.cuda.synchronize()
+        b0 = sum(Lr.slots()[1] for Lr in sl)
+        e0.record()
+        st.prefill(xw)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        moved = sum(Lr.slots()[1] for Lr in sl) - b0
+        assert all(Lr.status() == 0 for Lr in sl)
+        res[name] = {"tok_s": round(T / (ms * 1e-3), 1), "ms": round(ms, 2), "staged_MB": round(moved / 1e6, 1),
+                     "staging_GBs": round(moved / (ms * 1e-3) / 1e9, 1)}
+        log(f"prefill {T} tokens, streamed store ({name}): {ms:.1f} ms, {T / (ms * 1e-3):.0f} tok/s, "
+            f"{moved / 1e6:.0f} MB staged")
+    st.close()
+    for Lr in sl:
+        Lr.close()
+    return res
+
+
+def variant_costs(torch, np, moe, synth, shape, ws):
+    """Graph-replayed batch-1 decode of the 40-layer stack with the pages'
+    full heads (fc2(erf-GELU(fc1(x))) + l(x), fc1 width 256) and with the
+    recovery adapter on every shared expert (rank 16), against the plain
+    stack: the per-step cost of each."""
+    L = len(ws)
+    res = {}
+    for name in ("mlp_head_h256", "shared_adapter_r16"):
+        lay = []
+        for l, w in enumerate(ws):
+            extra = {}
+            if name.startswith("mlp") and l + 1 < L:
+                mw = synth.head_mlp_weights(shape, l, 256, device="cuda", tag="bench")
+                extra = dict(head_fc1=mw["head_fc1"], head_fc1_onehot=mw["head_fc1_onehot"],
+                             head_fc1_bias=mw["head_fc1_bias"], head_fc2=mw["head_fc2"])
+            if name.startswith("shared"):
+                aw = synth.shared_adapter(shape, l, 16, device="cuda", tag="bench")
+                extra = dict(shared_lora_a=aw["shared_lora_a"], shared_lora_b=aw["shared_lora_b"],
+                             shared_lora_ad=aw["shared_lora_ad"], shared_lora_bd=aw["shared_lora_bd"],
+                             shared_lora_alpha=aw["shared_lora_alpha"])
+            lay.append(make_layer(moe, shape, w, l, L, max_tokens=1, **extra))
+        st = moe.MoeStack(lay)
+        ms, _ = time_stack_steps(torch, st, L, 1, shape.k, shape.d, 64, 5, "bench_var", synth, shape)
+        assert all(Lr.status() == 0 for Lr in lay)
+        res[name] = {"ms_per_step": round(ms, 4), "tok_s": round(1e3 / ms, 1)}
+        log(f"decode with {name}: {ms * 1e3:.0f} us/step")
+        st.close()
+        for Lr in lay:
+            Lr.close()
+    return res
+
+
 def extra_measurements(args, torch, np, moe, synth, shape, ws, layers):
     """The other workloads of the method, each timed on this GPU: batched
     decode with Zipf-popular, sticky routing; streamed decode (experts staged
-    per step from pinned host memory) against on-demand staging; one layer per
-    call at batch 1 and 4; a long prefill for the matrix-core rate."""
+    per step from pinned host memory, device staging) one token ahead against
+    on demand at K = 2, 4, 8 next to the pinned host -> HBM rates; cold
+    prefill; the cost of the full head and of the shared expert's adapter; one
+    layer per call at batch 1 and 4; a long prefill for the matrix-core rate."""
     out = {}
     L, k, d, E, blob = len(layers), shape.k, shape.d, shape.E, shape.blob_bytes
 
@@ -189,54 +381,21 @@ def extra_measurements(args, torch, np, moe, synth, shape, ws, layers):
         Lr.close()
     del zl, zs
 
-    # ---- streamed decode, B = 1: every layer's routed experts staged per step
-    # from pinned host memory into a 5-slot HBM slab on a side stream (one pinned
-    # copy of a layer's experts serves all layers: the bytes moved are the same)
+    # ---- pinned host -> HBM: the copy engine and the device-staging copy kernel
     pstore = ws[0]["store"].cpu().pin_memory()
     pshared = ws[0]["shared"].cpu().pin_memory()
-    sl = [make_layer(moe, shape, w, l, L, max_tokens=1, resident=False, store=pstore, shared=pshared,
-                     slab_slots=k + 1) for l, w in enumerate(ws)]
-    ss = moe.MoeStack(sl)
-    cs = torch.cuda.Stream()
-    xs = [synth.activations(shape, 1, ("bench_str", t), device="cuda", dtype=torch.float32) for t in range(24)]
-    xo = torch.empty((1, d), dtype=torch.float32, device="cuda")
-    pidx = [torch.full((L, 1, k), -1, dtype=torch.int32, device="cuda") for _ in range(2)]
-    pw = [torch.zeros((L, 1, k), dtype=torch.float32, device="cuda") for _ in range(2)]
+    out["h2d_peak"] = measure_h2d(torch, moe, synth, shape, ws, pstore, pshared)
 
-    def streamed_step(t, reactive):
-        if reactive or t == 0:
-            # on demand: every layer routes itself and stages inside the call
-            ss.decode(xs[t], pidx[t % 2], pw[t % 2], pidx[(t + 1) % 2], pw[(t + 1) % 2], x_out=xo, first_step=True)
-            return
-        pred = pidx[t % 2].cpu().numpy()            # the previous step's predictions
-        for l in range(1, L):
-            sl[l].stage(sorted(set(int(e) for e in pred[l, 0] if e >= 0)), stream=cs)
-        ss.decode(xs[t], pidx[t % 2], pw[t % 2], pidx[(t + 1) % 2], pw[(t + 1) % 2], x_out=xo, first_step=False)
+    # ---- streamed decode, B = 1, K = 2 / 4 / 8: one token ahead vs on demand (device staging)
+    out["streamed_decode_b1"] = streamed_sweep(torch, np, moe, synth, shape, ws, pstore, pshared,
+                                               out["h2d_peak"]["copy_kernel_GBs"])
 
-    res = {}
-    for mode, reactive in (("prerouted", False), ("on_demand", True)):
-        for t in range(4):
-            streamed_step(t, reactive)
-        torch.cuda.synchronize()
-        b0 = sum(Lr.slots()[1] for Lr in sl)
-        n = 16
-        c0 = time.time()
-        for t in range(4, 4 + n):
-            streamed_step(t, reactive)
-        torch.cuda.synchronize()
-        el = time.time() - c0
-        moved = sum(Lr.slots()[1] for Lr in sl) - b0
-        assert all(Lr.status() == 0 for Lr in sl), [Lr.status() for Lr in sl]
-        res[mode] = {"tok_s": round(n / el, 1), "ms_per_step": round(el / n * 1e3, 3),
-                     "staged_MB_per_step": round(moved / n / 1e6, 1),
-                     "staging_GBs": round(moved / el / 1e9, 2)}
-        log(f"streamed decode ({mode}): {el / n * 1e3:.2f} ms/step, {n / el:.1f} tok/s, "
-            f"{moved / n / 1e6:.0f} MB staged/step, {moved / el / 1e9:.1f} GB/s host->HBM")
-    out["streamed_decode_b1"] = res
-    ss.close()
-    for Lr in sl:
-        Lr.close()
-    del sl, ss, pstore, pshared
+    # ---- cold prefill: the experts staged from pinned host memory inside the call
+    out["cold_prefill"] = cold_prefill(torch, moe, synth, shape, ws, pstore, pshared, args.prefill_tokens)
+    del pstore, pshared
+
+    # ---- the pages' full head (MLP branch) and the shared expert's adapter on the 40-layer decode
+    out["head_and_adapter_cost"] = variant_costs(torch, np, moe, synth, shape, ws)
 
     # ---- one layer per call, batch 1 and 4 (given routing; graph of 64 calls)
     lay = make_layer(moe, shape, ws[1], 1, L, max_tokens=4)
@@ -452,16 +611,17 @@ def main():
 
     extra = None if args.no_extra else extra_measurements(args, torch, np, moe, synth, shape, ws, layers)
 
-    # ---- CPU baseline: the fp64 oracle on a bounded sample (1 decode step of the stack)
+    # ---- CPU baseline: the fp64 oracle on bounded samples of the same workloads
     cpu = None
     if not args.no_cpu:
         import oracle
         cores = os.cpu_count()
         try:
-            from threadpoolctl import threadpool_info
-            thr = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+            from threadpoolctl import threadpool_info, threadpool_limits
+            blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+            thr = max([p.get("num_threads", 1) for p in blas] or [1])
         except Exception:
-            thr = cores
+            threadpool_limits, thr = None, cores
         ora = []
         for l, w in enumerate(ws):
             ora.append(oracle.LayerWeights(
@@ -471,14 +631,34 @@ def main():
                 lora_b=synth.bf16_bits(w["lora_b"]), gamma=w["gamma"].double().cpu().numpy(),
                 head=synth.bf16_bits(w["head"]) if l + 1 < L else None, router=synth.bf16_bits(w["router"])))
         xs = xbank[:args.cpu_steps].double().cpu().numpy()
-        # step 0 self-routes every layer; report steady-state-like cost per step incl. that
+        # decode: steps of the stack (the first step self-routes every layer)
         c0 = time.time()
         oracle.stack_decode(ora, xs, args.cpu_steps)
         cs = time.time() - c0
+        # the same with one BLAS thread (two steps)
+        cs1 = None
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1, user_api="blas"):
+                c0 = time.time()
+                oracle.stack_decode(ora, xs[:2], 2)
+                cs1 = time.time() - c0
+        # prefill: the first 16 tokens of the benchmarked prompt through the first 4 layers
+        pt, pl = 16, 4
+        xpf = synth.activations(shape, T, ("bench_prefill",), dtype=torch.float32)[:pt].double().numpy()
+        c0 = time.time()
+        oracle.stack_prefill(ora[:pl], xpf)
+        cp = time.time() - c0
+        pf_rate = pt / (cp * L / pl)
         cpu = {"value": round(B * args.cpu_steps / cs, 4), "unit": "tok/s", "cores": int(thr), "kind": "oracle",
                "sample": f"{args.cpu_steps} decode step(s) of the {L}-layer stack at batch {B}, fp64 NumPy "
-                         f"(first step: every layer self-routes), {cs:.1f} s"}
-        log(f"oracle: {cs:.1f} s for {args.cpu_steps} step(s)")
+                         f"(first step: every layer self-routes), {cs:.1f} s",
+               "host_cpus": cores, "blas_threads": int(thr),
+               "one_thread_tok_s": None if cs1 is None else round(2 / cs1, 4),
+               "prefill_tok_s": round(pf_rate, 3),
+               "prefill_sample": f"the first {pt} tokens of the {T}-token prompt through {pl} of the {L} layers "
+                                 f"({cp:.1f} s), scaled to {L} layers"}
+        log(f"oracle: decode {cs:.1f} s for {args.cpu_steps} step(s) on {thr} BLAS threads; one thread "
+            f"{cs1 if cs1 is None else round(cs1, 1)} s for 2 steps; prefill {pt} tokens x {pl} layers {cp:.1f} s")
 
     out = {
         "metric": "decode tok/s (40-layer MoE stack, bs=1) + % of HBM roofline; prefill tok/s",
@@ -500,6 +680,8 @@ def main():
         "hbm_roofline_tok_s": round(roof_tok_s, 1),
         "bytes_per_step": sb,
         "roofline": {"bound": "hbm", "kernel": "k_dec_a (norm + routed/shared gate-up GEMV + head)",
+                     "timing": "kernel-timestamp events (the dispatch's own begin and end) of every K_A launch "
+                               "over 16 eager replays of the timed steps",
                      "achieved": round(ab / (a_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ab / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": ab, "avg_launch_us": round(a_avg * 1e3, 3)},
