@@ -345,6 +345,96 @@ def variant_costs(torch, np, moe, synth, shape, ws):
     return res
 
 
+def stack_prefill_timing(torch, np, shape, stack, layers, T, k, reps=3):
+    """Prefill of T tokens through the resident stack (median of reps)."""
+    import synth
+    L = len(layers)
+    xp = synth.activations(shape, T, ("bench_prefill",), device="cuda", dtype=torch.float32)
+    xw = xp.clone()
+    stack.prefill(xw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        xw.copy_(xp)
+        torch.cuda.synchronize()
+        e0.record()
+        stack.prefill(xw)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    pms = float(np.median(times))
+    assert all(Lr.status() == 0 for Lr in layers)
+    # algorithmic bytes: every expert of every layer (all are touched at 512 tokens w.h.p.),
+    # shared, heads, routers (token 0 self-routes everywhere), LoRA
+    pb = L * ((shape.E + 1) * shape.blob_bytes + 2 * shape.E * shape.d + 4 * shape.r * shape.d) \
+        + (L - 1) * 2 * shape.E * shape.d
+    flops = L * T * (6 * shape.d * shape.f * (k + 1) + 2 * shape.d * shape.E * 2 + 4 * shape.r * shape.d)
+    prefill = {"value": round(T / (pms / 1e3), 1), "unit": "tok/s", "tokens": T, "ms": round(pms, 3),
+               "hbm_frac": round(pb / (pms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+               "mfma_frac_bf16": round(flops / (pms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 5)}
+    log(f"prefill {T} tokens: {pms:.2f} ms, {prefill['value']:.0f} tok/s, hbm frac {prefill['hbm_frac']:.3f}")
+    return prefill
+
+
+def batched_decode(torch, np, moe, synth, shape, ws, steps=32, warm=5):
+    """Batched decode, B = 32 sequences through the 40-layer stack whose heads
+    carry the calibrated Zipf(1.1) popularity bias and stickiness."""
+    L, k, d, E, blob = len(ws), shape.k, shape.d, shape.E, shape.blob_bytes
+    with open(os.path.join(ROOT, "tests", "golden", "zipf_calibration.json")) as fh:
+        cal = json.load(fh)
+    B = 32
+    hist = synth.sticky_history(E, cal["beta"], device="cuda")
+    zl = [make_layer(moe, shape, w, l, L, max_tokens=B,
+                     head_bias=synth.zipf_bias(E, cal["zipf_s"], cal["tau"], ("bench", l), device="cuda"),
+                     hist_cur=hist) for l, w in enumerate(ws)]
+    zs = moe.MoeStack(zl)
+    used = torch.full((L, B, k), -1, dtype=torch.int32, device="cuda")
+    ms, _ = time_stack_steps(torch, zs, L, B, k, d, steps, warm, "bench_zipf", synth, shape, used=used)
+    assert all(Lr.status() == 0 for Lr in zl)
+    u = used.cpu().numpy()
+    U = [len(set(u[l].ravel().tolist()) - {-1}) for l in range(L)]
+    bb = sum((x + 1) * blob for x in U) + (L - 1) * 2 * E * d + L * (4 * shape.r * d + 6 * d)
+    res = {"tok_s": round(B / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+           "distinct_experts_per_layer": round(float(np.mean(U)), 1),
+           "algorithmic_GBs": round(bb / (ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(bb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
+    log(f"batched decode B={B} (Zipf + sticky): {ms * 1e3:.0f} us/step, {B / (ms / 1e3):.0f} tok/s, "
+        f"U={np.mean(U):.1f} experts/layer, {bb / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic")
+    zs.close()
+    for Lr in zl:
+        Lr.close()
+    return res
+
+
+def long_prefill(torch, np, moe, synth, shape, ws, reps=3):
+    """Prefill of 8192 tokens through one layer (about 128 tokens per expert):
+    the matrix-core rate of the grouped GEMMs."""
+    L, k, d, E = len(ws), shape.k, shape.d, shape.E
+    T = 8192
+    lay = make_layer(moe, shape, ws[1], 1, L, max_tokens=T)
+    x = synth.activations(shape, T, ("bench_long",), device="cuda", dtype=torch.float32)
+    y = torch.empty_like(x)
+    lay.prefill(x, y=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        lay.prefill(x, y=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    assert lay.status() == 0
+    flops = T * (6 * d * shape.f * (k + 1) + 2 * d * E * 2 + 4 * shape.r * d)
+    res = {"ms": round(ms, 3), "tok_s": round(T / (ms / 1e3), 1),
+           "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+           "mfma_frac_bf16": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+    log(f"prefill T={T}, one layer: {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s "
+        f"({flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12):.3f} of bf16 MFMA peak)")
+    lay.close()
+    return res
+
+
 def extra_measurements(args, torch, np, moe, synth, shape, ws, layers):
     """The other workloads of the method, each timed on this GPU: batched
     decode with Zipf-popular, sticky routing; streamed decode (experts staged
@@ -355,31 +445,7 @@ def extra_measurements(args, torch, np, moe, synth, shape, ws, layers):
     out = {}
     L, k, d, E, blob = len(layers), shape.k, shape.d, shape.E, shape.blob_bytes
 
-    # ---- batched decode, B = 32, Zipf(1.1) popularity + stickiness (calibrated)
-    with open(os.path.join(ROOT, "tests", "golden", "zipf_calibration.json")) as fh:
-        cal = json.load(fh)
-    B = 32
-    hist = synth.sticky_history(E, cal["beta"], device="cuda")
-    zl = [make_layer(moe, shape, w, l, L, max_tokens=B,
-                     head_bias=synth.zipf_bias(E, cal["zipf_s"], cal["tau"], ("bench", l), device="cuda"),
-                     hist_cur=hist) for l, w in enumerate(ws)]
-    zs = moe.MoeStack(zl)
-    used = torch.full((L, B, k), -1, dtype=torch.int32, device="cuda")
-    ms, _ = time_stack_steps(torch, zs, L, B, k, d, 32, 5, "bench_zipf", synth, shape, used=used)
-    assert all(Lr.status() == 0 for Lr in zl)
-    u = used.cpu().numpy()
-    U = [len(set(u[l].ravel().tolist()) - {-1}) for l in range(L)]
-    bb = sum((x + 1) * blob for x in U) + (L - 1) * 2 * E * d + L * (4 * shape.r * d + 6 * d)
-    out["batched_decode_b32"] = {"tok_s": round(B / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-                                 "distinct_experts_per_layer": round(float(np.mean(U)), 1),
-                                 "algorithmic_GBs": round(bb / (ms * 1e-3) / 1e9, 1),
-                                 "hbm_frac": round(bb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
-    log(f"batched decode B={B} (Zipf + sticky): {ms * 1e3:.0f} us/step, {B / (ms / 1e3):.0f} tok/s, "
-        f"U={np.mean(U):.1f} experts/layer, {bb / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic")
-    zs.close()
-    for Lr in zl:
-        Lr.close()
-    del zl, zs
+    out["batched_decode_b32"] = batched_decode(torch, np, moe, synth, shape, ws)
 
     # ---- pinned host -> HBM: the copy engine and the device-staging copy kernel
     pstore = ws[0]["store"].cpu().pin_memory()
@@ -426,28 +492,7 @@ def extra_measurements(args, torch, np, moe, synth, shape, ws, layers):
         log(f"one layer, B={B}: {us:.2f} us/call, {lb / (us * 1e-6) / 1e9:.0f} GB/s algorithmic")
     lay.close()
 
-    # ---- long prefill (T = 8192 tokens through one layer): the matrix-core rate
-    T = 8192
-    lay = make_layer(moe, shape, ws[1], 1, L, max_tokens=T)
-    x = synth.activations(shape, T, ("bench_long",), device="cuda", dtype=torch.float32)
-    y = torch.empty_like(x)
-    lay.prefill(x, y=y)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(3):
-        lay.prefill(x, y=y)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 3
-    assert lay.status() == 0
-    flops = T * (6 * d * shape.f * (k + 1) + 2 * d * E * 2 + 4 * shape.r * d)
-    out["prefill_t8192_one_layer"] = {"ms": round(ms, 3), "tok_s": round(T / (ms / 1e3), 1),
-                                      "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
-                                      "mfma_frac_bf16": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
-    log(f"prefill T={T}, one layer: {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s "
-        f"({flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12):.3f} of bf16 MFMA peak)")
-    lay.close()
+    out["prefill_t8192_one_layer"] = long_prefill(torch, np, moe, synth, shape, ws)
     return out
 
 
@@ -463,6 +508,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads (batched, streamed, ...)")
+    ap.add_argument("--workload", default="all", choices=["all", "decode", "prefill", "long_prefill", "batched"],
+                    help="profiling runs: only this workload (all: the benchmark line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (scale for HBM counters)")
     args = ap.parse_args()
@@ -511,6 +558,17 @@ def main():
     torch.cuda.synchronize()
     log(f"built {L} layers ({L * shape.E * shape.blob_bytes / 2**30:.1f} GiB experts) in {time.time() - t0:.1f}s")
     stack = moe.MoeStack(layers)
+    if args.workload in ("long_prefill", "batched"):
+        # profiling runs of one other workload
+        fn = long_prefill if args.workload == "long_prefill" else batched_decode
+        print(json.dumps({"workload": args.workload, **fn(torch, np, moe, synth, shape, ws)}), flush=True)
+        return
+    if args.workload == "decode":
+        args.no_prefill, args.no_extra, args.no_cpu = True, True, True
+    if args.workload == "prefill":
+        print(json.dumps({"workload": "prefill", **stack_prefill_timing(torch, np, shape, stack, layers, T, k)}),
+              flush=True)
+        return
 
     # ---- decode: step inputs and rotating routing buffers
     xbank = torch.stack([synth.activations(shape, B, ("bench", t), device=dev, dtype=torch.float32)
@@ -581,33 +639,7 @@ def main():
         f"({bb_ / (b_avg * 1e-3) / 1e9:.0f} GB/s), router avg {np.mean(r_ms) * 1e3 if r_ms else -1:.2f} us")
 
     # ---- prefill
-    prefill = None
-    if not args.no_prefill:
-        xp = synth.activations(shape, T, ("bench_prefill",), device=dev, dtype=torch.float32)
-        xw = xp.clone()
-        stack.prefill(xw)
-        torch.cuda.synchronize()
-        reps = 3
-        times = []
-        for _ in range(reps):
-            xw.copy_(xp)
-            torch.cuda.synchronize()
-            e0.record()
-            stack.prefill(xw)
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        pms = float(np.median(times))
-        assert all(Lr.status() == 0 for Lr in layers)
-        # algorithmic bytes: every expert of every layer (all are touched at 512 tokens w.h.p.),
-        # shared, heads, routers (token 0 self-routes everywhere), LoRA
-        pb = L * ((shape.E + 1) * shape.blob_bytes + 2 * shape.E * shape.d + 4 * shape.r * shape.d) \
-            + (L - 1) * 2 * shape.E * shape.d
-        flops = L * T * (6 * shape.d * shape.f * (k + 1) + 2 * shape.d * shape.E * 2 + 4 * shape.r * shape.d)
-        prefill = {"value": round(T / (pms / 1e3), 1), "unit": "tok/s", "tokens": T, "ms": round(pms, 3),
-                   "hbm_frac": round(pb / (pms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-                   "mfma_frac_bf16": round(flops / (pms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 5)}
-        log(f"prefill {T} tokens: {pms:.2f} ms, {prefill['value']:.0f} tok/s, hbm frac {prefill['hbm_frac']:.3f}")
+    prefill = None if args.no_prefill else stack_prefill_timing(torch, np, shape, stack, layers, T, k)
 
     extra = None if args.no_extra else extra_measurements(args, torch, np, moe, synth, shape, ws, layers)
 
