@@ -319,7 +319,8 @@ void moe_layer_destroy(moe_layer* layer);
  *
  * moe_stack_workspace_bytes: device scratch the stack needs (two prediction
  *   buffers of min(max_tokens) * k entries for stack prefill calls without
- *   caller prediction buffers); 0 if the layers do not form a valid stack.
+ *   caller prediction buffers, the one-launch step's per-layer argument
+ *   table and its counters); 0 if the layers do not form a valid stack.
  * moe_stack_create: d_workspace is caller-owned device memory of at least
  *   that size, 256-byte aligned, kept until destroy. The library allocates
  *   only the host handle. Errors: MOE_E_INVALID (null, misaligned, layers
@@ -354,7 +355,31 @@ void moe_layer_destroy(moe_layer* layer);
  *   later stack call first copies layer l's input residual stream [n_tok][d]
  *   to d_x_trace + l * n_tok * d (a device-to-device copy per layer, for
  *   checking each layer on the input it saw); calls whose trace would not
- *   fit return MOE_E_CAPACITY. NULL / 0 turns the trace off.              */
+ *   fit return MOE_E_CAPACITY. NULL / 0 turns the trace off.
+ * moe_stack_set_one_launch: enable != 0 runs each later decode step that
+ *   qualifies as three launches in all (layer 0's router, a one-block patch
+ *   of the per-layer argument table, and one step kernel in which every
+ *   layer's K_A and K_B run as work items, each issuing its weight rows
+ *   before it waits, on device-scope counters, for its activations; the
+ *   addresses are known before the step starts because each layer's routing
+ *   is the previous token's prediction: guide, Q&A on why one token ahead).
+ *   A step qualifies when it is not the first step, staging is
+ *   MOE_STAGE_OFF and n_tok takes the fast path; other steps run per layer
+ *   as before. The stack qualifies (else MOE_E_UNSUPPORTED) when every layer
+ *   is resident, the layers share d, d_ff, the shared width, k, E, the LoRA
+ *   rank (0, 8 or 16) and the presence of the shared gate, heads have at
+ *   most 256 outputs, and no layer has the head's MLP branch or the shared
+ *   expert's adapter. The waits are bounded: a lost arrival sets
+ *   MOE_E_TIMEOUT in the layer's status (moe_layer_sync_status) instead of
+ *   hanging. Calls on one stack must not overlap (the table and counters
+ *   are per stack). Default: off.
+ * moe_stack_set_wait_limit: the bound of each of those waits, in polls of
+ *   about a microsecond each (0: the default, 2^18). A wait that runs out
+ *   sets MOE_E_TIMEOUT and lets every later wait of the launch give up at
+ *   once, so the launch ends (with wrong outputs) instead of hanging.
+ * moe_stack_set_profiling / moe_stack_kernel_ms: kernel-timestamp events on
+ *   the one-launch step's router launch and step kernel (as
+ *   moe_layer_set_profiling); -1 where not launched.                      */
 typedef struct moe_stack moe_stack;
 size_t moe_stack_workspace_bytes(moe_layer* const* layers, int n_layers);
 int moe_stack_create(moe_layer* const* layers, int n_layers, void* d_workspace, size_t ws_bytes, moe_stack** out);
@@ -365,6 +390,10 @@ int moe_stack_prefill(moe_stack* st, float* x, int n_tok, int32_t* used_idx, flo
                       int32_t* pred_idx, float* pred_w, void* stream);
 int moe_stack_set_trace(moe_stack* st, float* d_x_trace, size_t n_floats);
 int moe_stack_set_staging(moe_stack* st, void* copy_stream, int mode);
+int moe_stack_set_one_launch(moe_stack* st, int enable);
+int moe_stack_set_wait_limit(moe_stack* st, unsigned polls);
+int moe_stack_set_profiling(moe_stack* st, int enable);
+int moe_stack_kernel_ms(moe_stack* st, float* ms_router, float* ms_step);
 void moe_stack_destroy(moe_stack* st);
 
 /* ---- measurement --------------------------------------------------------

@@ -96,6 +96,10 @@ def _load():
         "moe_stack_decode": (I, [P, P, P, I, P, P, P, P, P, P, P, I, P]),
         "moe_stack_prefill": (I, [P, P, I, P, P, P, P, P]),
         "moe_stack_destroy": (None, [P]),
+        "moe_stack_set_one_launch": (I, [P, I]),
+        "moe_stack_set_wait_limit": (I, [P, ctypes.c_uint]),
+        "moe_stack_set_profiling": (I, [P, I]),
+        "moe_stack_kernel_ms": (I, [P, P, P]),
         "moe_layer_set_profiling": (I, [P, I]),
         "moe_layer_kernel_ms": (I, [P, P, P, P]),
     }
@@ -112,7 +116,8 @@ EXPORTED = ("moe_expert_blob_bytes", "moe_layer_workspace_bytes", "moe_layer_cre
             "moe_layer_slots", "moe_decode_step", "moe_decode_noalloc", "moe_prefill", "moe_layer_sync_status", "moe_layer_destroy",
             "moe_status_str", "moe_last_hip_error", "moe_plan_slots", "moe_stack_workspace_bytes",
             "moe_stack_create", "moe_stack_set_trace", "moe_stack_decode",
-            "moe_stack_prefill", "moe_stack_destroy", "moe_layer_set_profiling", "moe_layer_kernel_ms")
+            "moe_stack_prefill", "moe_stack_destroy", "moe_stack_set_one_launch", "moe_stack_set_wait_limit", "moe_stack_set_profiling",
+            "moe_stack_kernel_ms", "moe_layer_set_profiling", "moe_layer_kernel_ms")
 
 
 # ---------------------------------------------------------------------------
@@ -257,6 +262,32 @@ def moe_stack_prefill(stack: int, x: int, n_tok: int, used_idx: Optional[int], u
 
 def moe_stack_destroy(stack: int) -> None:
     _lib.moe_stack_destroy(stack)
+
+
+def moe_stack_set_one_launch(stack: int, enable: bool) -> None:
+    rc = _lib.moe_stack_set_one_launch(stack, 1 if enable else 0)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stack_set_one_launch")
+
+
+def moe_stack_set_wait_limit(stack: int, polls: int) -> None:
+    rc = _lib.moe_stack_set_wait_limit(stack, polls)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stack_set_wait_limit")
+
+
+def moe_stack_set_profiling(stack: int, enable: bool) -> None:
+    rc = _lib.moe_stack_set_profiling(stack, 1 if enable else 0)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stack_set_profiling")
+
+
+def moe_stack_kernel_ms(stack: int):
+    r, m = ctypes.c_float(), ctypes.c_float()
+    rc = _lib.moe_stack_kernel_ms(stack, ctypes.byref(r), ctypes.byref(m))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_stack_kernel_ms")
+    return r.value, m.value
 
 
 def moe_layer_set_profiling(handle: int, enable: bool) -> None:
@@ -410,6 +441,21 @@ class MoeStack:
         """Device staging driven by the stack (MOE_STAGE_PREROUTED / _ON_DEMAND / _OFF)."""
         self.copy_stream = copy_stream
         moe_stack_set_staging(self.handle, 0 if copy_stream is None else copy_stream.cuda_stream, mode)
+
+    def set_one_launch(self, enable=True):
+        """One launch per qualifying decode step (moe_stack_set_one_launch)."""
+        moe_stack_set_one_launch(self.handle, enable)
+
+    def set_wait_limit(self, polls):
+        """Bound of the one-launch step's device-side waits (0: default)."""
+        moe_stack_set_wait_limit(self.handle, polls)
+
+    def set_profiling(self, enable=True):
+        moe_stack_set_profiling(self.handle, enable)
+
+    def kernel_ms(self):
+        """(router ms, step-kernel ms) of the most recent one-launch step."""
+        return moe_stack_kernel_ms(self.handle)
 
     def set_trace(self, trace):
         """trace: device fp32 tensor [n_layers, n_tok, d] receiving each layer's

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_prerouter.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["moe_api.hip", "kernels_decode.hip", "kernels_dec2.hip", "kernels_deca.hip", "kernels_prefill.hip",
-           "kernels_shared.hip", "kernels_stage.hip"]
+           "kernels_shared.hip", "kernels_stage.hip", "kernels_stack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

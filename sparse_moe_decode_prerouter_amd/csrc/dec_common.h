@@ -25,11 +25,36 @@ __device__ __forceinline__ void wave_lds_sync() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// The value of a partner lane in the other half of each aligned block of
+// 2*off lanes. Within a row of 16 lanes the partner is taken by a DPP
+// permutation (xor 1, xor 2, then the half-row and row mirrors, which pair
+// each lane of one half with one of the other), with no trip through the
+// LDS crossbar that other lane shuffles take; offsets 16 and 32 shuffle.
+// Sums over a block come out the same with any such pairing.
+__device__ __forceinline__ int partner_i32(int v, int off) {
+    switch (off) {
+        case 1: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+        case 2: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+        case 4: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+        case 8: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);   // row_mirror
+        default: return __shfl_xor(v, off, 64);
+    }
+}
+__device__ __forceinline__ float partner(float v, int off) {
+    return __int_as_float(partner_i32(__float_as_int(v), off));
+}
+__device__ __forceinline__ double partner(double v, int off) {
+    const long long b = __double_as_longlong(v);
+    const int lo = partner_i32((int)(unsigned)b, off), hi = partner_i32((int)(b >> 32), off);
+    return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
 // Sum NP per-lane values over aligned groups of LPR lanes. Each halving step
-// trades half of the values with the partner lane, so after log2(NP) steps
-// every lane holds the partial of one of the NP values; plain butterflies
-// finish the sum. Returns the lane's total; *which gets its value index.
-// Every lane of a group of LPR/NP consecutive lanes ends with the same value.
+// trades half of the values with a partner lane in the other half of the
+// block, so after log2(NP) steps every lane holds the partial of one of the
+// NP values; butterflies finish the sum. Returns the lane's total; *which
+// gets its value index. Every lane of a group of LPR/NP consecutive lanes
+// ends with the same value.
 template <typename T, int NP, int LPR>
 __device__ __forceinline__ T row_reduce(const T (&v)[NP], int* which) {
     static_assert(LPR >= NP, "one value per lane at least");
@@ -46,16 +71,25 @@ __device__ __forceinline__ T row_reduce(const T (&v)[NP], int* which) {
         for (int i = 0; i < n / 2; ++i) {
             const T send = upper ? cur[i] : cur[i + n / 2];
             const T keep = upper ? cur[i + n / 2] : cur[i];
-            cur[i] = keep + __shfl_xor(send, off, 64);
+            cur[i] = keep + partner(send, off);
         }
         if (upper) lo += n / 2;
         off >>= 1;
     }
     T t = cur[0];
 #pragma unroll
-    for (int o = LPR / NP / 2; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+    for (int o = LPR / NP / 2; o > 0; o >>= 1) t += partner(t, o);
     *which = lo;
     return t;
+}
+
+// sum over aligned groups of `width` lanes (a power of two <= 64), every
+// lane of a group ending with the group's sum
+template <typename T, int WIDTH>
+__device__ __forceinline__ T group_sum_dpp(T v) {
+#pragma unroll
+    for (int o = WIDTH / 2; o > 0; o >>= 1) v += partner(v, o);
+    return v;
 }
 
 // The routing a decode call uses, one entry per lane (< n_assign): a row's

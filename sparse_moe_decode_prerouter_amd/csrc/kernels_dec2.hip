@@ -14,6 +14,7 @@
 #include "moe_internal.h"
 #include "topk.h"
 #include "dec_common.h"
+#include "dec_b_body.h"
 
 namespace moe {
 
@@ -213,250 +214,11 @@ hipError_t launch_dec_r(const DecAArgs& a, const RouteArgs& r, hipStream_t s, co
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// K_B: int4 down GEMV + combine. Block 0 takes the head's top-k (it is
-// dispatched first, so it overlaps the rest); every other block owns RB
-// consecutive output rows.
-//
-// Lane layout (F = d_ff): a Wd row holds F/2 bytes of packed int4, i.e.
-// LPR = F/8 dwords; lane c of a row group owns dword c, so it needs h
-// elements [8c, 8c+8) only (no lane loads h it does not use). RPP = 64/LPR
-// rows are covered per pass and kPassB passes per block: RB = kPassB * RPP.
-// Each wave runs the routed experts s = wave, wave + 4, ... and kPassB/4 of
-// the shared expert's passes, so all four waves do the same program: every
-// wave reads the routing digest itself (no cross-wave wait) and all loads
-// that need no routing are issued before the digest is consumed.
-// Partial sums go to LDS indexed by assignment id (t*k + j) or shared
-// token, and each (token, row) output sums them in routing order, so the
-// result does not depend on how slots are spread over waves.
-// ---------------------------------------------------------------------------
-constexpr int kPassB = 4;
-constexpr int kMaxTokB = 16;
-
-template <int F>
-struct BGeo {
-    static constexpr int LPR = F / 8;
-    static constexpr int RPP = 64 / LPR;
-    static constexpr int RB = kPassB * RPP;
-};
-
-// LoRA B row (r bf16) . LoRA A output row (r fp32): the loads are issued
-// together up front and the products summed later, in q order.
-constexpr int kLoraChunks = 2;                // r <= 16, r % 8 == 0
-struct LoraRegs {
-    u32x4 b[kLoraChunks];
-    float4 u[2 * kLoraChunks];
-};
-__device__ __forceinline__ void lora_issue(LoraRegs& R, const uint16_t* brow, const float* urow, int r) {
-#pragma unroll
-    for (int c = 0; c < kLoraChunks; ++c) {
-        const int cc = 8 * c < r ? c : 0;
-        R.b[c] = *(const u32x4*)(brow + 8 * cc);
-        R.u[2 * c] = *(const float4*)(urow + 8 * cc);
-        R.u[2 * c + 1] = *(const float4*)(urow + 8 * cc + 4);
-    }
-}
-__device__ __forceinline__ float lora_dot(const LoraRegs& R, int r) {
-    float l = 0.f;
-#pragma unroll
-    for (int c = 0; c < kLoraChunks; ++c) {
-        if (8 * c < r) {
-            const uint32_t bw[4] = {R.b[c].x, R.b[c].y, R.b[c].z, R.b[c].w};
-            const float uu[8] = {R.u[2 * c].x, R.u[2 * c].y, R.u[2 * c].z, R.u[2 * c].w,
-                                 R.u[2 * c + 1].x, R.u[2 * c + 1].y, R.u[2 * c + 1].z, R.u[2 * c + 1].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                l += bf16_to_f32(bw[i] & 0xFFFF) * uu[2 * i];
-                l += bf16_to_f32(bw[i] >> 16) * uu[2 * i + 1];
-            }
-        }
-    }
-    return l;
-}
-
-// One expert's Wd rows for this lane: NP passes of (dword of int4, (s,b)).
-template <int NP>
-struct DownRegs {
-    uint32_t q[NP];
-    uint32_t sb[NP];
-};
-
-// Rows row_first + i * STEP, i < NP: one base address, compile-time offsets.
-template <int F, int NP, int STEP>
-__device__ __forceinline__ void down_issue(DownRegs<NP>& R, const uint8_t* blob, const BlobLayout& L, int row_first) {
-    using G = BGeo<F>;
-    const int lane = threadIdx.x & 63, c = lane % G::LPR;
-    const uint32_t* q = (const uint32_t*)(blob + L.down_q) + (size_t)row_first * (F / 8) + c;
-    const uint32_t* sb = (const uint32_t*)(blob + L.down_sb) + (size_t)row_first * (F / 64) + c / 8;
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        R.q[i] = __builtin_nontemporal_load(q + i * STEP * (F / 8));
-        R.sb[i] = __builtin_nontemporal_load(sb + i * STEP * (F / 64));
-    }
-}
-
-__device__ __forceinline__ void h_issue(float4 (&hv)[2], const float* hrow, int c) {
-    hv[0] = *(const float4*)(hrow + 8 * c);
-    hv[1] = *(const float4*)(hrow + 8 * c + 4);
-}
-
-// Per-lane partial of each pass: sum_j (s q_j + b) h_j over the lane's 8 elements.
-template <int NP>
-__device__ __forceinline__ void down_partial(const DownRegs<NP>& R, const float4 (&hv)[2], float (&o)[NP]) {
-    const float h[8] = {hv[0].x, hv[0].y, hv[0].z, hv[0].w, hv[1].x, hv[1].y, hv[1].z, hv[1].w};
-    float hs = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) hs += h[j];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        float acc = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc += (float)((R.q[i] >> (4 * j)) & 0xFu) * h[j];
-        o[i] = f16_to_f32(R.sb[i] & 0xFFFF) * acc + f16_to_f32(R.sb[i] >> 16) * hs;
-    }
-}
-
+// K_B: its body is in dec_b_body.h (shared with the one-launch-per-layer
+// decode kernel); the standalone launch.
 template <int F>
 __global__ void __launch_bounds__(kThreads, 2) k_dec_b(DecBArgs a) {
-    using G = BGeo<F>;
-    constexpr int NPS = kPassB / kWaves;           // shared-expert passes per wave
-    __shared__ float part[(kMaxAssign + kMaxTokB) * G::RB];
-    __shared__ uint32_t sl[kWaves][64];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (blockIdx.x == 0) {
-        if (a.pred_idx)
-            topk_rows(false, a.logits_h, a.En, a.kn, a.n_tok, a.head_bias, a.hist_cur_m, a.hist_cur, a.hist_prev_m,
-                      a.hist_prev, nullptr, a.kn, a.pred_idx, a.pred_w);
-        return;
-    }
-    const int d = a.d, n_tok = a.n_tok, k = a.k;
-    const int n_assign = n_tok * k;
-    const int row0 = (blockIdx.x - 1) * G::RB;
-    const bool has_shared = a.fs != 0;
-    const BlobLayout L = BlobLayout::make(d, F);
-    const int c = lane % G::LPR, rsub = lane / G::LPR;
-
-    // ---- level 0, identical in every wave. The routing entries go first
-    // (K_A read them on every XCD, so they are L2 hits); all other loads need
-    // no routing and are issued unconditionally (clamped indices, stand-in
-    // pointers), so waiting for the routing never waits for them.
-    const RouteIn rin = route_load(a.route_idx, a.route_w, a.self_idx, a.self_w, n_assign);
-    const float v_sg = (a.sgate ? a.sgate : (const float*)a.err)[lane < n_tok ? lane : 0];
-    // epilogue operands: thread -> (token, row)
-    const int ep_n = n_tok * G::RB;
-    const int ep_q = tid < ep_n ? tid : 0;
-    const int et = ep_q / G::RB, er = ep_q % G::RB;
-    const float ep_x = a.fused ? a.x[(size_t)et * d + row0 + er] : 0.f;
-    const bool lora_on = a.lora_b && a.r;
-    const bool lora_vec = lora_on && (a.r & 7) == 0 && a.r <= 8 * kLoraChunks;
-    LoraRegs lr;
-    if (lora_vec) lora_issue(lr, a.lora_b + (size_t)(row0 + er) * a.r, a.au + (size_t)et * a.r, a.r);
-    // shared expert: passes [NPS*wave, NPS*wave + NPS), token 0's hidden state
-    const uint8_t* sh_blob = has_shared && a.ev.shared ? a.ev.shared : a.ev.base;
-    DownRegs<NPS> shr;
-    down_issue<F, NPS, G::RPP>(shr, sh_blob, L, row0 + NPS * wave * G::RPP + rsub);
-    const int sh_tag = *(a.ev.shared_tag ? a.ev.shared_tag : a.err);
-    const bool sh_ok = has_shared && a.ev.shared && (!a.ev.shared_tag || sh_tag == a.ev.E);
-    float4 shh[2];
-    h_issue(shh, has_shared ? a.hs : a.h, c);
-    // zero the partials: entries of invalid assignments are never written
-    for (int i = tid; i < (n_assign + n_tok) * G::RB; i += kThreads) part[i] = 0.f;
-    lds_barrier();
-
-    // ---- level 1: this wave sorts the routing (registers + its LDS slice),
-    // then the routed experts, two slots in flight per wave. The first pair
-    // is issued before the shared expert is computed (its loads are the
-    // oldest, so waiting for them does not wait for the routed rows).
-    int me;
-    float mw;
-    route_merge(rin, a.route_idx != nullptr, k, n_assign, &me, &mw);
-    const WaveDigest W = wave_digest(n_assign, me, a.E, sl[wave]);
-    const int n_active = W.n_active, n_valid = W.n_valid;
-    auto blob_of = [&](int s) -> const uint8_t* {
-        if (s >= n_active) return nullptr;
-        const int e = __builtin_amdgcn_readlane((int)(W.sk >> 16), nth_set(W.starts, s));
-        if (!a.ev.slot_of) return a.ev.base + (size_t)e * a.ev.blob;
-        const int sl = a.ev.slot_of[e];
-        if (sl < 0 || (a.ev.slot_tag && a.ev.slot_tag[sl] != e)) return nullptr;
-        return a.ev.base + (size_t)sl * a.ev.blob;
-    };
-    auto slot_compute = [&](const DownRegs<kPassB>& R, const uint8_t* blob, int s, const float4 (&h0)[2]) {
-        const int p0 = nth_set(W.starts, s);
-        const int p1 = s + 1 < n_active ? nth_set(W.starts, s + 1) : n_valid;
-        for (int p = p0; p < p1; ++p) {
-            float4 hv[2];
-            if (p == p0) { hv[0] = h0[0]; hv[1] = h0[1]; }
-            else h_issue(hv, a.h + (size_t)p * F, c);
-            float o[kPassB];
-            down_partial<kPassB>(R, hv, o);
-            int pass;
-            const float tot = row_reduce<float, kPassB, G::LPR>(o, &pass);
-            const int aid = __builtin_amdgcn_readlane((int)(W.sk & 0xFFFF), p);
-            const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mw), aid < n_assign ? aid : 0));
-            if (blob && (c % (G::LPR / kPassB)) == 0 && aid >= 0 && aid < n_assign)
-                part[aid * G::RB + pass * G::RPP + rsub] = wgt * tot;
-        }
-    };
-    auto pair_issue = [&](int s0, DownRegs<kPassB>& R0, DownRegs<kPassB>& R1, float4 (&h0)[2], float4 (&h1)[2],
-                          const uint8_t*& b0, const uint8_t*& b1) {
-        const int s1 = s0 + kWaves;
-        b0 = blob_of(s0);
-        b1 = blob_of(s1);
-        down_issue<F, kPassB, G::RPP>(R0, b0 ? b0 : a.ev.base, L, row0 + rsub);
-        down_issue<F, kPassB, G::RPP>(R1, b1 ? b1 : a.ev.base, L, row0 + rsub);
-        const int q0 = s0 < n_active ? nth_set(W.starts, s0) : 0;
-        const int q1 = s1 < n_active ? nth_set(W.starts, s1) : 0;
-        h_issue(h0, a.h + (size_t)q0 * F, c);
-        h_issue(h1, a.h + (size_t)q1 * F, c);
-    };
-    {
-        DownRegs<kPassB> R0, R1;
-        float4 h0[2], h1[2];
-        const uint8_t *b0, *b1;
-        pair_issue(wave, R0, R1, h0, h1, b0, b1);
-        if (has_shared) {
-            for (int t = 0; t < n_tok; ++t) {
-                float4 hv[2];
-                if (t == 0) { hv[0] = shh[0]; hv[1] = shh[1]; }
-                else h_issue(hv, a.hs + (size_t)t * F, c);
-                float o[NPS];
-                down_partial<NPS>(shr, hv, o);
-                int pass;
-                const float tot = row_reduce<float, NPS, G::LPR>(o, &pass);
-                const float wgt = a.sgate ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_sg), t)) : 1.f;
-                if (sh_ok && (c % (G::LPR / NPS)) == 0)
-                    part[(n_assign + t) * G::RB + (NPS * wave + pass) * G::RPP + rsub] = wgt * tot;
-            }
-        }
-        if (wave < n_active) slot_compute(R0, b0, wave, h0);
-        if (wave + kWaves < n_active) slot_compute(R1, b1, wave + kWaves, h1);
-    }
-    for (int s0 = wave + 2 * kWaves; s0 < n_active; s0 += 2 * kWaves) {
-        DownRegs<kPassB> R0, R1;
-        float4 h0[2], h1[2];
-        const uint8_t *b0, *b1;
-        pair_issue(s0, R0, R1, h0, h1, b0, b1);
-        slot_compute(R0, b0, s0, h0);
-        if (s0 + kWaves < n_active) slot_compute(R1, b1, s0 + kWaves, h1);
-    }
-    lds_barrier();
-
-    // ---- epilogue: shared, then routed in routing order, LoRA B, residual
-    if (tid < ep_n) {
-        float y = has_shared ? part[(n_assign + et) * G::RB + er] : 0.f;
-        for (int j = 0; j < k; ++j) y += part[(et * k + j) * G::RB + er];
-        if (lora_on) {
-            float l = 0.f;
-            if (lora_vec) l = lora_dot(lr, a.r);
-            else
-                for (int q = 0; q < a.r; ++q)
-                    l += bf16_to_f32(a.lora_b[(size_t)(row0 + er) * a.r + q]) * a.au[(size_t)et * a.r + q];
-            y += a.lora_scale * l;
-        }
-        if (a.fused) y += ep_x;
-        a.y[(size_t)et * d + row0 + er] = y;
-    }
+    dec_b_body<F, false>(a, (int)blockIdx.x, FuseSync{});
 }
 
 __global__ void __launch_bounds__(kThreads) k_topk_job(TopkJob j, int n_tok) {

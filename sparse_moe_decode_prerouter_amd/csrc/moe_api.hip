@@ -26,6 +26,9 @@ thread_local int g_last_hip = 0;
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kStageCopyBlocks = 32;     // blocks of a device staging copy (PCIe-bound)
+// polls before a device-side wait of the one-launch step gives up (each poll
+// is a device-scope load plus a short sleep, about a microsecond: ~0.25 s)
+constexpr unsigned kDefaultWaitPolls = 1u << 18;
 
 struct Carver {
     uint8_t* base;
@@ -318,29 +321,12 @@ int run_shared_lora_part2(moe_layer* L, const moe_io* io, int n_tok, hipStream_t
     return MOE_OK;
 }
 
-// defer_in: a previous layer's head top-k to run inside this layer's K_A.
-// defer_out (stack mode): this layer's head top-k is not run here but handed
-// back, for the next layer's K_A to run (its prediction is for the next step).
-// pred_ready (stack staging): recorded once the prediction of the previous
-// layer's head (run inside this call's first launch) is final
-int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const TopkJob* defer_in = nullptr,
-               TopkJob* defer_out = nullptr, const PrologueArgs* nxt = nullptr, bool skip_pro = false,
-               bool* took_nxt = nullptr, hipEvent_t pred_ready = nullptr) {
+// The arguments of the two fast-path launches of one layer's decode call
+// (without the deferred head top-k, which the caller adds).
+void fill_dec_args(const moe_layer* L, const moe_io* io, int n_tok, bool need_router, DecAArgs& a, DecBArgs& b) {
     const moe_layer_desc& D = L->desc;
-    if (defer_out) defer_out->pred_idx = nullptr;
-    if (took_nxt) *took_nxt = false;
-    // shapes outside the fused two-kernel path take the general grouped-GEMM path
-    if (!dec_fast_path_ok(D.d_model, D.d_ff, fs_main(L), n_tok, D.top_k)) {
-        if (defer_in && defer_in->pred_idx) HIPCHK(launch_topk_job(*defer_in, n_tok, st));
-        if (pred_ready) HIPCHK(hipEventRecord(pred_ready, st));
-        return run_prefill(L, io, n_tok, st, false, 0, nxt, skip_pro, took_nxt);
-    }
     const bool fused = D.flags & MOE_FUSE_NORM_RESIDUAL;
-    if (L->staged_pending_buf[L->cur_buf]) HIPCHK(hipStreamWaitEvent(st, L->ev_staged_buf[L->cur_buf], 0));
-    const bool need_router = io->route_idx == nullptr || io->self_rows;
-    if (need_router && !L->w.router) return MOE_E_INVALID;
-
-    DecAArgs a{};
+    a = DecAArgs{};
     a.x = io->x_in;
     a.x_is_bf16 = (!fused && D.act_dtype == MOE_ACT_BF16) ? 1 : 0;
     a.fused = fused; a.gamma = L->w.norm_gamma; a.eps = D.rms_eps;
@@ -359,6 +345,46 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
     a.err = L->s.err;
     dec_a_blocks(D.d_model, D.d_ff, fs_main(L), n_tok, D.top_k, D.n_experts, a.En, D.lora_rank,
                  a.sgate_w != nullptr, &a.nb_h, &a.nb_head, &a.nb_misc);
+    b = DecBArgs{};
+    b.ev = a.ev; b.d = D.d_model; b.f = D.d_ff; b.fs = fs_main(L); b.k = D.top_k; b.n_tok = n_tok;
+    b.E = D.n_experts;
+    b.route_idx = a.route_idx; b.route_w = a.route_w; b.self_idx = a.self_idx; b.self_w = a.self_w;
+    b.sgate = (fs_main(L) && L->w.shared_gate) ? L->s.sgate : nullptr;
+    b.h = L->s.h; b.hs = L->s.hs;
+    b.x = (const float*)io->x_in; b.fused = fused;
+    b.au = L->s.au; b.lora_b = D.lora_rank ? L->w.lora_b : nullptr; b.r = D.lora_rank;
+    b.lora_scale = D.lora_rank ? D.lora_alpha / (float)D.lora_rank : 0.f;
+    b.y = io->y_out;
+    b.logits_h = L->s.logits_h; b.En = D.next_n_experts; b.kn = D.next_top_k; b.head_bias = L->w.head_bias;
+    b.hist_cur_m = L->w.hist_cur; b.hist_prev_m = L->w.hist_prev; b.hist_cur = io->hist_cur; b.hist_prev = io->hist_prev;
+    b.pred_idx = io->pred_idx; b.pred_w = io->pred_w;
+    b.err = L->s.err;
+}
+
+// defer_in: a previous layer's head top-k to run inside this layer's K_A.
+// defer_out (stack mode): this layer's head top-k is not run here but handed
+// back, for the next layer's K_A to run (its prediction is for the next step).
+// pred_ready (stack staging): recorded once the prediction of the previous
+// layer's head (run inside this call's first launch) is final
+int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const TopkJob* defer_in = nullptr,
+               TopkJob* defer_out = nullptr, const PrologueArgs* nxt = nullptr, bool skip_pro = false,
+               bool* took_nxt = nullptr, hipEvent_t pred_ready = nullptr) {
+    const moe_layer_desc& D = L->desc;
+    if (defer_out) defer_out->pred_idx = nullptr;
+    if (took_nxt) *took_nxt = false;
+    // shapes outside the fused two-kernel path take the general grouped-GEMM path
+    if (!dec_fast_path_ok(D.d_model, D.d_ff, fs_main(L), n_tok, D.top_k)) {
+        if (defer_in && defer_in->pred_idx) HIPCHK(launch_topk_job(*defer_in, n_tok, st));
+        if (pred_ready) HIPCHK(hipEventRecord(pred_ready, st));
+        return run_prefill(L, io, n_tok, st, false, 0, nxt, skip_pro, took_nxt);
+    }
+    if (L->staged_pending_buf[L->cur_buf]) HIPCHK(hipStreamWaitEvent(st, L->ev_staged_buf[L->cur_buf], 0));
+    const bool need_router = io->route_idx == nullptr || io->self_rows;
+    if (need_router && !L->w.router) return MOE_E_INVALID;
+
+    DecAArgs a{};
+    DecBArgs b{};
+    fill_dec_args(L, io, n_tok, need_router, a, b);
     if (defer_in && defer_in->pred_idx) a.topk = *defer_in;
 
     if (need_router) {
@@ -399,19 +425,6 @@ int run_decode(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, const 
         if (rc != MOE_OK) return rc;
     }
 
-    DecBArgs b{};
-    b.ev = a.ev; b.d = D.d_model; b.f = D.d_ff; b.fs = fs_main(L); b.k = D.top_k; b.n_tok = n_tok;
-    b.E = D.n_experts;
-    b.route_idx = a.route_idx; b.route_w = a.route_w; b.self_idx = a.self_idx; b.self_w = a.self_w;
-    b.sgate = (fs_main(L) && L->w.shared_gate) ? L->s.sgate : nullptr;
-    b.h = L->s.h; b.hs = L->s.hs;
-    b.x = (const float*)io->x_in; b.fused = fused;
-    b.au = L->s.au; b.lora_b = D.lora_rank ? L->w.lora_b : nullptr; b.r = D.lora_rank;
-    b.lora_scale = D.lora_rank ? D.lora_alpha / (float)D.lora_rank : 0.f;
-    b.y = io->y_out;
-    b.logits_h = L->s.logits_h; b.En = D.next_n_experts; b.kn = D.next_top_k; b.head_bias = L->w.head_bias;
-    b.hist_cur_m = L->w.hist_cur; b.hist_prev_m = L->w.hist_prev; b.hist_cur = io->hist_cur; b.hist_prev = io->hist_prev;
-    b.pred_idx = io->pred_idx; b.pred_w = io->pred_w;
     if (defer_out && io->pred_idx && D.next_n_experts <= 64 * kDeferMaxPer) {
         TopkJob& j = *defer_out;
         j.logits = L->s.logits_h; j.En = D.next_n_experts; j.kn = D.next_top_k; j.bias = L->w.head_bias;
@@ -947,6 +960,29 @@ static size_t stack_pred_entries(moe_layer* const* layers, int n) {
     return (size_t)T * layers[0]->desc.top_k;
 }
 
+// The one-launch step needs layers whose experts are all resident, whose
+// shapes take the two-kernel fast path and agree from layer to layer (one
+// work-item layout for all), and that run nothing between K_A and K_B (no
+// head MLP branch, no adapter on the shared expert).
+static bool stack_one_launch_ok(moe_layer* const* layers, int n) {
+    const moe_layer_desc& D0 = layers[0]->desc;
+    const moe_layer* L0 = layers[0];
+    if (!stack_one_fast_ok(D0.d_model, D0.d_ff, fs_main(L0), 1, D0.top_k)) return false;
+    for (int l = 0; l < n; ++l) {
+        const moe_layer* L = layers[l];
+        const moe_layer_desc& D = L->desc;
+        if (!L->resident || D.head_hidden > 0 || has_shared_lora(L)) return false;
+        if (D.d_model != D0.d_model || D.d_ff != D0.d_ff || fs_main(L) != fs_main(L0) || D.top_k != D0.top_k ||
+            D.n_experts != D0.n_experts || D.lora_rank != D0.lora_rank ||
+            (L->w.shared_gate != nullptr) != (L0->w.shared_gate != nullptr))
+            return false;
+        if (D.lora_rank && (D.lora_rank % 8 || D.lora_rank > 16)) return false;
+        if (l + 1 < n && (D.next_n_experts > 64 * kStackHeadMaxPer || D.next_n_experts != layers[0]->desc.next_n_experts))
+            return false;
+    }
+    return true;
+}
+
 static size_t stack_carve(moe_layer* const* layers, int n, uint8_t* base, moe_stack* S) {
     Carver c{base};
     const size_t per = stack_pred_entries(layers, n);
@@ -956,7 +992,132 @@ static size_t stack_carve(moe_layer* const* layers, int n, uint8_t* base, moe_st
         if (S) { S->d_pred_idx[b] = pi; S->d_pred_w[b] = pw; }
     }
     if (S) S->pred_cap = per;
+    StackLayerArgs* tab = c.take<StackLayerArgs>((size_t)n);
+    uint32_t* sync = c.take<uint32_t>(stack_sync_words(n));
+    if (S) { S->d_tab = tab; S->d_sync = sync; }
+    if (stack_one_launch_ok(layers, n)) {
+        // exchange copies of the one-launch step, sized for the most tokens
+        // a step of this stack can take there
+        const moe_layer_desc& D = layers[0]->desc;
+        int nt = 0;
+        for (int t = 1; t <= 64; ++t)
+            if (stack_one_fast_ok(D.d_model, D.d_ff, fs_main(layers[0]), t, D.top_k)) nt = t;
+        for (int l = 0; l < n; ++l) nt = std::min(nt, layers[l]->desc.max_tokens);
+        auto al = [](size_t v) { return (v + 63) / 64 * 64; };
+        size_t off[5], o = 0;
+        off[0] = o; o += al((size_t)nt * D.d_model);
+        off[1] = o; o += al((size_t)nt * D.top_k * D.d_ff);
+        off[2] = o; o += al((size_t)nt * std::max(1, fs_main(layers[0])));
+        off[3] = o; o += al((size_t)nt * std::max(1, D.lora_rank));
+        off[4] = o; o += al((size_t)nt);
+        float* xchg = c.take<float>(o * kXchgCopies * n);
+        if (S) {
+            S->d_xchg = xchg;
+            S->xchg_stride = o;
+            for (int i = 0; i < 5; ++i) S->xchg_off[i] = off[i];
+            S->xchg_tokens = nt;
+        }
+    }
     return align_up(c.off, 256);
+}
+
+// the per-layer table of the one-launch step: the fields fixed at creation
+// (the per-call ones are written by the patch kernel before each launch)
+static int stack_one_launch_init(moe_stack* S) {
+    const int n = S->n;
+    std::vector<StackLayerArgs> tab(n);
+    int nb_head = 0;
+    for (int l = 0; l < n; ++l) {
+        moe_layer* L = S->layers[l];
+        moe_io io{};
+        io.x_in = nullptr;
+        io.y_out = nullptr;
+        int32_t dummy_pred = 0;
+        if (l + 1 < n) { io.pred_idx = &dummy_pred; io.pred_w = (float*)&dummy_pred; }
+        fill_dec_args(L, &io, 1, l == 0, tab[l].a, tab[l].b);
+        DecAArgs& a = tab[l].a;
+        DecBArgs& b = tab[l].b;
+        b.pred_idx = nullptr; b.pred_w = nullptr;
+        if (l == 0) nb_head = a.nb_head;
+        // the values handed from K_A to K_B, and x from layer l-1's K_B, go
+        // through kXchgCopies copies (readers spread over them)
+        float* reg = S->d_xchg + (size_t)l * kXchgCopies * S->xchg_stride;
+        a.h = reg + S->xchg_off[1];
+        b.h = a.h;
+        a.hs = reg + S->xchg_off[2];
+        b.hs = a.hs;
+        a.au = reg + S->xchg_off[3];
+        b.au = a.au;
+        a.sgate = reg + S->xchg_off[4];
+        if (b.sgate) b.sgate = a.sgate;
+        a.xstride = b.xstride = S->xchg_stride;
+        a.xcopies = b.xcopies = kXchgCopies;
+        a.x_repl = l > 0;
+        if (l > 0) { a.x = reg + S->xchg_off[0]; b.x = reg + S->xchg_off[0]; }
+        b.xnext = l + 1 < n ? S->d_xchg + (size_t)(l + 1) * kXchgCopies * S->xchg_stride + S->xchg_off[0] : nullptr;
+    }
+    // the last layer has no head: it keeps the others' item count, and its
+    // head items find no rows
+    tab[n - 1].a.nb_head = nb_head;
+    HIPCHK(hipMemcpy(S->d_tab, tab.data(), sizeof(StackLayerArgs) * n, hipMemcpyHostToDevice));
+    HIPCHK(hipMemset(S->d_sync, 0, sizeof(uint32_t) * stack_sync_words(n)));
+    int dev = 0, ncu = 0;
+    HIPCHK(hipGetDevice(&dev));
+    HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+    const int per_cu = stack_one_launch_blocks_per_cu(S->layers[0]->desc.d_model, S->layers[0]->desc.d_ff);
+    S->one_grid = std::max(1, per_cu) * std::max(1, ncu);
+    return MOE_OK;
+}
+
+static int trace_layer(moe_stack* S, int l, const void* x, int n_tok, hipStream_t st);
+
+// one decode step as a router launch (layer 0 routes itself) + the table
+// patch + the step kernel
+static int stack_decode_one(moe_stack* S, const float* x_in, float* x_out, int n_tok, const int32_t* route_idx,
+                            const float* route_w, int32_t* pred_idx, float* pred_w, int32_t* used_idx,
+                            float* used_w, const int32_t* hist_prev, hipStream_t st) {
+    moe_layer* L0 = S->layers[0];
+    const moe_layer_desc& D = L0->desc;
+    moe_io io{};
+    io.x_in = x_in;
+    io.y_out = x_out;
+    io.pred_idx = S->n > 1 ? pred_idx : nullptr;   // (head items counted as for every layer but the last)
+    io.pred_w = S->n > 1 ? pred_w : nullptr;
+    DecAArgs a{};
+    DecBArgs b{};
+    fill_dec_args(L0, &io, n_tok, true, a, b);
+    int rc = trace_layer(S, 0, x_in, n_tok, st);
+    if (rc != MOE_OK) return rc;
+    RouteArgs r{};
+    r.router = L0->w.router; r.router_bias = L0->w.router_bias; r.E = D.n_experts; r.k = D.top_k;
+    r.route_idx = nullptr; r.logits_r = L0->s.logits_r;
+    r.self_idx = L0->s.self_idx; r.self_w = L0->s.self_w; r.counters = L0->s.counters;
+    const KTime tr{S->profiling ? S->ev_t[0] : nullptr, S->profiling ? S->ev_t[1] : nullptr};
+    HIPCHK(launch_dec_r(a, r, st, &tr));
+    StackPatchArgs p{};
+    p.tab = S->d_tab; p.sync = S->d_sync; p.n_layers = S->n; p.n_tok = n_tok; p.k = D.top_k; p.d = D.d_model; p.f = D.d_ff;
+    const int hr = stack_one_hrows(D.d_model);
+    const int max_active = std::min(n_tok * D.top_k, D.n_experts);
+    p.nb_h = (fs_main(L0) + max_active * D.d_ff + hr - 1) / hr;
+    p.x_in = x_in; p.x_out = x_out;
+    p.route_idx = route_idx; p.route_w = route_w; p.pred_idx = pred_idx; p.pred_w = pred_w;
+    p.used_idx = used_idx; p.used_w = used_w; p.hist_prev = hist_prev;
+    p.trace = S->x_trace;
+    StackDecArgs sd{};
+    sd.tab = S->d_tab; sd.n_layers = S->n;
+    sd.nA = p.nb_h + a.nb_head + a.nb_misc;
+    sd.nB = 1 + D.d_model / stack_one_brows(D.d_ff);
+    sd.sync = S->d_sync;
+    sd.spin_limit = S->wait_polls;
+    const int total = S->n * (sd.nA + sd.nB);
+    const KTime tk{S->profiling ? S->ev_t[2] : nullptr, S->profiling ? S->ev_t[3] : nullptr};
+    // one block per work item of a layer when they fit on the chip at once
+    // (each block then keeps its role from layer to layer), else fewer
+    const int per_layer = sd.nA + sd.nB;
+    const int grid = per_layer <= S->one_grid ? per_layer : std::min(S->one_grid, total);
+    HIPCHK(launch_stack_one(p, sd, grid, st, &tk));
+    if (S->profiling) S->ev_used[0] = S->ev_used[1] = true;
+    return MOE_OK;
 }
 
 size_t moe_stack_workspace_bytes(moe_layer* const* layers, int n) {
@@ -977,8 +1138,51 @@ int moe_stack_create(moe_layer* const* layers, int n, void* d_workspace, size_t 
     if (!S->layers) { delete S; return MOE_E_INVALID; }
     for (int l = 0; l < n; ++l) S->layers[l] = layers[l];
     S->n = n;
+    S->wait_polls = kDefaultWaitPolls;
     stack_carve(layers, n, (uint8_t*)d_workspace, S);
+    S->one_ok = stack_one_launch_ok(layers, n) && S->d_xchg != nullptr && S->xchg_tokens >= 1;
+    if (S->one_ok) {
+        rc = stack_one_launch_init(S);
+        if (rc != MOE_OK) { moe_stack_destroy(S); return rc; }
+    }
     *out = S;
+    return MOE_OK;
+}
+
+int moe_stack_set_one_launch(moe_stack* S, int enable) {
+    if (!S) return MOE_E_INVALID;
+    if (enable && !S->one_ok) return MOE_E_UNSUPPORTED;
+    S->one_launch = enable != 0;
+    return MOE_OK;
+}
+
+int moe_stack_set_wait_limit(moe_stack* S, unsigned polls) {
+    if (!S) return MOE_E_INVALID;
+    S->wait_polls = polls ? polls : kDefaultWaitPolls;
+    return MOE_OK;
+}
+
+int moe_stack_set_profiling(moe_stack* S, int enable) {
+    if (!S) return MOE_E_INVALID;
+    if (enable && !S->ev_t[0]) {
+        for (int i = 0; i < 4; ++i) HIPCHK(hipEventCreate(&S->ev_t[i]));
+    }
+    S->profiling = enable != 0;
+    S->ev_used[0] = S->ev_used[1] = false;
+    return MOE_OK;
+}
+
+int moe_stack_kernel_ms(moe_stack* S, float* ms_router, float* ms_step) {
+    if (!S) return MOE_E_INVALID;
+    float* outs[2] = {ms_router, ms_step};
+    for (int i = 0; i < 2; ++i) {
+        if (!outs[i]) continue;
+        *outs[i] = -1.f;
+        if (S->ev_used[i] && S->ev_t[2 * i]) {
+            HIPCHK(hipEventSynchronize(S->ev_t[2 * i + 1]));
+            HIPCHK(hipEventElapsedTime(outs[i], S->ev_t[2 * i], S->ev_t[2 * i + 1]));
+        }
+    }
     return MOE_OK;
 }
 
@@ -1017,6 +1221,15 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
     if (n_tok < 1 || n_tok * k > 4096 || n_tok > 256) return MOE_E_UNSUPPORTED;
     if (S->x_trace && (size_t)S->n * n_tok * S->layers[0]->desc.d_model > S->trace_cap) return MOE_E_CAPACITY;
     if (first_step) S->step = 0;
+    if (S->one_launch && !first_step && S->stage_mode == MOE_STAGE_OFF && n_tok <= S->xchg_tokens &&
+        stack_one_fast_ok(S->layers[0]->desc.d_model, S->layers[0]->desc.d_ff, fs_main(S->layers[0]), n_tok, k)) {
+        for (int l = 0; l < S->n; ++l)
+            if (n_tok > S->layers[l]->desc.max_tokens) return MOE_E_INVALID;
+        const int rc = stack_decode_one(S, x_in, x_out, n_tok, route_idx, route_w, pred_idx, pred_w, used_idx,
+                                        used_w, hist_prev, (hipStream_t)stream);
+        if (rc == MOE_OK) S->step++;
+        return rc;
+    }
     const bool on_demand = S->stage_mode == MOE_STAGE_ON_DEMAND;
     const bool prerouted = S->stage_mode == MOE_STAGE_PREROUTED;
     TopkJob pend{};
@@ -1114,6 +1327,8 @@ int moe_stack_prefill(moe_stack* S, float* x, int n_tok, int32_t* used_idx, floa
 
 void moe_stack_destroy(moe_stack* S) {
     if (!S) return;
+    for (int i = 0; i < 4; ++i)
+        if (S->ev_t[i]) (void)hipEventDestroy(S->ev_t[i]);
     delete[] S->layers;
     delete S;
 }

@@ -132,6 +132,9 @@ struct moe_layer {
     bool ev_t_used[3];
 };
 
+namespace moe {
+struct StackLayerArgs;
+}
 struct moe_stack {
     moe_layer** layers;
     int n;
@@ -147,6 +150,21 @@ struct moe_stack {
     // optional trace of every layer's input residual stream (device fp32)
     float* x_trace;
     size_t trace_cap;        // floats
+    // one launch per decode step (moe_stack_set_one_launch)
+    moe::StackLayerArgs* d_tab;   // [n] per-layer arguments (caller's workspace)
+    float* d_xchg;           // per layer: copies of the activations handed between phases
+    size_t xchg_stride;      // floats per copy
+    size_t xchg_off[5];      // offsets in a copy: x, h, hs, au, sgate
+    int xchg_tokens;         // tokens a copy holds
+    uint32_t* d_sync;        // stack_sync_words(n) counters, zero between launches
+    bool one_ok;             // the layers qualify (resident, identical fast-path shapes)
+    bool one_launch;         // enabled
+    int one_grid;            // blocks resident on the chip at once
+    uint32_t wait_polls;     // bound of each device-side wait (polls)
+    // kernel timestamps (moe_stack_set_profiling): layer 0's router, the step kernel
+    bool profiling;
+    bool ev_used[2];
+    hipEvent_t ev_t[4];
 };
 
 // ---- kernel launchers (kernels_*.hip) -------------------------------------
@@ -323,6 +341,10 @@ struct DecAArgs {
     int32_t* err;
     int nb_h, nb_head, nb_misc;
     TopkJob topk;          // pred_idx == nullptr: none
+    // one-launch stack decode: h, hs, au and sgate are written to xcopies
+    // copies xstride floats apart, and x is read from one of them (0: unused)
+    size_t xstride; int xcopies;
+    int x_repl;            // x is read from the exchange copies too (else from a.x itself)
 };
 hipError_t launch_dec_a(const DecAArgs& a, hipStream_t s, const KTime* tm = nullptr);
 bool dec_fast_path_ok(int d, int f, int fs, int n_tok, int k);
@@ -338,12 +360,63 @@ struct DecBArgs {
     const float* sgate; const float* h; const float* hs;
     const float* x; int fused; const float* au; const uint16_t* lora_b; int r; float lora_scale;
     float* y;
+    float* y_copy;         // one-launch stack decode: a second copy of y (the layer trace), or nullptr
+    float* xnext;          // one-launch stack decode: the next layer's x exchange copies (or nullptr)
+    size_t xstride; int xcopies;
     // head top-k (extra block)
     const double* logits_h; int En; int kn; const float* head_bias; const float* hist_cur_m; const float* hist_prev_m;
     const int32_t* hist_cur; const int32_t* hist_prev; int32_t* pred_idx; float* pred_w;
     int32_t* err;
 };
 hipError_t launch_dec_b(const DecBArgs& a, hipStream_t s, const KTime* tm = nullptr);
+
+// One launch per decode step for a stack of identical layers (kernels_stack.hip)
+struct StackLayerArgs {
+    DecAArgs a;
+    DecBArgs b;
+};
+#ifndef MOE_STACK_SUB
+#define MOE_STACK_SUB 16
+#endif
+#ifndef MOE_STACK_FLAGS
+#define MOE_STACK_FLAGS 64
+#endif
+constexpr int kStackLine = 32;                 // words per 128-byte line
+#ifndef MOE_XCHG_COPIES
+#define MOE_XCHG_COPIES 16
+#endif
+constexpr int kXchgCopies = MOE_XCHG_COPIES;   // copies of the activations handed between phases
+constexpr int kStackAPass = 4;                 // the step kernel's gate/up passes per wave (16 h rows a block)
+constexpr int kStackBPass = 8;                 // the step kernel's down passes per block
+constexpr int kStackSub = MOE_STACK_SUB;       // arrival sub-counters per phase
+constexpr int kStackFlags = MOE_STACK_FLAGS;   // copies of each phase's completion flag (<= 64)
+// lines: epoch + abort, then per phase (2 per layer) kStackSub sub-counters,
+// then the phases' top counters, then kStackFlags flags per phase
+inline size_t stack_sync_words(int n_layers) {
+    return (1 + 2 * (size_t)n_layers * (kStackSub + 1 + kStackFlags)) * kStackLine;
+}
+struct StackDecArgs {
+    const StackLayerArgs* tab; int n_layers; int nA; int nB;
+    uint32_t* sync;               // stack_sync_words(n_layers): counters, flags, epoch
+    uint32_t spin_limit;
+};
+struct StackPatchArgs {
+    StackLayerArgs* tab; uint32_t* sync; int n_layers; int n_tok; int k; int d; int f; int nb_h;
+    const float* x_in; float* x_out;
+    const int32_t* route_idx; const float* route_w;          // [layer][n_tok * k] (layer 0 unused)
+    int32_t* pred_idx; float* pred_w;
+    int32_t* used_idx; float* used_w;
+    const int32_t* hist_prev;
+    float* trace;                 // [layer][n_tok * d] or nullptr (layer 0 copied by the host)
+};
+constexpr int kStackHeadMaxPer = 4;         // the step kernel's head top-k: E <= 64 * 4
+bool stack_one_launch_shape_ok(int d, int f);
+int stack_one_hrows(int d);                      // h rows per K_A item of the step kernel
+int stack_one_brows(int f);                      // output rows per K_B item of the step kernel
+bool stack_one_fast_ok(int d, int f, int fs, int n_tok, int k);
+int stack_one_launch_blocks_per_cu(int d, int f);
+hipError_t launch_stack_one(const StackPatchArgs& p, const StackDecArgs& s, int grid, hipStream_t st,
+                            const KTime* tm = nullptr);
 hipError_t launch_topk_job(const TopkJob& j, int n_tok, hipStream_t s);
 
 struct SlotUpdate {

@@ -178,29 +178,34 @@ def check_decode_stack(ora, g, mode, out_steps, rows=None, what=""):
 
 
 @pytest.mark.timeout(600)
-def test_decode_stack_40_layers():
+@pytest.mark.parametrize("one,steps", [(True, 128), (False, 16)], ids=["one_launch", "per_layer"])
+def test_decode_stack_40_layers(one, steps):
     """The benchmarked configuration at full size: 40 layers of the 35B shape
     (16.9 GiB of int4 experts resident), batch 1, the stack decode the bench
-    replays, for 128 steps. Every step's 40 routing decisions (layer 0's
-    self-routing, 39 head predictions with their history) are checked on the
-    input each layer saw; the block outputs of every layer and the output
-    after 40 layers on a subset of steps."""
+    replays (one launch per step), for 128 steps; the per-layer launches for
+    16. Every step's 40 routing decisions (layer 0's self-routing, 39 head
+    predictions with their history) are checked on the input each layer saw;
+    the block outputs of every layer and the output after 40 layers on a
+    subset of steps."""
     import sparse_moe_decode_prerouter_amd as moe
     from test_gpu_stack import run_gpu
     shape = synth.LAYER35B
-    L_, B, steps = 40, 1, 128
-    say(f"40-layer decode stack B={B} steps={steps}")
+    L_, B = 40, 1
+    say(f"40-layer decode stack B={B} steps={steps} one_launch={one}")
     ws = [synth.layer_weights(shape, l, device="cuda", tag="full40") for l in range(L_)]
     gpus = [gpu_layer(shape, w, fused=True, max_tokens=B, head=(l + 1 < L_)) for l, w in enumerate(ws)]
     ora = [_oracle_layer_dev(shape, w, l + 1 < L_) for l, w in enumerate(ws)]
     stack = moe.MoeStack(gpus)
+    if one:
+        stack.set_one_launch(True)
     xs = np.stack([synth.activations(shape, B, ("full40", t), dtype=torch.float32).double().numpy()
                    for t in range(steps)])
     g = run_gpu(stack, L_, xs, shape.k)
     for Lr in gpus:
         assert Lr.status() == 0
     say("  GPU steps done; checking")
-    flips, worst, e2e = check_decode_stack(ora, g, "f64", out_steps=[0, 1, 2, 63, 127], what="40-layer")
+    out_steps = [0, 1, 2, 63, 127] if steps == 128 else [0, 1, steps - 1]
+    flips, worst, e2e = check_decode_stack(ora, g, "f64", out_steps=out_steps, what="40-layer")
     say(f"  {steps * L_} routing decisions checked, certified near ties {flips}; per-layer max rel-L2 {worst:.2e}; "
         f"after {L_} layers {e2e:.2e}")
     stack.close()

@@ -12,6 +12,9 @@ compared with the oracle's stack on the same routing within rel-L2 1e-2.
 Two ways of driving it:
   forced - the oracle's free run gives the routing both sides take;
   free   - the GPU follows its own predictions (the realistic dataflow).
+Each runs per layer (two launches a layer) and as one launch per step
+(moe_stack_set_one_launch), whose steps after the first run every layer's
+K_A and K_B as work items of a single kernel.
 """
 import numpy as np
 import pytest
@@ -29,12 +32,15 @@ if not torch.cuda.is_available():
 STACK_TOL = 1e-2
 
 
-def build(shape, L, tag, max_tokens=8):
+def build(shape, L, tag, max_tokens=8, one=False):
     ws = [layer_tensors(shape, layer=l, tag=tag) for l in range(L)]
     ora = [oracle_layer(shape, w) for w in ws]
     gpus = [gpu_layer(shape, w, fused=True, max_tokens=max_tokens, head=(l + 1 < L)) for l, w in enumerate(ws)]
     import sparse_moe_decode_prerouter_amd as moe
-    return ora, gpus, moe.MoeStack(gpus)
+    stack = moe.MoeStack(gpus)
+    if one:
+        stack.set_one_launch(True)
+    return ora, gpus, stack
 
 
 def run_gpu(stack, L, xs, k, forced_routes=None, trace=True):
@@ -97,12 +103,13 @@ def check_steps(ora, g, mode, steps_out=None, rows=None, what=""):
     return flips, worst, e2e
 
 
+@pytest.mark.parametrize("one", [False, True], ids=["per_layer", "one_launch"])
 @pytest.mark.parametrize("B", [1, 3])
-def test_stack_forced_routing(B):
+def test_stack_forced_routing(B, one):
     shape = synth.LAYER35B
     L, steps = 4, 4
-    say(f"stack forced L={L} B={B} steps={steps}")
-    ora, gpus, stack = build(shape, L, f"stackF{B}")
+    say(f"stack forced L={L} B={B} steps={steps} one_launch={one}")
+    ora, gpus, stack = build(shape, L, f"stackF{B}", one=one)
     xs = np.stack([synth.activations(shape, B, ("stk", B, t), dtype=torch.float32).double().numpy()
                    for t in range(steps)])
     recs = oracle.stack_decode(ora, xs, steps)
@@ -118,11 +125,12 @@ def test_stack_forced_routing(B):
     say(f"  per-layer max rel-L2 {worst:.2e}, stack {e2e:.2e}, certified near ties {flips}")
 
 
-def test_stack_free_running():
+@pytest.mark.parametrize("one", [False, True], ids=["per_layer", "one_launch"])
+def test_stack_free_running(one):
     shape = synth.LAYER35B
     L, steps, B = 4, 6, 2
-    say(f"stack free-running L={L} B={B} steps={steps}")
-    ora, gpus, stack = build(shape, L, "stackR")
+    say(f"stack free-running L={L} B={B} steps={steps} one_launch={one}")
+    ora, gpus, stack = build(shape, L, "stackR", one=one)
     xs = np.stack([synth.activations(shape, B, ("stkR", t), dtype=torch.float32).double().numpy()
                    for t in range(steps)])
     g = run_gpu(stack, L, xs, shape.k)
@@ -136,19 +144,49 @@ def test_stack_free_running():
     say(f"  per-layer max rel-L2 {worst:.2e}, stack {e2e:.2e}, certified near ties {flips}")
 
 
-def test_stack_tiny_shape_free_running():
-    """The fp32-activation toy shape through a 3-layer stack (general-path
-    kernels for d = 256)."""
+@pytest.mark.parametrize("one", [False, True], ids=["per_layer", "one_launch"])
+def test_stack_tiny_shape_free_running(one):
+    """The fp32-activation toy shape through a 3-layer stack."""
     shape = synth.TINY
     L, steps, B = 3, 4, 2
-    say(f"tiny stack free-running L={L} B={B} steps={steps}")
-    ora, gpus, stack = build(shape, L, "stackT")
+    say(f"tiny stack free-running L={L} B={B} steps={steps} one_launch={one}")
+    ora, gpus, stack = build(shape, L, "stackT", one=one)
     xs = np.stack([synth.activations(shape, B, ("stkT", t), dtype=torch.float32).double().numpy()
                    for t in range(steps)])
     g = run_gpu(stack, L, xs, shape.k)
     for L_ in gpus:
         assert L_.status() == 0
     flips, worst, e2e = check_steps(ora, g, "f64", what="tiny")
+    say(f"  per-layer max rel-L2 {worst:.2e}, stack {e2e:.2e}, certified near ties {flips}")
+
+
+def test_one_launch_wait_timeout_reported():
+    """The one-launch step's bounded waits, forced to run out from the host
+    (a bound of one poll): the launch still ends, a layer reports
+    MOE_E_TIMEOUT, and with the default bound the next steps are correct
+    again (the counters were reset by the launch that timed out)."""
+    import sparse_moe_decode_prerouter_amd as moe
+    shape = synth.TINY
+    L, B = 3, 2
+    ora, gpus, stack = build(shape, L, "stackTO", one=True)
+    xs = np.stack([synth.activations(shape, B, ("stkTO", t), dtype=torch.float32).double().numpy()
+                   for t in range(4)])
+    timeouts = 0
+    for attempt in range(3):
+        stack.set_wait_limit(1)
+        run_gpu(stack, L, xs[:2], shape.k, trace=False)
+        st = [Lr.status() for Lr in gpus]
+        assert all(c in (moe.MOE_OK, moe.MOE_E_TIMEOUT) for c in st), st
+        timeouts += sum(c == moe.MOE_E_TIMEOUT for c in st)
+        if timeouts:
+            break
+    say(f"  layers reporting a timeout: {timeouts}")
+    assert timeouts > 0
+    stack.set_wait_limit(0)
+    g = run_gpu(stack, L, xs, shape.k)
+    for Lr in gpus:
+        assert Lr.status() == 0
+    flips, worst, e2e = check_steps(ora, g, "f64", what="after timeout")
     say(f"  per-layer max rel-L2 {worst:.2e}, stack {e2e:.2e}, certified near ties {flips}")
 
 
