@@ -63,12 +63,13 @@ struct XThread {
 };
 
 // COH: x of this launch, read from copy xo of the exchange buffer
-template <bool XB, bool COH = false>
-__device__ __forceinline__ void x_issue(const DecAArgs& a, int t, int e0, uint32_t (&w)[8], size_t xo = 0) {
+template <bool XB, bool COH = false, typename AA>
+__device__ __forceinline__ void x_issue(const AA& a, int t, int e0, uint32_t (&w)[8], size_t xo = 0) {
     if constexpr (COH) {
         static_assert(!XB, "in-launch x is fp32");
-        const float* p = (const float*)a.x + xo + (size_t)t * a.d + e0;
-        const u32x4 v0 = ld_vol4(p), v1 = ld_vol4(p + 4);
+        const float* base = (const float*)a.x + xo;
+        const uint32_t el = (uint32_t)(t * a.d + e0);
+        const u32x4 v0 = ld_coh4(base, el), v1 = ld_coh4(base, el + 4);
         w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
         w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
     } else if (XB) {
@@ -88,8 +89,8 @@ __device__ __forceinline__ float x_elem(const uint32_t (&w)[8], int i) {
 }
 
 // All threads of the block: u of one token into LDS (two block barriers).
-template <int D, bool XB>
-__device__ __forceinline__ void u_to_lds(const DecAArgs& a, const XThread& X, ULds<D>& S) {
+template <int D, bool XB, typename AA>
+__device__ __forceinline__ void u_to_lds(const AA& a, const XThread& X, ULds<D>& S) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool mine = tid * 8 < D;
     double inv = 1.0;
@@ -230,9 +231,11 @@ __device__ __forceinline__ void gateup_rows(const GateUpRegs<AP>& R, const ULds<
 
 // ---- the body -------------------------------------------------------------
 // bid: the block's index in K_A's grid. FUSED: x comes from the same launch
-// (see the file comment); wait for it with fs.
-template <int D, bool XB, bool FUSED, int AP = kAPass>
-__device__ __forceinline__ void dec_a_body(const DecAArgs& a, int bid, const FuseSync& fs) {
+// (see the file comment); wait for it with fs. AA: DecAArgs, or the same in
+// the constant address space (a table the kernel only reads: its fields load
+// as scalar loads, and the pointers in it are known to be global).
+template <int D, bool XB, bool FUSED, int AP = kAPass, typename AA = DecAArgs>
+__device__ __forceinline__ void dec_a_body(const AA& a, int bid, const FuseSync& fs) {
     using G = AGeo<D, AP>;
     __shared__ __align__(16) ULds<D> S;
     __shared__ uint32_t sl[kWaves][64];
@@ -347,7 +350,7 @@ __device__ __forceinline__ void dec_a_body(const DecAArgs& a, int bid, const Fus
     if (bid >= a.nb_h + a.nb_head + a.nb_misc) {
         // the previous layer's head top-k, deferred to this launch (its logits
         // were written two launches ago; the prediction is for the next step)
-        const TopkJob& j = a.topk;
+        const auto& j = a.topk;
         topk_rows<kDeferMaxPer>(false, j.logits, j.En, j.kn, n_tok, j.bias, j.mc, j.hc, j.mp, j.hp, nullptr, j.kn,
                                 j.pred_idx, j.pred_w);
         return;

@@ -57,16 +57,17 @@ __device__ __forceinline__ void lora_issue_b(LoraRegs& R, const uint16_t* brow, 
         R.b[c] = *(const u32x4*)(brow + 8 * cc);
     }
 }
+// COH: LoRA A u of this launch (base: the same for the whole wave)
 template <bool COH>
-__device__ __forceinline__ void lora_issue_u(LoraRegs& R, const float* urow, int r) {
+__device__ __forceinline__ void lora_issue_u(LoraRegs& R, const float* base, size_t row_off, int r) {
 #pragma unroll
     for (int c = 0; c < kLoraChunks; ++c) {
         const int cc = 8 * c < r ? c : 0;
         if constexpr (COH) {
-            const float* p = urow + 8 * cc;
-            R.u[2 * c] = u4_as_f4(ld_vol4(p));
-            R.u[2 * c + 1] = u4_as_f4(ld_vol4(p + 4));
+            R.u[2 * c] = u4_as_f4(ld_coh4(base, (uint32_t)(row_off + 8 * cc)));
+            R.u[2 * c + 1] = u4_as_f4(ld_coh4(base, (uint32_t)(row_off + 8 * cc + 4)));
         } else {
+            const float* urow = base + row_off;
             R.u[2 * c] = *(const float4*)(urow + 8 * cc);
             R.u[2 * c + 1] = *(const float4*)(urow + 8 * cc + 4);
         }
@@ -111,13 +112,15 @@ __device__ __forceinline__ void down_issue(DownRegs<NP>& R, const uint8_t* blob,
     }
 }
 
+// the lane's 8 elements of h row `row_off` past `base` (COH: published in
+// this launch; base the same for the whole wave)
 template <bool COH>
-__device__ __forceinline__ void h_issue(float4 (&hv)[2], const float* hrow, int c) {
+__device__ __forceinline__ void h_issue(float4 (&hv)[2], const float* base, size_t row_off, int c) {
     if constexpr (COH) {
-        const float* p = hrow + 8 * c;
-        hv[0] = u4_as_f4(ld_vol4(p));
-        hv[1] = u4_as_f4(ld_vol4(p + 4));
+        hv[0] = u4_as_f4(ld_coh4(base, (uint32_t)(row_off + 8 * c)));
+        hv[1] = u4_as_f4(ld_coh4(base, (uint32_t)(row_off + 8 * c + 4)));
     } else {
+        const float* hrow = base + row_off;
         hv[0] = *(const float4*)(hrow + 8 * c);
         hv[1] = *(const float4*)(hrow + 8 * c + 4);
     }
@@ -139,8 +142,8 @@ __device__ __forceinline__ void down_partial(const DownRegs<NP>& R, const float4
     }
 }
 
-template <int F, bool FUSED, int PB = kPassB>
-__device__ __forceinline__ void dec_b_body(const DecBArgs& a, int bid, const FuseSync& fs) {
+template <int F, bool FUSED, int PB = kPassB, typename BA = DecBArgs>
+__device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync& fs) {
     using G = BGeo<F, PB>;
     constexpr int NPS = PB / kWaves;               // shared-expert passes per wave
     __shared__ float part[(kMaxAssign + kMaxTokB) * G::RB];
@@ -184,7 +187,7 @@ __device__ __forceinline__ void dec_b_body(const DecBArgs& a, int bid, const Fus
     LoraRegs lr;
     if (lora_vec) {
         lora_issue_b(lr, a.lora_b + (size_t)(row0 + er) * a.r, a.r);
-        if constexpr (!FUSED) lora_issue_u<false>(lr, a.au + (size_t)et * a.r, a.r);
+        if constexpr (!FUSED) lora_issue_u<false>(lr, a.au, (size_t)et * a.r, a.r);
     }
     // shared expert: passes [NPS*wave, NPS*wave + NPS), token 0's hidden state
     const uint8_t* sh_blob = has_shared && a.ev.shared ? a.ev.shared : a.ev.base;
@@ -193,7 +196,7 @@ __device__ __forceinline__ void dec_b_body(const DecBArgs& a, int bid, const Fus
     const int sh_tag = *(a.ev.shared_tag ? a.ev.shared_tag : a.err);
     const bool sh_ok = has_shared && a.ev.shared && (!a.ev.shared_tag || sh_tag == a.ev.E);
     float4 shh[2];
-    if constexpr (!FUSED) h_issue<false>(shh, has_shared ? a.hs : a.h, c);
+    if constexpr (!FUSED) h_issue<false>(shh, has_shared ? a.hs : a.h, 0, c);
     // zero the partials: entries of invalid assignments are never written
     for (int i = tid; i < (n_assign + n_tok) * G::RB; i += kThreads) part[i] = 0.f;
     lds_barrier();
@@ -221,7 +224,7 @@ __device__ __forceinline__ void dec_b_body(const DecBArgs& a, int bid, const Fus
         for (int p = p0; p < p1; ++p) {
             float4 hv[2];
             if (p == p0) { hv[0] = h0[0]; hv[1] = h0[1]; }
-            else h_issue<FUSED>(hv, a.h + xo + (size_t)p * F, c);
+            else h_issue<FUSED>(hv, a.h + xo, (size_t)p * F, c);
             float o[PB];
             down_partial<PB>(R, hv, o);
             int pass;
@@ -243,15 +246,15 @@ __device__ __forceinline__ void dec_b_body(const DecBArgs& a, int bid, const Fus
         const int s1 = s0 + kWaves;
         const int q0 = s0 < n_active ? nth_set(W.starts, s0) : 0;
         const int q1 = s1 < n_active ? nth_set(W.starts, s1) : 0;
-        h_issue<FUSED>(h0, a.h + (size_t)q0 * F, c);
-        h_issue<FUSED>(h1, a.h + (size_t)q1 * F, c);
+        h_issue<FUSED>(h0, a.h, (size_t)q0 * F, c);
+        h_issue<FUSED>(h1, a.h, (size_t)q1 * F, c);
     };
     auto shared_compute = [&]() {
         if (has_shared) {
             for (int t = 0; t < n_tok; ++t) {
                 float4 hv[2];
                 if (t == 0) { hv[0] = shh[0]; hv[1] = shh[1]; }
-                else h_issue<FUSED>(hv, a.hs + xo + (size_t)t * F, c);
+                else h_issue<FUSED>(hv, a.hs + xo, (size_t)t * F, c);
                 float o[NPS];
                 down_partial<NPS>(shr, hv, o);
                 int pass;
@@ -271,7 +274,7 @@ __device__ __forceinline__ void dec_b_body(const DecBArgs& a, int bid, const Fus
         };
         auto slot_h = [&](int s, float4 (&hh)[2]) {
             const int q = s < n_active ? nth_set(W.starts, s) : 0;
-            h_issue<true>(hh, a.h + xo + (size_t)q * F, c);
+            h_issue<true>(hh, a.h + xo, (size_t)q * F, c);
         };
         {
             DownRegs<PB> R0;
@@ -281,8 +284,8 @@ __device__ __forceinline__ void dec_b_body(const DecBArgs& a, int bid, const Fus
             fuse_wait(fs, a.err);
             v_sg = a.sgate ? ld_dev(a.sgate + xo + (lane < n_tok ? lane : 0)) : 0.f;
             ep_x = a.fused ? ld_dev(a.x + (size_t)et * d + row0 + er) : 0.f;
-            if (lora_vec) lora_issue_u<true>(lr, a.au + xo + (size_t)et * a.r, a.r);
-            h_issue<true>(shh, (has_shared ? a.hs : a.h) + xo, c);
+            if (lora_vec) lora_issue_u<true>(lr, a.au + xo, (size_t)et * a.r, a.r);
+            h_issue<true>(shh, (has_shared ? a.hs : a.h) + xo, 0, c);
             slot_h(wave, h0);
             shared_compute();
             if (wave < n_active) slot_compute(R0, b0, wave, h0);

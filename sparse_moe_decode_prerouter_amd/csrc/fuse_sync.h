@@ -72,11 +72,16 @@ __device__ __forceinline__ void fuse_stores_done() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// 16 bytes of data published in this launch: a volatile load, which the
-// compiler issues as one 128-bit load with system-scope coherence bits (it
-// is served at the coherent level, like ld_dev, at a quarter of the
-// instructions of four 32-bit ld_dev)
-__device__ __forceinline__ u32x4 ld_vol4(const float* p) { return *(const volatile u32x4*)p; }
+// 16 bytes of data published in this launch, at element `elem` past a
+// base address that is the same for the whole wave: a buffer load with the
+// device-scope cache policy (sc1), which is served at the device-coherent
+// level like ld_dev, one 128-bit load instead of four 32-bit ones, and
+// (unlike a volatile access) not followed by a wait of its own.
+__device__ __forceinline__ u32x4 ld_coh4(const float* base, uint32_t elem) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 0x7fffffff, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)(elem * 4u), 0, 16 /* sc1 */);
+}
 __device__ __forceinline__ float4 u4_as_f4(u32x4 v) {
     return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }

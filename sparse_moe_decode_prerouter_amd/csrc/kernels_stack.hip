@@ -82,30 +82,21 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_stack(StackDecArgs s) {
     const int per_layer = s.nA + s.nB;
     const int total = s.n_layers * per_layer;
     const int rf = blockIdx.x % kStackFlags;
-    // the item's layer arguments, copied to LDS at the item's start (one
-    // load per thread, long before the item's wait ends), so that the body
-    // reads them without a memory round trip after the wait
-    __shared__ __align__(16) StackLayerArgs s_args;
-    constexpr int kArgWords = sizeof(StackLayerArgs) / 4;
-    static_assert(sizeof(StackLayerArgs) % 4 == 0 && kArgWords <= 2 * kThreads, "argument copy");
+    // the per-layer arguments, read as constant memory (the kernel never
+    // writes the table): scalar loads, and pointers known to be global, so
+    // waiting for one load never waits for the others
+    typedef __attribute__((address_space(4))) const StackLayerArgs CLayerArgs;
+    const CLayerArgs* tab = (const CLayerArgs*)s.tab;
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
         const int l = t / per_layer, r = t - l * per_layer;
         const bool role_a = r < s.nA;
-        {
-            const uint32_t* src = (const uint32_t*)(s.tab + l);
-            uint32_t* dst = (uint32_t*)&s_args;
-            const int n0 = role_a ? 0 : (int)(sizeof(DecAArgs) / 4);     // the half the item reads
-            for (int i = n0 + (int)threadIdx.x; i < (role_a ? (int)(sizeof(DecAArgs) / 4) : kArgWords); i += kThreads)
-                dst[i] = src[i];
-            __syncthreads();
-        }
         if (role_a) {
             const FuseSync fs{l > 0 ? m.flag(2 * (l - 1) + 1, rf) : nullptr, epoch, m.abort(), s.spin_limit};
-            dec_a_body<D, false, true, kStackAPass>(s_args.a, r, fs);
+            dec_a_body<D, false, true, kStackAPass>(tab[l].a, r, fs);
             stack_arrive(m, 2 * l, r, s.nA, epoch);
         } else {
             const FuseSync fs{m.flag(2 * l, rf), epoch, m.abort(), s.spin_limit};
-            dec_b_body<F, true, kStackBPass>(s_args.b, r - s.nA, fs);
+            dec_b_body<F, true, kStackBPass>(tab[l].b, r - s.nA, fs);
             stack_arrive(m, 2 * l + 1, r - s.nA, s.nB, epoch);
         }
     }

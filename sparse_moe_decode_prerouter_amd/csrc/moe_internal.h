@@ -383,7 +383,7 @@ struct StackLayerArgs {
 #endif
 constexpr int kStackLine = 32;                 // words per 128-byte line
 #ifndef MOE_XCHG_COPIES
-#define MOE_XCHG_COPIES 16
+#define MOE_XCHG_COPIES 8
 #endif
 constexpr int kXchgCopies = MOE_XCHG_COPIES;   // copies of the activations handed between phases
 constexpr int kStackAPass = 4;                 // the step kernel's gate/up passes per wave (16 h rows a block)
