@@ -435,6 +435,56 @@ def long_prefill(torch, np, moe, synth, shape, ws, reps=3):
     return res
 
 
+def one_launch_decode(torch, np, stack, layers, step, W, K, B, sb, roof_tok_s):
+    """The timed decode steps run as one launch each (layer 0's router, the
+    argument patch and the step kernel): graph-replayed ms per step, and the
+    step kernel's own duration (kernel-timestamp events over 16 eager steps)."""
+    try:
+        stack.set_one_launch(True)
+    except Exception as e:
+        log(f"one-launch step not available: {e}")
+        return None
+    s = torch.cuda.Stream()
+    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm, stream=s):
+        for t in range(1, W):
+            step(t)
+    with torch.cuda.graph(g_timed, stream=s):
+        for t in range(W, W + K):
+            step(t)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_timed.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    st = [Lr.status() for Lr in layers]
+    assert all(v == 0 for v in st), st
+    stack.set_profiling(True)
+    rk, kk = [], []
+    with torch.cuda.stream(s):
+        for t in range(W, W + min(K, 16)):
+            step(t)
+            torch.cuda.current_stream().synchronize()
+            r, m = stack.kernel_ms()
+            rk.append(r)
+            kk.append(m)
+    stack.set_profiling(False)
+    stack.set_one_launch(False)
+    tok_s = B / (ms / 1e3)
+    k_us = float(np.mean(kk)) * 1e3
+    res = {"ms_per_step": round(ms, 4), "tok_s": round(tok_s, 1), "hbm_frac": round(tok_s / roof_tok_s, 4),
+           "step_kernel_us": round(k_us, 2), "router_us": round(float(np.mean(rk)) * 1e3, 2),
+           "step_kernel_GBs": round(sb / (k_us * 1e-6) / 1e9, 1),
+           "timing": "graph-replayed steps (router + argument patch + step kernel); kernel-timestamp events of "
+                     "the step kernel over 16 eager steps"}
+    log(f"decode, one launch per step: {ms * 1e3:.1f} us/step, {tok_s:.0f} tok/s; step kernel {k_us:.1f} us "
+        f"({res['step_kernel_GBs']:.0f} GB/s of weights)")
+    return res
+
+
 def extra_measurements(args, torch, np, moe, synth, shape, ws, layers):
     """The other workloads of the method, each timed on this GPU: batched
     decode with Zipf-popular, sticky routing; streamed decode (experts staged
@@ -608,6 +658,7 @@ def main():
     assert all(v == 0 for v in st), st
     ms_step = ms / K
     tok_s = B * K / (ms / 1e3)
+    per_layer_ms, per_layer_tok_s = ms_step, tok_s
     sb = step_bytes(shape, L, k)
     roof_tok_s = HBM_PEAK_GBS * 1e9 / sb * B
     log(f"decode: {ms_step * 1e3:.1f} us/step, {tok_s:.0f} tok/s, {sb / ms_step / 1e6:.0f} GB/s algorithmic, "
@@ -637,6 +688,13 @@ def main():
     bb_ = kernel_b_bytes(shape, k)
     log(f"K_A avg {a_avg * 1e3:.2f} us ({ab / (a_avg * 1e-3) / 1e9:.0f} GB/s), K_B avg {b_avg * 1e3:.2f} us "
         f"({bb_ / (b_avg * 1e-3) / 1e9:.0f} GB/s), router avg {np.mean(r_ms) * 1e3 if r_ms else -1:.2f} us")
+
+    # ---- the same steps as one launch each (moe_stack_set_one_launch): graph-replayed
+    # step time, and the step kernel's own duration from kernel-timestamp events
+    one = one_launch_decode(torch, np, stack, layers, step, W, K, B, sb, roof_tok_s)
+    mode = "per_layer"
+    if one is not None and one["tok_s"] > tok_s:
+        mode, tok_s, ms_step = "one_launch", one["tok_s"], one["ms_per_step"]
 
     # ---- prefill
     prefill = None if args.no_prefill else stack_prefill_timing(torch, np, shape, stack, layers, T, k)
@@ -707,7 +765,8 @@ def main():
         "data": "synthetic: seeded N(0,0.02) weights quantised to int4 g64, N(0,1) step inputs",
         "config": {"workload": f"{L}-layer MoE-only stack, batch-{B} decode", "layers": L, "batch": B,
                    "hidden": shape.d, "experts": shape.E, "top_k": k, "expert_intermediate": shape.f,
-                   "shared_intermediate": shape.fs, "lora_rank": shape.r, "experts_resident": True},
+                   "shared_intermediate": shape.fs, "lora_rank": shape.r, "experts_resident": True,
+                   "decode_launches": mode},
         "hbm_roofline_frac": round(tok_s / roof_tok_s, 4),
         "hbm_roofline_tok_s": round(roof_tok_s, 1),
         "bytes_per_step": sb,
@@ -719,6 +778,8 @@ def main():
                      "bytes_per_launch": ab, "avg_launch_us": round(a_avg * 1e3, 3)},
         "kernel_b": {"kernel": "k_dec_b", "avg_launch_us": round(b_avg * 1e3, 3), "bytes_per_launch": bb_,
                      "achieved_GBs": round(bb_ / (b_avg * 1e-3) / 1e9, 1)},
+        "decode_per_layer_launches": {"ms_per_step": round(per_layer_ms, 4), "tok_s": round(per_layer_tok_s, 1)},
+        "decode_one_launch": one,
         "prefill": prefill,
         "other_workloads": extra,
         "cpu_baseline": cpu,
