@@ -173,13 +173,18 @@ __device__ __forceinline__ float chunk_dot(u32x4 w, const u32x4 (&up)[4], float 
     // opaque copy: keeps the nibble unpacking after u is ready instead of
     // hoisted out of the position loop, where it would wait for the weights
     asm volatile("" : "+v"(w));
+    // the mask and exponent in registers the compiler cannot see through: each
+    // (128 + q) pair is then one v_and_or_b32 (after the shift) instead of an
+    // AND and an OR with literal operands
+    uint32_t nm = 0x000F000Fu, nc = 0x43004300u;
+    asm volatile("" : "+v"(nm), "+v"(nc));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        acc = dot2_bf16(nib_pair_bf16(ws[i], 0), up[i].x, acc);
-        acc = dot2_bf16(nib_pair_bf16(ws[i], 1), up[i].y, acc);
-        acc = dot2_bf16(nib_pair_bf16(ws[i], 2), up[i].z, acc);
-        acc = dot2_bf16(nib_pair_bf16(ws[i], 3), up[i].w, acc);
+        acc = dot2_bf16((ws[i] & nm) | nc, up[i].x, acc);
+        acc = dot2_bf16(((ws[i] >> 4) & nm) | nc, up[i].y, acc);
+        acc = dot2_bf16(((ws[i] >> 8) & nm) | nc, up[i].z, acc);
+        acc = dot2_bf16(((ws[i] >> 12) & nm) | nc, up[i].w, acc);
     }
     return acc;
 }

@@ -133,11 +133,20 @@ __device__ __forceinline__ void down_partial(const DownRegs<NP>& R, const float4
     float hs = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) hs += h[j];
+    // codes split into even and odd nibbles, one per byte (a mask held in a
+    // register the compiler cannot see through, so it is not re-materialised
+    // per use): each code then converts with one v_cvt_f32_ubyte
+    uint32_t m0f = 0x0F0F0F0Fu;
+    asm volatile("" : "+v"(m0f));
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
+        const uint32_t ev = R.q[i] & m0f, od = (R.q[i] >> 4) & m0f;
         float acc = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc += (float)((R.q[i] >> (4 * j)) & 0xFu) * h[j];
+        for (int b = 0; b < 4; ++b) {
+            acc += (float)((ev >> (8 * b)) & 0xFFu) * h[2 * b];
+            acc += (float)((od >> (8 * b)) & 0xFFu) * h[2 * b + 1];
+        }
         o[i] = f16_to_f32(R.sb[i] & 0xFFFF) * acc + f16_to_f32(R.sb[i] >> 16) * hs;
     }
 }
