@@ -57,6 +57,8 @@ def kernel_b_bytes(shape, k):
 
 
 KA_SOURCES = ("sparse_moe_decode_prerouter_amd/csrc/kernels_deca.hip",
+              "sparse_moe_decode_prerouter_amd/csrc/dec_a_body.h",
+              "sparse_moe_decode_prerouter_amd/csrc/fuse_sync.h",
               "sparse_moe_decode_prerouter_amd/csrc/dec_common.h",
               "sparse_moe_decode_prerouter_amd/csrc/device_common.h",
               "sparse_moe_decode_prerouter_amd/csrc/moe_internal.h",
@@ -435,10 +437,11 @@ def long_prefill(torch, np, moe, synth, shape, ws, reps=3):
     return res
 
 
-def one_launch_decode(torch, np, stack, layers, step, W, K, B, sb, roof_tok_s):
+def one_launch_decode(torch, np, stack, layers, step, W, K, B, kernel_bytes, roof_tok_s):
     """The timed decode steps run as one launch each (layer 0's router, the
     argument patch and the step kernel): graph-replayed ms per step, and the
-    step kernel's own duration (kernel-timestamp events over 16 eager steps)."""
+    step kernel's own duration (kernel-timestamp events over 16 eager steps)
+    against its algorithmic bytes (every layer's K_A and K_B bytes)."""
     try:
         stack.set_one_launch(True)
     except Exception as e:
@@ -477,7 +480,9 @@ def one_launch_decode(torch, np, stack, layers, step, W, K, B, sb, roof_tok_s):
     k_us = float(np.mean(kk)) * 1e3
     res = {"ms_per_step": round(ms, 4), "tok_s": round(tok_s, 1), "hbm_frac": round(tok_s / roof_tok_s, 4),
            "step_kernel_us": round(k_us, 2), "router_us": round(float(np.mean(rk)) * 1e3, 2),
-           "step_kernel_GBs": round(sb / (k_us * 1e-6) / 1e9, 1),
+           "step_kernel_bytes": kernel_bytes,
+           "step_kernel_GBs": round(kernel_bytes / (k_us * 1e-6) / 1e9, 1),
+           "step_kernel_hbm_frac": round(kernel_bytes / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
            "timing": "graph-replayed steps (router + argument patch + step kernel); kernel-timestamp events of "
                      "the step kernel over 16 eager steps"}
     log(f"decode, one launch per step: {ms * 1e3:.1f} us/step, {tok_s:.0f} tok/s; step kernel {k_us:.1f} us "
@@ -691,7 +696,8 @@ def main():
 
     # ---- the same steps as one launch each (moe_stack_set_one_launch): graph-replayed
     # step time, and the step kernel's own duration from kernel-timestamp events
-    one = one_launch_decode(torch, np, stack, layers, step, W, K, B, sb, roof_tok_s)
+    one = one_launch_decode(torch, np, stack, layers, step, W, K, B, step_bytes(shape, L, k, with_router_l0=False),
+                            roof_tok_s)
     mode = "per_layer"
     if one is not None and one["tok_s"] > tok_s:
         mode, tok_s, ms_step = "one_launch", one["tok_s"], one["ms_per_step"]

@@ -248,8 +248,10 @@ __device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync&
         const int s1 = s0 + kWaves;
         b0 = blob_of(s0);
         b1 = blob_of(s1);
+        // (a slot past the active experts loads the first slot's rows again,
+        // which the L2 already holds, instead of rows of some other blob)
         down_issue<F, PB, G::RPP>(R0, b0 ? b0 : a.ev.base, L, row0 + rsub);
-        down_issue<F, PB, G::RPP>(R1, b1 ? b1 : a.ev.base, L, row0 + rsub);
+        down_issue<F, PB, G::RPP>(R1, b1 ? b1 : (b0 ? b0 : a.ev.base), L, row0 + rsub);
     };
     auto hs_issue = [&](int s0, float4 (&h0)[2], float4 (&h1)[2]) {
         const int s1 = s0 + kWaves;
