@@ -160,6 +160,42 @@ def test_stack_tiny_shape_free_running(one):
     say(f"  per-layer max rel-L2 {worst:.2e}, stack {e2e:.2e}, certified near ties {flips}")
 
 
+@pytest.mark.parametrize("B", [8, 16])
+def test_stack_one_launch_largest_batches(B):
+    """The one-launch step at the largest batches it takes (n_tok * k up to 64
+    assignments at k = 4), free-running, every layer checked on its input."""
+    shape = synth.LAYER35B
+    L, steps = 3, 3
+    say(f"stack one-launch L={L} B={B} steps={steps}")
+    ora, gpus, stack = build(shape, L, f"stackOB{B}", max_tokens=B, one=True)
+    xs = np.stack([synth.activations(shape, B, ("stkOB", B, t), dtype=torch.float32).double().numpy()
+                   for t in range(steps)])
+    g = run_gpu(stack, L, xs, shape.k)
+    for L_ in gpus:
+        assert L_.status() == 0
+    flips, worst, e2e = check_steps(ora, g, "f64", what=f"one-launch B={B}")
+    say(f"  per-layer max rel-L2 {worst:.2e}, stack {e2e:.2e}, certified near ties {flips}")
+    assert one_launch_ran(stack, L, B, shape), "the step did not take the one-launch path"
+
+
+def one_launch_ran(stack, L, B, shape):
+    """Two more steps with kernel timestamps on: the second (not a first step)
+    must have launched the step kernel."""
+    dev = "cuda"
+    k = shape.k
+    pidx = [torch.full((L, B, k), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+    pw = [torch.zeros((L, B, k), dtype=torch.float32, device=dev) for _ in range(2)]
+    x = synth.activations(shape, B, ("stkOBx",), dtype=torch.float32).to(dev).contiguous()
+    xo = torch.empty_like(x)
+    stack.set_profiling(True)
+    stack.decode(x, pidx[0], pw[0], pidx[1], pw[1], x_out=xo, first_step=True)
+    stack.decode(x, pidx[1], pw[1], pidx[0], pw[0], x_out=xo)
+    torch.cuda.synchronize()
+    _, ms = stack.kernel_ms()
+    stack.set_profiling(False)
+    return ms > 0
+
+
 def test_one_launch_wait_timeout_reported():
     """The one-launch step's bounded waits, forced to run out from the host
     (a bound of one poll): the launch still ends, a layer reports
