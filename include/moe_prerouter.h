@@ -357,10 +357,11 @@ void moe_layer_destroy(moe_layer* layer);
  *   checking each layer on the input it saw); calls whose trace would not
  *   fit return MOE_E_CAPACITY. NULL / 0 turns the trace off.
  * moe_stack_set_one_launch: enable != 0 runs each later decode step that
- *   qualifies as three launches in all (layer 0's router, a one-block patch
- *   of the per-layer argument table, and one step kernel in which every
- *   layer's K_A and K_B run as work items, each issuing its weight rows
- *   before it waits, on device-scope counters, for its activations; the
+ *   qualifies as three launches in all (layer 0's router, a patch of the
+ *   per-layer argument table that also marks every exchange word the step
+ *   will publish as empty, and one step kernel in which every layer's K_A
+ *   and K_B run as work items, each issuing its weight rows before it
+ *   reads, until they have been published, the activations it needs; the
  *   addresses are known before the step starts because each layer's routing
  *   is the previous token's prediction: guide, Q&A on why one token ahead).
  *   A step qualifies when it is not the first step, staging is
@@ -369,10 +370,11 @@ void moe_layer_destroy(moe_layer* layer);
  *   is resident, the layers share d, d_ff, the shared width, k, E, the LoRA
  *   rank (0, 8 or 16) and the presence of the shared gate, heads have at
  *   most 256 outputs, and no layer has the head's MLP branch or the shared
- *   expert's adapter. The waits are bounded: a lost arrival sets
- *   MOE_E_TIMEOUT in the layer's status (moe_layer_sync_status) instead of
- *   hanging. Calls on one stack must not overlap (the table and counters
- *   are per stack). Default: off.
+ *   expert's adapter. The activations must be finite (a value whose bits
+ *   are all ones reads as not yet published). The waits are bounded: a
+ *   value that never arrives sets MOE_E_TIMEOUT in the layer's status
+ *   (moe_layer_sync_status) instead of hanging. Calls on one stack must not
+ *   overlap (the table and exchange buffers are per stack). Default: off.
  * moe_stack_set_wait_limit: the bound of each of those waits, in polls of
  *   about a microsecond each (0: the default, 2^18). A wait that runs out
  *   sets MOE_E_TIMEOUT and lets every later wait of the launch give up at

@@ -3,8 +3,8 @@
 // LoRA A u + shared-expert gate. Shared by the standalone launch and by the
 // one-launch-per-step stack decode kernel, where x is produced inside the same
 // launch (by the previous layer's K_B blocks): there the block issues every
-// load that does not depend on x, waits for the previous layer (fuse_wait),
-// then reads x with device-scope loads and publishes its outputs with
+// load that does not depend on x, then reads x with device-scope loads until
+// every word has arrived (fuse_poll), and publishes its outputs with
 // device-scope stores.
 //
 // A block (4 waves) computes the block input u of a token once: thread g
@@ -81,6 +81,21 @@ __device__ __forceinline__ void x_issue(const AA& a, int t, int e0, uint32_t (&w
         w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
         w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
     }
+}
+
+// (one-launch step) x of token t, read until every word of this lane's
+// elements has been published (a plain read when fs is off: layer 0's x is
+// the caller's)
+template <bool XB, typename AA>
+__device__ __forceinline__ void x_poll(const AA& a, int t, int e0, uint32_t (&w)[8], size_t xo, const FuseSync& fs) {
+    const float* probe = (const float*)a.x + xo + (size_t)t * a.d + __builtin_amdgcn_readfirstlane(e0);
+    fuse_poll(fs, a.err, probe, [&]() {
+        x_issue<XB, true>(a, t, e0, w, xo);
+        bool empty = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) empty |= w[i] == kEmptyWord;
+        return !empty;
+    });
 }
 
 template <bool XB>
@@ -335,15 +350,18 @@ __device__ __forceinline__ void dec_a_body(const AA& a, int bid, const FuseSync&
             if (!ok && blob && bid == 0 && tid == 0) set_err(a.err, ERR_NOT_STAGED);
         }
         if constexpr (FUSED) {
-            fuse_wait(fs, a.err);
             const int t0 = shared ? p0 : (int)(__builtin_amdgcn_readlane((int)(W.sk & 0xFFFF), p0)) / k;
-            x_issue<XB, true>(a, t0, e0, X.w, xo_x);
+            x_poll<XB>(a, t0, e0, X.w, xo_x, fs);
         }
         // ---- level 2: per position, u of its token (whole block), then the rows
         int t_loaded = FUSED ? (shared ? p0 : (int)(__builtin_amdgcn_readlane((int)(W.sk & 0xFFFF), p0)) / k) : 0;
         for (int p = p0; p < p1; ++p) {
             const int t = shared ? p : (int)(__builtin_amdgcn_readlane((int)(W.sk & 0xFFFF), p)) / k;
-            if (t != t_loaded) { x_issue<XB, FUSED>(a, t, e0, X.w, xo_x); t_loaded = t; }
+            if (t != t_loaded) {
+                if constexpr (FUSED) x_poll<XB>(a, t, e0, X.w, xo_x, fs);
+                else x_issue<XB>(a, t, e0, X.w);
+                t_loaded = t;
+            }
             u_to_lds<D, XB>(a, X, S);
             float* h_out = shared ? a.hs + (size_t)t * f : a.h + (size_t)p * f;
             gateup_rows<D, FUSED, AP>(R, S, with_lo, ok, h_out, row0, a.xstride, ncopy);
@@ -373,12 +391,12 @@ __device__ __forceinline__ void dec_a_body(const AA& a, int bid, const FuseSync&
     u32x4 wb[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wb[q] = __builtin_nontemporal_load((const u32x4*)(wrow + 32 * c) + q);
-    if constexpr (FUSED) {
-        fuse_wait(fs, a.err);
-        x_issue<XB, true>(a, 0, e0, X.w, xo_x);
-    }
+    if constexpr (FUSED) x_poll<XB>(a, 0, e0, X.w, xo_x, fs);
     for (int t = 0; t < n_tok; ++t) {
-        if (t > 0) x_issue<XB, FUSED>(a, t, e0, X.w, xo_x);
+        if (t > 0) {
+            if constexpr (FUSED) x_poll<XB>(a, t, e0, X.w, xo_x, fs);
+            else x_issue<XB>(a, t, e0, X.w);
+        }
         u_to_lds<D, XB>(a, X, S);
         double acc = 0.0;
 #pragma unroll

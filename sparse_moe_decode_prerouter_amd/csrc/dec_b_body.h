@@ -20,10 +20,10 @@
 //
 // FUSED (the one-launch stack decode): the values produced in the same
 // launch (K_A's h, shared h, shared gate, LoRA A u and head logits; the
-// residual rows x, written by the previous layer) are read only after the
-// block has seen every K_A block of its layer arrive (fuse_wait), with
-// device-scope loads, and y is published with device-scope stores;
-// everything else, weights included, is issued before the wait.
+// residual rows x, written by the previous layer) are read with device-scope
+// loads until every word a wave needs has been published (fuse_poll), and y
+// is published with device-scope stores; everything else, weights included,
+// is issued before the first poll.
 #pragma once
 #include "dec_common.h"
 #include "fuse_sync.h"
@@ -126,6 +126,15 @@ __device__ __forceinline__ void h_issue(float4 (&hv)[2], const float* base, size
     }
 }
 
+// (one-launch step) h_issue<true>, read until its 8 words have been published
+__device__ __forceinline__ void h_poll(float4 (&hv)[2], const float* base, size_t row_off, int c, const FuseSync& fs,
+                                       int32_t* err) {
+    fuse_poll(fs, err, nullptr, [&]() {
+        h_issue<true>(hv, base, row_off, c);
+        return !(any_empty(hv[0]) | any_empty(hv[1]));
+    });
+}
+
 // Per-lane partial of each pass: sum_j (s q_j + b) h_j over the lane's 8 elements.
 template <int NP>
 __device__ __forceinline__ void down_partial(const DownRegs<NP>& R, const float4 (&hv)[2], float (&o)[NP]) {
@@ -160,7 +169,16 @@ __device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync&
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (bid == 0) {
-        if constexpr (FUSED) fuse_wait(fs, a.err);
+        if constexpr (FUSED) {
+            // this wave's logit rows (those topk_rows gives it), until published
+            if (a.pred_idx)
+                for (int t = wave; t < a.n_tok; t += kWaves)
+                    fuse_poll(fs, a.err, nullptr, [&]() {
+                        bool empty = false;
+                        for (int e = lane; e < a.En; e += 64) empty |= empty_word(ld_dev(a.logits_h + (size_t)t * a.En + e));
+                        return !empty;
+                    });
+        }
         // (the one-launch kernel takes heads of up to 256 experts: smaller
         // register arrays, which keep its register budget)
         if (a.pred_idx)
@@ -233,7 +251,8 @@ __device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync&
         for (int p = p0; p < p1; ++p) {
             float4 hv[2];
             if (p == p0) { hv[0] = h0[0]; hv[1] = h0[1]; }
-            else h_issue<FUSED>(hv, a.h + xo, (size_t)p * F, c);
+            else if constexpr (FUSED) h_poll(hv, a.h + xo, (size_t)p * F, c, fs, a.err);
+            else h_issue<false>(hv, a.h, (size_t)p * F, c);
             float o[PB];
             down_partial<PB>(R, hv, o);
             int pass;
@@ -265,7 +284,8 @@ __device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync&
             for (int t = 0; t < n_tok; ++t) {
                 float4 hv[2];
                 if (t == 0) { hv[0] = shh[0]; hv[1] = shh[1]; }
-                else h_issue<FUSED>(hv, a.hs + xo, (size_t)t * F, c);
+                else if constexpr (FUSED) h_poll(hv, a.hs + xo, (size_t)t * F, c, fs, a.err);
+                else h_issue<false>(hv, a.hs, (size_t)t * F, c);
                 float o[NPS];
                 down_partial<NPS>(shr, hv, o);
                 int pass;
@@ -283,30 +303,53 @@ __device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync&
             bb = blob_of(s);
             down_issue<F, PB, G::RPP>(R, bb ? bb : a.ev.base, L, row0 + rsub);
         };
-        auto slot_h = [&](int s, float4 (&hh)[2]) {
-            const int q = s < n_active ? nth_set(W.starts, s) : 0;
-            h_issue<true>(hh, a.h + xo, (size_t)q * F, c);
-        };
         {
             DownRegs<PB> R0;
-            float4 h0[2];
+            float4 h0[2] = {};
             const uint8_t* b0;
             slot_issue(wave, R0, b0);
-            fuse_wait(fs, a.err);
-            v_sg = a.sgate ? ld_dev(a.sgate + xo + (lane < n_tok ? lane : 0)) : 0.f;
-            ep_x = a.fused ? ld_dev(a.x + (size_t)et * d + row0 + er) : 0.f;
-            if (lora_vec) lora_issue_u<true>(lr, a.au + xo, (size_t)et * a.r, a.r);
-            h_issue<true>(shh, (has_shared ? a.hs : a.h) + xo, 0, c);
-            slot_h(wave, h0);
+            // every value of this launch the wave reads before its first
+            // slot: the shared gate, the residual rows (published by the
+            // previous layer, or the caller's x at layer 0), LoRA A u, the
+            // shared expert's h and the first slot's h; the probe is the
+            // first slot's h (else the shared h, else nothing)
+            const bool h0_on = wave < n_active;
+            const int q0 = h0_on ? nth_set(W.starts, wave) : 0;
+            const float* probe = h0_on ? a.h + xo + (size_t)q0 * F : (has_shared ? a.hs + xo : nullptr);
+            fuse_poll(fs, a.err, probe, [&]() {
+                bool empty = false;
+                if (a.sgate) {
+                    v_sg = ld_dev(a.sgate + xo + (lane < n_tok ? lane : 0));
+                    empty |= empty_word(v_sg);
+                }
+                if (a.fused) {
+                    ep_x = ld_dev(a.x + (size_t)et * d + row0 + er);
+                    empty |= a.x_repl && empty_word(ep_x);
+                }
+                if (lora_vec) {
+                    lora_issue_u<true>(lr, a.au + xo, (size_t)et * a.r, a.r);
+#pragma unroll
+                    for (int q = 0; q < 2 * kLoraChunks; ++q) empty |= any_empty(lr.u[q]);
+                }
+                if (has_shared) {
+                    h_issue<true>(shh, a.hs + xo, 0, c);
+                    empty |= any_empty(shh[0]) | any_empty(shh[1]);
+                }
+                if (h0_on) {
+                    h_issue<true>(h0, a.h + xo, (size_t)q0 * F, c);
+                    empty |= any_empty(h0[0]) | any_empty(h0[1]);
+                }
+                return !empty;
+            });
             shared_compute();
-            if (wave < n_active) slot_compute(R0, b0, wave, h0);
+            if (h0_on) slot_compute(R0, b0, wave, h0);
         }
         for (int s0 = wave + kWaves; s0 < n_active; s0 += kWaves) {
             DownRegs<PB> R0;
             float4 h0[2];
             const uint8_t* b0;
             slot_issue(s0, R0, b0);
-            slot_h(s0, h0);
+            h_poll(h0, a.h + xo, (size_t)nth_set(W.starts, s0) * F, c, fs, a.err);
             slot_compute(R0, b0, s0, h0);
         }
     } else {

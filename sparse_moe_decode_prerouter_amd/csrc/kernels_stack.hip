@@ -8,22 +8,17 @@
 // t is layer t / P, and K_A block (t % P) of it or K_B block (t % P - nA),
 // with P = nA + nB. The grid is launched cooperatively (all its blocks are
 // resident at once) and block b runs items b, b + G, b + 2G, ... in order.
-// An item waits only for items with lower numbers (K_A of layer l for every
-// K_B item of layer l - 1, K_B of layer l for every K_A item of layer l):
-// the smallest unfinished item's block has finished all its earlier items,
-// so it is running that item, whose inputs are complete; every wait ends.
+// An item waits only for values published by items with lower numbers (K_A
+// of layer l for x, from K_B of layer l - 1; K_B of layer l for h, the
+// shared gate, LoRA A u and the head logits, from K_A of layer l): the
+// smallest unfinished item's block has finished all its earlier items, so
+// it is running that item, whose inputs are complete; every wait ends.
 //
-// Phase completion (a phase is the K_A or the K_B items of one layer) is
-// counted in two levels so that no memory word is hit by more than a few
-// dozen atomics per phase (same-word device-scope atomics serialise):
-// item i adds one to sub-counter i % kSub; the item that completes a
-// sub-counter adds one to the phase's top counter; the one that completes
-// the top counter writes the launch's epoch into kFlags copies of the
-// phase's flag, and a waiting block polls copy (block % kFlags), so at most
-// a few blocks poll any one word. Counters, flags and the epoch sit on
-// separate 128-byte lines. The patch kernel that runs before each launch
-// zeroes the counters and the abort word and advances the epoch (flags are
-// never cleared: a flag is current when it holds this launch's epoch).
+// The values carry their own readiness (the hand-off is described with
+// fuse_poll): the patch kernel that runs before each launch sets every
+// exchange word the launch will publish to the empty word and clears the
+// abort word; producers store, consumers read until no word is empty. There
+// are no arrival counters and no flags.
 //
 // The per-layer arguments live in a device table: the pointers fixed when
 // the stack is created are written once, and the patch kernel writes the
@@ -38,50 +33,11 @@
 
 namespace moe {
 
-static_assert(kStackFlags <= 64 && kStackSub >= 1, "flags are written by one wave");
-
-struct SyncMap {
-    uint32_t* base;
-    int n_layers;
-    __host__ __device__ uint32_t* line(size_t i) const { return base + i * kStackLine; }
-    __host__ __device__ uint32_t* epoch() const { return line(0); }
-    __host__ __device__ uint32_t* abort() const { return line(0) + 1; }
-    __host__ __device__ uint32_t* sub(int p, int j) const { return line(1 + (size_t)p * kStackSub + j); }
-    __host__ __device__ uint32_t* top(int p) const { return line(1 + (size_t)2 * n_layers * kStackSub + p); }
-    __host__ __device__ uint32_t* flag(int p, int r) const {
-        return line(1 + (size_t)2 * n_layers * (kStackSub + 1) + (size_t)p * kStackFlags + r);
-    }
-};
-
-// every thread of the block, after the item's last store: item i of phase p
-// (n_items items) has arrived
-__device__ __forceinline__ void stack_arrive(const SyncMap& m, int p, int i, int n_items, uint32_t epoch) {
-    fuse_stores_done();
-    if (threadIdx.x < 64) {
-        int complete = 0;
-        if (threadIdx.x == 0) {
-            const int j = i % kStackSub;
-            const int nsubs = n_items < kStackSub ? n_items : kStackSub;
-            const uint32_t cnt = (uint32_t)((n_items - j + kStackSub - 1) / kStackSub);
-            const uint32_t old = __hip_atomic_fetch_add(m.sub(p, j), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (old + 1 == cnt) {
-                const uint32_t o2 = __hip_atomic_fetch_add(m.top(p), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                complete = o2 + 1 == (uint32_t)nsubs;
-            }
-        }
-        complete = __shfl(complete, 0, 64);
-        if (complete && (int)threadIdx.x < kStackFlags)
-            __hip_atomic_store(m.flag(p, threadIdx.x), epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
 template <int D, int F>
 __global__ void __launch_bounds__(kThreads, 2) k_dec_stack(StackDecArgs s) {
-    const SyncMap m{s.sync, s.n_layers};
-    const uint32_t epoch = __builtin_amdgcn_readfirstlane(ld_dev(m.epoch()));
+    uint32_t* abort = s.sync;
     const int per_layer = s.nA + s.nB;
     const int total = s.n_layers * per_layer;
-    const int rf = blockIdx.x % kStackFlags;
     // the per-layer arguments, read as constant memory (the kernel never
     // writes the table): scalar loads, and pointers known to be global, so
     // waiting for one load never waits for the others
@@ -89,31 +45,41 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_stack(StackDecArgs s) {
     const CLayerArgs* tab = (const CLayerArgs*)s.tab;
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
         const int l = t / per_layer, r = t - l * per_layer;
-        const bool role_a = r < s.nA;
-        if (role_a) {
-            const FuseSync fs{l > 0 ? m.flag(2 * (l - 1) + 1, rf) : nullptr, epoch, m.abort(), s.spin_limit};
+        if (r < s.nA) {
+            // layer 0 reads the caller's x
+            const FuseSync fs{l > 0, abort, s.spin_limit};
             dec_a_body<D, false, true, kStackAPass>(tab[l].a, r, fs);
-            stack_arrive(m, 2 * l, r, s.nA, epoch);
         } else {
-            const FuseSync fs{m.flag(2 * l, rf), epoch, m.abort(), s.spin_limit};
+            const FuseSync fs{true, abort, s.spin_limit};
             dec_b_body<F, true, kStackBPass>(tab[l].b, r - s.nA, fs);
-            stack_arrive(m, 2 * l + 1, r - s.nA, s.nB, epoch);
         }
     }
 }
 
-// per-call fields of every layer's arguments
+// Before each launch: the per-call fields of every layer's arguments, the
+// abort word, and the empty word in every exchange word the launch will
+// publish. Block u takes (layer u / (C + 1), copy u % (C + 1)) of the
+// exchange (C copies per layer; copy C stands for the layer's head logits).
 __global__ void k_stack_patch(StackPatchArgs p) {
-    const SyncMap m{p.sync, p.n_layers};
-    if (blockIdx.x == 0) {
-        // the step kernel's counters (sub and top lines of every phase) and abort word
-        const int n_ctr = 2 * p.n_layers * (kStackSub + 1);
-        for (int i = threadIdx.x; i < n_ctr; i += blockDim.x) *m.line(1 + (size_t)i) = 0u;
-        if (threadIdx.x == 0) {
-            *m.abort() = 0u;
-            *m.epoch() = *m.epoch() + 1u;
+    const u32x4 e4 = {kEmptyWord, kEmptyWord, kEmptyWord, kEmptyWord};
+    for (int u = blockIdx.x; u < p.n_layers * (kXchgCopies + 1); u += gridDim.x) {
+        const int l = u / (kXchgCopies + 1), c = u % (kXchgCopies + 1);
+        if (c < kXchgCopies) {
+            float* base = p.xchg + ((size_t)l * kXchgCopies + c) * p.xstride;
+            // parts start 64 floats apart at least and are padded to it, so a
+            // length rounded up to 4 floats stays inside its part
+            for (int i = 0; i < kXchgParts; ++i) {
+                const uint32_t len = ((uint32_t)p.n_tok * p.xw[i] + 3u) & ~3u;
+                for (uint32_t j = 4u * threadIdx.x; j < len; j += 4u * blockDim.x) st_coh4(base + p.xoff[i], j, e4);
+            }
+        } else {
+            double* lg = p.tab[l].a.logits_h;
+            const int n = lg ? p.n_tok * p.tab[l].b.En : 0;
+            for (int j = threadIdx.x; j < n; j += blockDim.x)
+                __hip_atomic_store(lg + j, __longlong_as_double(-1ll), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *p.sync = 0u;     // the abort word
     const int l = blockIdx.x * blockDim.x + threadIdx.x;
     if (l >= p.n_layers) return;
     StackLayerArgs& L = p.tab[l];
@@ -174,7 +140,8 @@ int stack_one_launch_blocks_per_cu(int d, int f) {
 
 hipError_t launch_stack_one(const StackPatchArgs& p, const StackDecArgs& s, int grid, hipStream_t st,
                             const KTime* tm) {
-    hipLaunchKernelGGL(k_stack_patch, dim3((p.n_layers + 255) / 256), dim3(256), 0, st, p);
+    const int pgrid = std::max(p.n_layers * (kXchgCopies + 1), (p.n_layers + 255) / 256);
+    hipLaunchKernelGGL(k_stack_patch, dim3(pgrid), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const void* fn = nullptr;

@@ -1052,7 +1052,7 @@ static int stack_one_launch_init(moe_stack* S) {
         if (b.sgate) b.sgate = a.sgate;
         a.xstride = b.xstride = S->xchg_stride;
         a.xcopies = b.xcopies = kXchgCopies;
-        a.x_repl = l > 0;
+        a.x_repl = b.x_repl = l > 0;
         if (l > 0) { a.x = reg + S->xchg_off[0]; b.x = reg + S->xchg_off[0]; }
         b.xnext = l + 1 < n ? S->d_xchg + (size_t)(l + 1) * kXchgCopies * S->xchg_stride + S->xchg_off[0] : nullptr;
     }
@@ -1103,6 +1103,11 @@ static int stack_decode_one(moe_stack* S, const float* x_in, float* x_out, int n
     p.route_idx = route_idx; p.route_w = route_w; p.pred_idx = pred_idx; p.pred_w = pred_w;
     p.used_idx = used_idx; p.used_w = used_w; p.hist_prev = hist_prev;
     p.trace = S->x_trace;
+    p.xchg = S->d_xchg;
+    p.xstride = S->xchg_stride;
+    const uint32_t xw[kXchgParts] = {(uint32_t)D.d_model, (uint32_t)(D.top_k * D.d_ff), (uint32_t)fs_main(L0),
+                                     (uint32_t)D.lora_rank, 1u};
+    for (int i = 0; i < kXchgParts; ++i) { p.xoff[i] = (uint32_t)S->xchg_off[i]; p.xw[i] = xw[i]; }
     StackDecArgs sd{};
     sd.tab = S->d_tab; sd.n_layers = S->n;
     sd.nA = p.nb_h + a.nb_head + a.nb_misc;

@@ -363,6 +363,7 @@ struct DecBArgs {
     float* y_copy;         // one-launch stack decode: a second copy of y (the layer trace), or nullptr
     float* xnext;          // one-launch stack decode: the next layer's x exchange copies (or nullptr)
     size_t xstride; int xcopies;
+    int x_repl;            // x is the previous layer's exchange copy (else the caller's x)
     // head top-k (extra block)
     const double* logits_h; int En; int kn; const float* head_bias; const float* hist_cur_m; const float* hist_prev_m;
     const int32_t* hist_cur; const int32_t* hist_prev; int32_t* pred_idx; float* pred_w;
@@ -375,12 +376,6 @@ struct StackLayerArgs {
     DecAArgs a;
     DecBArgs b;
 };
-#ifndef MOE_STACK_SUB
-#define MOE_STACK_SUB 16
-#endif
-#ifndef MOE_STACK_FLAGS
-#define MOE_STACK_FLAGS 64
-#endif
 constexpr int kStackLine = 32;                 // words per 128-byte line
 #ifndef MOE_XCHG_COPIES
 #define MOE_XCHG_COPIES 8
@@ -388,16 +383,12 @@ constexpr int kStackLine = 32;                 // words per 128-byte line
 constexpr int kXchgCopies = MOE_XCHG_COPIES;   // copies of the activations handed between phases
 constexpr int kStackAPass = 4;                 // the step kernel's gate/up passes per wave (16 h rows a block)
 constexpr int kStackBPass = 8;                 // the step kernel's down passes per block
-constexpr int kStackSub = MOE_STACK_SUB;       // arrival sub-counters per phase
-constexpr int kStackFlags = MOE_STACK_FLAGS;   // copies of each phase's completion flag (<= 64)
-// lines: epoch + abort, then per phase (2 per layer) kStackSub sub-counters,
-// then the phases' top counters, then kStackFlags flags per phase
-inline size_t stack_sync_words(int n_layers) {
-    return (1 + 2 * (size_t)n_layers * (kStackSub + 1 + kStackFlags)) * kStackLine;
-}
+constexpr int kXchgParts = 5;                  // x, h, shared h, LoRA A u, shared gate
+// one line: the abort word of the step kernel's waits
+inline size_t stack_sync_words(int) { return kStackLine; }
 struct StackDecArgs {
     const StackLayerArgs* tab; int n_layers; int nA; int nB;
-    uint32_t* sync;               // stack_sync_words(n_layers): counters, flags, epoch
+    uint32_t* sync;               // stack_sync_words(n_layers): the abort word
     uint32_t spin_limit;
 };
 struct StackPatchArgs {
@@ -408,6 +399,10 @@ struct StackPatchArgs {
     int32_t* used_idx; float* used_w;
     const int32_t* hist_prev;
     float* trace;                 // [layer][n_tok * d] or nullptr (layer 0 copied by the host)
+    // the exchange words the step kernel publishes, set to the empty word
+    // before it runs: per layer kXchgCopies copies xstride floats apart, part
+    // i at xoff[i] with xw[i] floats per token; and each layer's head logits
+    float* xchg; size_t xstride; uint32_t xoff[kXchgParts]; uint32_t xw[kXchgParts];
 };
 constexpr int kStackHeadMaxPer = 4;         // the step kernel's head top-k: E <= 64 * 4
 bool stack_one_launch_shape_ok(int d, int f);
