@@ -316,29 +316,26 @@ __device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync&
             const bool h0_on = wave < n_active;
             const int q0 = h0_on ? nth_set(W.starts, wave) : 0;
             const float* probe = h0_on ? a.h + xo + (size_t)q0 * F : (has_shared ? a.hs + xo : nullptr);
+            // every load is issued on every poll, absent inputs from a
+            // readable stand-in, and only then tested: a load under a branch
+            // would be waited for before the next one is issued
+            const float* sg_p = a.sgate ? a.sgate + xo + (lane < n_tok ? lane : 0) : (const float*)a.err;
+            const float* ex_p = a.fused ? a.x + (size_t)et * d + row0 + er : (const float*)a.err;
+            const float* au_p = lora_vec ? a.au + xo : a.h + xo;
+            const float* hs_p = has_shared ? a.hs + xo : a.h + xo;
             fuse_poll(fs, a.err, probe, [&]() {
-                bool empty = false;
-                if (a.sgate) {
-                    v_sg = ld_dev(a.sgate + xo + (lane < n_tok ? lane : 0));
-                    empty |= empty_word(v_sg);
-                }
-                if (a.fused) {
-                    ep_x = ld_dev(a.x + (size_t)et * d + row0 + er);
-                    empty |= a.x_repl && empty_word(ep_x);
-                }
-                if (lora_vec) {
-                    lora_issue_u<true>(lr, a.au + xo, (size_t)et * a.r, a.r);
+                v_sg = ld_dev(sg_p);
+                ep_x = ld_dev(ex_p);
+                lora_issue_u<true>(lr, au_p, lora_vec ? (size_t)et * a.r : 0, lora_vec ? a.r : 8);
+                h_issue<true>(shh, hs_p, 0, c);
+                h_issue<true>(h0, a.h + xo, (size_t)q0 * F, c);
+                bool empty = (a.sgate && empty_word(v_sg)) | (a.fused && a.x_repl && empty_word(ep_x));
+                bool eu = false;
 #pragma unroll
-                    for (int q = 0; q < 2 * kLoraChunks; ++q) empty |= any_empty(lr.u[q]);
-                }
-                if (has_shared) {
-                    h_issue<true>(shh, a.hs + xo, 0, c);
-                    empty |= any_empty(shh[0]) | any_empty(shh[1]);
-                }
-                if (h0_on) {
-                    h_issue<true>(h0, a.h + xo, (size_t)q0 * F, c);
-                    empty |= any_empty(h0[0]) | any_empty(h0[1]);
-                }
+                for (int q = 0; q < 2 * kLoraChunks; ++q) eu |= any_empty(lr.u[q]);
+                empty |= lora_vec && eu;
+                empty |= has_shared && (any_empty(shh[0]) | any_empty(shh[1]));
+                empty |= h0_on && (any_empty(h0[0]) | any_empty(h0[1]));
                 return !empty;
             });
             shared_compute();

@@ -29,7 +29,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // 2*off lanes. Within a row of 16 lanes the partner is taken by a DPP
 // permutation (xor 1, xor 2, then the half-row and row mirrors, which pair
 // each lane of one half with one of the other), with no trip through the
-// LDS crossbar that other lane shuffles take; offsets 16 and 32 shuffle.
+// LDS crossbar that other lane shuffles take; offsets 16 and 32 shuffle
+// (the sums below take those offsets with lane swaps instead).
 // Sums over a block come out the same with any such pairing.
 __device__ __forceinline__ int partner_i32(int v, int off) {
     switch (off) {
@@ -49,6 +50,46 @@ __device__ __forceinline__ double partner(double v, int off) {
     return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
 }
 
+// Offsets 16 and 32 without the crossbar: v_permlane16_swap trades the odd
+// rows (of 16 lanes) of one register with the even rows of another, and
+// v_permlane32_swap the upper half of one with the lower half of another.
+// After swap_pair(x, y, off) a lane in the lower half of its 2*off block
+// holds its own x and its partner's x, one in the upper half its partner's y
+// and its own y: x + y is the halving step of row_reduce in one add.
+__device__ __forceinline__ void swap_pair_u32(uint32_t& x, uint32_t& y, int off) {
+    if (off == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+        x = r[0]; y = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+        x = r[0]; y = r[1];
+    }
+}
+__device__ __forceinline__ void swap_pair(float& x, float& y, int off) {
+    uint32_t a = __float_as_uint(x), b = __float_as_uint(y);
+    swap_pair_u32(a, b, off);
+    x = __uint_as_float(a); y = __uint_as_float(b);
+}
+__device__ __forceinline__ void swap_pair(double& x, double& y, int off) {
+    const uint64_t a = (uint64_t)__double_as_longlong(x), b = (uint64_t)__double_as_longlong(y);
+    uint32_t alo = (uint32_t)a, ahi = (uint32_t)(a >> 32), blo = (uint32_t)b, bhi = (uint32_t)(b >> 32);
+    swap_pair_u32(alo, blo, off);
+    swap_pair_u32(ahi, bhi, off);
+    x = __longlong_as_double((long long)(((uint64_t)ahi << 32) | alo));
+    y = __longlong_as_double((long long)(((uint64_t)bhi << 32) | blo));
+}
+// v + the partner lane's v (a butterfly step; both lanes get the same sum,
+// addition being commutative)
+template <typename T>
+__device__ __forceinline__ T pair_sum(T v, int off) {
+    if (off >= 16) {
+        T x = v, y = v;
+        swap_pair(x, y, off);
+        return x + y;
+    }
+    return v + partner(v, off);
+}
+
 // Sum NP per-lane values over aligned groups of LPR lanes. Each halving step
 // trades half of the values with a partner lane in the other half of the
 // block, so after log2(NP) steps every lane holds the partial of one of the
@@ -66,19 +107,30 @@ __device__ __forceinline__ T row_reduce(const T (&v)[NP], int* which) {
     for (int i = 0; i < NP; ++i) cur[i] = v[i];
 #pragma unroll
     for (int n = NP; n > 1; n >>= 1) {
-        const bool upper = (lane & off) != 0;
+        // (opaque: otherwise the compiler merges the lane tests of all the
+        // levels into one index and selects each value from the original
+        // NP with a chain of compares)
+        uint32_t up = (uint32_t)(lane & off);
+        asm volatile("" : "+v"(up));
+        const bool upper = up != 0;
 #pragma unroll
         for (int i = 0; i < n / 2; ++i) {
-            const T send = upper ? cur[i] : cur[i + n / 2];
-            const T keep = upper ? cur[i + n / 2] : cur[i];
-            cur[i] = keep + partner(send, off);
+            if (off >= 16) {
+                T x = cur[i], y = cur[i + n / 2];
+                swap_pair(x, y, off);
+                cur[i] = x + y;
+            } else {
+                const T send = upper ? cur[i] : cur[i + n / 2];
+                const T keep = upper ? cur[i + n / 2] : cur[i];
+                cur[i] = keep + partner(send, off);
+            }
         }
         if (upper) lo += n / 2;
         off >>= 1;
     }
     T t = cur[0];
 #pragma unroll
-    for (int o = LPR / NP / 2; o > 0; o >>= 1) t += partner(t, o);
+    for (int o = LPR / NP / 2; o > 0; o >>= 1) t = pair_sum(t, o);
     *which = lo;
     return t;
 }
@@ -88,7 +140,7 @@ __device__ __forceinline__ T row_reduce(const T (&v)[NP], int* which) {
 template <typename T, int WIDTH>
 __device__ __forceinline__ T group_sum_dpp(T v) {
 #pragma unroll
-    for (int o = WIDTH / 2; o > 0; o >>= 1) v += partner(v, o);
+    for (int o = WIDTH / 2; o > 0; o >>= 1) v = pair_sum(v, o);
     return v;
 }
 
