@@ -126,25 +126,43 @@ __device__ __forceinline__ void u_to_lds(const AA& a, const XThread& X, ULds<D>&
         for (int w = 0; w < kWaves; ++w) tot += S.red[w];
         inv = 1.0 / sqrt(tot / (double)D + (double)a.eps);
     }
+    // one branch around each form of the loop, not one per element; with
+    // bf16 activations the lo part is zero and is not formed; without the
+    // norm, inv and the gains are 1, and (x * 1) * 1 is x exactly
     uint32_t hb[8], lb[8];
     float uf[8];
+    const bool act_bf16 = a.act_bf16;
+    double gd[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const double xv = x_elem<XB>(X.w, j);
-        const double uv = a.fused ? (xv * inv) * (double)X.g[j] : xv;
-        if (a.act_bf16) { hb[j] = f64_to_bf16(uv); uf[j] = bf16_to_f32(hb[j]); }
-        else { uf[j] = (float)uv; hb[j] = f32_to_bf16(uf[j]); }
-        lb[j] = f32_to_bf16(uf[j] - bf16_to_f32(hb[j]));
+    for (int j = 0; j < 8; ++j) gd[j] = a.fused ? (double)X.g[j] : 1.0;
+    if (act_bf16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            hb[j] = f64_to_bf16((x_elem<XB>(X.w, j) * inv) * gd[j]);
+            uf[j] = bf16_to_f32(hb[j]);
+            lb[j] = 0u;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uf[j] = (float)((x_elem<XB>(X.w, j) * inv) * gd[j]);
+            hb[j] = f32_to_bf16(uf[j]);
+            lb[j] = f32_to_bf16(uf[j] - bf16_to_f32(hb[j]));
+        }
     }
     float sh = 0.f, sl = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { sh += bf16_to_f32(hb[j]); sl += bf16_to_f32(lb[j]); }
+    for (int j = 0; j < 8; ++j) sh += bf16_to_f32(hb[j]);
+    if (!act_bf16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sl += bf16_to_f32(lb[j]);
+    }
     const int c = tid >> 2, i = tid & 3;                 // chunk, piece
     if (mine) {
         u32x4 v;
         v.x = hb[0] | (hb[4] << 16); v.y = hb[1] | (hb[5] << 16); v.z = hb[2] | (hb[6] << 16); v.w = hb[3] | (hb[7] << 16);
         *(u32x4*)&S.pk[(i * AGeo<D>::C + c) * 4] = v;
-        if (!a.act_bf16) {
+        if (!act_bf16) {
             u32x4 l;
             l.x = lb[0] | (lb[4] << 16); l.y = lb[1] | (lb[5] << 16); l.z = lb[2] | (lb[6] << 16); l.w = lb[3] | (lb[7] << 16);
             *(u32x4*)&S.pk_lo[(i * AGeo<D>::C + c) * 4] = l;
@@ -154,7 +172,7 @@ __device__ __forceinline__ void u_to_lds(const AA& a, const XThread& X, ULds<D>&
     }
     // chunk sums: the 4 threads of a chunk are 4 consecutive lanes
     sh = group_sum_dpp<float, 4>(sh);
-    sl = group_sum_dpp<float, 4>(sl);
+    if (!act_bf16) sl = group_sum_dpp<float, 4>(sl);
     if (mine && i == 0) { S.usum[c] = sh; S.usum_lo[c] = sl; }
     lds_barrier();
 }
