@@ -357,9 +357,9 @@ void moe_layer_destroy(moe_layer* layer);
  *   checking each layer on the input it saw); calls whose trace would not
  *   fit return MOE_E_CAPACITY. NULL / 0 turns the trace off.
  * moe_stack_set_one_launch: enable != 0 runs each later decode step that
- *   qualifies as three launches in all (layer 0's router, a patch of the
- *   per-layer argument table that also marks every exchange word the step
- *   will publish as empty, and one step kernel in which every layer's K_A
+ *   qualifies as two launches (layer 0's router together with a patch of
+ *   the per-layer argument table that also marks every exchange word the
+ *   step will publish as empty, then one step kernel in which every layer's K_A
  *   and K_B run as work items, each issuing its weight rows before it
  *   reads, until they have been published, the activations it needs; the
  *   addresses are known before the step starts because each layer's routing

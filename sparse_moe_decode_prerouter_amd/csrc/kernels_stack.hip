@@ -30,6 +30,7 @@
 #include "fuse_sync.h"
 #include "dec_a_body.h"
 #include "dec_b_body.h"
+#include "dec_r_body.h"
 
 namespace moe {
 
@@ -58,11 +59,12 @@ __global__ void __launch_bounds__(kThreads, 2) k_dec_stack(StackDecArgs s) {
 
 // Before each launch: the per-call fields of every layer's arguments, the
 // abort word, and the empty word in every exchange word the launch will
-// publish. Block u takes (layer u / (C + 1), copy u % (C + 1)) of the
-// exchange (C copies per layer; copy C stands for the layer's head logits).
-__global__ void k_stack_patch(StackPatchArgs p) {
+// publish. Block pb of npb takes units pb, pb + npb, ..., unit u being
+// (layer u / (C + 1), copy u % (C + 1)) of the exchange (C copies per layer;
+// copy C stands for the layer's head logits).
+__device__ __forceinline__ void stack_patch_body(const StackPatchArgs& p, int pb, int npb) {
     const u32x4 e4 = {kEmptyWord, kEmptyWord, kEmptyWord, kEmptyWord};
-    for (int u = blockIdx.x; u < p.n_layers * (kXchgCopies + 1); u += gridDim.x) {
+    for (int u = pb; u < p.n_layers * (kXchgCopies + 1); u += npb) {
         const int l = u / (kXchgCopies + 1), c = u % (kXchgCopies + 1);
         if (c < kXchgCopies) {
             float* base = p.xchg + ((size_t)l * kXchgCopies + c) * p.xstride;
@@ -79,8 +81,8 @@ __global__ void k_stack_patch(StackPatchArgs p) {
                 __hip_atomic_store(lg + j, __longlong_as_double(-1ll), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) *p.sync = 0u;     // the abort word
-    const int l = blockIdx.x * blockDim.x + threadIdx.x;
+    if (pb == 0 && threadIdx.x == 0) *p.sync = 0u;     // the abort word
+    const int l = pb * blockDim.x + threadIdx.x;
     if (l >= p.n_layers) return;
     StackLayerArgs& L = p.tab[l];
     const size_t per = (size_t)p.n_tok * p.k;
@@ -105,6 +107,15 @@ __global__ void k_stack_patch(StackPatchArgs p) {
     b.pred_w = last ? nullptr : p.pred_w + (l + 1) * per;
     b.hist_cur = last ? nullptr : p.route_idx + (l + 1) * per;
     b.hist_prev = (last || !p.hist_prev) ? nullptr : p.hist_prev + (l + 1) * per;
+}
+
+// The launch before the step kernel: blocks [0, nb_r) route layer 0's rows
+// (K_R's body), the others patch the table and mark the exchange empty; the
+// two are independent, so the patch's stores overlap the router's latency.
+__global__ void __launch_bounds__(kThreads) k_stack_prep(StackPatchArgs p, DecAArgs a, RouteArgs r, int nb_r) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    if ((int)blockIdx.x < nb_r) dec_r_body(a, r, (int)blockIdx.x, nb_r, (float*)lds);
+    else stack_patch_body(p, (int)blockIdx.x - nb_r, (int)gridDim.x - nb_r);
 }
 
 int stack_one_hrows(int d) { return kWaves * kStackAPass * (64 / (d / 32)); }
@@ -138,10 +149,12 @@ int stack_one_launch_blocks_per_cu(int d, int f) {
     return 0;
 }
 
-hipError_t launch_stack_one(const StackPatchArgs& p, const StackDecArgs& s, int grid, hipStream_t st,
-                            const KTime* tm) {
-    const int pgrid = std::max(p.n_layers * (kXchgCopies + 1), (p.n_layers + 255) / 256);
-    hipLaunchKernelGGL(k_stack_patch, dim3(pgrid), dim3(256), 0, st, p);
+hipError_t launch_stack_one(const StackPatchArgs& p, const DecAArgs& a0, const RouteArgs& r0,
+                            const StackDecArgs& s, int grid, hipStream_t st, const KTime* tprep, const KTime* tm) {
+    if (a0.d > 2048) return hipErrorInvalidValue;
+    const int nb_r = dec_r_blocks(r0.E);
+    const int pgrid = std::max(p.n_layers * (kXchgCopies + 1), (p.n_layers + kThreads - 1) / kThreads);
+    MOE_LAUNCH(k_stack_prep, dim3(nb_r + pgrid), dim3(kThreads), (size_t)a0.d * 4, st, tprep, p, a0, r0, nb_r);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const void* fn = nullptr;

@@ -1093,7 +1093,6 @@ static int stack_decode_one(moe_stack* S, const float* x_in, float* x_out, int n
     r.route_idx = nullptr; r.logits_r = L0->s.logits_r;
     r.self_idx = L0->s.self_idx; r.self_w = L0->s.self_w; r.counters = L0->s.counters;
     const KTime tr{S->profiling ? S->ev_t[0] : nullptr, S->profiling ? S->ev_t[1] : nullptr};
-    HIPCHK(launch_dec_r(a, r, st, &tr));
     StackPatchArgs p{};
     p.tab = S->d_tab; p.sync = S->d_sync; p.n_layers = S->n; p.n_tok = n_tok; p.k = D.top_k; p.d = D.d_model; p.f = D.d_ff;
     const int hr = stack_one_hrows(D.d_model);
@@ -1120,7 +1119,7 @@ static int stack_decode_one(moe_stack* S, const float* x_in, float* x_out, int n
     // (each block then keeps its role from layer to layer), else fewer
     const int per_layer = sd.nA + sd.nB;
     const int grid = per_layer <= S->one_grid ? per_layer : std::min(S->one_grid, total);
-    HIPCHK(launch_stack_one(p, sd, grid, st, &tk));
+    HIPCHK(launch_stack_one(p, a, r, sd, grid, st, &tr, &tk));
     if (S->profiling) S->ev_used[0] = S->ev_used[1] = true;
     return MOE_OK;
 }

@@ -378,7 +378,7 @@ struct StackLayerArgs {
 };
 constexpr int kStackLine = 32;                 // words per 128-byte line
 #ifndef MOE_XCHG_COPIES
-#define MOE_XCHG_COPIES 8
+#define MOE_XCHG_COPIES 4
 #endif
 constexpr int kXchgCopies = MOE_XCHG_COPIES;   // copies of the activations handed between phases
 constexpr int kStackAPass = 4;                 // the step kernel's gate/up passes per wave (16 h rows a block)
@@ -410,7 +410,9 @@ int stack_one_hrows(int d);                      // h rows per K_A item of the s
 int stack_one_brows(int f);                      // output rows per K_B item of the step kernel
 bool stack_one_fast_ok(int d, int f, int fs, int n_tok, int k);
 int stack_one_launch_blocks_per_cu(int d, int f);
-hipError_t launch_stack_one(const StackPatchArgs& p, const StackDecArgs& s, int grid, hipStream_t st,
+// layer 0's router and the table patch (one launch), then the step kernel
+hipError_t launch_stack_one(const StackPatchArgs& p, const DecAArgs& a0, const RouteArgs& r0,
+                            const StackDecArgs& s, int grid, hipStream_t st, const KTime* tprep = nullptr,
                             const KTime* tm = nullptr);
 hipError_t launch_topk_job(const TopkJob& j, int n_tok, hipStream_t s);
 
