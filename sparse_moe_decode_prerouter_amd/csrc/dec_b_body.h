@@ -195,6 +195,16 @@ __device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync&
     // (one-launch step) the exchange-buffer copy this block reads
     const int ncopy = FUSED ? (a.xcopies > 0 ? a.xcopies : 1) : 1;
     const size_t xo = FUSED ? (size_t)((int)blockIdx.x % ncopy) * a.xstride : 0;
+    // the epilogue's fields, read here and (one-launch step) held in scalar
+    // registers: read after the waits, each would be a dependent scalar load
+    // on the critical path
+    float* ep_y = a.y;
+    float* ep_xn = FUSED ? a.xnext : nullptr;
+    float* ep_yc = FUSED ? a.y_copy : nullptr;
+    float ep_ls = a.lora_scale;
+    size_t ep_xs = FUSED ? a.xstride : 0;
+    int ep_k = a.k;
+    if constexpr (FUSED) asm volatile("" : "+s"(ep_y), "+s"(ep_xn), "+s"(ep_yc), "+s"(ep_ls), "+s"(ep_xs), "+s"(ep_k));
 
     // ---- level 0, identical in every wave. The routing entries go first
     // (K_A read them on every XCD, so they are L2 hits); all other loads need
@@ -375,7 +385,7 @@ __device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync&
     // ---- epilogue: shared, then routed in routing order, LoRA B, residual
     if (tid < ep_n) {
         float y = has_shared ? part[(n_assign + et) * G::RB + er] : 0.f;
-        for (int j = 0; j < k; ++j) y += part[(et * k + j) * G::RB + er];
+        for (int j = 0; j < ep_k; ++j) y += part[(et * ep_k + j) * G::RB + er];
         if (lora_on) {
             float l = 0.f;
             if (lora_vec) l = lora_dot(lr, a.r);
@@ -383,17 +393,17 @@ __device__ __forceinline__ void dec_b_body(const BA& a, int bid, const FuseSync&
                 for (int q = 0; q < a.r; ++q)
                     l += bf16_to_f32(a.lora_b[(size_t)(row0 + er) * a.r + q]) *
                          (FUSED ? ld_dev(a.au + xo + (size_t)et * a.r + q) : a.au[(size_t)et * a.r + q]);
-            y += a.lora_scale * l;
+            y += ep_ls * l;
         }
         if (a.fused) y += ep_x;
         if constexpr (FUSED) {
             const size_t yi = (size_t)et * d + row0 + er;
-            if (a.y) st_dev(a.y + yi, y);
-            if (a.xnext)
-                for (int cc = 0; cc < ncopy; ++cc) st_dev(a.xnext + cc * a.xstride + yi, y);
-            if (a.y_copy) a.y_copy[yi] = y;
+            if (ep_y) st_dev(ep_y + yi, y);
+            if (ep_xn)
+                for (int cc = 0; cc < ncopy; ++cc) st_dev(ep_xn + cc * ep_xs + yi, y);
+            if (ep_yc) ep_yc[yi] = y;
         } else {
-            a.y[(size_t)et * d + row0 + er] = y;
+            ep_y[(size_t)et * d + row0 + er] = y;
         }
     }
 }

@@ -3,6 +3,7 @@
 #pragma once
 #include "device_common.h"
 #include "moe_internal.h"
+#include "dec_common.h"
 
 namespace moe {
 
@@ -20,19 +21,31 @@ __device__ __forceinline__ void best_row_ror(double& v, int& i) {
     if (better(ov, oi, v, i)) { v = ov; i = oi; }
 }
 
+// (v, i) becomes the best of (v, i) and the pair of lane l ^ OFF (OFF 16
+// or 32): a v_permlane swap of the pair with itself leaves the partner's
+// value in one of the two results (which one depends on the lane's half)
+template <int OFF>
+__device__ __forceinline__ void best_swap(double& v, int& i) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    uint32_t lo0 = (uint32_t)b, lo1 = lo0, hi0 = (uint32_t)(b >> 32), hi1 = hi0, i0 = (uint32_t)i, i1 = i0;
+    swap_pair_u32(lo0, lo1, OFF);
+    swap_pair_u32(hi0, hi1, OFF);
+    swap_pair_u32(i0, i1, OFF);
+    const bool upper = (threadIdx.x & OFF) != 0;
+    const double ov = __longlong_as_double((long long)(((uint64_t)(upper ? hi0 : hi1) << 32) | (upper ? lo0 : lo1)));
+    const int oi = (int)(upper ? i0 : i1);
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
 // every lane ends with the best (v, i) of the wave: rotations by 1, 2, 4
-// and 8 cover each row of 16 lanes, two shuffles join the four rows
+// and 8 cover each row of 16 lanes, two lane swaps join the four rows
 __device__ __forceinline__ void wave_best(double& v, int& i) {
     best_row_ror<1>(v, i);
     best_row_ror<2>(v, i);
     best_row_ror<4>(v, i);
     best_row_ror<8>(v, i);
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-        const double ov = __shfl_xor(v, o, 64);
-        const int oi = __shfl_xor(i, o, 64);
-        if (better(ov, oi, v, i)) { v = ov; i = oi; }
-    }
+    best_swap<16>(v, i);
+    best_swap<32>(v, i);
 }
 
 // lane j < k: the j-th selection and its weight (as also written out)
