@@ -172,15 +172,20 @@ def tie_stack(shape, L_, group, max_tokens, key):
     return ora, gpus, moe.MoeStack(gpus)
 
 
+@pytest.mark.parametrize("one", [False, True], ids=["per_layer", "one_launch"])
 @pytest.mark.parametrize("B", [1, 3])
-def test_ties_stack_decode(B):
+def test_ties_stack_decode(B, one):
     """Stack decode: layer 0's router every step, the deferred head top-k in
-    the next layer's gate/up launch, the final top-k launch."""
-    from test_gpu_stack import run_gpu
+    the next layer's gate/up launch, the final top-k launch; or, as one launch
+    per step, the router beside the argument patch and every head's top-k in
+    its layer's top-k work item of the step kernel."""
+    from test_gpu_stack import run_gpu, one_launch_ran
     shape = TIE35
     L_, steps = 4, 3
-    say(f"ties stack decode L={L_} B={B} steps={steps}")
+    say(f"ties stack decode L={L_} B={B} steps={steps} one_launch={one}")
     ora, gpus, stack = tie_stack(shape, L_, 3, B, ("sd", B))
+    if one:
+        stack.set_one_launch(True)
     xs = np.stack([tie_inputs(shape, B, ("sd", B, t)).double().numpy() for t in range(steps)])
     assert_ties_exercised(ora[0], xs[0], True, shape.k)
     g = run_gpu(stack, L_, xs, shape.k)
@@ -190,6 +195,8 @@ def test_ties_stack_decode(B):
         f, _ = check_stack_layers(ora, s["trace"], s["x_out"], s["used"], s["used_w"], s["given"], s["pred"],
                                   s["pred_w"], "exact", outputs=False, what=f"ties step {t}")
         assert f == 0
+    if one:
+        assert one_launch_ran(stack, L_, B, shape)
 
 
 @pytest.mark.parametrize("T", [37, 150])
