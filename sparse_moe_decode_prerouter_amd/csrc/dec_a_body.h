@@ -201,16 +201,14 @@ __device__ __forceinline__ void gateup_issue(GateUpRegs<AP>& R, const uint8_t* b
     }
 }
 
-// sum over the chunk of (128 + q) * u
-__device__ __forceinline__ float chunk_dot(u32x4 w, const u32x4 (&up)[4], float acc) {
+// sum over the chunk of (128 + q) * u; nm, nc: the nibble-pair mask and the
+// exponent in registers the compiler cannot see through (made once by the
+// caller), so that each (128 + q) pair is one v_and_or_b32 (after the shift)
+// instead of an AND and an OR with literal operands
+__device__ __forceinline__ float chunk_dot(u32x4 w, const u32x4 (&up)[4], float acc, uint32_t nm, uint32_t nc) {
     // opaque copy: keeps the nibble unpacking after u is ready instead of
     // hoisted out of the position loop, where it would wait for the weights
     asm volatile("" : "+v"(w));
-    // the mask and exponent in registers the compiler cannot see through: each
-    // (128 + q) pair is then one v_and_or_b32 (after the shift) instead of an
-    // AND and an OR with literal operands
-    uint32_t nm = 0x000F000Fu, nc = 0x43004300u;
-    asm volatile("" : "+v"(nm), "+v"(nc));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -239,13 +237,15 @@ __device__ __forceinline__ void gateup_rows(const GateUpRegs<AP>& R, const ULds<
         usm += S.usum_lo[c];
     }
     float ga[AP], ua[AP];
+    uint32_t nm = 0x000F000Fu, nc = 0x43004300u;
+    asm volatile("" : "+v"(nm), "+v"(nc));
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
-        float accg = chunk_dot(R.g[i], up, 0.f);
-        float accu = chunk_dot(R.u[i], up, 0.f);
+        float accg = chunk_dot(R.g[i], up, 0.f, nm, nc);
+        float accu = chunk_dot(R.u[i], up, 0.f, nm, nc);
         if (with_lo) {
-            accg = chunk_dot(R.g[i], lo, accg);
-            accu = chunk_dot(R.u[i], lo, accu);
+            accg = chunk_dot(R.g[i], lo, accg, nm, nc);
+            accu = chunk_dot(R.u[i], lo, accu, nm, nc);
         }
         uint32_t sgw = R.sg[i], suw = R.su[i];
         asm volatile("" : "+v"(sgw), "+v"(suw));   // opaque copies, as in chunk_dot
