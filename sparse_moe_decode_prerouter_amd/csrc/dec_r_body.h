@@ -158,8 +158,8 @@ __device__ __forceinline__ void bf16_row_load(u32x4 (&wr)[NLD], const uint16_t* 
 constexpr int kHeadRowsPerBlock = 4;  // router rows per K_R block: 1 per wave
 
 // Router rows of block bid of nblocks (one row per wave); logits are
-// published with device-scope stores and counted with a relaxed atomic, so
-// the last block to finish reads them coherently and takes the top-k.
+// published with device-scope stores, then counted after a device-scope
+// release fence; the last block to finish acquires and takes the top-k.
 // suf: d floats of LDS.
 __device__ __forceinline__ void dec_r_body(const DecAArgs& a, const RouteArgs& r, int bid, int nblocks, float* suf) {
     constexpr int kNld = 4;
@@ -183,9 +183,16 @@ __device__ __forceinline__ void dec_r_body(const DecAArgs& a, const RouteArgs& r
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
+        // release: the block's logit stores (ordered before this thread by
+        // the barrier) happen before the count; the last block acquires
+        // before it reads the other blocks' logits
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const unsigned old = __hip_atomic_fetch_add(r.counters + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         is_last = old == (unsigned)nblocks - 1;
-        if (is_last) __hip_atomic_store(r.counters + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (is_last) {
+            __hip_atomic_store(r.counters + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
     }
     __syncthreads();
     if (!is_last) return;
