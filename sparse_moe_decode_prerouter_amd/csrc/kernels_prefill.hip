@@ -1363,15 +1363,20 @@ __global__ void __launch_bounds__(64 * kFrWaves) k_route_mm_fr(RouteMMArgs a) {
     }
     if (!pre) return;
     // the last of these blocks to finish takes the top-k of rows 0 .. pre_rows-1
-    // (device-scope stores, waited for, then a relaxed device-scope count:
-    // the last block reads every block's logits with coherent loads)
+    // (device-scope stores, a barrier, a device-scope release fence, then the
+    // count; the last block acquires and reads every block's logits with
+    // coherent loads)
     __shared__ int is_last;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const unsigned old = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         is_last = old == (unsigned)fs.tiles(0) - 1;
-        if (is_last) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (is_last) {
+            __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
     }
     __syncthreads();
     if (!is_last) return;
