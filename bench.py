@@ -235,19 +235,23 @@ def streamed_sweep(torch, np, moe, synth, shape, ws, pstore, pshared, copy_GBs):
         row = {}
         for mode, name in ((moe.MOE_STAGE_PREROUTED, "prerouted"), (moe.MOE_STAGE_ON_DEMAND, "on_demand")):
             ss.set_staging(mode, cs)
-            ms = eager_steps(torch, ss, L, K, d, synth, shape, steps, warm, ("bench_str", K),
-                             on_warm=lambda: sum(Lr.slots()[1] for Lr in sl))
-            moved = sum(Lr.slots()[1] for Lr in sl)
-            assert all(Lr.status() == 0 for Lr in sl), [Lr.status() for Lr in sl]
-            row[name] = (ms, (moved - eager_steps.last_warm_value) / steps)
+            # best of two timed runs: the first streamed run of the process
+            # has come out up to ~2 ms per step slower than the same run again
+            best = None
+            for _ in range(2):
+                ms = eager_steps(torch, ss, L, K, d, synth, shape, steps, warm, ("bench_str", K),
+                                 on_warm=lambda: sum(Lr.slots()[1] for Lr in sl))
+                moved = sum(Lr.slots()[1] for Lr in sl)
+                assert all(Lr.status() == 0 for Lr in sl), [Lr.status() for Lr in sl]
+                if best is None or ms < best[0]:
+                    best = (ms, (moved - eager_steps.last_warm_value) / steps)
+            row[name] = best
         ss.set_staging(moe.MOE_STAGE_OFF, None)
         ss.close()
         for Lr in sl:
             Lr.close()
         # compute-only reference: the same layers with the experts resident,
-        # timed after the streamed runs (timed before them, the first streamed
-        # run that followed came out ~2 ms per step slower than the same run
-        # timed on its own or again)
+        # timed after the streamed runs
         rl = [moe.MoeLayer(
             d_model=shape.d, n_experts=shape.E, top_k=K, d_ff=shape.f, d_ff_shared=shape.fs, lora_rank=shape.r,
             lora_alpha=shape.alpha, act_dtype=moe.MOE_ACT_BF16, max_tokens=1, expert_store=w["store"],

@@ -330,7 +330,12 @@ void moe_layer_destroy(moe_layer* layer);
  *   x_out      device fp32 [n_tok][d]: residual stream after the last layer
  *   route_*    device [n_layers][n_tok][k]: this step's routing (entry l = 0
  *              and every entry on the first step are ignored: those layers
- *              self-route with their router)
+ *              self-route with their router). Entries of layers l >= 1 must
+ *              be expert indices (the previous step's predictions are): a
+ *              negative entry is MOE_E_BAD_INDEX in that layer's status on the
+ *              general path (batches beyond the fused one), where the sorts of
+ *              layers 1..n-1 run as one launch at the start of the step; it
+ *              must not alias pred_* (the step's heads overwrite pred_*).
  *   pred_*     device [n_layers][n_tok][k] out: pred[l] for l >= 1 (pred[0]
  *              is left untouched); the next step's route
  *   used_*     optional out [n_layers][n_tok][k]: routing each layer used

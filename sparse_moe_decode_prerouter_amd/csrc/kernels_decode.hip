@@ -149,7 +149,7 @@ __device__ __forceinline__ unsigned long long match_expert(int e, bool valid, in
     return valid ? m : 0ull;
 }
 
-__global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
+__device__ __forceinline__ void sort_body(const SortArgs& a) {
     extern __shared__ int sm[];
     const int n = a.n_tok * a.k, E = a.E;
     int* wcnt = sm;                          // [kSortWaves][E]: counts, then first positions
@@ -256,7 +256,9 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
         const size_t gi = (size_t)i - (size_t)a.route_shift * a.k;   // the given routing's entry (t >= shift)
         const bool self = !a.route_idx || t < a.route_shift || a.route_idx[gi - (size_t)(i % a.k)] < 0;
         if (self && own_topk && t >= a.pre_rows) continue;      // written by the top-k above
-        place(i, self ? a.self_idx[i] : a.route_idx[gi], self ? a.self_w[i] : a.route_w[gi]);
+        // (without self-routing results a self-routed row is a bad index)
+        if (self) place(i, a.self_idx ? a.self_idx[i] : -1, a.self_idx ? a.self_w[i] : 0.f);
+        else place(i, a.route_idx[gi], a.route_w[gi]);
     }
     __threadfence_block();
     __syncthreads();                         // the experts are read below by other threads
@@ -424,6 +426,33 @@ __global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) {
         a.meta[0] = tot_active;
         a.meta[1] = tot_valid;
     }
+}
+
+__global__ void __launch_bounds__(kSortThreads) k_sort(SortArgs a) { sort_body(a); }
+
+// The sorts of several layers' given routing in one launch: block b takes
+// table entry b (a layer's fixed arguments) with the call's routing, used
+// routing outputs and token count patched in (entry b's routing starts
+// (b + 1) * per entries past the call's base: the stack's layers 1, 2, ...).
+// No row may self-route here: a row whose first entry is negative is a bad
+// index (the table has no self-routing results).
+__global__ void __launch_bounds__(kSortThreads) k_sort_layers(const SortArgs* __restrict__ tab, SortCall c) {
+    SortArgs a = tab[blockIdx.x];
+    const size_t off = (size_t)(blockIdx.x + 1) * c.per;
+    a.route_idx = c.route_idx + off;
+    a.route_w = c.route_w + off;
+    a.user_used_idx = c.used_idx ? c.used_idx + off : nullptr;
+    a.user_used_w = c.used_w ? c.used_w + off : nullptr;
+    a.n_tok = c.n_tok;
+    if (!c.big) a.tiles64 = nullptr;
+    sort_body(a);
+}
+
+hipError_t launch_sort_layers(const SortArgs* tab, int n_layers, int E, const SortCall& c, hipStream_t s) {
+    const size_t lds = sort_lds_bytes((int)c.per, E);
+    if (E > kSortThreads || lds > 64 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_sort_layers, dim3(n_layers), dim3(kSortThreads), lds, s, tab, c);
+    return hipGetLastError();
 }
 
 hipError_t launch_sort(const SortArgs& a, hipStream_t s) {

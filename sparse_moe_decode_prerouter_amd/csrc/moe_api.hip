@@ -530,7 +530,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     sa.tiles16 = mm ? L->s.tiles : nullptr;
     sa.tiles64 = big ? L->s.tiles64 : nullptr;
     sa.resolve_blobs = !reactive;
-    HIPCHK(launch_sort(sa, st));
+    if (!L->presorted) HIPCHK(launch_sort(sa, st));
 
     if (reactive && L->dev_staging) {
         // reactive on the device: the sorted routing drives the staging
@@ -994,7 +994,8 @@ static size_t stack_carve(moe_layer* const* layers, int n, uint8_t* base, moe_st
     if (S) S->pred_cap = per;
     StackLayerArgs* tab = c.take<StackLayerArgs>((size_t)n);
     uint32_t* sync = c.take<uint32_t>(stack_sync_words(n));
-    if (S) { S->d_tab = tab; S->d_sync = sync; }
+    SortArgs* stab = n > 1 ? c.take<SortArgs>((size_t)n - 1) : nullptr;
+    if (S) { S->d_tab = tab; S->d_sync = sync; S->d_sort_tab = stab; }
     if (stack_one_launch_ok(layers, n)) {
         // exchange copies of the one-launch step, sized for the most tokens
         // a step of this stack can take there
@@ -1124,6 +1125,57 @@ static int stack_decode_one(moe_stack* S, const float* x_in, float* x_out, int n
     return MOE_OK;
 }
 
+// Batched decode beyond the fused path: the given routing of layers 1..n-1
+// (the previous step's predictions) is known when the step starts, so their
+// token->expert sorts run as one launch there instead of one launch on each
+// layer's chain. The table holds each layer's fixed sort arguments; no row
+// self-routes there (self_idx null: a negative entry is a bad index).
+static int stack_sort_init(moe_stack* S) {
+    S->sort_ok = false;
+    if (S->n < 2 || !S->d_sort_tab) return MOE_OK;
+    const moe_layer_desc& D0 = S->layers[0]->desc;
+    for (int l = 0; l < S->n; ++l) {
+        const moe_layer* L = S->layers[l];
+        const moe_layer_desc& D = L->desc;
+        if (!L->resident || D.d_model != D0.d_model || D.d_ff != D0.d_ff || fs_main(L) != fs_main(S->layers[0]) ||
+            D.n_experts != D0.n_experts || D.top_k != D0.top_k || D.act_dtype != D0.act_dtype)
+            return MOE_OK;
+    }
+    std::vector<SortArgs> tab((size_t)S->n - 1);
+    for (int l = 1; l < S->n; ++l) {
+        moe_layer* L = S->layers[l];
+        const moe_layer_desc& D = L->desc;
+        SortArgs& sa = tab[(size_t)l - 1];
+        sa = SortArgs{};
+        sa.k = D.top_k; sa.E = D.n_experts;
+        sa.used_idx = L->s.used_idx; sa.used_w = L->s.used_w;
+        sa.meta = L->s.sort_meta; sa.active = L->s.active; sa.act_off = L->s.act_off; sa.perm = L->s.perm;
+        sa.err = L->s.err;
+        sa.ev = view_of(L); sa.fs = fs_main(L);
+        sa.tiles16 = prefill_mm_ok(D.d_model, D.d_ff, fs_main(L)) ? L->s.tiles : nullptr;
+        sa.tiles64 = L->s.tiles64;
+        sa.resolve_blobs = true;
+    }
+    HIPCHK(hipMemcpy(S->d_sort_tab, tab.data(), tab.size() * sizeof(SortArgs), hipMemcpyHostToDevice));
+    S->sort_ok = true;
+    return MOE_OK;
+}
+
+// whether this step's sorts of layers 1..n-1 run as one launch (every such
+// layer takes the general path at n_tok tokens); big: its 64-row tile lists
+static bool stack_sort_hoist(const moe_stack* S, int n_tok, int first_step, bool* big) {
+    if (!S->sort_ok || first_step || S->stage_mode != MOE_STAGE_OFF) return false;
+    const moe_layer* L = S->layers[1];
+    const moe_layer_desc& D = L->desc;
+    if (dec_fast_path_ok(D.d_model, D.d_ff, fs_main(L), n_tok, D.top_k)) return false;
+    for (int l = 1; l < S->n; ++l)
+        if (n_tok > S->layers[l]->desc.max_tokens) return false;
+    const bool mm = prefill_mm_ok(D.d_model, D.d_ff, fs_main(L));
+    *big = mm && prefill_big_tiles(D.d_model, D.d_ff, fs_main(L), D.act_dtype != MOE_ACT_BF16, n_tok, D.top_k,
+                                   std::min(D.n_experts, n_tok * D.top_k));
+    return true;
+}
+
 size_t moe_stack_workspace_bytes(moe_layer* const* layers, int n) {
     if (validate_stack(layers, n) != MOE_OK) return 0;
     return stack_carve(layers, n, nullptr, nullptr);
@@ -1144,6 +1196,8 @@ int moe_stack_create(moe_layer* const* layers, int n, void* d_workspace, size_t 
     S->n = n;
     S->wait_polls = kDefaultWaitPolls;
     stack_carve(layers, n, (uint8_t*)d_workspace, S);
+    rc = stack_sort_init(S);
+    if (rc != MOE_OK) { moe_stack_destroy(S); return rc; }
     S->one_ok = stack_one_launch_ok(layers, n) && S->d_xchg != nullptr && S->xchg_tokens >= 1;
     if (S->one_ok) {
         rc = stack_one_launch_init(S);
@@ -1236,6 +1290,12 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
     }
     const bool on_demand = S->stage_mode == MOE_STAGE_ON_DEMAND;
     const bool prerouted = S->stage_mode == MOE_STAGE_PREROUTED;
+    bool big = false;
+    const bool presort = stack_sort_hoist(S, n_tok, first_step, &big);
+    if (presort) {
+        SortCall c{route_idx, route_w, used_idx, used_w, per, n_tok, big ? 1 : 0};
+        HIPCHK(launch_sort_layers(S->d_sort_tab, S->n - 1, S->layers[1]->desc.n_experts, c, (hipStream_t)stream));
+    }
     TopkJob pend{};
     bool pro_done = false;                   // this layer's prologue was taken by the previous combine
     for (int l = 0; l < S->n; ++l) {
@@ -1264,9 +1324,11 @@ int moe_stack_decode(moe_stack* S, const float* x_in, float* x_out, int n_tok, c
         if (l + 1 < S->n) nxt = prologue_args(S->layers[l + 1], x_out, n_tok);
         bool took = false;
         const bool stage_next = prerouted && l >= 1;
+        L->presorted = presort && l >= 1;
         rc = run_decode(L, &io, n_tok, (hipStream_t)stream, pend.pred_idx ? &pend : nullptr,
                         l + 1 < S->n ? &out : nullptr, l + 1 < S->n ? &nxt : nullptr, pro_done, &took,
                         stage_next ? L->ev_pred : nullptr);
+        L->presorted = false;
         if (rc != MOE_OK) return rc;
         pend = out;
         pro_done = took;

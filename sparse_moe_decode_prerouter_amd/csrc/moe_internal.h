@@ -130,10 +130,12 @@ struct moe_layer {
     bool profiling;
     hipEvent_t ev_t[6];        // router start/end, A start/end, B start/end
     bool ev_t_used[3];
+    bool presorted;            // set by the stack around a call whose sort already ran
 };
 
 namespace moe {
 struct StackLayerArgs;
+struct SortArgs;
 }
 struct moe_stack {
     moe_layer** layers;
@@ -161,6 +163,10 @@ struct moe_stack {
     bool one_launch;         // enabled
     int one_grid;            // blocks resident on the chip at once
     uint32_t wait_polls;     // bound of each device-side wait (polls)
+    // batched decode beyond the fused path: layers 1..n-1 sort their given
+    // routing in one launch at the start of the step
+    moe::SortArgs* d_sort_tab;    // [n - 1] fixed sort arguments of layers 1..n-1 (caller's workspace)
+    bool sort_ok;            // every layer resident with the same shape
     // kernel timestamps (moe_stack_set_profiling): layer 0's router, the step kernel
     bool profiling;
     bool ev_used[2];
@@ -286,6 +292,14 @@ struct SortArgs {
     bool resolve_blobs;                 // false: blob fields left -1, resolved after staging (launch_tile_blobs)
 };
 hipError_t launch_sort(const SortArgs& a, hipStream_t s);
+// one call's part of several layers' sorts (k_sort_layers): routing
+// [layer][n_tok][k] from route_idx / route_w (per = n_tok * k entries per
+// layer), optional used-routing outputs of the same shape
+struct SortCall {
+    const int32_t* route_idx; const float* route_w; int32_t* used_idx; float* used_w;
+    size_t per; int n_tok; int big;
+};
+hipError_t launch_sort_layers(const SortArgs* tab, int n_layers, int E, const SortCall& c, hipStream_t s);
 
 struct GemvArgs {
     ExpertView ev; int d; int f; int fs; int k; int n_tok;

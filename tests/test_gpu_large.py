@@ -138,6 +138,33 @@ def test_batched_sticky_stack():
         f"mean next-token reuse of the predictions {np.mean(reuse):.3f}")
 
 
+def test_batched_stack_presorted_bad_route_flagged():
+    """At B = 32 (the general path) the given routing of layers >= 1 is sorted
+    in one launch at the start of the step; a negative entry there is not
+    self-routed but flagged on that layer (MOE_E_BAD_INDEX), the other layers
+    stay clean. The routing comes from a host-side edit, so every kernel runs
+    to its end."""
+    import sparse_moe_decode_prerouter_amd as moe
+    shape = synth.LAYER35B
+    L_, B = 2, 32
+    ws = [synth.layer_weights(shape, l, tag="badroute") for l in range(L_)]
+    gpus = [gpu_layer(shape, w, fused=True, max_tokens=B, head=(l + 1 < L_)) for l, w in enumerate(ws)]
+    stack = moe.MoeStack(gpus)
+    say(f"presorted batched stack L={L_} B={B}: a negative routing entry of layer 1")
+    x = synth.activations(shape, B, ("badroute",), dtype=torch.float32).cuda()
+    xo = torch.empty_like(x)
+    pidx = [torch.full((L_, B, shape.k), -1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    pw = [torch.zeros((L_, B, shape.k), dtype=torch.float32, device="cuda") for _ in range(2)]
+    stack.decode(x, pidx[0], pw[0], pidx[1], pw[1], x_out=xo, first_step=True)
+    torch.cuda.synchronize()
+    assert [Lr.status() for Lr in gpus] == [0, 0]
+    assert bool((pidx[1][1] >= 0).all())
+    pidx[1][1, 5, 0] = -1
+    stack.decode(x, pidx[1], pw[1], pidx[0], pw[0], x_out=xo, first_step=False)
+    torch.cuda.synchronize()
+    assert [Lr.status() for Lr in gpus] == [0, moe.MOE_E_BAD_INDEX]
+
+
 class _BlobsOnDemand:
     """Host view of a device (or pinned) expert store for the oracle: blob e
     is copied on first use (a decode step touches only the experts it routes
