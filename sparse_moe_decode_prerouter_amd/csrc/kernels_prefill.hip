@@ -201,18 +201,18 @@ __device__ __forceinline__ u32x2 gu_b_read(const GuLds<LO>& S, int r, int q, int
 // NB LDS stage buffers: one keeps blocks small (three per CU) for calls with
 // many tiles; two save a barrier per stage when there are few
 template <bool LO, int NB>
-__global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
+__device__ __forceinline__ void gateup_body(const PrefillArgs& a, int bx, int by) {
     const GemvArgs& g = a.g;
     __shared__ __align__(16) GuLds<LO> S[NB];
     __shared__ float us64[kTileM][kMaxGroupsPf + 1];
     __shared__ int tok[kTileM];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if ((int)blockIdx.x >= g.meta[2]) return;
-    const PfItem it = pf_item(a, blockIdx.x);
+    if (bx >= g.meta[2]) return;
+    const PfItem it = pf_item(a, bx);
     const bool shared = it.slot < 0;
     const int f = shared ? g.fs : g.f;
-    const int rb0 = blockIdx.y * kGuRows;
+    const int rb0 = by * kGuRows;
     if (rb0 >= f || it.M <= 0) return;
     const uint8_t* blob = pf_blob(g, it.blob);
     const int d = g.d, G = d / 64, NS = d / kStageK;
@@ -301,6 +301,11 @@ __global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
             else g.h[(size_t)(it.p0 + m) * f + n] = hv;
         }
     }
+}
+
+template <bool LO, int NB>
+__global__ void __launch_bounds__(256) k_pf_gateup(PrefillArgs a) {
+    gateup_body<LO, NB>(a, blockIdx.x, blockIdx.y);
 }
 
 template <int V>
@@ -1300,21 +1305,21 @@ __device__ __host__ __forceinline__ FrSets fr_sets(const RouteMMArgs& a) {
     return FrSets{a.router ? a.E : 0, a.head ? a.En : 0, a.lora_a ? a.r : 0, a.sgate_w ? 1 : 0};
 }
 
-__global__ void __launch_bounds__(64 * kFrWaves) k_route_mm_fr(RouteMMArgs a) {
+__device__ __forceinline__ void route_mm_fr_body(const RouteMMArgs& a, int bx, int by) {
     __shared__ double red[kFrWaves - 1][4][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pc = lane >> 4, ml = lane & 15;
     const int d = a.d, T = a.n_tok, S = d / 32;
     const FrSets fs = fr_sets(a);
-    int rt = blockIdx.x, set = 0;
+    int rt = bx, set = 0;
     while (set < 3 && rt >= fs.tiles(set)) { rt -= fs.tiles(set); ++set; }
-    const int t0 = blockIdx.y * 16;
+    const int t0 = by * 16;
     // router rows are needed only for self-routed tokens
     if (set == 0 && !route_tile_needed(a, t0, 16)) return;
     const uint32_t* wf = set == 0 ? a.wf_router : set == 1 ? a.wf_head : set == 2 ? a.wf_lora : a.wf_sgate;
     const u32x4* wq = (const u32x4*)wf + (size_t)rt * S * 64 + lane;
-    const u32x4* aq = (const u32x4*)a.u_frag + (size_t)blockIdx.y * S * 64 + lane;
+    const u32x4* aq = (const u32x4*)a.u_frag + (size_t)by * S * 64 + lane;
     // wave w takes k-steps [w * ns, (w + 1) * ns), loads issued 16 steps at a time
     const int ns = S / kFrWaves, c0 = wave * ns;
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
@@ -1341,7 +1346,7 @@ __global__ void __launch_bounds__(64 * kFrWaves) k_route_mm_fr(RouteMMArgs a) {
         for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
     __syncthreads();
     // router rows of the first token tile when it holds rows before the shift
-    const bool pre = set == 0 && blockIdx.y == 0 && a.pre_rows > 0;
+    const bool pre = set == 0 && by == 0 && a.pre_rows > 0;
     const int r = 16 * rt + ml;                          // row within its set
     if (wave == 0 && r < fs.rows(set)) {
 #pragma unroll 1
@@ -1385,6 +1390,28 @@ __global__ void __launch_bounds__(64 * kFrWaves) k_route_mm_fr(RouteMMArgs a) {
         else if (a.E <= 128) topk_row<2>(true, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
         else topk_row<4>(true, a.logits_r, a.E, a.k, t, a.router_bias, nullptr, nullptr, nullptr, nullptr, a.self_idx, a.self_w);
     }
+}
+
+__global__ void __launch_bounds__(64 * kFrWaves) k_route_mm_fr(RouteMMArgs a) {
+    route_mm_fr_body(a, blockIdx.x, blockIdx.y);
+}
+
+// Gate/up and the routing-side GEMM of the same layer in one launch, for
+// calls whose routing is given and already sorted (batched stack decode):
+// nothing the routing GEMM writes (head logits, LoRA A u, shared gate) is
+// read before the combine, so its blocks run beside the gate/up blocks
+// instead of in a launch of their own ahead of them. Blocks [0, gx gy) are
+// gate/up tiles (x fastest, as in k_pf_gateup's grid), the rest routing tiles.
+static_assert(64 * kFrWaves == 256, "one block size for both bodies");
+template <int NB>
+__global__ void __launch_bounds__(256) k_pf_gateup_route(PrefillArgs a, RouteMMArgs r, int gx, int gy) {
+    const int b = blockIdx.x, ng = gx * gy;
+    if (b < ng) {
+        gateup_body<false, NB>(a, b % gx, b / gx);
+        return;
+    }
+    const int rx = fr_sets(r).total();
+    route_mm_fr_body(r, (b - ng) % rx, (b - ng) / rx);
 }
 
 // The same products for many tokens: block = 64 tokens x 64 rows staged
@@ -1525,6 +1552,14 @@ __global__ void __launch_bounds__(256) k_route_topk(RouteMMArgs a, int job0) {
     }
 }
 
+// whether launch_route_mm would take k_route_mm_fr for these arguments
+bool route_fr_ok(const RouteMMArgs& a) {
+    const int R = (a.router ? a.E : 0) + (a.head ? a.En : 0) + (a.lora_a ? a.r : 0) + (a.sgate_w ? 1 : 0);
+    const long long big_blocks = (long long)((R + kRmTile - 1) / kRmTile) * ((a.n_tok + kRmTile - 1) / kRmTile);
+    return R > 0 && a.d % 128 == 0 && big_blocks < 512 && a.u_frag && !a.u_pk_lo && a.d % (32 * kFrWaves) == 0 &&
+           (!a.router || a.wf_router) && (!a.head || a.wf_head) && (!a.lora_a || a.wf_lora) && (!a.sgate_w || a.wf_sgate);
+}
+
 hipError_t launch_route_mm(const RouteMMArgs& a_in, hipStream_t s, bool router_topk, bool head_topk, int* pre_done) {
     RouteMMArgs a = a_in;
     if (pre_done) *pre_done = 0;
@@ -1571,13 +1606,28 @@ bool prefill_mm_ok(int d, int f, int fs) {
     return d % kStageK == 0 && d % 128 == 0 && d / 64 <= kMaxGroupsPf && fok(f) && (fs == 0 || fok(fs));
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, const RouteMMArgs* route) {
     const GemvArgs& g = a.g;
     if (!prefill_mm_ok(g.d, g.f, g.fs)) return hipErrorInvalidValue;
     hipError_t e;
     const int fmax = g.f > g.fs ? g.f : g.fs;
+    const bool big = prefill_big_tiles(g.d, g.f, g.fs, g.u_pk_lo != nullptr, g.n_tok, g.k, g.max_active);
+    // routing GEMM handed over (its results are read from the combine on):
+    // in the gate/up launch when both take their 16-token forms, else ahead
+    if (route && (big || g.u_pk_lo || route->pre_rows > 0 || !route_fr_ok(*route))) {
+        if ((e = launch_route_mm(*route, s, false, false, nullptr)) != hipSuccess) return e;
+        route = nullptr;
+    }
     // the tile lists were written by the sort (64-row ones when big)
-    if (prefill_big_tiles(g.d, g.f, g.fs, g.u_pk_lo != nullptr, g.n_tok, g.k, g.max_active)) {
+    if (route) {
+        const int gx = a.max_tiles, gy = (fmax + kGuRows - 1) / kGuRows;
+        const int nr = fr_sets(*route).total() * ((route->n_tok + 15) / 16);
+        const dim3 grid((unsigned)(gx * gy + nr));
+        if ((long long)g.n_tok * g.k >= 4LL * g.max_active)
+            hipLaunchKernelGGL(k_pf_gateup_route<1>, grid, dim3(256), 0, s, a, *route, gx, gy);
+        else
+            hipLaunchKernelGGL(k_pf_gateup_route<2>, grid, dim3(256), 0, s, a, *route, gx, gy);
+    } else if (big) {
         hipLaunchKernelGGL((k_pf_gateup_big<kBgGs, kBgNst, kTileBig, kBgRt, kBgWaves>), dim3(a.max_tiles64, (fmax + kBgRows - 1) / kBgRows),
                            dim3(64 * kBgWaves), 0, s, a);
     } else {

@@ -504,7 +504,11 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     ra.counter = L->s.counters + 3;
     int pre_done = 0;
     const bool mlp = io->pred_idx && L->w.head && D.head_hidden > 0;
-    HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm && !mlp, &pre_done));
+    // sorted ahead (batched stack decode): no row self-routes, and what the
+    // routing GEMM writes is first read by the combine, so it goes with the
+    // grouped GEMM's launch
+    const bool route_later = L->presorted && mm && !mlp && !has_shared_lora(L);
+    if (!route_later) HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm && !mlp, &pre_done));
     if (mlp) {
         int rc = run_head_mlp(L, io, n_tok, st, false);
         if (rc != MOE_OK) return rc;
@@ -586,7 +590,7 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
             else if (took_nxt) *took_nxt = true;
         }
         if (reactive) HIPCHK(launch_tile_blobs(pf, big, st));
-        HIPCHK(launch_prefill(pf, st));
+        HIPCHK(launch_prefill(pf, st, route_later ? &ra : nullptr));
     } else {
         HIPCHK(launch_gateup(ga, st));
         HIPCHK(launch_down(ga, st));

@@ -336,7 +336,11 @@ int prefill_max_tiles(int T, int K, int E, int tm = 16);
 bool prefill_mm_ok(int d, int f, int fs);
 // whether the gate/up projection takes 64-token tiles (many tokens per expert)
 bool prefill_big_tiles(int d, int f, int fs, bool act_lo, int n_tok, int k, int max_active);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+// route (optional): the layer's routing-side GEMM, whose outputs nothing
+// before the combine reads; it runs in the gate/up launch when it can, else
+// just before it. Its top-k steps are the caller's (none may be pending).
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, const RouteMMArgs* route = nullptr);
+bool route_fr_ok(const RouteMMArgs& a);
 // resolve the blob field of the tile records once the experts are staged
 hipError_t launch_tile_blobs(const PrefillArgs& a, bool big, hipStream_t s);
 
