@@ -218,7 +218,7 @@ def measure_h2d(torch, moe, synth, shape, ws, pstore, pshared):
     return res
 
 
-def streamed_sweep(torch, np, moe, synth, shape, ws, pstore, pshared, copy_GBs):
+def streamed_sweep(torch, np, moe, synth, shape, ws, pstore, pshared, copy_GBs, cs):
     """Batch-1 decode through 40 streamed layers at top-k K = 2, 4, 8, with
     the experts staged on the device into two slab buffers of K + 1 slots:
     one token ahead (layer l's experts for step t+1 copied on a side stream
@@ -231,7 +231,6 @@ def streamed_sweep(torch, np, moe, synth, shape, ws, pstore, pshared, copy_GBs):
     for K in (2, 4, 8):
         sl = [streamed_layer(moe, shape, w, l, L, K, pstore, pshared, K) for l, w in enumerate(ws)]
         ss = moe.MoeStack(sl)
-        cs = torch.cuda.Stream()
         row = {}
         for mode, name in ((moe.MOE_STAGE_PREROUTED, "prerouted"), (moe.MOE_STAGE_ON_DEMAND, "on_demand")):
             ss.set_staging(mode, cs)
@@ -537,7 +536,7 @@ def extra_measurements(args, torch, np, moe, synth, shape, ws, layers):
 
     # ---- streamed decode, B = 1, K = 2 / 4 / 8: one token ahead vs on demand (device staging)
     out["streamed_decode_b1"] = streamed_sweep(torch, np, moe, synth, shape, ws, pstore, pshared,
-                                               out["h2d_peak"]["copy_kernel_GBs"])
+                                               out["h2d_peak"]["copy_kernel_GBs"], args.copy_stream)
 
     # ---- cold prefill: the experts staged from pinned host memory inside the call
     out["cold_prefill"] = cold_prefill(torch, moe, synth, shape, ws, pstore, pshared, args.prefill_tokens)
@@ -621,6 +620,11 @@ def main():
     import sparse_moe_decode_prerouter_amd as moe
 
     assert torch.cuda.is_available()
+    # the staging side stream, made before any other: HIP spreads streams over
+    # a few hardware queues in creation order, and a copy stream that shares
+    # the compute stream's queue cannot overlap it (made later, the K = 2
+    # streamed sweep came out with no overlap at all)
+    args.copy_stream = torch.cuda.Stream()
     dev = "cuda"
     L, B, K, W = args.layers, args.batch, args.steps, args.warmup
     shape = synth.scaled_stack(L) if L != 40 else synth.STACK35B

@@ -504,11 +504,18 @@ int run_prefill(moe_layer* L, const moe_io* io, int n_tok, hipStream_t st, bool 
     ra.counter = L->s.counters + 3;
     int pre_done = 0;
     const bool mlp = io->pred_idx && L->w.head && D.head_hidden > 0;
-    // sorted ahead (batched stack decode): no row self-routes, and what the
-    // routing GEMM writes is first read by the combine, so it goes with the
-    // grouped GEMM's launch
-    const bool route_later = L->presorted && mm && !mlp && !has_shared_lora(L);
-    if (!route_later) HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm && !mlp, &pre_done));
+    // Sorted ahead (batched stack decode): no row self-routes, so the sort
+    // needs no router rows, and what the routing GEMM writes (head logits,
+    // LoRA A u, shared gate) is first read by the combine: it goes with the
+    // gate/up launch. (Splitting off only the router rows before the sort
+    // of a 512-token stacked prefill measured slower: 6.82 against 6.75 ms.)
+    const bool route_later = L->presorted && mm && !big && !mlp && !has_shared_lora(L) && route_fr_ok(ra);
+    if (route_later) {
+        ra.router = nullptr;
+        ra.pre_rows = 0;
+    } else {
+        HIPCHK(launch_route_mm(ra, st, !sort_topk, !mm && !mlp, &pre_done));
+    }
     if (mlp) {
         int rc = run_head_mlp(L, io, n_tok, st, false);
         if (rc != MOE_OK) return rc;
