@@ -281,6 +281,30 @@ def streamed_sweep(torch, np, moe, synth, shape, ws, pstore, pshared, copy_GBs, 
     return res
 
 
+def pick_side_stream(torch, n=4):
+    """A side stream that runs beside the default stream. Streams share a few
+    hardware queues (GPU_MAX_HW_QUEUES), and work on a stream that shares the
+    default stream's queue waits behind it: the streamed sweep's copies then
+    overlap nothing. Of the first n pool streams, the one whose spin kernel
+    overlaps best with one on the default stream is taken."""
+    cands = [torch.cuda.Stream() for _ in range(n)]
+    best = None
+    try:
+        for c in cands:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            torch.cuda._sleep(20_000_000)
+            with torch.cuda.stream(c):
+                torch.cuda._sleep(20_000_000)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            if best is None or dt < best[0]:
+                best = (dt, c)
+    except Exception:
+        return cands[-1]
+    return best[1]
+
+
 def eager_steps(torch, stack, L, K, d, synth, shape, steps, warm, key, on_warm=None):
     """ms per decode step over `steps` eager steps after `warm` (the first of
     which self-routes); on_warm() is evaluated after the warm-up (its value is
@@ -620,11 +644,7 @@ def main():
     import sparse_moe_decode_prerouter_amd as moe
 
     assert torch.cuda.is_available()
-    # the staging side stream, made before any other: HIP spreads streams over
-    # a few hardware queues in creation order, and a copy stream that shares
-    # the compute stream's queue cannot overlap it (made later, the K = 2
-    # streamed sweep came out with no overlap at all)
-    args.copy_stream = torch.cuda.Stream()
+    args.copy_stream = pick_side_stream(torch)
     dev = "cuda"
     L, B, K, W = args.layers, args.batch, args.steps, args.warmup
     shape = synth.scaled_stack(L) if L != 40 else synth.STACK35B
