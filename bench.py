@@ -286,7 +286,9 @@ def pick_side_stream(torch, n=4):
     hardware queues (GPU_MAX_HW_QUEUES), and work on a stream that shares the
     default stream's queue waits behind it: the streamed sweep's copies then
     overlap nothing. Of the first n pool streams, the one whose spin kernel
-    overlaps best with one on the default stream is taken."""
+    overlaps best with one on the default stream is taken. (Made just before
+    the sweep: taking pool streams at the start of the run moved the decode
+    graph onto other queues and cost its one-launch form ~100 us per step.)"""
     cands = [torch.cuda.Stream() for _ in range(n)]
     best = None
     try:
@@ -560,7 +562,7 @@ def extra_measurements(args, torch, np, moe, synth, shape, ws, layers):
 
     # ---- streamed decode, B = 1, K = 2 / 4 / 8: one token ahead vs on demand (device staging)
     out["streamed_decode_b1"] = streamed_sweep(torch, np, moe, synth, shape, ws, pstore, pshared,
-                                               out["h2d_peak"]["copy_kernel_GBs"], args.copy_stream)
+                                               out["h2d_peak"]["copy_kernel_GBs"], pick_side_stream(torch))
 
     # ---- cold prefill: the experts staged from pinned host memory inside the call
     out["cold_prefill"] = cold_prefill(torch, moe, synth, shape, ws, pstore, pshared, args.prefill_tokens)
@@ -644,7 +646,6 @@ def main():
     import sparse_moe_decode_prerouter_amd as moe
 
     assert torch.cuda.is_available()
-    args.copy_stream = pick_side_stream(torch)
     dev = "cuda"
     L, B, K, W = args.layers, args.batch, args.steps, args.warmup
     shape = synth.scaled_stack(L) if L != 40 else synth.STACK35B
