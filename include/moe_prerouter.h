@@ -418,7 +418,8 @@ int moe_last_hip_error(void);
 
 /* ---- pure host helper (no device use) ------------------------------------
  * The sticky-slot plan moe_stage_experts applies. resident[n_slots]: expert
- * per slot (-1 empty), updated in place. wanted[n_wanted] (duplicates ok).
+ * per slot (-1 empty), updated in place; an expert may sit in one slot only
+ * (in two: MOE_E_INVALID). wanted[n_wanted] (duplicates ok).
  * copies_slot/copies_expert receive up to n_slots entries; *n_copies is set.
  * Returns MOE_OK, MOE_E_INVALID or MOE_E_CAPACITY (resident unchanged).     */
 int moe_plan_slots(int32_t* resident, int n_slots, const int32_t* wanted, int n_wanted,

@@ -530,9 +530,13 @@ def plan_slots(resident: Sequence[int], wanted: Sequence[int]):
     Experts already resident keep their slot; missing experts (ascending id)
     take the slots not holding a wanted expert (ascending slot index).
     Returns (new_resident, copies [(slot, expert)]); raises ValueError when
-    the distinct wanted experts exceed the slots."""
+    the distinct wanted experts exceed the slots or an expert sits in two
+    slots."""
     want = sorted(set(int(e) for e in wanted))
     res = list(int(e) for e in resident)
+    held = [e for e in res if e >= 0]
+    if len(held) != len(set(held)):
+        raise ValueError("an expert in two slots")   # a slot table holds each expert once
     if len(want) > len(res):
         raise ValueError("capacity")
     have = set(res)

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_prerouter.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["moe_api.hip", "kernels_decode.hip", "kernels_dec2.hip", "kernels_deca.hip", "kernels_prefill.hip",
-           "kernels_shared.hip", "kernels_stage.hip", "kernels_stack.hip"]
+           "kernels_shared.hip", "kernels_stage.hip", "kernels_stack.hip", "host_plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -38,7 +38,7 @@ def compile_cmds(csrc: str = CSRC, objdir: str = OBJDIR, include: str | None = N
     include = include or os.path.join(HERE, "..", "include")
     out = []
     for s in SOURCES:
-        obj = os.path.join(objdir, s.replace(".hip", ".o"))
+        obj = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
         out.append((obj, [HIPCC, *FLAGS, *EXTRA.get(s, []), "-I", include, "-c", os.path.join(csrc, s), "-o", obj]))
     return out
 

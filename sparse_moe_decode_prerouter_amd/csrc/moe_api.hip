@@ -1426,34 +1426,6 @@ const char* moe_status_str(int status) {
 
 int moe_last_hip_error(void) { return g_last_hip; }
 
-int moe_plan_slots(int32_t* resident, int n_slots, const int32_t* wanted, int n_wanted, int n_experts,
-                   int32_t* copies_slot, int32_t* copies_expert, int* n_copies) {
-    if (!resident || n_slots < 0 || n_wanted < 0 || (n_wanted && !wanted) || !n_copies) return MOE_E_INVALID;
-    std::vector<int32_t> want(wanted, wanted + n_wanted);
-    for (int32_t e : want)
-        if (e < 0 || e >= n_experts) return MOE_E_INVALID;
-    std::sort(want.begin(), want.end());
-    want.erase(std::unique(want.begin(), want.end()), want.end());
-    if ((int)want.size() > n_slots) return MOE_E_CAPACITY;
-    std::vector<char> wanted_flag(n_experts, 0), present(n_experts, 0);
-    for (int32_t e : want) wanted_flag[e] = 1;
-    for (int s = 0; s < n_slots; ++s)
-        if (resident[s] >= 0 && resident[s] < n_experts) present[resident[s]] = 1;
-    std::vector<int> free_slots;
-    for (int s = 0; s < n_slots; ++s)
-        if (!(resident[s] >= 0 && resident[s] < n_experts && wanted_flag[resident[s]])) free_slots.push_back(s);
-    int nc = 0;
-    size_t fi = 0;
-    for (int32_t e : want) {
-        if (present[e]) continue;
-        const int s = free_slots[fi++];
-        resident[s] = e;
-        if (copies_slot) copies_slot[nc] = s;
-        if (copies_expert) copies_expert[nc] = e;
-        ++nc;
-    }
-    *n_copies = nc;
-    return MOE_OK;
-}
+// moe_plan_slots: host_plan.cpp (plain C++, also built with the host sanitizers in the CPU tests)
 
 }  // extern "C"

@@ -88,6 +88,12 @@ def test_plan_slots_errors():
     with pytest.raises(moe.MoeError) as e:
         moe.moe_plan_slots([-1, -1], [9], 8)
     assert e.value.code == moe.MOE_E_INVALID
+    # an expert in two slots: not a slot table (both planners refuse it)
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_plan_slots([5, 5, -1], [5, 7], 8)
+    assert e.value.code == moe.MOE_E_INVALID
+    with pytest.raises(ValueError):
+        oracle.plan_slots([5, 5, -1], [5, 7])
 
 
 def test_status_strings():
