@@ -450,7 +450,17 @@ __global__ void __launch_bounds__(kSortThreads) k_sort_layers(const SortArgs* __
 
 hipError_t launch_sort_layers(const SortArgs* tab, int n_layers, int E, const SortCall& c, hipStream_t s) {
     const size_t lds = sort_lds_bytes((int)c.per, E);
-    if (E > kSortThreads || lds > 64 * 1024) return hipErrorInvalidValue;
+    if (E > kSortThreads || lds > kSortLdsMax) return hipErrorInvalidValue;
+    if (lds > 64 * 1024) {
+        // above the default dynamic LDS limit: raise it to what this call needs
+        static size_t raised = 0;
+        if (lds > raised) {
+            const hipError_t e =
+                hipFuncSetAttribute((const void*)k_sort_layers, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            raised = lds;
+        }
+    }
     hipLaunchKernelGGL(k_sort_layers, dim3(n_layers), dim3(kSortThreads), lds, s, tab, c);
     return hipGetLastError();
 }
